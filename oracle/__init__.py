@@ -1,0 +1,20 @@
+"""CPU float64 oracle for absorbed paged MLA decode -- test infrastructure only.
+
+Only the tests, the smoke entry and the bench's CPU-baseline leg use it; the
+product library never does.
+"""
+from .mla_oracle import (  # noqa: F401
+    absorbed_scores,
+    default_scale,
+    latent_row_bytes,
+    latent_row_elements,
+    mha_row_bytes,
+    mla_decode,
+    mqa_row_elements,
+    naive_scores,
+    page_bytes,
+    rope_angles,
+    rope_rotate,
+    softmax_rows,
+    staged_tile_bytes,
+)

@@ -1,0 +1,71 @@
+"""The seeded input generator: determinism, bf16 rounding, paging layout, ragged recipe."""
+import numpy as np
+import torch
+
+from mla_latent_kv_09_amd import workloads as wl
+
+
+def test_bf16_rounding_matches_torch_rne():
+    rng = np.random.default_rng(0)
+    x = np.concatenate([rng.standard_normal(100000).astype(np.float32) * 10,
+                        np.array([1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -2.5, 0.0, 65504.0], np.float32)])
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(wl.bf16_bits(x), ref)
+    assert np.array_equal(wl.bf16_bits_to_f32(wl.bf16_bits(x)),
+                          torch.from_numpy(x).to(torch.bfloat16).float().numpy())
+    assert wl.bf16_bits(np.array([np.nan], np.float32))[0] == wl.BF16_NAN_BITS
+
+
+def test_deterministic_per_seed():
+    cfg = wl.CONFIGS["dsv3_b16_l4096"].replace(batch=2, seq_len=200)
+    a, b = wl.make_workload(cfg), wl.make_workload(cfg)
+    c = wl.make_workload(cfg, seed=1)
+    assert np.array_equal(a.q_c, b.q_c) and np.array_equal(a.pool, b.pool)
+    assert not np.array_equal(a.q_c, c.q_c)
+
+
+def test_values_are_exact_bf16():
+    w = wl.make_workload(wl.CONFIGS["dsv3_b16_l4096"].replace(batch=1, seq_len=70))
+    for x in (w.q_c, w.q_r, w.w_uk, w.w_uv, w.latents[0]):
+        assert np.array_equal(wl.round_bf16(x), x)
+
+
+def test_paged_pool_round_trip_and_nan_fill():
+    cfg = wl.CONFIGS["dsv3_b16_l4096"].replace(batch=3, seq_len=None, seq_len_range=(1, 200))
+    w = wl.make_workload(cfg)
+    n_pages = [(int(L) + 63) // 64 for L in w.seq_lens]
+    assert w.num_pool_pages == sum(n_pages)
+    used = np.concatenate([w.page_table[b, :n] for b, n in enumerate(n_pages)])
+    assert sorted(used.tolist()) == list(range(w.num_pool_pages))          # a permutation
+    for b, n in enumerate(n_pages):
+        assert (w.page_table[b, n:] == -1).all()
+        assert np.array_equal(wl.gather_sequence(w, b), w.latents[b])
+        L = int(w.seq_lens[b])
+        if L % 64:
+            tail = w.pool[w.page_table[b, n - 1], L % 64:]
+            assert (tail == wl.BF16_NAN_BITS).all()
+
+
+def test_identity_pages_for_contiguous_fp32():
+    w = wl.make_workload(wl.CONFIGS["tiny_fp32"])
+    assert w.pool.dtype == np.float32 and w.pool.shape == (4, 64, 80)
+    assert np.array_equal(w.page_table[0], np.arange(4))
+    assert np.array_equal(w.pool.reshape(256, 80), w.latents[0])
+    assert abs(w.w_uk.std() - 1 / 8) < 0.01
+
+
+def test_ragged_recipe():
+    cfg = wl.CONFIGS["ragged_b64"]
+    rng_lens = wl._rng(cfg.seed, "lengths").integers(1024, 32769, size=64)
+    w = wl.make_workload(cfg.replace(seq_len_range=(3, 40)))   # small lengths, same q_len split
+    assert int(w.q_lens.sum()) == 96 and (np.sort(w.q_lens) == [1] * 32 + [2] * 32).all()
+    assert np.array_equal(w.cu_q[1:], np.cumsum(w.q_lens))
+    assert rng_lens.min() >= 1024 and rng_lens.max() <= 32768
+    assert (w.seq_lens >= 3).all() and (w.seq_lens <= 40).all()
+
+
+def test_config_table_shapes():
+    c = wl.CONFIGS
+    assert [c[k].row for k in wl.CONFIG_ORDER] == [80, 576, 576, 576, 576]
+    assert c["gla2_b32_l16384"].d_cg == 256 and c["gla2_b32_l16384"].heads // 2 == 64
+    assert c["long_b16_l65536"].batch * c["long_b16_l65536"].seq_len * 576 * 2 == 1_207_959_552
