@@ -1,0 +1,175 @@
+/*
+ * mla_kv.h -- C ABI of the MI355X (gfx950) absorbed-MLA decode library.
+ *
+ * One decode step of Multi-head Latent Attention over a paged latent cache,
+ * split into four stream-ordered calls:
+ *
+ *   mla_absorb_q      q_abs[t,h,:] = q_c[t,h,:] . W_UK[h]            (absorption)
+ *   mla_decode_paged  split-KV attention of q_abs / RoPE(q_R) against the
+ *                     paged latent rows [c_KV | k_R]; per-split partial
+ *                     outputs and log-sum-exp
+ *   mla_combine       log-sum-exp merge of the splits -> o_latent
+ *   mla_up_v          out[t,h,:] = W_UV[h] . o_latent[t,h,:]            (value up-projection)
+ *
+ * plus mla_rope_table (the fp32 cos/sin table the decode call reads) and
+ * mla_status_string.
+ *
+ * Sources, cited by page address and section:
+ *   P3 = www.nxmr.cn/news/151634  (MLA operators: absorption, paged latent cache)
+ *   P2 = m.xxqk.cn/news/443191    (attention from MHA to MoBA)
+ *   P1 = www.hotelren.com/news/5324130 (from MLA to GLA)
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - All tensors are dense, row-major, in device memory allocated and owned by
+ *   the caller.  The library never allocates, frees or keeps a pointer after a
+ *   call returns, and never synchronizes.  Work is enqueued on `stream`
+ *   (a hipStream_t; NULL = the default stream) and runs asynchronously.
+ *   Calls keep no global state and may be issued from several host threads.
+ * - Every pointer must be 16-byte aligned (the pages' "misaligned address"
+ *   failure of a vectorized gather, P3 §5).
+ * - dtype selects the storage type of the non-float32 tensors: MLA_DTYPE_BF16
+ *   (bfloat16 storage and MFMA operands, fp32 accumulation) or MLA_DTYPE_FP32.
+ *   Softmax state, split partials and the log-sum-exp are always float32.
+ * - Indices: T = total query tokens of the batch (queries of all sequences
+ *   packed back to back), H = heads, G = latent groups (1 = MLA; >1 = grouped
+ *   latent attention, P1 §1), d_cg = d_c / G.  Head h belongs to group
+ *   h / (H/G) and sees latent columns [g*d_cg, (g+1)*d_cg) plus the shared k_R.
+ * - Return value: MLA_OK (0) or a negative MLA_ERR_* code.  Every code except
+ *   MLA_ERR_LAUNCH is detected on the host before anything is enqueued.  A call
+ *   with total_q == 0 validates nothing but its scalars and enqueues nothing.
+ *
+ * Memory-resident contents (page ids, sequence lengths, query offsets) are
+ * trusted: the kernels clamp every index they derive from them so no access
+ * leaves the buffers described here, but the result for out-of-range contents
+ * is unspecified.
+ */
+#ifndef MLA_KV_H
+#define MLA_KV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum mla_status {
+  MLA_OK = 0,
+  MLA_ERR_NULL = -1,        /* a required pointer is NULL */
+  MLA_ERR_DIM = -2,         /* a size <= 0 (or < 0 where 0 is allowed), H % G, d_c % G, odd d_R */
+  MLA_ERR_UNSUPPORTED = -3, /* valid but not implemented: page_size != 64, dims beyond limits */
+  MLA_ERR_ALIGN = -4,       /* a pointer not 16-byte aligned */
+  MLA_ERR_LAUNCH = -5,      /* the HIP runtime rejected a kernel launch */
+  MLA_ERR_DTYPE = -6        /* dtype is not one of MLA_DTYPE_* */
+};
+
+enum mla_dtype {
+  MLA_DTYPE_BF16 = 0,
+  MLA_DTYPE_FP32 = 1
+};
+
+/* Only page size the library implements: 64 tokens per page (P3 §3: a 64-token
+ * page of 576-element bf16 rows is about 72 KB; 16-token pages fragment the
+ * page table and the transfers). */
+#define MLA_PAGE_SIZE 64
+
+/*
+ * mla_absorb_q -- fold W_UK into the content query (P3 §1 intro and §4 path B:
+ * q_abs = q_c W_UK, so scores are taken against the latent directly and K is
+ * never re-expanded).
+ *
+ *   q_c    [T, H, d_hc]      dtype
+ *   w_uk   [H, d_hc, d_cg]   dtype   ("hdc" order of P3 §4)
+ *   q_abs  [T, H, d_cg]      dtype   output; q_abs[t,h,c] = sum_d q_c[t,h,d] w_uk[h,d,c],
+ *                                    accumulated in fp32, rounded once to dtype
+ */
+int mla_absorb_q(const void* q_c, const void* w_uk, void* q_abs,
+                 int total_q, int heads, int groups, int d_hc, int d_c,
+                 int dtype, void* stream);
+
+/*
+ * mla_rope_table -- fp32 RoPE table for positions [0, max_pos) (P3 §3
+ * rope_compute_dtype fp32; P3 §4: generate the table in FP32 and apply it with
+ * FP32 multiply-adds, since an fp16 table shifts the phase).
+ *
+ *   cos_out, sin_out  [max_pos, d_R/2] float32 outputs:
+ *     angle(p, k) = p * base^(-2k/d_R), evaluated in float64, then
+ *     cos_out[p,k] = (float)cos(angle), sin_out[p,k] = (float)sin(angle).
+ * The decode call rotates the interleaved pairs (q_R[2k], q_R[2k+1]) with it.
+ */
+int mla_rope_table(float* cos_out, float* sin_out, int max_pos, int d_R, double base,
+                   void* stream);
+
+/*
+ * mla_decode_paged -- split-KV attention of the absorbed queries over the
+ * paged latent cache (P3 §1: the cache row of a token is the 512-d c_KV plus
+ * the 64-d decoupled RoPE key k_R; P3 §3: bf16 rows, page_size 64; P3 §4:
+ * score = (q_abs . c_KV + q_R . k_R) * scale with scale = 1/sqrt(d_hc + d_R)).
+ *
+ * Inputs
+ *   q_abs       [T, H, d_cg]  dtype    from mla_absorb_q
+ *   q_r         [T, H, d_R]   dtype    RoPE query, before rotation
+ *   kv_cache    [num_pool_pages, page_size, d_c + d_R] dtype; row = [c_KV | k_R],
+ *               k_R already rotated at its own position
+ *   page_table  [batch, max_pages_per_seq] int32: logical page p of sequence b
+ *               lives in physical page page_table[b][p]
+ *   seq_lens    [batch] int32: keys of sequence b, including its new tokens
+ *   cu_q        [batch+1] int32: sequence b owns query rows cu_q[b] .. cu_q[b+1]-1
+ *   rope_cos, rope_sin  [rope_max_pos, d_R/2] float32 from mla_rope_table, or
+ *               both NULL for no rotation.  Query i of sequence b sits at
+ *               position seq_lens[b] - q_len_b + i (clamped into the table).
+ * Outputs (caller-allocated workspace, float32)
+ *   o_part      [T, H, num_splits, d_cg]: split s's softmax-normalised output
+ *   lse_part    [T, H, num_splits]: split s's natural-log log-sum-exp of the
+ *               scaled scores; -INFINITY (with o_part = 0) for an empty split
+ * Split plan: sequence b has n_b = ceil(seq_lens[b] / page_size) pages; split s
+ * covers pages [s*c_b, (s+1)*c_b) with c_b = ceil(n_b / num_splits).  With
+ * causal != 0 query i sees keys j <= its position; otherwise all keys.
+ * softmax_scale <= 0 selects 1/sqrt(d_hc + d_R).
+ */
+int mla_decode_paged(const void* q_abs, const void* q_r, const void* kv_cache,
+                     const int32_t* page_table, const int32_t* seq_lens, const int32_t* cu_q,
+                     const float* rope_cos, const float* rope_sin, int rope_max_pos,
+                     float* o_part, float* lse_part,
+                     int batch, int total_q, int max_pages_per_seq, int num_pool_pages,
+                     int heads, int groups, int d_hc, int d_c, int d_R, int page_size,
+                     int num_splits, float softmax_scale, int causal, int dtype, void* stream);
+
+/*
+ * mla_combine -- merge the split partials by their log-sum-exp:
+ *   M = max_s lse[s],  w_s = exp(lse[s] - M),
+ *   o_latent = sum_s w_s o_part[s] / sum_s w_s,  lse = M + log(sum_s w_s).
+ * A row whose splits are all empty gets o_latent = 0 and lse = -INFINITY.
+ *
+ *   o_part   [T, H, num_splits, d_cg] float32, lse_part [T, H, num_splits] float32
+ *   o_latent [T, H, d_cg] dtype output
+ *   lse_out  [T, H] float32 output, or NULL
+ */
+int mla_combine(const float* o_part, const float* lse_part, void* o_latent, float* lse_out,
+                int total_q, int heads, int groups, int d_c, int num_splits,
+                int dtype, void* stream);
+
+/*
+ * mla_up_v -- map the latent attention output back up to the value space
+ * (P2 §2.4: the latent is mapped back up to full K/V when needed; P3 §1: K/V
+ * are 128 heads x 128 dims):
+ *   out[t,h,d] = sum_c w_uv[h,d,c] o_latent[t,h,c], fp32 accumulation.
+ *
+ *   o_latent [T, H, d_cg] dtype, w_uv [H, d_hc, d_cg] dtype, out [T, H, d_hc] dtype
+ */
+int mla_up_v(const void* o_latent, const void* w_uv, void* out,
+             int total_q, int heads, int groups, int d_hc, int d_c,
+             int dtype, void* stream);
+
+/* Bytes of the o_part + lse_part workspace mla_decode_paged needs (0 on bad sizes). */
+size_t mla_decode_workspace_bytes(int total_q, int heads, int groups, int d_c, int num_splits);
+
+/* Static text for a status code (never NULL). */
+const char* mla_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_KV_H */

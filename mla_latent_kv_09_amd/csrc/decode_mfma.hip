@@ -1,0 +1,375 @@
+// Split-KV absorbed-MLA decode on bf16 MFMA (gfx950), 128 query rows per workgroup.
+//
+// Computes, for one query token t and one split of its sequence's pages, the
+// softmax-normalised latent output and log-sum-exp of
+//     s_j = scale * (q_abs . c_KV[j] + RoPE(q_R) . k_R[j])          (nxmr.cn/news/151634 §4)
+// over the split's keys, for all H = 128 heads at once, so every streamed latent
+// page is read from HBM once per (token, split) and shared by all heads
+// (nxmr.cn/news/151634 §1: the 512-d latent plus the 64-d shared RoPE key is all a
+// token stores).  Softmax statistics are fp32 (online, one page at a time).
+//
+// Work layout (workgroup = 8 waves, two per SIMD):
+//   wave w owns heads 16w .. 16w+15; lane l owns head 16w + l%16, and the four
+//   lanes l%16 + 16g (g = 0..3) split that head's keys (scores) and latent
+//   columns (output) between them.
+//   Scores:  S^T[64 tok x 16 heads] = C[64 x 576] . Q^T   on v_mfma_f32_16x16x32_bf16,
+//            C read from LDS (ds_read_b128), Q held in registers for the whole split.
+//   Output:  O^T[512 x 16 heads] += C^T[512 x 64] . P^T    on the same MFMA,
+//            C^T read from LDS with ds_read_b64_tr_b16, P taken straight from the
+//            score accumulators (no LDS round trip).
+// Pages: one 64-token page (72 KB) per stage, two stages in LDS (144 KB of 160 KB),
+// fetched with global_load_lds (16 B per lane) in a swizzled layout that keeps both
+// the b128 score reads and the transposing output reads free of bank conflicts.
+#include <math.h>
+
+#include "mla_device.h"
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
+
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * 64;
+constexpr int kHeads = 128;              // rows per workgroup (8 waves x 16)
+constexpr int kTok = 64;                 // tokens per stage = one page
+constexpr int kDc = 512;                 // latent width
+constexpr int kDr = 64;                  // RoPE key width
+constexpr int kRowBytes = (kDc + kDr) * 2;
+constexpr int kCBytes = kTok * kDc * 2;  // 64 KB latent part of a stage
+constexpr int kRBytes = kTok * kDr * 2;  // 8 KB RoPE part
+constexpr int kStageBytes = kCBytes + kRBytes;
+constexpr int kQrOff = 2 * kStageBytes;   // rotated q_R of all heads lives after the two stages
+constexpr int kLdsBytes = kQrOff + kHeads * kDr * 2;
+constexpr int kQSteps = kDc / 32;          // 16 latent K-steps of 32 dims (+2 RoPE steps)
+static_assert(kLdsBytes <= 160 * 1024, "stages + q_R must fit the 160 KB LDS of a gfx950 CU");
+
+// Swizzles (16-byte chunk index XOR).  Latent part: token t's chunk c sits at slot
+// c ^ swz_c(t).  16 consecutive tokens x one chunk hit 16 distinct bank groups
+// (b128 score reads), and 8 aligned tokens x 2 aligned chunks do too (transposing
+// reads, 32 lanes per cycle).
+__device__ __forceinline__ int swz_c(int t) { return 2 * (t & 7) + ((t >> 3) & 1); }
+// RoPE part (8 chunks per token): 16 consecutive tokens x one chunk -> 16 groups.
+__device__ __forceinline__ int swz_r(int t) { return (t & 7) ^ ((t >> 3) & 1); }
+// Rotated q_R (8 chunks per head): 16 consecutive heads x one chunk -> 16 groups.
+__device__ __forceinline__ uint32_t qr_slot(int h, int c) { return h * 128 + ((c ^ ((h >> 1) & 7)) << 4); }
+
+// LDS byte offset of a pointer into a __shared__ array, and back.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
+}
+__device__ __forceinline__ lds_void_t* lds_void(const void* p) { return (lds_void_t*)(p); }
+__device__ __forceinline__ lds_bf16x4_t* lds_bf16x4(uint32_t byte) { return (lds_bf16x4_t*)(uintptr_t)(byte); }
+
+// Pass a value through an empty asm so the compiler treats it as unknown: used on
+// per-iteration LDS base addresses so that only compile-time offsets vary between
+// the reads of a page (they fold into the ds_read offset field) and no per-read
+// address is hoisted out of the page loop.
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
+__device__ __forceinline__ bf16x8 to_bf16x8(float x0, float x1, float x2, float x3, float x4,
+                                            float x5, float x6, float x7) {
+  return bf16x8{static_cast<__bf16>(x0), static_cast<__bf16>(x1), static_cast<__bf16>(x2),
+                static_cast<__bf16>(x3), static_cast<__bf16>(x4), static_cast<__bf16>(x5),
+                static_cast<__bf16>(x6), static_cast<__bf16>(x7)};
+}
+
+// Issue this wave's share of one page into LDS stage `stage`: latent rows 8w..8w+7
+// and the RoPE rows of the same 8 tokens.  Rows at or past n_valid fetch row 0
+// instead (always valid), so no stale or uninitialised slot enters the MFMAs.
+// For row t = 8w + k the latent swizzle key is swz_c(t) = 2k + (w & 1).
+// `lane_v` is the lane index passed through an empty asm each call, so the per-lane
+// offsets are recomputed here (two VALU ops each) instead of being hoisted out of
+// the page loop and kept live across it.
+__device__ __forceinline__ void load_page(char* smem, int stage, const char* page, int n_valid,
+                                          int wave, int lane_v) {
+  asm volatile("" : "+v"(lane_v));
+  char* c_base = smem + stage * kStageBytes;
+  char* r_base = c_base + kCBytes;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int t = wave * 8 + k;
+    const int src_t = t < n_valid ? t : 0;
+    const int key = 2 * k + (wave & 1);
+    const char* g = page + src_t * kRowBytes + ((lane_v ^ key) << 4);
+    __builtin_amdgcn_global_load_lds(g, lds_void(c_base + t * 1024), 16, 0, 0);
+  }
+  const int t = wave * 8 + (lane_v >> 3);
+  const int src_t = t < n_valid ? t : 0;
+  const char* g = page + src_t * kRowBytes + kDc * 2 + (((lane_v & 7) ^ swz_r(t)) << 4);
+  __builtin_amdgcn_global_load_lds(g, lds_void(r_base + wave * 1024), 16, 0, 0);
+}
+
+constexpr int kRing = 4;  // LDS fragments in flight per wave
+
+// Latent score-step fragment st = mb * 16 + k: A operand of S^T for tokens 16mb + j,
+// latent dims 32k + 8g .. +7.  sb[i] = stage base + per-lane base for k % 4 == i.
+__device__ __forceinline__ bf16x8 score_frag(const uint32_t* sb, int st) {
+  const int mb = st / kQSteps, k = st % kQSteps;
+  return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(sb[k & 3] + 16384 * mb +
+                                                                      256 * (k >> 2));
+}
+
+// Output-step fragment st = ks * 32 + nb: A operand of O^T for columns 16nb + j,
+// tokens 32ks + 4g + {0..3} and 32ks + 16 + 4g + {0..3}, via two transposing reads.
+// ob[i] = stage base + per-lane base for nb % 8 == i.
+__device__ __forceinline__ bf16x8 out_frag(const uint32_t* ob, int st) {
+  const int ks = st / 32, nb = st % 32;
+  const uint32_t a1 = ob[nb & 7] + 32768 * ks + 256 * (nb >> 3);
+  const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lds_bf16x4(a1));
+  const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lds_bf16x4(a1 + 16384));
+  return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+decode_mfma_kernel(DecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int t = blockIdx.x, split = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
+  const int g = lane >> 4, j = lane & 15;   // 16-lane group, position in group
+  const int head = wave * 16 + j;
+  const int S = a.num_splits;
+  const QueryWork w = query_work(a.cu_q, a.seq_lens, a.batch, t, split, S, kTok, a.max_pages,
+                                 a.causal);
+  const size_t row = (static_cast<size_t>(t) * kHeads + head) * S + split;
+  float* o_out = a.o_part + row * kDc;
+  if (w.k0 >= w.k1) {  // empty split: O = 0, LSE = -inf
+    for (int c = g * 4; c < kDc; c += 16)
+      *reinterpret_cast<f32x4*>(o_out + c) = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (g == 0) a.lse_part[row] = -INFINITY;
+    return;
+  }
+  const char* kv = static_cast<const char*>(a.kv);
+  const int32_t* ptab = a.page_table + static_cast<size_t>(w.b) * a.max_pages;
+  // Page ids of the split, 64 at a time: lane l holds the id of page 64c + l of the
+  // split, read out with readlane when a page is issued.
+  const int page0 = w.k0 / kTok;
+  const int n_split_pages = (w.k1 - w.k0 + kTok - 1) / kTok;
+  int pid_v = 0;
+  auto fetch_ids = [&](int chunk) {
+    const int idx = chunk * 64 + lane;
+    pid_v = idx < n_split_pages ? ptab[page0 + idx] : 0;
+  };
+  auto page_ptr = [&](int i) {  // i = page index within the split (wave-uniform)
+    const int id = clamp_page(__builtin_amdgcn_readlane(pid_v, i & 63), a.num_pool_pages);
+    return kv + static_cast<size_t>(id) * kTok * kRowBytes;
+  };
+  fetch_ids(0);
+
+  // First page in flight before anything else.
+  int j0 = w.k0;
+  load_page(smem, 0, page_ptr(0), min(kTok, w.k1 - j0), wave, lane);
+
+  // Q fragments: B operand of S^T = C . Q^T.  K-step k covers latent dims 32k .. 32k+31;
+  // this lane holds dims 32k + 8g .. +7 of its head.  The RoPE half of the query is
+  // rotated here in fp32 and parked, as bf16, in LDS (read back twice per page).
+  bf16x8 q[kQSteps];
+  {
+    const uint16_t* qa = static_cast<const uint16_t*>(a.q_abs) +
+                         (static_cast<size_t>(t) * kHeads + head) * kDc + g * 8;
+#pragma unroll
+    for (int k = 0; k < kQSteps; ++k) q[k] = *reinterpret_cast<const bf16x8*>(qa + 32 * k);
+    const uint16_t* qr = static_cast<const uint16_t*>(a.q_r) +
+                         (static_cast<size_t>(t) * kHeads + head) * kDr + g * 8;
+    const int p = min(max(w.pos, 0), max(a.rope_max_pos - 1, 0));
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = bf16_to_f32(qr[32 * k + e]);
+      if (a.rope_cos != nullptr) {
+        const int pair0 = (32 * k + g * 8) / 2;
+        const float* cs = a.rope_cos + static_cast<size_t>(p) * (kDr / 2) + pair0;
+        const float* sn = a.rope_sin + static_cast<size_t>(p) * (kDr / 2) + pair0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x0 = x[2 * i], x1 = x[2 * i + 1];
+          x[2 * i] = fmaf(x0, cs[i], -x1 * sn[i]);
+          x[2 * i + 1] = fmaf(x0, sn[i], x1 * cs[i]);
+        }
+      }
+      *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)(lds_addr(smem) + kQrOff +
+                                                             qr_slot(head, 4 * k + g)) =
+          to_bf16x8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+    }
+  }
+
+  const float scale_log2 = a.scale * kLog2e;
+  float m_run = -INFINITY;   // running max of scaled scores (log2 units), same in the 4 lanes of a head
+  float l_run = 0.f;         // this lane's share of the running sum
+  f32x4 o[32];               // O^T block nb: columns 16nb + 4g .. +3 of this lane's head
+#pragma unroll
+  for (int nb = 0; nb < 32; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // Per-lane LDS offsets inside a stage.  The swizzle keys depend only on the low
+  // four bits of the token index, so every address splits into a per-lane base
+  // plus a compile-time immediate:
+  //   score read  (token 16mb + j, chunk 4k + g):  base_s(k%4)  + 16384 mb + 256 (k/4)
+  //   RoPE read   (token 16mb + j, chunk 4k + g):  base_r(k)    + 2048 mb
+  //   output read (token 32ks + 4g + j/4 (+16), column 16nb + 4(j%4)):
+  //                                               base_o(nb%8) + 32768 ks (+16384) + 256 (nb/8)
+  // The bases are recomputed from the lane index every page (a few VALU ops) rather
+  // than kept in registers across the loop.
+  const uint32_t smem_base = lds_addr(smem);
+  int stage = 0;
+  for (; j0 < w.k1; j0 += kTok) {
+    const int n_valid = min(kTok, w.k1 - j0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's page loads have landed
+    __syncthreads();                     // ... and every wave's; the other stage is free again
+    const int j_next = j0 + kTok;
+    if (j_next < w.k1) {
+      const int i_next = (j_next - w.k0) / kTok;
+      if ((i_next & 63) == 0) fetch_ids(i_next >> 6);
+      load_page(smem, stage ^ 1, page_ptr(i_next), min(kTok, w.k1 - j_next), wave, lane);
+    }
+    const uint32_t st_base = smem_base + stage * kStageBytes;
+    const int lv = static_cast<int>(opaque(static_cast<uint32_t>(lane)));
+    const int lj = lv & 15, lg = lv >> 4;
+    uint32_t sb[4], ob[8];
+    {
+      const int sw = swz_c(lj);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sb[i] = st_base + lj * 1024 + (((4 * i + lg) ^ sw) << 4);
+    }
+
+    // ---- scores S^T for tokens mb*16 .. mb*16+15 of the page.  RoPE part first
+    // (the q_R fragments are live only here), then the 64 latent (mb, k) steps in
+    // order through a ring of kRing prefetched LDS fragments.
+    f32x4 s[4];
+    {
+      const int swr = swz_r(lj);
+      const uint32_t rb0 = st_base + kCBytes + lj * 128 + (((lg) ^ swr) << 4);
+      const uint32_t rb1 = st_base + kCBytes + lj * 128 + (((4 + lg) ^ swr) << 4);
+      const uint32_t qr_head = smem_base + kQrOff + (wave * 16 + lj) * 128;
+      const int swq = (lj >> 1) & 7;
+      const uint32_t qr_addr0 = qr_head + ((lg ^ swq) << 4);
+      const uint32_t qr_addr1 = qr_head + (((4 + lg) ^ swq) << 4);
+      const bf16x8 qr0 = *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(qr_addr0);
+      const bf16x8 qr1 = *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(qr_addr1);
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb) {
+        const bf16x8 c0 = *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(
+            rb0 + 2048 * mb);
+        const bf16x8 c1 = *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(
+            rb1 + 2048 * mb);
+        s[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c0, qr0, f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        s[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c1, qr1, s[mb], 0, 0, 0);
+      }
+    }
+    {
+      constexpr int kSteps = 4 * kQSteps;
+      bf16x8 ring[kRing];
+#pragma unroll
+      for (int st = 0; st < kRing; ++st) ring[st] = score_frag(sb, st);
+#pragma unroll
+      for (int st = 0; st < kSteps; ++st) {
+        const bf16x8 c = ring[st % kRing];
+        if (st + kRing < kSteps) ring[st % kRing] = score_frag(sb, st + kRing);
+        const int mb = st / kQSteps, k = st % kQSteps;
+        s[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c, q[k], s[mb], 0, 0, 0);
+      }
+    }
+
+    // ---- online softmax.  s[mb][i] is the score of token mb*16 + 4g + i.
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tok = mb * 16 + 4 * g + i;
+        const float x = tok < n_valid ? s[mb][i] * scale_log2 : -INFINITY;
+        s[mb][i] = x;
+        mx = fmaxf(mx, x);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = m_run == m_new ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    float psum = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = __builtin_amdgcn_exp2f(s[mb][i] - m_new);
+        s[mb][i] = p;
+        psum += p;
+      }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int nb = 0; nb < 32; ++nb) o[nb] *= alpha;
+    }
+
+    // ---- P^T operands: K-step ks covers tokens 32ks + 4g + {0..3} and 32ks + 16 + 4g + {0..3}
+    bf16x8 pb[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+      pb[ks] = to_bf16x8(s[2 * ks][0], s[2 * ks][1], s[2 * ks][2], s[2 * ks][3],
+                         s[2 * ks + 1][0], s[2 * ks + 1][1], s[2 * ks + 1][2], s[2 * ks + 1][3]);
+
+    // ---- O^T[cols 16nb .. +15] += C^T . P^T, 64 (ks, nb) steps through the ring
+    {
+      const int tok = 4 * lg + (lj >> 2);
+      const int swo = swz_c(tok);
+      const int colb = 4 * (lj & 3);
+      const uint32_t rowb = st_base + tok * 1024 + (colb & 7) * 2;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) ob[i] = rowb + (((2 * i + (colb >> 3)) ^ swo) << 4);
+    }
+    {
+      constexpr int kSteps = 64;
+      bf16x8 ring[kRing];
+#pragma unroll
+      for (int st = 0; st < kRing; ++st) ring[st] = out_frag(ob, st);
+#pragma unroll
+      for (int st = 0; st < kSteps; ++st) {
+        const bf16x8 ct = ring[st % kRing];
+        if (st + kRing < kSteps) ring[st % kRing] = out_frag(ob, st + kRing);
+        const int ks = st / 32, nb = st % 32;
+        o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ct, pb[ks], o[nb], 0, 0, 0);
+      }
+    }
+    stage ^= 1;
+  }
+
+  // ---- finalize: normalise and write this split's partial output and LSE
+  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
+  l_tot += __shfl_xor(l_tot, 32, 64);
+  const float inv = 1.f / l_tot;
+#pragma unroll
+  for (int nb = 0; nb < 32; ++nb)
+    *reinterpret_cast<f32x4*>(o_out + nb * 16 + 4 * g) = o[nb] * inv;
+  if (g == 0) a.lse_part[row] = (m_run + __log2f(l_tot)) * kLn2;
+}
+
+}  // namespace
+
+bool decode_mfma_supported(const DecodeArgs& a, bool bf16) {
+  return bf16 && a.heads == kHeads && a.groups == 1 && a.d_c == kDc && a.d_R == kDr &&
+         a.page_size == kTok;
+}
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_mfma_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const dim3 grid(a.total_q, a.num_splits);
+  decode_mfma_kernel<<<grid, kThreads, kLdsBytes, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

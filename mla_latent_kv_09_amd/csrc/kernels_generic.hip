@@ -1,0 +1,311 @@
+// Shape-generic HIP kernels of the MLA decode step.
+//
+// These handle any supported dimensions in either storage type with plain
+// fp32 FMA arithmetic.  They are the path for small or unusual shapes (the
+// 16-head fp32 tiny workload among them); the production shapes (d_cg 512 or
+// 256, d_R 64, bf16) go to the MFMA kernels.  Both produce the same results up
+// to fp32 rounding order.
+//
+// Sources: www.nxmr.cn/news/151634 §1 (latent row = c_KV | k_R), §4 (absorbed
+// score q_abs . c_KV + q_R . k_R, scale 1/sqrt(d_hc + d_R)), §3/§4 (RoPE in
+// fp32); m.xxqk.cn/news/443191 §2.4 (up-projection back to the value space)
+// and §2.5 (softmax attention).
+#include <math.h>
+
+#include "mla_device.h"
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kRowsPerPass = 16;  // query rows handled per pass of the projection kernels
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// q_abs[t,h,c] = sum_d q_c[t,h,d] * w_uk[h,d,c].  Block: one head, 256 latent columns.
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+absorb_generic_kernel(const T* __restrict__ q_c, const T* __restrict__ w_uk, T* __restrict__ q_abs,
+                      int Tq, int H, int d_hc, int d_cg) {
+  extern __shared__ float q_s[];  // [kRowsPerPass][d_hc]
+  const int h = blockIdx.y;
+  const int c = blockIdx.x * kThreads + threadIdx.x;
+  const T* w = w_uk + static_cast<size_t>(h) * d_hc * d_cg;
+  for (int t0 = 0; t0 < Tq; t0 += kRowsPerPass) {
+    const int nt = min(kRowsPerPass, Tq - t0);
+    __syncthreads();
+    for (int e = threadIdx.x; e < kRowsPerPass * d_hc; e += kThreads) {
+      const int i = e / d_hc, d = e - i * d_hc;
+      q_s[e] = i < nt ? load_elem(q_c, (static_cast<size_t>(t0 + i) * H + h) * d_hc + d) : 0.f;
+    }
+    __syncthreads();
+    if (c < d_cg) {
+      float acc[kRowsPerPass];
+#pragma unroll
+      for (int i = 0; i < kRowsPerPass; ++i) acc[i] = 0.f;
+      for (int d = 0; d < d_hc; ++d) {
+        const float wv = load_elem(w, static_cast<size_t>(d) * d_cg + c);
+#pragma unroll
+        for (int i = 0; i < kRowsPerPass; ++i) acc[i] = fmaf(q_s[i * d_hc + d], wv, acc[i]);
+      }
+      for (int i = 0; i < nt; ++i)
+        store_elem(q_abs, (static_cast<size_t>(t0 + i) * H + h) * d_cg + c, acc[i]);
+    }
+  }
+}
+
+// out[t,h,d] = sum_c w_uv[h,d,c] * o[t,h,c].  Block: one head, 16 output dims (4 per wave).
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+up_v_generic_kernel(const T* __restrict__ o_lat, const T* __restrict__ w_uv, T* __restrict__ out,
+                    int Tq, int H, int d_hc, int d_cg) {
+  extern __shared__ float o_s[];  // [kRowsPerPass][d_cg]
+  const int h = blockIdx.y;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const T* w = w_uv + static_cast<size_t>(h) * d_hc * d_cg;
+  for (int t0 = 0; t0 < Tq; t0 += kRowsPerPass) {
+    const int nt = min(kRowsPerPass, Tq - t0);
+    __syncthreads();
+    for (int e = threadIdx.x; e < kRowsPerPass * d_cg; e += kThreads) {
+      const int i = e / d_cg, c = e - i * d_cg;
+      o_s[e] = i < nt ? load_elem(o_lat, (static_cast<size_t>(t0 + i) * H + h) * d_cg + c) : 0.f;
+    }
+    __syncthreads();
+    for (int k = 0; k < 4; ++k) {
+      const int d = blockIdx.x * 16 + wave * 4 + k;
+      if (d >= d_hc) break;
+      float acc[kRowsPerPass];
+#pragma unroll
+      for (int i = 0; i < kRowsPerPass; ++i) acc[i] = 0.f;
+      for (int c = lane; c < d_cg; c += 64) {
+        const float wv = load_elem(w, static_cast<size_t>(d) * d_cg + c);
+#pragma unroll
+        for (int i = 0; i < kRowsPerPass; ++i) acc[i] = fmaf(o_s[i * d_cg + c], wv, acc[i]);
+      }
+      for (int i = 0; i < nt; ++i) {
+        const float v = wave_sum(acc[i]);
+        if (lane == 0) store_elem(out, (static_cast<size_t>(t0 + i) * H + h) * d_hc + d, v);
+      }
+    }
+  }
+}
+
+// One block per (query row t, split s, head h): online softmax over the split's
+// keys, one page (<= 64 keys) at a time.
+template <typename T>
+__global__ void __launch_bounds__(kThreads) decode_generic_kernel(DecodeArgs a) {
+  constexpr int kMaxCols = 1024, kMaxRope = 256, kTile = 64;
+  __shared__ float q_s[kMaxCols];
+  __shared__ float qr_s[kMaxRope];
+  __shared__ float s_s[kTile];
+  const int t = blockIdx.x, split = blockIdx.y, h = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int H = a.heads, S = a.num_splits, d_cg = a.d_c / a.groups, d_R = a.d_R;
+  const int width = a.d_c + a.d_R;
+  const int g = h / (H / a.groups);
+  const QueryWork w = query_work(a.cu_q, a.seq_lens, a.batch, t, split, S, a.page_size,
+                                 a.max_pages, a.causal);
+  const size_t row = (static_cast<size_t>(t) * H + h) * S + split;
+  float* o_out = a.o_part + row * d_cg;
+  if (w.k0 >= w.k1) {
+    for (int c = tid; c < d_cg; c += kThreads) o_out[c] = 0.f;
+    if (tid == 0) a.lse_part[row] = -INFINITY;
+    return;
+  }
+  const T* q = static_cast<const T*>(a.q_abs) + (static_cast<size_t>(t) * H + h) * d_cg;
+  for (int c = tid; c < d_cg; c += kThreads) q_s[c] = load_elem(q, c);
+  const T* qr = static_cast<const T*>(a.q_r) + (static_cast<size_t>(t) * H + h) * d_R;
+  const int half = d_R / 2;
+  for (int k = tid; k < half; k += kThreads) {
+    const float x0 = load_elem(qr, 2 * k), x1 = load_elem(qr, 2 * k + 1);
+    if (a.rope_cos != nullptr) {
+      const int p = min(max(w.pos, 0), a.rope_max_pos - 1);
+      const float cs = a.rope_cos[static_cast<size_t>(p) * half + k];
+      const float sn = a.rope_sin[static_cast<size_t>(p) * half + k];
+      qr_s[2 * k] = fmaf(x0, cs, -x1 * sn);
+      qr_s[2 * k + 1] = fmaf(x0, sn, x1 * cs);
+    } else {
+      qr_s[2 * k] = x0;
+      qr_s[2 * k + 1] = x1;
+    }
+  }
+  __syncthreads();
+
+  const float scale_log2 = a.scale * kLog2e;
+  constexpr int kColsPerThread = kMaxCols / kThreads;
+  float acc[kColsPerThread];
+#pragma unroll
+  for (int k = 0; k < kColsPerThread; ++k) acc[k] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  for (int j0 = w.k0; j0 < w.k1; j0 += a.page_size) {
+    const int n = min(a.page_size, w.k1 - j0);
+    const int page = clamp_page(a.page_table[static_cast<size_t>(w.b) * a.max_pages + j0 / a.page_size],
+                                a.num_pool_pages);
+    const T* kv = static_cast<const T*>(a.kv) + static_cast<size_t>(page) * a.page_size * width;
+    for (int jj = wave; jj < n; jj += kThreads / 64) {
+      const T* r = kv + static_cast<size_t>(jj) * width;
+      float part = 0.f;
+      for (int c = lane; c < d_cg; c += 64) part = fmaf(q_s[c], load_elem(r, g * d_cg + c), part);
+      for (int c = lane; c < d_R; c += 64) part = fmaf(qr_s[c], load_elem(r, a.d_c + c), part);
+      part = wave_sum(part);
+      if (lane == 0) s_s[jj] = part * scale_log2;
+    }
+    __syncthreads();
+    float tmax = -INFINITY;
+    for (int jj = 0; jj < n; ++jj) tmax = fmaxf(tmax, s_s[jj]);
+    const float m_new = fmaxf(m, tmax);
+    const float alpha = exp2f(m - m_new);
+    l *= alpha;
+#pragma unroll
+    for (int k = 0; k < kColsPerThread; ++k) acc[k] *= alpha;
+    for (int jj = 0; jj < n; ++jj) {
+      const float p = exp2f(s_s[jj] - m_new);
+      l += p;
+      const T* r = kv + static_cast<size_t>(jj) * width + g * d_cg;
+#pragma unroll
+      for (int k = 0; k < kColsPerThread; ++k) {
+        const int c = tid + k * kThreads;
+        if (c < d_cg) acc[k] = fmaf(p, load_elem(r, c), acc[k]);
+      }
+    }
+    m = m_new;
+    __syncthreads();
+  }
+  const float inv = 1.f / l;
+#pragma unroll
+  for (int k = 0; k < kColsPerThread; ++k) {
+    const int c = tid + k * kThreads;
+    if (c < d_cg) o_out[c] = acc[k] * inv;
+  }
+  if (tid == 0) a.lse_part[row] = (m + log2f(l)) * kLn2;
+}
+
+// One block per (t, h): merge num_splits partials by their log-sum-exp.
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+combine_kernel(const float* __restrict__ o_part, const float* __restrict__ lse_part,
+               T* __restrict__ o_lat, float* __restrict__ lse_out, int d_cg, int S) {
+  constexpr int kMaxSplits = 256;
+  __shared__ float w_s[kMaxSplits];
+  __shared__ float red_s[kThreads / 64];
+  __shared__ float stat_s[2];
+  const size_t r = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float v = tid < S ? lse_part[r * S + tid] : -INFINITY;
+  float mx = v;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  if (lane == 0) red_s[wave] = mx;
+  __syncthreads();
+  if (tid == 0) {
+    float M = red_s[0];
+    for (int i = 1; i < kThreads / 64; ++i) M = fmaxf(M, red_s[i]);
+    stat_s[0] = M;
+  }
+  __syncthreads();
+  const float M = stat_s[0];
+  const float wt = (tid < S && M != -INFINITY) ? expf(v - M) : 0.f;
+  if (tid < S) w_s[tid] = wt;
+  const float ws = wave_sum(wt);
+  __syncthreads();
+  if (lane == 0) red_s[wave] = ws;
+  __syncthreads();
+  if (tid == 0) {
+    float sum = 0.f;
+    for (int i = 0; i < kThreads / 64; ++i) sum += red_s[i];
+    stat_s[1] = sum;
+  }
+  __syncthreads();
+  const float sum = stat_s[1];
+  const float inv = M == -INFINITY ? 0.f : 1.f / sum;
+  for (int c = tid; c < d_cg; c += kThreads) {
+    float acc = 0.f;
+    for (int s = 0; s < S; ++s) {
+      const float ww = w_s[s];
+      if (ww != 0.f) acc = fmaf(ww, o_part[(r * S + s) * d_cg + c], acc);
+    }
+    store_elem(o_lat, r * d_cg + c, acc * inv);
+  }
+  if (tid == 0 && lse_out != nullptr) lse_out[r] = M == -INFINITY ? -INFINITY : M + logf(sum);
+}
+
+__global__ void __launch_bounds__(kThreads)
+rope_table_kernel(float* __restrict__ cos_out, float* __restrict__ sin_out, int max_pos, int half,
+                  double base) {
+  const size_t i = static_cast<size_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (i >= static_cast<size_t>(max_pos) * half) return;
+  const int p = static_cast<int>(i / half), k = static_cast<int>(i % half);
+  const double theta = pow(base, -2.0 * k / (2.0 * half));
+  const double ang = static_cast<double>(p) * theta;
+  cos_out[i] = static_cast<float>(cos(ang));
+  sin_out[i] = static_cast<float>(sin(ang));
+}
+
+}  // namespace
+
+hipError_t launch_absorb_generic(const void* q_c, const void* w_uk, void* q_abs, int T, int H,
+                                 int d_hc, int d_cg, bool bf16, hipStream_t s) {
+  const dim3 grid((d_cg + kThreads - 1) / kThreads, H);
+  const size_t lds = sizeof(float) * kRowsPerPass * d_hc;
+  if (bf16)
+    absorb_generic_kernel<uint16_t><<<grid, kThreads, lds, s>>>(
+        static_cast<const uint16_t*>(q_c), static_cast<const uint16_t*>(w_uk),
+        static_cast<uint16_t*>(q_abs), T, H, d_hc, d_cg);
+  else
+    absorb_generic_kernel<float><<<grid, kThreads, lds, s>>>(
+        static_cast<const float*>(q_c), static_cast<const float*>(w_uk), static_cast<float*>(q_abs),
+        T, H, d_hc, d_cg);
+  return hipGetLastError();
+}
+
+hipError_t launch_up_v_generic(const void* o_lat, const void* w_uv, void* out, int T, int H,
+                               int d_hc, int d_cg, bool bf16, hipStream_t s) {
+  const dim3 grid((d_hc + 15) / 16, H);
+  const size_t lds = sizeof(float) * kRowsPerPass * d_cg;
+  if (bf16)
+    up_v_generic_kernel<uint16_t><<<grid, kThreads, lds, s>>>(
+        static_cast<const uint16_t*>(o_lat), static_cast<const uint16_t*>(w_uv),
+        static_cast<uint16_t*>(out), T, H, d_hc, d_cg);
+  else
+    up_v_generic_kernel<float><<<grid, kThreads, lds, s>>>(
+        static_cast<const float*>(o_lat), static_cast<const float*>(w_uv), static_cast<float*>(out),
+        T, H, d_hc, d_cg);
+  return hipGetLastError();
+}
+
+hipError_t launch_decode_generic(const DecodeArgs& a, bool bf16, hipStream_t s) {
+  const dim3 grid(a.total_q, a.num_splits, a.heads);
+  if (bf16)
+    decode_generic_kernel<uint16_t><<<grid, kThreads, 0, s>>>(a);
+  else
+    decode_generic_kernel<float><<<grid, kThreads, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(const float* o_part, const float* lse_part, void* o_lat, float* lse_out,
+                          int T, int H, int d_cg, int S, bool bf16, hipStream_t s) {
+  const dim3 grid(static_cast<unsigned>(T) * H);
+  if (bf16)
+    combine_kernel<uint16_t><<<grid, kThreads, 0, s>>>(o_part, lse_part, static_cast<uint16_t*>(o_lat),
+                                                       lse_out, d_cg, S);
+  else
+    combine_kernel<float><<<grid, kThreads, 0, s>>>(o_part, lse_part, static_cast<float*>(o_lat),
+                                                    lse_out, d_cg, S);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_table(float* cos_out, float* sin_out, int max_pos, int d_R, double base,
+                             hipStream_t s) {
+  const int half = d_R / 2;
+  const size_t n = static_cast<size_t>(max_pos) * half;
+  const dim3 grid(static_cast<unsigned>((n + kThreads - 1) / kThreads));
+  rope_table_kernel<<<grid, kThreads, 0, s>>>(cos_out, sin_out, max_pos, half, base);
+  return hipGetLastError();
+}
+
+}  // namespace mla

@@ -1,0 +1,187 @@
+// C ABI of the MLA decode library: argument validation on the host, then one
+// kernel launch per call on the caller's stream.  See include/mla_kv.h for the
+// contract of every entry point.
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "mla_internal.h"
+#include "mla_kv.h"
+
+namespace {
+
+constexpr int kMaxSplits = 256;
+constexpr int kMaxGenericCols = 1024;  // d_cg limit of the generic kernels
+constexpr int kMaxGenericRope = 256;   // d_R limit of the generic kernels
+constexpr int kMaxGenericHeadDim = 1024;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_dtype(int dtype) {
+  return (dtype == MLA_DTYPE_BF16 || dtype == MLA_DTYPE_FP32) ? MLA_OK : MLA_ERR_DTYPE;
+}
+
+// Shared checks of heads / groups / latent width.
+int check_heads(int heads, int groups, int d_c) {
+  if (heads <= 0 || groups <= 0 || d_c <= 0) return MLA_ERR_DIM;
+  if (heads % groups != 0 || d_c % groups != 0) return MLA_ERR_DIM;
+  return MLA_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH; }
+
+// Decode kernel selection: MLA_KV_DECODE_KERNEL = "generic" forces the shape-generic
+// kernel, "mfma" requires the MFMA kernel (unsupported shapes then fail with
+// MLA_ERR_UNSUPPORTED), anything else picks the MFMA kernel whenever the shape has one.
+enum class DecodeKernel { kAuto, kGeneric, kMfma };
+DecodeKernel decode_kernel_choice() {
+  const char* v = getenv("MLA_KV_DECODE_KERNEL");
+  if (v != nullptr && strcmp(v, "generic") == 0) return DecodeKernel::kGeneric;
+  if (v != nullptr && strcmp(v, "mfma") == 0) return DecodeKernel::kMfma;
+  return DecodeKernel::kAuto;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* mla_status_string(int status) {
+  switch (status) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_NULL: return "a required pointer is NULL";
+    case MLA_ERR_DIM: return "invalid dimension (non-positive size, heads or d_c not divisible by "
+                             "groups, or odd d_R)";
+    case MLA_ERR_UNSUPPORTED: return "unsupported configuration (page_size must be 64; "
+                                     "dimension or split count beyond the implemented limits)";
+    case MLA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case MLA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    case MLA_ERR_DTYPE: return "unknown dtype";
+    default: return "unknown status";
+  }
+}
+
+size_t mla_decode_workspace_bytes(int total_q, int heads, int groups, int d_c, int num_splits) {
+  if (total_q < 0 || num_splits <= 0 || check_heads(heads, groups, d_c) != MLA_OK) return 0;
+  const size_t rows = static_cast<size_t>(total_q) * heads * num_splits;
+  return rows * (static_cast<size_t>(d_c / groups) + 1) * sizeof(float);
+}
+
+int mla_absorb_q(const void* q_c, const void* w_uk, void* q_abs, int total_q, int heads, int groups,
+                 int d_hc, int d_c, int dtype, void* stream) {
+  int st = check_dtype(dtype);
+  if (st != MLA_OK) return st;
+  if (total_q < 0 || d_hc <= 0) return MLA_ERR_DIM;
+  if ((st = check_heads(heads, groups, d_c)) != MLA_OK) return st;
+  if (d_hc > kMaxGenericHeadDim) return MLA_ERR_UNSUPPORTED;
+  if (total_q == 0) return MLA_OK;
+  if (!q_c || !w_uk || !q_abs) return MLA_ERR_NULL;
+  if (!aligned16(q_c) || !aligned16(w_uk) || !aligned16(q_abs)) return MLA_ERR_ALIGN;
+  const bool bf16 = dtype == MLA_DTYPE_BF16;
+  return launch_status(mla::launch_absorb_generic(q_c, w_uk, q_abs, total_q, heads, d_hc,
+                                                  d_c / groups, bf16,
+                                                  static_cast<hipStream_t>(stream)));
+}
+
+int mla_rope_table(float* cos_out, float* sin_out, int max_pos, int d_R, double base, void* stream) {
+  if (max_pos <= 0 || d_R <= 0 || (d_R & 1) || !(base > 0.0)) return MLA_ERR_DIM;
+  if (!cos_out || !sin_out) return MLA_ERR_NULL;
+  if (!aligned16(cos_out) || !aligned16(sin_out)) return MLA_ERR_ALIGN;
+  return launch_status(mla::launch_rope_table(cos_out, sin_out, max_pos, d_R, base,
+                                              static_cast<hipStream_t>(stream)));
+}
+
+int mla_decode_paged(const void* q_abs, const void* q_r, const void* kv_cache,
+                     const int32_t* page_table, const int32_t* seq_lens, const int32_t* cu_q,
+                     const float* rope_cos, const float* rope_sin, int rope_max_pos,
+                     float* o_part, float* lse_part, int batch, int total_q, int max_pages_per_seq,
+                     int num_pool_pages, int heads, int groups, int d_hc, int d_c, int d_R,
+                     int page_size, int num_splits, float softmax_scale, int causal, int dtype,
+                     void* stream) {
+  int st = check_dtype(dtype);
+  if (st != MLA_OK) return st;
+  if (total_q < 0 || batch <= 0 || d_hc <= 0 || d_R <= 0 || (d_R & 1) || num_splits <= 0 ||
+      max_pages_per_seq <= 0 || num_pool_pages <= 0 || page_size <= 0)
+    return MLA_ERR_DIM;
+  if ((st = check_heads(heads, groups, d_c)) != MLA_OK) return st;
+  if (page_size != MLA_PAGE_SIZE || num_splits > kMaxSplits) return MLA_ERR_UNSUPPORTED;
+  if (d_c / groups > kMaxGenericCols || d_R > kMaxGenericRope) return MLA_ERR_UNSUPPORTED;
+  if ((rope_cos == nullptr) != (rope_sin == nullptr)) return MLA_ERR_NULL;
+  if (rope_cos != nullptr && rope_max_pos <= 0) return MLA_ERR_DIM;
+  if (total_q == 0) return MLA_OK;
+  if (!q_abs || !q_r || !kv_cache || !page_table || !seq_lens || !cu_q || !o_part || !lse_part)
+    return MLA_ERR_NULL;
+  const void* ptrs[] = {q_abs, q_r, kv_cache, page_table, seq_lens, cu_q, o_part, lse_part};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MLA_ERR_ALIGN;
+  if (rope_cos && (!aligned16(rope_cos) || !aligned16(rope_sin))) return MLA_ERR_ALIGN;
+
+  mla::DecodeArgs a{};
+  a.q_abs = q_abs;
+  a.q_r = q_r;
+  a.kv = kv_cache;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.cu_q = cu_q;
+  a.rope_cos = rope_cos;
+  a.rope_sin = rope_sin;
+  a.rope_max_pos = rope_max_pos;
+  a.o_part = o_part;
+  a.lse_part = lse_part;
+  a.batch = batch;
+  a.total_q = total_q;
+  a.max_pages = max_pages_per_seq;
+  a.num_pool_pages = num_pool_pages;
+  a.heads = heads;
+  a.groups = groups;
+  a.d_c = d_c;
+  a.d_R = d_R;
+  a.page_size = page_size;
+  a.num_splits = num_splits;
+  a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(d_hc + d_R));
+  a.causal = causal != 0;
+  const bool bf16 = dtype == MLA_DTYPE_BF16;
+  const DecodeKernel choice = decode_kernel_choice();
+  const bool mfma_ok = mla::decode_mfma_supported(a, bf16);
+  if (choice == DecodeKernel::kMfma && !mfma_ok) return MLA_ERR_UNSUPPORTED;
+  if (mfma_ok && choice != DecodeKernel::kGeneric)
+    return launch_status(mla::launch_decode_mfma(a, static_cast<hipStream_t>(stream)));
+  return launch_status(mla::launch_decode_generic(a, bf16, static_cast<hipStream_t>(stream)));
+}
+
+int mla_combine(const float* o_part, const float* lse_part, void* o_latent, float* lse_out,
+                int total_q, int heads, int groups, int d_c, int num_splits, int dtype,
+                void* stream) {
+  int st = check_dtype(dtype);
+  if (st != MLA_OK) return st;
+  if (total_q < 0 || num_splits <= 0) return MLA_ERR_DIM;
+  if ((st = check_heads(heads, groups, d_c)) != MLA_OK) return st;
+  if (num_splits > kMaxSplits) return MLA_ERR_UNSUPPORTED;
+  if (total_q == 0) return MLA_OK;
+  if (!o_part || !lse_part || !o_latent) return MLA_ERR_NULL;
+  if (!aligned16(o_part) || !aligned16(lse_part) || !aligned16(o_latent) ||
+      (lse_out && !aligned16(lse_out)))
+    return MLA_ERR_ALIGN;
+  const bool bf16 = dtype == MLA_DTYPE_BF16;
+  return launch_status(mla::launch_combine(o_part, lse_part, o_latent, lse_out, total_q, heads,
+                                           d_c / groups, num_splits, bf16,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int mla_up_v(const void* o_latent, const void* w_uv, void* out, int total_q, int heads, int groups,
+             int d_hc, int d_c, int dtype, void* stream) {
+  int st = check_dtype(dtype);
+  if (st != MLA_OK) return st;
+  if (total_q < 0 || d_hc <= 0) return MLA_ERR_DIM;
+  if ((st = check_heads(heads, groups, d_c)) != MLA_OK) return st;
+  if (d_c / groups > kMaxGenericCols) return MLA_ERR_UNSUPPORTED;
+  if (total_q == 0) return MLA_OK;
+  if (!o_latent || !w_uv || !out) return MLA_ERR_NULL;
+  if (!aligned16(o_latent) || !aligned16(w_uv) || !aligned16(out)) return MLA_ERR_ALIGN;
+  const bool bf16 = dtype == MLA_DTYPE_BF16;
+  return launch_status(mla::launch_up_v_generic(o_latent, w_uv, out, total_q, heads, d_hc,
+                                                d_c / groups, bf16,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

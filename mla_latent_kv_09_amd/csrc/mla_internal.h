@@ -1,0 +1,47 @@
+// Host-side launch entry points of the kernels behind the C ABI.  The ABI
+// layer (mla_abi.hip) validates arguments and then calls exactly one of these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mla {
+
+struct DecodeArgs {
+  const void* q_abs;
+  const void* q_r;
+  const void* kv;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  const int32_t* cu_q;
+  const float* rope_cos;
+  const float* rope_sin;
+  int rope_max_pos;
+  float* o_part;
+  float* lse_part;
+  int batch, total_q, max_pages, num_pool_pages;
+  int heads, groups, d_c, d_R, page_size, num_splits;
+  float scale;
+  int causal;
+};
+
+// Generic kernels: any (d_cg <= 1024, d_R <= 256), bf16 or fp32 storage.
+hipError_t launch_absorb_generic(const void* q_c, const void* w_uk, void* q_abs, int T, int H,
+                                 int d_hc, int d_cg, bool bf16, hipStream_t s);
+hipError_t launch_up_v_generic(const void* o_lat, const void* w_uv, void* out, int T, int H,
+                               int d_hc, int d_cg, bool bf16, hipStream_t s);
+hipError_t launch_decode_generic(const DecodeArgs& a, bool bf16, hipStream_t s);
+
+// Combine and RoPE table (one implementation each).
+hipError_t launch_combine(const float* o_part, const float* lse_part, void* o_lat, float* lse_out,
+                          int T, int H, int d_cg, int S, bool bf16, hipStream_t s);
+hipError_t launch_rope_table(float* cos_out, float* sin_out, int max_pos, int d_R, double base,
+                             hipStream_t s);
+
+}  // namespace mla
+
+namespace mla {
+// MFMA split-KV decode: bf16, 128 heads, d_c 512, d_R 64, one latent group.
+bool decode_mfma_supported(const DecodeArgs& a, bool bf16);
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s);
+}  // namespace mla

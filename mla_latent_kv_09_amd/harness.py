@@ -1,0 +1,63 @@
+"""Move a generated workload into GPU memory and wire up one decode step.
+
+Marshalling only: numpy host arrays become torch device tensors of the
+storage dtype; the decode step itself is ``mla.DecodeStep`` (the four C-ABI
+calls).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import mla
+from .workloads import Workload
+
+
+@dataclass
+class DeviceWorkload:
+    q_c: torch.Tensor
+    q_r: torch.Tensor
+    w_uk: torch.Tensor
+    w_uv: torch.Tensor
+    kv: torch.Tensor
+    page_table: torch.Tensor
+    seq_lens: torch.Tensor
+    cu_q: torch.Tensor
+    rope: Optional[tuple]
+
+
+def _storage_tensor(w: Workload, x: np.ndarray, device) -> torch.Tensor:
+    if w.cfg.dtype == "bf16":
+        bits = x if x.dtype == np.uint16 else w.storage(x)
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+
+
+def to_device(w: Workload, device="cuda", *, rope: bool = True) -> DeviceWorkload:
+    """Copy ``w`` to ``device``; with ``rope`` the fp32 table is built there by the library."""
+    dev = torch.device(device)
+    table = None
+    if rope and w.cfg.rope_base is not None:
+        max_pos = max(1, int(w.seq_lens.max()))
+        table = mla.rope_table(max_pos, w.cfg.d_R, w.cfg.rope_base, device=dev)
+    return DeviceWorkload(
+        q_c=_storage_tensor(w, w.q_c, dev),
+        q_r=_storage_tensor(w, w.q_r, dev),
+        w_uk=_storage_tensor(w, w.w_uk, dev),
+        w_uv=_storage_tensor(w, w.w_uv, dev),
+        kv=_storage_tensor(w, w.pool, dev),
+        page_table=torch.from_numpy(w.page_table).to(dev),
+        seq_lens=torch.from_numpy(w.seq_lens).to(dev),
+        cu_q=torch.from_numpy(w.cu_q).to(dev),
+        rope=table,
+    )
+
+
+def make_step(w: Workload, d: DeviceWorkload, num_splits: Optional[int] = None) -> mla.DecodeStep:
+    return mla.DecodeStep(q_c=d.q_c, q_r=d.q_r, w_uk=d.w_uk, w_uv=d.w_uv, kv_cache=d.kv,
+                          page_table=d.page_table, seq_lens=d.seq_lens, cu_q=d.cu_q,
+                          groups=w.cfg.groups, num_splits=num_splits, rope=d.rope,
+                          causal=w.cfg.causal, seq_lens_host=w.seq_lens.tolist())

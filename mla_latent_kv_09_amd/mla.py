@@ -1,0 +1,237 @@
+"""Thin Python binding of ``libmla_kv.so`` (C ABI in ``include/mla_kv.h``).
+
+Argument marshalling only: every function checks the torch tensors it is
+given (device, dtype, contiguity, shape), passes their device pointers and
+sizes to the C entry point of the same name on the current HIP stream, and
+raises ``MLAError`` on a non-zero status.  All arithmetic runs in the HIP
+kernels; there is no CPU fallback, and loading fails loudly when the library
+has not been built.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmla_kv.so")
+
+DTYPE_BF16 = 0
+DTYPE_FP32 = 1
+PAGE_SIZE = 64
+
+EXPORTED = ("mla_absorb_q", "mla_rope_table", "mla_decode_paged", "mla_combine", "mla_up_v",
+            "mla_decode_workspace_bytes", "mla_status_string")
+
+_lib = None
+
+
+class MLAError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed with status {status}: {status_string(status)}")
+        self.status = status
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load the library once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m mla_latent_kv_09_amd.build_lib` "
+            "(there is no CPU fallback)")
+    lib = ctypes.CDLL(path)
+    P, I, F, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_double
+    lib.mla_absorb_q.argtypes = [P, P, P, I, I, I, I, I, I, P]
+    lib.mla_rope_table.argtypes = [P, P, I, I, D, P]
+    lib.mla_decode_paged.argtypes = ([P] * 8 + [I] + [P] * 2 + [I] * 11 + [F, I, I, P])
+    lib.mla_combine.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
+    lib.mla_up_v.argtypes = [P, P, P, I, I, I, I, I, I, P]
+    lib.mla_decode_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.mla_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.mla_status_string.argtypes = [I]
+    lib.mla_status_string.restype = ctypes.c_char_p
+    for name in ("mla_absorb_q", "mla_rope_table", "mla_decode_paged", "mla_combine", "mla_up_v"):
+        getattr(lib, name).restype = I
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().mla_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise MLAError(fn, status)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    if t.dtype == torch.float32:
+        return DTYPE_FP32
+    raise TypeError(f"storage dtype must be bfloat16 or float32, got {t.dtype}")
+
+
+def _dev(*ts: Optional[torch.Tensor]) -> None:
+    for t in ts:
+        if t is None:
+            continue
+        if not t.is_cuda:
+            raise ValueError("tensors must live in GPU memory")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def absorb_q(q_c: torch.Tensor, w_uk: torch.Tensor, q_abs: Optional[torch.Tensor] = None, *,
+             groups: int = 1, stream=None) -> torch.Tensor:
+    """q_abs[t,h,:] = q_c[t,h,:] @ w_uk[h]; q_c [T,H,d_hc], w_uk [H,d_hc,d_c/G]."""
+    T, H, d_hc = q_c.shape
+    d_cg = w_uk.shape[2]
+    if w_uk.shape != (H, d_hc, d_cg) or w_uk.dtype != q_c.dtype:
+        raise ValueError("w_uk must be [H, d_hc, d_c/G] with q_c's dtype")
+    if q_abs is None:
+        q_abs = torch.empty((T, H, d_cg), dtype=q_c.dtype, device=q_c.device)
+    _dev(q_c, w_uk, q_abs)
+    _check("mla_absorb_q", load().mla_absorb_q(
+        _ptr(q_c), _ptr(w_uk), _ptr(q_abs), T, H, groups, d_hc, d_cg * groups, _dtype_code(q_c),
+        _stream(stream)))
+    return q_abs
+
+
+def rope_table(max_pos: int, d_R: int, base: float = 10000.0, *, device="cuda", stream=None):
+    """fp32 (cos, sin) tables [max_pos, d_R/2] computed on the GPU."""
+    cos = torch.empty((max_pos, d_R // 2), dtype=torch.float32, device=device)
+    sin = torch.empty_like(cos)
+    _check("mla_rope_table", load().mla_rope_table(_ptr(cos), _ptr(sin), max_pos, d_R, float(base),
+                                                   _stream(stream)))
+    return cos, sin
+
+
+def workspace(total_q: int, heads: int, d_cg: int, num_splits: int, device="cuda"):
+    """Allocate the (o_part, lse_part) split workspace."""
+    o_part = torch.empty((total_q, heads, num_splits, d_cg), dtype=torch.float32, device=device)
+    lse_part = torch.empty((total_q, heads, num_splits), dtype=torch.float32, device=device)
+    return o_part, lse_part
+
+
+def decode_paged(q_abs, q_r, kv_cache, page_table, seq_lens, cu_q, o_part, lse_part, *,
+                 d_hc: int, groups: int = 1, rope: Optional[tuple] = None, softmax_scale: float = 0.0,
+                 causal: bool = True, stream=None) -> None:
+    """Split-KV attention over the paged cache into (o_part, lse_part)."""
+    T, H, d_cg = q_abs.shape
+    d_R = q_r.shape[2]
+    P, ps, width = kv_cache.shape
+    B, max_pages = page_table.shape
+    S = o_part.shape[2]
+    if q_r.shape[:2] != (T, H) or width != d_cg * groups + d_R:
+        raise ValueError("inconsistent q_r / kv_cache shapes")
+    if o_part.shape != (T, H, S, d_cg) or lse_part.shape != (T, H, S):
+        raise ValueError("o_part must be [T,H,S,d_c/G] and lse_part [T,H,S]")
+    for t, dt in ((page_table, torch.int32), (seq_lens, torch.int32), (cu_q, torch.int32),
+                  (o_part, torch.float32), (lse_part, torch.float32)):
+        if t.dtype != dt:
+            raise TypeError(f"expected {dt}, got {t.dtype}")
+    if seq_lens.shape != (B,) or cu_q.shape != (B + 1,):
+        raise ValueError("seq_lens must be [B] and cu_q [B+1]")
+    if q_r.dtype != q_abs.dtype or kv_cache.dtype != q_abs.dtype:
+        raise TypeError("q_abs, q_r and kv_cache must share the storage dtype")
+    cos, sin = rope if rope is not None else (None, None)
+    rope_max_pos = 0 if cos is None else cos.shape[0]
+    _dev(q_abs, q_r, kv_cache, page_table, seq_lens, cu_q, o_part, lse_part, cos, sin)
+    _check("mla_decode_paged", load().mla_decode_paged(
+        _ptr(q_abs), _ptr(q_r), _ptr(kv_cache), _ptr(page_table), _ptr(seq_lens), _ptr(cu_q),
+        _ptr(cos), _ptr(sin), rope_max_pos, _ptr(o_part), _ptr(lse_part),
+        B, T, max_pages, P, H, groups, d_hc, d_cg * groups, d_R, ps, S, float(softmax_scale),
+        int(bool(causal)), _dtype_code(q_abs), _stream(stream)))
+
+
+def combine(o_part, lse_part, o_latent=None, lse_out=None, *, dtype=torch.bfloat16, stream=None):
+    """LSE merge of the splits -> o_latent [T,H,d_c/G] (and optionally lse [T,H])."""
+    T, H, S, d_cg = o_part.shape
+    if o_latent is None:
+        o_latent = torch.empty((T, H, d_cg), dtype=dtype, device=o_part.device)
+    _dev(o_part, lse_part, o_latent, lse_out)
+    _check("mla_combine", load().mla_combine(
+        _ptr(o_part), _ptr(lse_part), _ptr(o_latent), _ptr(lse_out), T, H, 1, d_cg, S,
+        _dtype_code(o_latent), _stream(stream)))
+    return o_latent
+
+
+def up_v(o_latent, w_uv, out=None, *, groups: int = 1, stream=None):
+    """out[t,h,:] = w_uv[h] @ o_latent[t,h,:]; w_uv [H,d_hc,d_c/G]."""
+    T, H, d_cg = o_latent.shape
+    d_hc = w_uv.shape[1]
+    if w_uv.shape != (H, d_hc, d_cg) or w_uv.dtype != o_latent.dtype:
+        raise ValueError("w_uv must be [H, d_hc, d_c/G] with o_latent's dtype")
+    if out is None:
+        out = torch.empty((T, H, d_hc), dtype=o_latent.dtype, device=o_latent.device)
+    _dev(o_latent, w_uv, out)
+    _check("mla_up_v", load().mla_up_v(
+        _ptr(o_latent), _ptr(w_uv), _ptr(out), T, H, groups, d_hc, d_cg * groups,
+        _dtype_code(o_latent), _stream(stream)))
+    return out
+
+
+def default_num_splits(seq_lens_host, total_q: int, cu_count: int = 256) -> int:
+    """Splits per sequence so that total_q x splits workgroups cover the CUs about twice."""
+    max_pages = max(1, max(int(math.ceil(int(L) / PAGE_SIZE)) for L in seq_lens_host))
+    want = max(1, math.ceil(2 * cu_count / max(1, total_q)))
+    return int(min(want, max_pages, 256))
+
+
+class DecodeStep:
+    """The four calls of one decode step over preallocated buffers (no allocation per call)."""
+
+    def __init__(self, *, q_c, q_r, w_uk, w_uv, kv_cache, page_table, seq_lens, cu_q, groups=1,
+                 num_splits=None, rope=None, causal=True, seq_lens_host=None):
+        self.q_c, self.q_r, self.w_uk, self.w_uv = q_c, q_r, w_uk, w_uv
+        self.kv, self.page_table, self.seq_lens, self.cu_q = kv_cache, page_table, seq_lens, cu_q
+        self.groups, self.rope, self.causal = groups, rope, causal
+        T, H, d_hc = q_c.shape
+        d_cg = w_uk.shape[2]
+        if num_splits is None:
+            num_splits = default_num_splits(seq_lens_host if seq_lens_host is not None
+                                            else seq_lens.cpu().tolist(), T)
+        self.num_splits = num_splits
+        dev = q_c.device
+        self.q_abs = torch.empty((T, H, d_cg), dtype=q_c.dtype, device=dev)
+        self.o_part, self.lse_part = workspace(T, H, d_cg, num_splits, dev)
+        self.o_latent = torch.empty((T, H, d_cg), dtype=q_c.dtype, device=dev)
+        self.lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+        self.out = torch.empty((T, H, d_hc), dtype=q_c.dtype, device=dev)
+        self.d_hc = d_hc
+
+    def absorb(self, stream=None):
+        absorb_q(self.q_c, self.w_uk, self.q_abs, groups=self.groups, stream=stream)
+
+    def attend(self, stream=None):
+        decode_paged(self.q_abs, self.q_r, self.kv, self.page_table, self.seq_lens, self.cu_q,
+                     self.o_part, self.lse_part, d_hc=self.d_hc, groups=self.groups, rope=self.rope,
+                     causal=self.causal, stream=stream)
+
+    def merge(self, stream=None):
+        combine(self.o_part, self.lse_part, self.o_latent, self.lse, stream=stream)
+
+    def project(self, stream=None):
+        up_v(self.o_latent, self.w_uv, self.out, groups=self.groups, stream=stream)
+
+    def __call__(self, stream=None):
+        self.absorb(stream)
+        self.attend(stream)
+        self.merge(stream)
+        self.project(stream)
+        return self.out

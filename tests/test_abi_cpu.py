@@ -1,0 +1,141 @@
+"""The C-ABI library on the CPU: it loads, exports what the header declares, and
+rejects bad arguments on the host before anything is enqueued.
+
+No case here reaches a kernel launch: every call carries at least one argument
+that validation rejects, so the fake (never dereferenced) device addresses are
+safe even on a machine with a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from mla_latent_kv_09_amd import build_lib, mla
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mla_kv.h")
+
+OK, NULL, DIM, UNSUP, ALIGN, LAUNCH, DTYPE = 0, -1, -2, -3, -4, -5, -6
+A = 0x10000          # fake 16-byte-aligned address (never dereferenced)
+MIS = 0x10008        # fake misaligned address
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mla.LIB_PATH):
+        build_lib.build()
+    return mla.load()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mla_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_four_calls():
+    names = _declared_functions()
+    for n in ("mla_absorb_q", "mla_decode_paged", "mla_combine", "mla_up_v"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert set(mla.EXPORTED) == set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings(lib):
+    for code in (OK, NULL, DIM, UNSUP, ALIGN, LAUNCH, DTYPE, 12345):
+        s = mla.status_string(code)
+        assert isinstance(s, str) and s
+
+
+def test_workspace_bytes(lib):
+    assert lib.mla_decode_workspace_bytes(16, 128, 1, 512, 16) == 16 * 128 * 16 * 513 * 4
+    assert lib.mla_decode_workspace_bytes(32, 128, 2, 512, 8) == 32 * 128 * 8 * 257 * 4
+    assert lib.mla_decode_workspace_bytes(16, 128, 3, 512, 16) == 0      # 128 % 3 != 0
+    assert lib.mla_decode_workspace_bytes(16, 128, 1, 512, 0) == 0
+
+
+# -------------------------------------------------------------- absorb / up_v
+
+def _absorb(lib, q=A, w=A, o=A, T=16, H=128, G=1, d_hc=128, d_c=512, dt=0):
+    return lib.mla_absorb_q(q, w, o, T, H, G, d_hc, d_c, dt, None)
+
+
+def test_absorb_validation(lib):
+    assert _absorb(lib, q=None) == NULL
+    assert _absorb(lib, o=None) == NULL
+    assert _absorb(lib, w=MIS) == ALIGN
+    assert _absorb(lib, H=0) == DIM
+    assert _absorb(lib, T=-1) == DIM
+    assert _absorb(lib, H=128, G=3) == DIM
+    assert _absorb(lib, d_c=511, G=2) == DIM
+    assert _absorb(lib, dt=7) == DTYPE
+    assert _absorb(lib, d_hc=4096, q=None) == UNSUP
+    assert _absorb(lib, T=0, q=None) == OK        # nothing to do, nothing enqueued
+
+
+def test_up_v_validation(lib):
+    f = lambda o=A, w=A, out=A, T=16, H=128, G=1, d_hc=128, d_c=512, dt=0: lib.mla_up_v(
+        o, w, out, T, H, G, d_hc, d_c, dt, None)
+    assert f(out=None) == NULL
+    assert f(o=MIS) == ALIGN
+    assert f(d_hc=0) == DIM
+    assert f(d_c=4096, o=None) == UNSUP
+    assert f(dt=-1) == DTYPE
+    assert f(T=0, w=None) == OK
+
+
+def test_combine_validation(lib):
+    f = lambda op=A, lp=A, ol=A, lo=None, T=16, H=128, G=1, d_c=512, S=16, dt=0: lib.mla_combine(
+        op, lp, ol, lo, T, H, G, d_c, S, dt, None)
+    assert f(op=None) == NULL
+    assert f(lo=MIS, ol=A, op=A, lp=A, S=0) == DIM
+    assert f(lo=MIS) == ALIGN
+    assert f(S=257, op=None) == UNSUP
+    assert f(dt=3) == DTYPE
+
+
+def test_rope_table_validation(lib):
+    assert lib.mla_rope_table(A, A, 0, 64, 10000.0, None) == DIM
+    assert lib.mla_rope_table(A, A, 10, 63, 10000.0, None) == DIM
+    assert lib.mla_rope_table(A, A, 10, 64, -1.0, None) == DIM
+    assert lib.mla_rope_table(None, A, 10, 64, 10000.0, None) == NULL
+    assert lib.mla_rope_table(A, MIS, 10, 64, 10000.0, None) == ALIGN
+
+
+# -------------------------------------------------------------- decode
+
+def _decode(lib, **kw):
+    a = dict(q=A, qr=A, kv=A, pt=A, sl=A, cu=A, cos=None, sin=None, rmp=0, op=A, lp=A,
+             B=16, T=16, maxp=64, pool=1024, H=128, G=1, d_hc=128, d_c=512, d_R=64, ps=64, S=16,
+             scale=0.0, causal=1, dt=0)
+    a.update(kw)
+    return lib.mla_decode_paged(a["q"], a["qr"], a["kv"], a["pt"], a["sl"], a["cu"], a["cos"],
+                                a["sin"], a["rmp"], a["op"], a["lp"], a["B"], a["T"], a["maxp"],
+                                a["pool"], a["H"], a["G"], a["d_hc"], a["d_c"], a["d_R"], a["ps"],
+                                a["S"], a["scale"], a["causal"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kv=None), NULL), (dict(pt=None), NULL), (dict(op=None), NULL), (dict(cu=None), NULL),
+    (dict(cos=A), NULL),                       # rope tables come in pairs
+    (dict(kv=MIS), ALIGN), (dict(lp=MIS), ALIGN), (dict(cos=A, sin=MIS, rmp=10), ALIGN),
+    (dict(d_R=63, kv=None), DIM), (dict(H=100, G=3, kv=None), DIM), (dict(S=0, kv=None), DIM),
+    (dict(B=0, kv=None), DIM), (dict(maxp=0, kv=None), DIM), (dict(cos=A, sin=A, rmp=0), DIM),
+    (dict(ps=16, kv=None), UNSUP), (dict(S=257, kv=None), UNSUP), (dict(d_c=4096, kv=None), UNSUP),
+    (dict(dt=2), DTYPE),
+    (dict(T=0, kv=None), OK),
+])
+def test_decode_validation(lib, kw, code):
+    assert _decode(lib, **kw) == code
+
+
+def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
+    monkeypatch.setattr(mla, "_lib", None)
+    with pytest.raises(RuntimeError, match="no CPU fallback"):
+        mla.load(str(tmp_path / "missing.so"))
