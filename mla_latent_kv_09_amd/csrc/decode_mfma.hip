@@ -31,7 +31,6 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
 
 constexpr int kWaves = 8;
@@ -63,7 +62,6 @@ __device__ __forceinline__ uint32_t qr_slot(int h, int c) { return h * 128 + ((c
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
 }
-__device__ __forceinline__ lds_void_t* lds_void(const void* p) { return (lds_void_t*)(p); }
 __device__ __forceinline__ lds_bf16x4_t* lds_bf16x4(uint32_t byte) { return (lds_bf16x4_t*)(uintptr_t)(byte); }
 
 // Pass a value through an empty asm so the compiler treats it as unknown: used on
@@ -82,6 +80,20 @@ __device__ __forceinline__ bf16x8 to_bf16x8(float x0, float x1, float x2, float 
                 static_cast<__bf16>(x6), static_cast<__bf16>(x7)};
 }
 
+// One 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4): lane i's 16
+// bytes land at LDS byte lds + 16 i.  Issued as inline asm on purpose: the
+// compiler then does not know that an LDS DMA is in flight, so it does not make
+// every later LDS read of the page being computed wait for the *next* page's copy
+// (it cannot prove they do not alias).  Completion is awaited explicitly with
+// s_waitcnt vmcnt(0) + a barrier before a stage is read; every wait the compiler
+// emits for its own loads only counts ops it knows about, which stays safe.
+__device__ __forceinline__ void dma16(const char* gptr, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(gptr)
+               : "memory");
+}
+
 // Issue this wave's share of one page into LDS stage `stage`: latent rows 8w..8w+7
 // and the RoPE rows of the same 8 tokens.  Rows at or past n_valid fetch row 0
 // instead (always valid), so no stale or uninitialised slot enters the MFMAs.
@@ -89,23 +101,22 @@ __device__ __forceinline__ bf16x8 to_bf16x8(float x0, float x1, float x2, float 
 // `lane_v` is the lane index passed through an empty asm each call, so the per-lane
 // offsets are recomputed here (two VALU ops each) instead of being hoisted out of
 // the page loop and kept live across it.
-__device__ __forceinline__ void load_page(char* smem, int stage, const char* page, int n_valid,
-                                          int wave, int lane_v) {
+__device__ __forceinline__ void load_page(uint32_t smem_base, int stage, const char* page,
+                                          int n_valid, int wave, int lane_v) {
   asm volatile("" : "+v"(lane_v));
-  char* c_base = smem + stage * kStageBytes;
-  char* r_base = c_base + kCBytes;
+  const uint32_t c_base = smem_base + stage * kStageBytes;
+  const uint32_t r_base = c_base + kCBytes;
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int t = wave * 8 + k;
     const int src_t = t < n_valid ? t : 0;
     const int key = 2 * k + (wave & 1);
-    const char* g = page + src_t * kRowBytes + ((lane_v ^ key) << 4);
-    __builtin_amdgcn_global_load_lds(g, lds_void(c_base + t * 1024), 16, 0, 0);
+    dma16(page + src_t * kRowBytes + ((lane_v ^ key) << 4), c_base + t * 1024);
   }
   const int t = wave * 8 + (lane_v >> 3);
   const int src_t = t < n_valid ? t : 0;
-  const char* g = page + src_t * kRowBytes + kDc * 2 + (((lane_v & 7) ^ swz_r(t)) << 4);
-  __builtin_amdgcn_global_load_lds(g, lds_void(r_base + wave * 1024), 16, 0, 0);
+  dma16(page + src_t * kRowBytes + kDc * 2 + (((lane_v & 7) ^ swz_r(t)) << 4),
+        r_base + wave * 1024);
 }
 
 constexpr int kRing = 4;  // LDS fragments in flight per wave
@@ -167,7 +178,7 @@ decode_mfma_kernel(DecodeArgs a) {
 
   // First page in flight before anything else.
   int j0 = w.k0;
-  load_page(smem, 0, page_ptr(0), min(kTok, w.k1 - j0), wave, lane);
+  load_page(lds_addr(smem), 0, page_ptr(0), min(kTok, w.k1 - j0), wave, lane);
 
   // Q fragments: B operand of S^T = C . Q^T.  K-step k covers latent dims 32k .. 32k+31;
   // this lane holds dims 32k + 8g .. +7 of its head.  The RoPE half of the query is
@@ -229,7 +240,7 @@ decode_mfma_kernel(DecodeArgs a) {
     if (j_next < w.k1) {
       const int i_next = (j_next - w.k0) / kTok;
       if ((i_next & 63) == 0) fetch_ids(i_next >> 6);
-      load_page(smem, stage ^ 1, page_ptr(i_next), min(kTok, w.k1 - j_next), wave, lane);
+      load_page(smem_base, stage ^ 1, page_ptr(i_next), min(kTok, w.k1 - j_next), wave, lane);
     }
     const uint32_t st_base = smem_base + stage * kStageBytes;
     const int lv = static_cast<int>(opaque(static_cast<uint32_t>(lane)));

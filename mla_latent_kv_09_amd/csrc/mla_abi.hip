@@ -78,9 +78,12 @@ int mla_absorb_q(const void* q_c, const void* w_uk, void* q_abs, int total_q, in
   if (!q_c || !w_uk || !q_abs) return MLA_ERR_NULL;
   if (!aligned16(q_c) || !aligned16(w_uk) || !aligned16(q_abs)) return MLA_ERR_ALIGN;
   const bool bf16 = dtype == MLA_DTYPE_BF16;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (mla::absorb_mfma_supported(d_hc, d_c / groups, bf16))
+    return launch_status(mla::launch_absorb_mfma(q_c, w_uk, q_abs, total_q, heads, d_hc,
+                                                 d_c / groups, s));
   return launch_status(mla::launch_absorb_generic(q_c, w_uk, q_abs, total_q, heads, d_hc,
-                                                  d_c / groups, bf16,
-                                                  static_cast<hipStream_t>(stream)));
+                                                  d_c / groups, bf16, s));
 }
 
 int mla_rope_table(float* cos_out, float* sin_out, int max_pos, int d_R, double base, void* stream) {
@@ -179,9 +182,12 @@ int mla_up_v(const void* o_latent, const void* w_uv, void* out, int total_q, int
   if (!o_latent || !w_uv || !out) return MLA_ERR_NULL;
   if (!aligned16(o_latent) || !aligned16(w_uv) || !aligned16(out)) return MLA_ERR_ALIGN;
   const bool bf16 = dtype == MLA_DTYPE_BF16;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (mla::up_v_mfma_supported(d_hc, d_c / groups, bf16))
+    return launch_status(mla::launch_up_v_mfma(o_latent, w_uv, out, total_q, heads, d_hc,
+                                               d_c / groups, s));
   return launch_status(mla::launch_up_v_generic(o_latent, w_uv, out, total_q, heads, d_hc,
-                                                d_c / groups, bf16,
-                                                static_cast<hipStream_t>(stream)));
+                                                d_c / groups, bf16, s));
 }
 
 }  // extern "C"

@@ -45,3 +45,14 @@ namespace mla {
 bool decode_mfma_supported(const DecodeArgs& a, bool bf16);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s);
 }  // namespace mla
+
+namespace mla {
+// MFMA projections: bf16; absorb needs d_hc == 128 and d_cg % 64 == 0, up_v needs
+// d_hc % 16 == 0 and d_cg in {256, 512}.
+bool absorb_mfma_supported(int d_hc, int d_cg, bool bf16);
+bool up_v_mfma_supported(int d_hc, int d_cg, bool bf16);
+hipError_t launch_absorb_mfma(const void* q_c, const void* w_uk, void* q_abs, int T, int H,
+                              int d_hc, int d_cg, hipStream_t s);
+hipError_t launch_up_v_mfma(const void* o_lat, const void* w_uv, void* out, int T, int H, int d_hc,
+                            int d_cg, hipStream_t s);
+}  // namespace mla

@@ -1,0 +1,163 @@
+// The two per-head projections of the absorbed MLA decode step on bf16 MFMA (gfx950):
+//
+//   absorb  q_abs[t,h,:] = q_c[t,h,:] . W_UK[h]      W_UK [H, d_hc, d_cg]
+//           (nxmr.cn/news/151634 §1, §4 path B: fold W_UK into the query so scores are
+//           taken against the cached latent and K is never re-expanded)
+//   up_v    out[t,h,:]   = W_UV[h] . o_latent[t,h,:]  W_UV [H, d_hc, d_cg]
+//           (m.xxqk.cn/news/443191 §2.4: the latent is mapped back up to the value space)
+//
+// Both are batched GEMMs with small M (the T query rows) and read each weight
+// element exactly once, so they are bound by streaming the 2*H*d_hc*d_cg bytes of
+// weights.  Tiles use v_mfma_f32_16x16x32_bf16 (M = 16 query rows per block),
+// fp32 accumulation, one rounding to bf16 on the way out.
+#include "mla_device.h"
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
+
+// ---------------------------------------------------------------- up_v
+// One wave per (head h, 16 output dims d0..d0+15).  B operand = W_UV[h][d][c]:
+// lane (n = d0 + l%16, k = 8*(l/16) + e) reads 16 contiguous bytes of row d, so
+// the wave's 16 x d_cg weight slice goes straight from HBM into registers (once).
+// A operand = o_latent[t][h][c], 16 bytes per lane, one M-block of 16 rows at a time.
+template <int kSteps>  // d_cg / 32
+__global__ void __launch_bounds__(64)
+up_v_mfma_kernel(const uint16_t* __restrict__ o_lat, const uint16_t* __restrict__ w_uv,
+                 uint16_t* __restrict__ out, int T, int H, int d_hc) {
+  constexpr int d_cg = kSteps * 32;
+  const int h = blockIdx.y;
+  const int d0 = blockIdx.x * 16;
+  const int lane = threadIdx.x, g = lane >> 4, j = lane & 15;
+  const uint16_t* wrow = w_uv + (static_cast<size_t>(h) * d_hc + d0 + j) * d_cg + 8 * g;
+  bf16x8 b[kSteps];
+#pragma unroll
+  for (int k = 0; k < kSteps; ++k) b[k] = *reinterpret_cast<const bf16x8*>(wrow + 32 * k);
+  for (int t0 = 0; t0 < T; t0 += 16) {
+    const int ta = t0 + j;  // A-operand row of this lane
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (ta < T) {
+      const uint16_t* arow = o_lat + (static_cast<size_t>(ta) * H + h) * d_cg + 8 * g;
+#pragma unroll
+      for (int k = 0; k < kSteps; ++k) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + 32 * k);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[k], acc, 0, 0, 0);
+      }
+    } else {
+      const bf16x8 z = {};
+#pragma unroll
+      for (int k = 0; k < kSteps; ++k) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(z, b[k], acc, 0, 0, 0);
+    }
+    // D layout: lane holds rows t0 + 4g + i, column d0 + j.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 4 * g + i;
+      if (t < T) out[(static_cast<size_t>(t) * H + h) * d_hc + d0 + j] = f32_to_bf16(acc[i]);
+    }
+  }
+}
+
+// ---------------------------------------------------------------- absorb
+// One workgroup (4 waves) per (head h, 64 latent columns c0..c0+63).  The
+// [d_hc x 64] slice of W_UK[h] is staged in LDS (rows padded to 144 B) and read
+// back transposed with ds_read_b64_tr_b16, which hands each lane 4 consecutive d
+// of one column c -- the K-contiguous B operand the MFMA needs.  Wave w owns
+// columns c0 + 16w .. +15; A operand = q_c[t][h][d], 16 bytes per lane.
+constexpr int kAbsCols = 64;
+constexpr int kAbsRowBytes = kAbsCols * 2 + 16;
+
+template <int kSteps>  // d_hc / 32
+__global__ void __launch_bounds__(256)
+absorb_mfma_kernel(const uint16_t* __restrict__ q_c, const uint16_t* __restrict__ w_uk,
+                   uint16_t* __restrict__ q_abs, int T, int H, int d_cg) {
+  constexpr int d_hc = kSteps * 32;
+  __shared__ __attribute__((aligned(16))) char tile[d_hc * kAbsRowBytes];
+  const int h = blockIdx.y;
+  const int c0 = blockIdx.x * kAbsCols;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, j = lane & 15;
+  // Stage the tile: thread -> (row d = tid/8 + 32r, chunk tid%8 of 8 columns).
+  const uint16_t* wsrc = w_uk + static_cast<size_t>(h) * d_hc * d_cg + c0;
+#pragma unroll
+  for (int r = 0; r < d_hc / 32; ++r) {
+    const int d = tid / 8 + 32 * r, ch = tid % 8;
+    *reinterpret_cast<bf16x8*>(tile + d * kAbsRowBytes + ch * 16) =
+        *reinterpret_cast<const bf16x8*>(wsrc + static_cast<size_t>(d) * d_cg + ch * 8);
+  }
+  __syncthreads();
+  // B fragments: K-step k covers d = 32k + 8g + {0..3} (first read) and {4..7} (second).
+  const uint32_t tile_base = static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)tile));
+  const int col = 16 * wave + 4 * (j & 3);
+  bf16x8 b[kSteps];
+#pragma unroll
+  for (int k = 0; k < kSteps; ++k) {
+    const int d = 32 * k + 8 * g + (j >> 2);
+    const uint32_t a1 = tile_base + d * kAbsRowBytes + col * 2;
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(uintptr_t)(a1));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4_t*)(uintptr_t)(a1 + 4 * kAbsRowBytes));
+    b[k] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+  const int cout = c0 + 16 * wave + j;
+  for (int t0 = 0; t0 < T; t0 += 16) {
+    const int ta = t0 + j;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    bf16x8 a[kSteps];
+    if (ta < T) {
+      const uint16_t* arow = q_c + (static_cast<size_t>(ta) * H + h) * d_hc + 8 * g;
+#pragma unroll
+      for (int k = 0; k < kSteps; ++k) a[k] = *reinterpret_cast<const bf16x8*>(arow + 32 * k);
+    } else {
+#pragma unroll
+      for (int k = 0; k < kSteps; ++k) a[k] = bf16x8{};
+    }
+#pragma unroll
+    for (int k = 0; k < kSteps; ++k) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[k], b[k], acc, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 4 * g + i;
+      if (t < T) q_abs[(static_cast<size_t>(t) * H + h) * d_cg + cout] = f32_to_bf16(acc[i]);
+    }
+  }
+}
+
+}  // namespace
+
+bool up_v_mfma_supported(int d_hc, int d_cg, bool bf16) {
+  return bf16 && d_hc % 16 == 0 && (d_cg == 256 || d_cg == 512);
+}
+
+bool absorb_mfma_supported(int d_hc, int d_cg, bool bf16) {
+  return bf16 && d_hc == 128 && d_cg % kAbsCols == 0;
+}
+
+hipError_t launch_up_v_mfma(const void* o_lat, const void* w_uv, void* out, int T, int H, int d_hc,
+                            int d_cg, hipStream_t s) {
+  const dim3 grid(d_hc / 16, H);
+  const auto* o = static_cast<const uint16_t*>(o_lat);
+  const auto* wt = static_cast<const uint16_t*>(w_uv);
+  auto* dst = static_cast<uint16_t*>(out);
+  if (d_cg == 512)
+    up_v_mfma_kernel<16><<<grid, 64, 0, s>>>(o, wt, dst, T, H, d_hc);
+  else
+    up_v_mfma_kernel<8><<<grid, 64, 0, s>>>(o, wt, dst, T, H, d_hc);
+  return hipGetLastError();
+}
+
+hipError_t launch_absorb_mfma(const void* q_c, const void* w_uk, void* q_abs, int T, int H,
+                              int d_hc, int d_cg, hipStream_t s) {
+  (void)d_hc;
+  const dim3 grid(d_cg / kAbsCols, H);
+  absorb_mfma_kernel<4><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(q_c),
+                                             static_cast<const uint16_t*>(w_uk),
+                                             static_cast<uint16_t*>(q_abs), T, H, d_cg);
+  return hipGetLastError();
+}
+
+}  // namespace mla

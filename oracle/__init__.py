@@ -4,6 +4,7 @@ Only the tests, the smoke entry and the bench's CPU-baseline leg use it; the
 product library never does.
 """
 from .mla_oracle import (  # noqa: F401
+    absorb_reference,
     absorbed_scores,
     default_scale,
     latent_row_bytes,
@@ -17,4 +18,5 @@ from .mla_oracle import (  # noqa: F401
     rope_rotate,
     softmax_rows,
     staged_tile_bytes,
+    up_v_reference,
 )

@@ -228,6 +228,20 @@ def mla_decode(q_c, q_r, latents, w_uk, w_uv, cu_q, *, groups=1, d_c=None,
     return {"out": out, "o_latent": o_lat, "lse": lse}
 
 
+def absorb_reference(q_c, w_uk):
+    """q_abs[t,h,:] = q_c[t,h,:] @ W_UK[h]  (P3 §4 path B, first product), float64."""
+    q_c = np.asarray(q_c, np.float64)
+    w_uk = np.asarray(w_uk, np.float64)
+    return np.einsum("thd,hdc->thc", q_c, w_uk)
+
+
+def up_v_reference(o_latent, w_uv):
+    """out[t,h,:] = W_UV[h] @ o_latent[t,h,:]  (P2 §2.4 up-projection), float64."""
+    o_latent = np.asarray(o_latent, np.float64)
+    w_uv = np.asarray(w_uv, np.float64)
+    return np.einsum("hdc,thc->thd", w_uv, o_latent)
+
+
 def softmax_rows(q_c, q_r, latent, w_uk_h, pos, *, rope_base=None, scale=None, causal=True,
                  group_cols=None):
     """Softmax probabilities of one (sequence, head, query) row, float64 [n_visible]."""

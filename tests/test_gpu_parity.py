@@ -190,3 +190,35 @@ def test_zero_queries_is_a_no_op():
     w_uk = d.w_uk
     q_abs = mla.absorb_q(empty, w_uk)
     assert q_abs.shape == (0, 16, 512)
+
+
+@pytest.mark.parametrize("T", [1, 16, 37, 96])
+@pytest.mark.parametrize("d_cg", [512, 256])
+def test_projections_against_reference(T, d_cg):
+    """mla_absorb_q and mla_up_v alone, on the MFMA shapes and a ragged row count."""
+    rng = np.random.default_rng(T + d_cg)
+    H, d_hc = 128, 128
+    q_c = wl.round_bf16(rng.standard_normal((T, H, d_hc)).astype(np.float32))
+    w = wl.round_bf16((rng.standard_normal((H, d_hc, d_cg)) / np.sqrt(d_cg)).astype(np.float32))
+    o = wl.round_bf16(rng.standard_normal((T, H, d_cg)).astype(np.float32))
+    dev = lambda x: torch.from_numpy(x).to("cuda").to(torch.bfloat16)
+    q_abs = mla.absorb_q(dev(q_c), dev(w))
+    out = mla.up_v(dev(o), dev(w))
+    torch.cuda.synchronize()
+    assert_parity(_f64(q_abs), om.absorb_reference(q_c, w), what="q_abs")
+    assert_parity(_f64(out), om.up_v_reference(o, w), what="up_v")
+
+
+@pytest.mark.parametrize("case", ["dsv3_small", "ragged_small", "long_small"])
+def test_mfma_decode_matches_generic_decode(case, monkeypatch):
+    """Both decode kernels on the same inputs: each within tolerance of the oracle and of each other."""
+    cfg = SMALL_CASES[case]
+    w = wl.make_workload(cfg)
+    outs = {}
+    for kind in ("mfma", "generic"):
+        monkeypatch.setenv("MLA_KV_DECODE_KERNEL", kind)
+        outs[kind] = _f64(run_step(w, num_splits=3).out)
+    ref = oracle_for(w)["out"]
+    assert_parity(outs["mfma"], ref, what="mfma")
+    assert_parity(outs["generic"], ref, what="generic")
+    assert_parity(outs["mfma"], outs["generic"], what="mfma vs generic")

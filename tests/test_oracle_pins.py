@@ -322,3 +322,22 @@ def test_planted_mistakes_are_caught(kind):
                                groups=1, rope_base=10000.0)
     bf_out, _ = _brute_force(p, rope_base=10000.0)
     assert np.max(np.abs(bad["out"] - bf_out)) > 1e-6 * np.max(np.abs(bf_out))
+
+
+def test_projection_references_match_scalar_sums():
+    rng = np.random.default_rng(43)
+    q = rng.standard_normal((3, 2, 5))
+    w = rng.standard_normal((2, 5, 7))
+    qa = om.absorb_reference(q, w)
+    o = rng.standard_normal((3, 2, 7))
+    ov = om.up_v_reference(o, w)
+    for t in range(3):
+        for h in range(2):
+            for c in range(7):
+                assert abs(qa[t, h, c] - sum(q[t, h, d] * w[h, d, c] for d in range(5))) < 1e-12
+            for d in range(5):
+                assert abs(ov[t, h, d] - sum(w[h, d, c] * o[t, h, c] for c in range(7))) < 1e-12
+    # the absorbed query against the latent reproduces the naive content score (P3 section 4)
+    c = rng.standard_normal((4, 7))
+    naive = om.naive_scores(q[1, 1], np.zeros(2), c, np.zeros((4, 2)), w[1], 1.0)
+    assert np.allclose(c @ qa[1, 1], naive, rtol=1e-12, atol=1e-12)
