@@ -1,4 +1,7 @@
 // Split-KV absorbed-MLA decode on bf16 MFMA (gfx950), 128 query rows per workgroup.
+// Instantiated for one latent group (MLA: every head sees the 512-d latent) and for
+// two groups (grouped latent attention, www.hotelren.com/news/5324130 §1: heads
+// 0-63 see latent columns 0-255, heads 64-127 columns 256-511, all share k_R).
 //
 // Computes, for one query token t and one split of its sequence's pages, the
 // softmax-normalised latent output and log-sum-exp of
@@ -45,7 +48,12 @@ constexpr int kRBytes = kTok * kDr * 2;  // 8 KB RoPE part
 constexpr int kStageBytes = kCBytes + kRBytes;
 constexpr int kQrOff = 2 * kStageBytes;   // rotated q_R of all heads lives after the two stages
 constexpr int kLdsBytes = kQrOff + kHeads * kDr * 2;
-constexpr int kQSteps = kDc / 32;          // 16 latent K-steps of 32 dims (+2 RoPE steps)
+template <int G> struct Shape {
+  static constexpr int kDcg = kDc / G;        // latent columns seen by one head
+  static constexpr int kQSteps = kDcg / 32;   // latent K-steps of 32 dims (+2 RoPE steps)
+  static constexpr int kColBlocks = kDcg / 16;  // 16-column output tiles
+  static constexpr int kWavesPerGroup = kWaves / G;
+};
 static_assert(kLdsBytes <= 160 * 1024, "stages + q_R must fit the 160 KB LDS of a gfx950 CU");
 
 // Swizzles (16-byte chunk index XOR).  Latent part: token t's chunk c sits at slot
@@ -121,10 +129,12 @@ __device__ __forceinline__ void load_page(uint32_t smem_base, int stage, const c
 
 constexpr int kRing = 4;  // LDS fragments in flight per wave
 
-// Latent score-step fragment st = mb * 16 + k: A operand of S^T for tokens 16mb + j,
-// latent dims 32k + 8g .. +7.  sb[i] = stage base + per-lane base for k % 4 == i.
+// Latent score-step fragment st = k * 4 + mb: A operand of S^T for tokens 16mb + j,
+// latent dims 32k + 8g .. +7.  The four token blocks alternate so that consecutive
+// MFMAs accumulate into different registers.  sb[i] = stage base + per-lane base
+// for k % 4 == i.
 __device__ __forceinline__ bf16x8 score_frag(const uint32_t* sb, int st) {
-  const int mb = st / kQSteps, k = st % kQSteps;
+  const int mb = st % 4, k = st / 4;  // k < kQSteps of the instantiation
   return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(sb[k & 3] + 16384 * mb +
                                                                       256 * (k >> 2));
 }
@@ -132,29 +142,35 @@ __device__ __forceinline__ bf16x8 score_frag(const uint32_t* sb, int st) {
 // Output-step fragment st = ks * 32 + nb: A operand of O^T for columns 16nb + j,
 // tokens 32ks + 4g + {0..3} and 32ks + 16 + 4g + {0..3}, via two transposing reads.
 // ob[i] = stage base + per-lane base for nb % 8 == i.
+template <int kColBlocks>
 __device__ __forceinline__ bf16x8 out_frag(const uint32_t* ob, int st) {
-  const int ks = st / 32, nb = st % 32;
+  const int ks = st / kColBlocks, nb = st % kColBlocks;
   const uint32_t a1 = ob[nb & 7] + 32768 * ks + 256 * (nb >> 3);
   const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lds_bf16x4(a1));
   const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lds_bf16x4(a1 + 16384));
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+template <int G>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_mfma_kernel(DecodeArgs a) {
+  using Sh = Shape<G>;
+  constexpr int kDcg = Sh::kDcg, kQSteps = Sh::kQSteps, kColBlocks = Sh::kColBlocks;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int t = blockIdx.x, split = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
   const int g = lane >> 4, j = lane & 15;   // 16-lane group, position in group
   const int head = wave * 16 + j;
+  const int grp = wave / Sh::kWavesPerGroup;             // latent group of this wave
+  const uint32_t grp_off = static_cast<uint32_t>(grp) * kDcg * 2;  // its columns in a token row
   const int S = a.num_splits;
   const QueryWork w = query_work(a.cu_q, a.seq_lens, a.batch, t, split, S, kTok, a.max_pages,
                                  a.causal);
   const size_t row = (static_cast<size_t>(t) * kHeads + head) * S + split;
-  float* o_out = a.o_part + row * kDc;
+  float* o_out = a.o_part + row * kDcg;
   if (w.k0 >= w.k1) {  // empty split: O = 0, LSE = -inf
-    for (int c = g * 4; c < kDc; c += 16)
+    for (int c = g * 4; c < kDcg; c += 16)
       *reinterpret_cast<f32x4*>(o_out + c) = f32x4{0.f, 0.f, 0.f, 0.f};
     if (g == 0) a.lse_part[row] = -INFINITY;
     return;
@@ -183,10 +199,10 @@ decode_mfma_kernel(DecodeArgs a) {
   // Q fragments: B operand of S^T = C . Q^T.  K-step k covers latent dims 32k .. 32k+31;
   // this lane holds dims 32k + 8g .. +7 of its head.  The RoPE half of the query is
   // rotated here in fp32 and parked, as bf16, in LDS (read back twice per page).
-  bf16x8 q[kQSteps];
+  bf16x8 q[kQSteps];  // latent part of the query
   {
     const uint16_t* qa = static_cast<const uint16_t*>(a.q_abs) +
-                         (static_cast<size_t>(t) * kHeads + head) * kDc + g * 8;
+                         (static_cast<size_t>(t) * kHeads + head) * kDcg + g * 8;
 #pragma unroll
     for (int k = 0; k < kQSteps; ++k) q[k] = *reinterpret_cast<const bf16x8*>(qa + 32 * k);
     const uint16_t* qr = static_cast<const uint16_t*>(a.q_r) +
@@ -217,9 +233,9 @@ decode_mfma_kernel(DecodeArgs a) {
   const float scale_log2 = a.scale * kLog2e;
   float m_run = -INFINITY;   // running max of scaled scores (log2 units), same in the 4 lanes of a head
   float l_run = 0.f;         // this lane's share of the running sum
-  f32x4 o[32];               // O^T block nb: columns 16nb + 4g .. +3 of this lane's head
+  f32x4 o[kColBlocks];       // O^T block nb: columns 16nb + 4g .. +3 of this lane's head
 #pragma unroll
-  for (int nb = 0; nb < 32; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int nb = 0; nb < kColBlocks; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Per-lane LDS offsets inside a stage.  The swizzle keys depend only on the low
   // four bits of the token index, so every address splits into a per-lane base
@@ -249,7 +265,7 @@ decode_mfma_kernel(DecodeArgs a) {
     {
       const int sw = swz_c(lj);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sb[i] = st_base + lj * 1024 + (((4 * i + lg) ^ sw) << 4);
+      for (int i = 0; i < 4; ++i) sb[i] = st_base + grp_off + lj * 1024 + (((4 * i + lg) ^ sw) << 4);
     }
 
     // ---- scores S^T for tokens mb*16 .. mb*16+15 of the page.  RoPE part first
@@ -277,7 +293,7 @@ decode_mfma_kernel(DecodeArgs a) {
       }
     }
     {
-      constexpr int kSteps = 4 * kQSteps;
+      constexpr int kSteps = 4 * kQSteps;  // (mb, k) steps
       bf16x8 ring[kRing];
 #pragma unroll
       for (int st = 0; st < kRing; ++st) ring[st] = score_frag(sb, st);
@@ -285,7 +301,7 @@ decode_mfma_kernel(DecodeArgs a) {
       for (int st = 0; st < kSteps; ++st) {
         const bf16x8 c = ring[st % kRing];
         if (st + kRing < kSteps) ring[st % kRing] = score_frag(sb, st + kRing);
-        const int mb = st / kQSteps, k = st % kQSteps;
+        const int mb = st % 4, k = st / 4;
         s[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c, q[k], s[mb], 0, 0, 0);
       }
     }
@@ -318,7 +334,7 @@ decode_mfma_kernel(DecodeArgs a) {
     m_run = m_new;
     if (__any(alpha != 1.f)) {
 #pragma unroll
-      for (int nb = 0; nb < 32; ++nb) o[nb] *= alpha;
+      for (int nb = 0; nb < kColBlocks; ++nb) o[nb] *= alpha;
     }
 
     // ---- P^T operands: K-step ks covers tokens 32ks + 4g + {0..3} and 32ks + 16 + 4g + {0..3}
@@ -333,20 +349,20 @@ decode_mfma_kernel(DecodeArgs a) {
       const int tok = 4 * lg + (lj >> 2);
       const int swo = swz_c(tok);
       const int colb = 4 * (lj & 3);
-      const uint32_t rowb = st_base + tok * 1024 + (colb & 7) * 2;
+      const uint32_t rowb = st_base + grp_off + tok * 1024 + (colb & 7) * 2;
 #pragma unroll
       for (int i = 0; i < 8; ++i) ob[i] = rowb + (((2 * i + (colb >> 3)) ^ swo) << 4);
     }
     {
-      constexpr int kSteps = 64;
+      constexpr int kSteps = 2 * kColBlocks;
       bf16x8 ring[kRing];
 #pragma unroll
-      for (int st = 0; st < kRing; ++st) ring[st] = out_frag(ob, st);
+      for (int st = 0; st < kRing; ++st) ring[st] = out_frag<kColBlocks>(ob, st);
 #pragma unroll
       for (int st = 0; st < kSteps; ++st) {
         const bf16x8 ct = ring[st % kRing];
-        if (st + kRing < kSteps) ring[st % kRing] = out_frag(ob, st + kRing);
-        const int ks = st / 32, nb = st % 32;
+        if (st + kRing < kSteps) ring[st % kRing] = out_frag<kColBlocks>(ob, st + kRing);
+        const int ks = st / kColBlocks, nb = st % kColBlocks;
         o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ct, pb[ks], o[nb], 0, 0, 0);
       }
     }
@@ -358,7 +374,7 @@ decode_mfma_kernel(DecodeArgs a) {
   l_tot += __shfl_xor(l_tot, 32, 64);
   const float inv = 1.f / l_tot;
 #pragma unroll
-  for (int nb = 0; nb < 32; ++nb)
+  for (int nb = 0; nb < kColBlocks; ++nb)
     *reinterpret_cast<f32x4*>(o_out + nb * 16 + 4 * g) = o[nb] * inv;
   if (g == 0) a.lse_part[row] = (m_run + __log2f(l_tot)) * kLn2;
 }
@@ -366,21 +382,26 @@ decode_mfma_kernel(DecodeArgs a) {
 }  // namespace
 
 bool decode_mfma_supported(const DecodeArgs& a, bool bf16) {
-  return bf16 && a.heads == kHeads && a.groups == 1 && a.d_c == kDc && a.d_R == kDr &&
-         a.page_size == kTok;
+  return bf16 && a.heads == kHeads && (a.groups == 1 || a.groups == 2) && a.d_c == kDc &&
+         a.d_R == kDr && a.page_size == kTok;
 }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s) {
+template <int G>
+hipError_t launch_decode_mfma_g(const DecodeArgs& a, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_mfma_kernel),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_mfma_kernel<G>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const dim3 grid(a.total_q, a.num_splits);
-  decode_mfma_kernel<<<grid, kThreads, kLdsBytes, s>>>(a);
+  decode_mfma_kernel<G><<<grid, kThreads, kLdsBytes, s>>>(a);
   return hipGetLastError();
+}
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s) {
+  return a.groups == 2 ? launch_decode_mfma_g<2>(a, s) : launch_decode_mfma_g<1>(a, s);
 }
 
 }  // namespace mla
