@@ -122,11 +122,15 @@ int mla_rope_table(float* cos_out, float* sin_out, int max_pos, int d_R, double 
  * Outputs (caller-allocated workspace, float32)
  *   o_part      [T, H, num_splits, d_cg]: split s's softmax-normalised output
  *   lse_part    [T, H, num_splits]: split s's natural-log log-sum-exp of the
- *               scaled scores; -INFINITY (with o_part = 0) for an empty split
- * Split plan: sequence b has n_b = ceil(seq_lens[b] / page_size) pages; split s
- * covers pages [s*c_b, (s+1)*c_b) with c_b = ceil(n_b / num_splits).  With
- * causal != 0 query i sees keys j <= its position; otherwise all keys.
- * softmax_scale <= 0 selects 1/sqrt(d_hc + d_R).
+ *               scaled scores; -INFINITY for an empty split, whose o_part rows
+ *               are then left unwritten (mla_combine never reads them)
+ * Split plan: sequence b has n_b = ceil(seq_lens[b] / page_size) pages, cut into
+ * chunks of c_b pages: c_b = pages_per_split if pages_per_split > 0, else
+ * ceil(n_b / num_splits).  Split s covers pages [s*c_b, (s+1)*c_b); the last
+ * split (s = num_splits - 1) runs to the end of the sequence, so no key is ever
+ * dropped whatever the two numbers are.  With causal != 0 query i sees keys
+ * j <= its position; otherwise all keys.  softmax_scale <= 0 selects
+ * 1/sqrt(d_hc + d_R).
  */
 int mla_decode_paged(const void* q_abs, const void* q_r, const void* kv_cache,
                      const int32_t* page_table, const int32_t* seq_lens, const int32_t* cu_q,
@@ -134,7 +138,8 @@ int mla_decode_paged(const void* q_abs, const void* q_r, const void* kv_cache,
                      float* o_part, float* lse_part,
                      int batch, int total_q, int max_pages_per_seq, int num_pool_pages,
                      int heads, int groups, int d_hc, int d_c, int d_R, int page_size,
-                     int num_splits, float softmax_scale, int causal, int dtype, void* stream);
+                     int num_splits, int pages_per_split, float softmax_scale, int causal,
+                     int dtype, void* stream);
 
 /*
  * mla_combine -- merge the split partials by their log-sum-exp:

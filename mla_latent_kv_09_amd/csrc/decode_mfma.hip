@@ -165,13 +165,11 @@ decode_mfma_kernel(DecodeArgs a) {
   const int grp = wave / Sh::kWavesPerGroup;             // latent group of this wave
   const uint32_t grp_off = static_cast<uint32_t>(grp) * kDcg * 2;  // its columns in a token row
   const int S = a.num_splits;
-  const QueryWork w = query_work(a.cu_q, a.seq_lens, a.batch, t, split, S, kTok, a.max_pages,
-                                 a.causal);
+  const QueryWork w = query_work(a.cu_q, a.seq_lens, a.batch, t, split, S,
+                                 a.pages_per_split, kTok, a.max_pages, a.causal);
   const size_t row = (static_cast<size_t>(t) * kHeads + head) * S + split;
   float* o_out = a.o_part + row * kDcg;
-  if (w.k0 >= w.k1) {  // empty split: O = 0, LSE = -inf
-    for (int c = g * 4; c < kDcg; c += 16)
-      *reinterpret_cast<f32x4*>(o_out + c) = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (w.k0 >= w.k1) {  // empty split: only the LSE is written
     if (g == 0) a.lse_part[row] = -INFINITY;
     return;
   }

@@ -108,12 +108,11 @@ __global__ void __launch_bounds__(kThreads) decode_generic_kernel(DecodeArgs a) 
   const int H = a.heads, S = a.num_splits, d_cg = a.d_c / a.groups, d_R = a.d_R;
   const int width = a.d_c + a.d_R;
   const int g = h / (H / a.groups);
-  const QueryWork w = query_work(a.cu_q, a.seq_lens, a.batch, t, split, S, a.page_size,
-                                 a.max_pages, a.causal);
+  const QueryWork w = query_work(a.cu_q, a.seq_lens, a.batch, t, split, S,
+                                 a.pages_per_split, a.page_size, a.max_pages, a.causal);
   const size_t row = (static_cast<size_t>(t) * H + h) * S + split;
   float* o_out = a.o_part + row * d_cg;
-  if (w.k0 >= w.k1) {
-    for (int c = tid; c < d_cg; c += kThreads) o_out[c] = 0.f;
+  if (w.k0 >= w.k1) {  // empty split: only the LSE is written
     if (tid == 0) a.lse_part[row] = -INFINITY;
     return;
   }

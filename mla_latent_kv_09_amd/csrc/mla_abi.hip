@@ -99,12 +99,12 @@ int mla_decode_paged(const void* q_abs, const void* q_r, const void* kv_cache,
                      const float* rope_cos, const float* rope_sin, int rope_max_pos,
                      float* o_part, float* lse_part, int batch, int total_q, int max_pages_per_seq,
                      int num_pool_pages, int heads, int groups, int d_hc, int d_c, int d_R,
-                     int page_size, int num_splits, float softmax_scale, int causal, int dtype,
-                     void* stream) {
+                     int page_size, int num_splits, int pages_per_split, float softmax_scale,
+                     int causal, int dtype, void* stream) {
   int st = check_dtype(dtype);
   if (st != MLA_OK) return st;
   if (total_q < 0 || batch <= 0 || d_hc <= 0 || d_R <= 0 || (d_R & 1) || num_splits <= 0 ||
-      max_pages_per_seq <= 0 || num_pool_pages <= 0 || page_size <= 0)
+      pages_per_split < 0 || max_pages_per_seq <= 0 || num_pool_pages <= 0 || page_size <= 0)
     return MLA_ERR_DIM;
   if ((st = check_heads(heads, groups, d_c)) != MLA_OK) return st;
   if (page_size != MLA_PAGE_SIZE || num_splits > kMaxSplits) return MLA_ERR_UNSUPPORTED;
@@ -141,6 +141,7 @@ int mla_decode_paged(const void* q_abs, const void* q_r, const void* kv_cache,
   a.d_R = d_R;
   a.page_size = page_size;
   a.num_splits = num_splits;
+  a.pages_per_split = pages_per_split;
   a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(d_hc + d_R));
   a.causal = causal != 0;
   const bool bf16 = dtype == MLA_DTYPE_BF16;

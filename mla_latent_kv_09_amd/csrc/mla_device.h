@@ -48,7 +48,8 @@ struct QueryWork {
 
 __device__ __forceinline__ QueryWork query_work(const int32_t* __restrict__ cu_q,
                                                 const int32_t* __restrict__ seq_lens, int batch,
-                                                int t, int split, int num_splits, int page_size,
+                                                int t, int split, int num_splits,
+                                                int pages_per_split, int page_size,
                                                 int max_pages, int causal) {
   QueryWork w;
   w.b = find_seq(cu_q, batch, t);
@@ -62,9 +63,10 @@ __device__ __forceinline__ QueryWork query_work(const int32_t* __restrict__ cu_q
   int n_vis = causal ? min(L, w.pos + 1) : L;
   if (n_vis < 0) n_vis = 0;
   const int n_pages = (L + page_size - 1) / page_size;
-  const int per_split = (n_pages + num_splits - 1) / num_splits;  // pages per split
+  const int per_split = pages_per_split > 0 ? pages_per_split
+                                            : (n_pages + num_splits - 1) / num_splits;
   w.k0 = split * per_split * page_size;
-  w.k1 = min((split + 1) * per_split * page_size, n_vis);
+  w.k1 = split == num_splits - 1 ? n_vis : min((split + 1) * per_split * page_size, n_vis);
   return w;
 }
 

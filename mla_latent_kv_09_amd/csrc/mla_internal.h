@@ -20,7 +20,7 @@ struct DecodeArgs {
   float* o_part;
   float* lse_part;
   int batch, total_q, max_pages, num_pool_pages;
-  int heads, groups, d_c, d_R, page_size, num_splits;
+  int heads, groups, d_c, d_R, page_size, num_splits, pages_per_split;
   float scale;
   int causal;
 };

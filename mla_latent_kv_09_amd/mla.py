@@ -47,7 +47,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     P, I, F, D = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_double
     lib.mla_absorb_q.argtypes = [P, P, P, I, I, I, I, I, I, P]
     lib.mla_rope_table.argtypes = [P, P, I, I, D, P]
-    lib.mla_decode_paged.argtypes = ([P] * 8 + [I] + [P] * 2 + [I] * 11 + [F, I, I, P])
+    lib.mla_decode_paged.argtypes = ([P] * 8 + [I] + [P] * 2 + [I] * 12 + [F, I, I, P])
     lib.mla_combine.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
     lib.mla_up_v.argtypes = [P, P, P, I, I, I, I, I, I, P]
     lib.mla_decode_workspace_bytes.argtypes = [I, I, I, I, I]
@@ -130,7 +130,7 @@ def workspace(total_q: int, heads: int, d_cg: int, num_splits: int, device="cuda
 
 def decode_paged(q_abs, q_r, kv_cache, page_table, seq_lens, cu_q, o_part, lse_part, *,
                  d_hc: int, groups: int = 1, rope: Optional[tuple] = None, softmax_scale: float = 0.0,
-                 causal: bool = True, stream=None) -> None:
+                 causal: bool = True, pages_per_split: int = 0, stream=None) -> None:
     """Split-KV attention over the paged cache into (o_part, lse_part)."""
     T, H, d_cg = q_abs.shape
     d_R = q_r.shape[2]
@@ -155,7 +155,8 @@ def decode_paged(q_abs, q_r, kv_cache, page_table, seq_lens, cu_q, o_part, lse_p
     _check("mla_decode_paged", load().mla_decode_paged(
         _ptr(q_abs), _ptr(q_r), _ptr(kv_cache), _ptr(page_table), _ptr(seq_lens), _ptr(cu_q),
         _ptr(cos), _ptr(sin), rope_max_pos, _ptr(o_part), _ptr(lse_part),
-        B, T, max_pages, P, H, groups, d_hc, d_cg * groups, d_R, ps, S, float(softmax_scale),
+        B, T, max_pages, P, H, groups, d_hc, d_cg * groups, d_R, ps, S, int(pages_per_split),
+        float(softmax_scale),
         int(bool(causal)), _dtype_code(q_abs), _stream(stream)))
 
 
@@ -186,11 +187,18 @@ def up_v(o_latent, w_uv, out=None, *, groups: int = 1, stream=None):
     return out
 
 
-def default_num_splits(seq_lens_host, total_q: int, cu_count: int = 256) -> int:
-    """Splits per sequence so that total_q x splits workgroups cover the CUs about twice."""
-    max_pages = max(1, max(int(math.ceil(int(L) / PAGE_SIZE)) for L in seq_lens_host))
-    want = max(1, math.ceil(2 * cu_count / max(1, total_q)))
-    return int(min(want, max_pages, 256))
+def split_plan(seq_lens_host, q_lens_host, cu_count: int = 256):
+    """(num_splits, pages_per_split) for a batch: about one workgroup per CU when
+    all sequences have about the same length, four per CU when they differ (long
+    sequences are cut finer so the dispatcher can balance), never fewer than 4
+    pages per split (a split pays a fixed prologue and epilogue)."""
+    pages = [max(1, math.ceil(int(L) / PAGE_SIZE)) for L in seq_lens_host]
+    q = [int(x) for x in q_lens_host]
+    total = sum(p * n for p, n in zip(pages, q))
+    ragged = max(pages) > 1.25 * min(pages)
+    pps = max(4, math.ceil(total / (cu_count * (4 if ragged else 1))))
+    num_splits = max(1, min(256, max(math.ceil(p / pps) for p in pages)))
+    return num_splits, pps
 
 
 class DecodeStep:
@@ -204,8 +212,11 @@ class DecodeStep:
         T, H, d_hc = q_c.shape
         d_cg = w_uk.shape[2]
         if num_splits is None:
-            num_splits = default_num_splits(seq_lens_host if seq_lens_host is not None
-                                            else seq_lens.cpu().tolist(), T)
+            lens = seq_lens_host if seq_lens_host is not None else seq_lens.cpu().tolist()
+            cu = cu_q.cpu().tolist()
+            num_splits, self.pages_per_split = split_plan(lens, [b - a for a, b in zip(cu, cu[1:])])
+        else:
+            self.pages_per_split = 0
         self.num_splits = num_splits
         dev = q_c.device
         self.q_abs = torch.empty((T, H, d_cg), dtype=q_c.dtype, device=dev)
@@ -221,7 +232,7 @@ class DecodeStep:
     def attend(self, stream=None):
         decode_paged(self.q_abs, self.q_r, self.kv, self.page_table, self.seq_lens, self.cu_q,
                      self.o_part, self.lse_part, d_hc=self.d_hc, groups=self.groups, rope=self.rope,
-                     causal=self.causal, stream=stream)
+                     causal=self.causal, pages_per_split=self.pages_per_split, stream=stream)
 
     def merge(self, stream=None):
         combine(self.o_part, self.lse_part, self.o_latent, self.lse, stream=stream)

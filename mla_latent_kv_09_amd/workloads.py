@@ -8,8 +8,9 @@ without sharing any code of the method.
 Input recipe (the same for every consumer):
 
 * Every tensor has its own numpy ``PCG64`` stream, seeded by
-  ``SeedSequence([seed, tensor_index])``, so adding a tensor never shifts the
-  draws of another one.
+  ``SeedSequence([seed, tensor_index])`` (the latent rows of sequence b by
+  ``SeedSequence([seed, tensor_index, b])``), so adding a tensor or a sequence
+  never shifts the draws of another one, and sequences can be drawn in parallel.
 * Activations q_c, q_R, c_KV and k_R are standard normal.  Weights W_UK and W_UV
   are normal with standard deviation ``w_std`` (1/sqrt(d_c) unless stated).
 * Draws are float32 and then rounded to the storage dtype: bf16 with
@@ -26,8 +27,11 @@ Input recipe (the same for every consumer):
 """
 from __future__ import annotations
 
+import concurrent.futures as cf
 import dataclasses
 import math
+import os
+from collections.abc import Sequence
 from dataclasses import dataclass, field
 from typing import Optional
 
@@ -41,8 +45,9 @@ _STREAMS = {
 }
 
 
-def _rng(seed: int, name: str) -> np.random.Generator:
-    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([int(seed), _STREAMS[name]])))
+def _rng(seed: int, name: str, *sub: int) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(
+        np.random.SeedSequence([int(seed), _STREAMS[name], *map(int, sub)])))
 
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -134,6 +139,26 @@ CONFIGS = {
 CONFIG_ORDER = ["tiny_fp32", "dsv3_b16_l4096", "long_b16_l65536", "ragged_b64", "gla2_b32_l16384"]
 
 
+class PagedRows(Sequence):
+    """Per-sequence logical latent rows [L_b, d_c + d_R] (float32), read back out of
+    the paged pool on access, so no second copy of a multi-GB cache is kept."""
+
+    def __init__(self, w: "Workload"):
+        self._w = w
+
+    def __len__(self) -> int:
+        return len(self._w.seq_lens)
+
+    def __getitem__(self, b):
+        if isinstance(b, slice):
+            return [self[i] for i in range(*b.indices(len(self)))]
+        if b < 0:
+            b += len(self)
+        if not 0 <= b < len(self):
+            raise IndexError(b)
+        return gather_sequence(self._w, b)
+
+
 @dataclass
 class Workload:
     """One generated decode step: host arrays shared by the device path and the oracle."""
@@ -144,7 +169,7 @@ class Workload:
     cu_q: np.ndarray            # int32 [B+1]
     q_c: np.ndarray             # float32 [T, H, d_hc]   (values exact in the storage dtype)
     q_r: np.ndarray             # float32 [T, H, d_R]
-    latents: list               # B x float32 [L_b, d_c + d_R]
+    latents: Sequence           # B x float32 [L_b, d_c + d_R] (PagedRows, or a list)
     w_uk: np.ndarray            # float32 [H, d_hc, d_c/G]
     w_uv: np.ndarray            # float32 [H, d_hc, d_c/G]
     page_table: np.ndarray      # int32 [B, max_pages]   (-1 = unused)
@@ -197,8 +222,6 @@ def make_workload(cfg: MLAConfig, *, seed: Optional[int] = None, nan_fill: bool 
 
     q_c = rnd(_normal(_rng(seed, "q_c"), (T, H, cfg.d_hc)))
     q_r = rnd(_normal(_rng(seed, "q_r"), (T, H, cfg.d_R)))
-    lat_rng = _rng(seed, "latent")
-    latents = [rnd(_normal(lat_rng, (int(L), cfg.row))) for L in seq_lens]
     w_uk = rnd(_normal(_rng(seed, "w_uk"), (H, cfg.d_hc, cfg.d_cg), cfg.weight_std))
     w_uv = rnd(_normal(_rng(seed, "w_uv"), (H, cfg.d_hc, cfg.d_cg), cfg.weight_std))
 
@@ -208,23 +231,30 @@ def make_workload(cfg: MLAConfig, *, seed: Optional[int] = None, nan_fill: bool 
     perm = np.arange(P) if cfg.identity_pages else _rng(seed, "pages").permutation(P)
     max_pages = max(pages_per_seq) if pages_per_seq else 0
     page_table = np.full((B, max(max_pages, 1)), -1, dtype=np.int32)
+    offsets = np.concatenate([[0], np.cumsum(pages_per_seq)]).astype(np.int64)
+    for b in range(B):
+        page_table[b, :pages_per_seq[b]] = perm[offsets[b]:offsets[b + 1]]
 
     if cfg.dtype == "bf16":
         pool = np.full((P, ps, cfg.row), BF16_NAN_BITS if nan_fill else 0, dtype=np.uint16)
     else:
         pool = np.full((P, ps, cfg.row), np.nan if nan_fill else 0.0, dtype=np.float32)
-    off = 0
-    for b, L in enumerate(seq_lens):
-        rows = latents[b] if cfg.dtype == "fp32" else bf16_bits(latents[b])
-        for k in range(pages_per_seq[b]):
-            phys = int(perm[off + k])
-            page_table[b, k] = phys
-            chunk = rows[k * ps:(k + 1) * ps]
-            pool[phys, :chunk.shape[0]] = chunk
-        off += pages_per_seq[b]
-    return Workload(cfg=cfg, seq_lens=seq_lens, q_lens=q_lens, cu_q=cu_q, q_c=q_c, q_r=q_r,
-                    latents=latents, w_uk=w_uk, w_uv=w_uv, page_table=page_table, pool=pool)
 
+    def fill(b: int) -> None:
+        L = int(seq_lens[b])
+        x = _normal(_rng(seed, "latent", b), (L, cfg.row))
+        rows = bf16_bits(x) if cfg.dtype == "bf16" else x
+        for k in range(pages_per_seq[b]):
+            chunk = rows[k * ps:(k + 1) * ps]
+            pool[page_table[b, k], :chunk.shape[0]] = chunk
+
+    workers = min(16, os.cpu_count() or 1, max(1, B))
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(fill, range(B)))
+    w = Workload(cfg=cfg, seq_lens=seq_lens, q_lens=q_lens, cu_q=cu_q, q_c=q_c, q_r=q_r,
+                 latents=[], w_uk=w_uk, w_uv=w_uv, page_table=page_table, pool=pool)
+    w.latents = PagedRows(w)
+    return w
 
 def gather_sequence(w: Workload, b: int) -> np.ndarray:
     """Read sequence b's rows back out of the paged pool (float32), for layout checks."""

@@ -113,12 +113,12 @@ def test_rope_table_validation(lib):
 def _decode(lib, **kw):
     a = dict(q=A, qr=A, kv=A, pt=A, sl=A, cu=A, cos=None, sin=None, rmp=0, op=A, lp=A,
              B=16, T=16, maxp=64, pool=1024, H=128, G=1, d_hc=128, d_c=512, d_R=64, ps=64, S=16,
-             scale=0.0, causal=1, dt=0)
+             pps=0, scale=0.0, causal=1, dt=0)
     a.update(kw)
     return lib.mla_decode_paged(a["q"], a["qr"], a["kv"], a["pt"], a["sl"], a["cu"], a["cos"],
                                 a["sin"], a["rmp"], a["op"], a["lp"], a["B"], a["T"], a["maxp"],
                                 a["pool"], a["H"], a["G"], a["d_hc"], a["d_c"], a["d_R"], a["ps"],
-                                a["S"], a["scale"], a["causal"], a["dt"], None)
+                                a["S"], a["pps"], a["scale"], a["causal"], a["dt"], None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -127,6 +127,7 @@ def _decode(lib, **kw):
     (dict(kv=MIS), ALIGN), (dict(lp=MIS), ALIGN), (dict(cos=A, sin=MIS, rmp=10), ALIGN),
     (dict(d_R=63, kv=None), DIM), (dict(H=100, G=3, kv=None), DIM), (dict(S=0, kv=None), DIM),
     (dict(B=0, kv=None), DIM), (dict(maxp=0, kv=None), DIM), (dict(cos=A, sin=A, rmp=0), DIM),
+    (dict(pps=-1, kv=None), DIM),
     (dict(ps=16, kv=None), UNSUP), (dict(S=257, kv=None), UNSUP), (dict(d_c=4096, kv=None), UNSUP),
     (dict(dt=2), DTYPE),
     (dict(T=0, kv=None), OK),

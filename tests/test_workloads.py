@@ -39,7 +39,9 @@ def test_paged_pool_round_trip_and_nan_fill():
     assert sorted(used.tolist()) == list(range(w.num_pool_pages))          # a permutation
     for b, n in enumerate(n_pages):
         assert (w.page_table[b, n:] == -1).all()
-        assert np.array_equal(wl.gather_sequence(w, b), w.latents[b])
+        redrawn = wl.round_bf16(wl._normal(wl._rng(cfg.seed, "latent", b), (int(w.seq_lens[b]), cfg.row)))
+        assert np.array_equal(wl.gather_sequence(w, b), redrawn)
+        assert np.array_equal(w.latents[b], redrawn)
         L = int(w.seq_lens[b])
         if L % 64:
             tail = w.pool[w.page_table[b, n - 1], L % 64:]
@@ -50,7 +52,9 @@ def test_identity_pages_for_contiguous_fp32():
     w = wl.make_workload(wl.CONFIGS["tiny_fp32"])
     assert w.pool.dtype == np.float32 and w.pool.shape == (4, 64, 80)
     assert np.array_equal(w.page_table[0], np.arange(4))
-    assert np.array_equal(w.pool.reshape(256, 80), w.latents[0])
+    redrawn = wl._normal(wl._rng(0, "latent", 0), (256, 80))
+    assert np.array_equal(w.pool.reshape(256, 80), redrawn)
+    assert np.array_equal(w.latents[0], redrawn) and len(w.latents) == 1
     assert abs(w.w_uk.std() - 1 / 8) < 0.01
 
 
