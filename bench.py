@@ -5,11 +5,13 @@
 
 A step is the whole hot path over one batch of synthetic input already resident
 in HBM: mla_absorb_q -> mla_decode_paged -> mla_combine -> mla_up_v, all on the
-current HIP stream.  Before every timed step a 1 GiB buffer is rewritten so the
-L2 and the 256 MB Infinity Cache hold nothing of the step's working set (a real
-decode step reads a different layer's cache every time).  Each step is bracketed
-by HIP events, and the decode kernel by its own pair of events on the same
-stream; the reported time is the median over the K timed steps.
+current HIP stream, captured once as a HIP graph and replayed (--no-graph
+launches the four calls eagerly).  Before every timed step a 1 GiB buffer is
+rewritten so the L2 and the 256 MB Infinity Cache hold nothing of the step's
+working set (a real decode step reads a different layer's cache every time).
+Each step is bracketed by HIP events; the reported time is the median over the
+K timed steps.  Per-kernel times (and the decode kernel's time in the roofline
+object) come from a second pass of K eager steps with events between the calls.
 
 Prints one JSON line.  `value` is the algorithmic TFLOP/s of the whole step
 (attention flops of the absorbed method plus the two projections, divided by the
@@ -121,6 +123,7 @@ def main():
     ap.add_argument("--splits", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-flush", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="launch the four calls eagerly")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the decode path is built "
@@ -165,22 +168,44 @@ def main():
         one_step()
     torch.cuda.synchronize()
 
+    # Per-kernel times: the four calls issued one by one with events between them
+    # (the flush before each step keeps the GPU busy long enough for all four
+    # launches to be queued, so the events bracket kernel execution).
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
     for k in range(args.steps):
         if flush is not None:
             flush.add_(1.0)
         one_step(events[k])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-
-    step_ms = [e[0].elapsed_time(e[4]) for e in events]
     dec_ms = [e[1].elapsed_time(e[2]) for e in events]
     parts = {name: statistics.median([e[i].elapsed_time(e[i + 1]) for e in events])
              for i, name in enumerate(["absorb_q", "decode_paged", "combine", "up_v"])}
-    ms = statistics.median(step_ms)
     dec = statistics.median(dec_ms)
+
+    # Step time: the four calls captured once as a HIP graph and replayed, so the
+    # host's per-call launch cost does not sit between the kernels.
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+    ev_step = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for k in range(args.steps):
+        if flush is not None:
+            flush.add_(1.0)
+        ev_step[k][0].record(stream)
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
+        ev_step[k][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = [e[0].elapsed_time(e[1]) for e in ev_step]
+    ms = statistics.median(step_ms)
 
     att, proj, kv_bytes, w_bytes = algorithmic_work(cfg, w.seq_lens, w.q_lens)
     flops = att + proj
@@ -212,7 +237,9 @@ def main():
         "config": {"workload": cfg.name, "batch": cfg.batch, "heads": cfg.heads, "d_hc": cfg.d_hc,
                    "d_c": cfg.d_c, "d_R": cfg.d_R, "groups": cfg.groups, "page_size": cfg.page_size,
                    "seq_len": cfg.seq_len, "seq_len_range": cfg.seq_len_range,
-                   "total_q": int(w.total_q), "num_splits": S, "cache_flushed": flush is not None},
+                   "total_q": int(w.total_q), "num_splits": S,
+                   "pages_per_split": step.pages_per_split, "cache_flushed": flush is not None,
+                   "hip_graph": graph is not None},
         "latent_kv_gbps": kv_gbps, "latent_kv_frac_hbm_peak": kv_gbps / HBM_PEAK_GBPS,
         "tflops_frac_mfma_peak": tflops / peak_f, "seqs_per_s": seqs,
         "kernel_ms": parts, "wall_s_timed_region": wall,

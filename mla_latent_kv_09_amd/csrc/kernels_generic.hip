@@ -233,6 +233,59 @@ combine_kernel(const float* __restrict__ o_part, const float* __restrict__ lse_p
   if (tid == 0 && lse_out != nullptr) lse_out[r] = M == -INFINITY ? -INFINITY : M + logf(sum);
 }
 
+// One wave per (t, h) row, four rows per block, for latent widths 256 and 512:
+// each lane owns kDcg/64 consecutive-by-4 columns and streams the non-empty
+// splits' partials with 16-byte loads, four splits per iteration.
+template <typename T, int kDcg>
+__global__ void __launch_bounds__(kThreads)
+combine_vec_kernel(const float* __restrict__ o_part, const float* __restrict__ lse_part,
+                   T* __restrict__ o_lat, float* __restrict__ lse_out, int rows, int S) {
+  constexpr int kVec = kDcg / 256;  // float4 groups per lane
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  const int lane = threadIdx.x & 63;
+  const size_t r = static_cast<size_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
+  if (r >= static_cast<size_t>(rows)) return;
+  const float* lse = lse_part + r * S;
+  float mx = -INFINITY;
+  for (int s = lane; s < S; s += 64) mx = fmaxf(mx, lse[s]);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  float sum = 0.f;
+  if (mx != -INFINITY)
+    for (int s = lane; s < S; s += 64) sum += expf(lse[s] - mx);
+  sum = wave_sum(sum);
+  f32x4 acc[kVec];
+#pragma unroll
+  for (int v = 0; v < kVec; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (mx != -INFINITY) {
+    const float* base = o_part + r * S * kDcg + 4 * lane;
+    for (int s0 = 0; s0 < S; s0 += 4) {
+      float wt[4];
+      f32x4 x[4][kVec];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int s = s0 + u;
+        const float l = s < S ? lse[s] : -INFINITY;
+        wt[u] = l == -INFINITY ? 0.f : expf(l - mx);
+#pragma unroll
+        for (int v = 0; v < kVec; ++v)
+          x[u][v] = wt[u] != 0.f ? *reinterpret_cast<const f32x4*>(base + s * kDcg + 256 * v)
+                                 : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int v = 0; v < kVec; ++v) acc[v] += wt[u] * x[u][v];
+    }
+  }
+  const float inv = mx == -INFINITY ? 0.f : 1.f / sum;
+#pragma unroll
+  for (int v = 0; v < kVec; ++v)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store_elem(o_lat, r * kDcg + 256 * v + 4 * lane + e, acc[v][e] * inv);
+  if (lane == 0 && lse_out != nullptr) lse_out[r] = mx == -INFINITY ? -INFINITY : mx + logf(sum);
+}
+
 __global__ void __launch_bounds__(kThreads)
 rope_table_kernel(float* __restrict__ cos_out, float* __restrict__ sin_out, int max_pos, int half,
                   double base) {
@@ -288,6 +341,24 @@ hipError_t launch_decode_generic(const DecodeArgs& a, bool bf16, hipStream_t s) 
 
 hipError_t launch_combine(const float* o_part, const float* lse_part, void* o_lat, float* lse_out,
                           int T, int H, int d_cg, int S, bool bf16, hipStream_t s) {
+  const int rows = T * H;
+  if (d_cg == 512 || d_cg == 256) {
+    const dim3 vgrid((rows + 3) / 4);
+    if (bf16) {
+      auto* o = static_cast<uint16_t*>(o_lat);
+      if (d_cg == 512)
+        combine_vec_kernel<uint16_t, 512><<<vgrid, kThreads, 0, s>>>(o_part, lse_part, o, lse_out, rows, S);
+      else
+        combine_vec_kernel<uint16_t, 256><<<vgrid, kThreads, 0, s>>>(o_part, lse_part, o, lse_out, rows, S);
+    } else {
+      auto* o = static_cast<float*>(o_lat);
+      if (d_cg == 512)
+        combine_vec_kernel<float, 512><<<vgrid, kThreads, 0, s>>>(o_part, lse_part, o, lse_out, rows, S);
+      else
+        combine_vec_kernel<float, 256><<<vgrid, kThreads, 0, s>>>(o_part, lse_part, o, lse_out, rows, S);
+    }
+    return hipGetLastError();
+  }
   const dim3 grid(static_cast<unsigned>(T) * H);
   if (bf16)
     combine_kernel<uint16_t><<<grid, kThreads, 0, s>>>(o_part, lse_part, static_cast<uint16_t*>(o_lat),

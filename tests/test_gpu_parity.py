@@ -222,3 +222,35 @@ def test_mfma_decode_matches_generic_decode(case, monkeypatch):
     assert_parity(outs["mfma"], ref, what="mfma")
     assert_parity(outs["generic"], ref, what="generic")
     assert_parity(outs["mfma"], outs["generic"], what="mfma vs generic")
+
+
+def test_combine_ignores_unwritten_empty_splits():
+    """Empty splits leave their o_part rows unwritten; NaN there must not reach the output."""
+    w = wl.make_workload(_small("ragged_b64", batch=4, seq_len_range=(10, 300)))
+    d = harness.to_device(w)
+    step = harness.make_step(w, d, 40)         # far more splits than pages
+    step.o_part.fill_(float("nan"))
+    step()
+    torch.cuda.synchronize()
+    assert_parity(_f64(step.out), oracle_for(w)["out"])
+
+
+@pytest.mark.parametrize("case", ["dsv3_small", "gla2_small"])
+def test_hip_graph_replay_matches_eager(case):
+    """The four calls captured as a HIP graph: every replay equals the eager result bitwise."""
+    w = wl.make_workload(SMALL_CASES[case])
+    d = harness.to_device(w)
+    step = harness.make_step(w, d)
+    eager = step().clone()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        step.out.zero_()
+        torch.randn(1 << 20, device="cuda").sum()     # unrelated eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(step.out, eager)
