@@ -1,0 +1,120 @@
+"""Summarise rocprofv3 result databases (rocpd SQLite) as short markdown tables.
+
+    python -m mla_latent_kv_09_amd.profile_summary trace DB [--regex R]
+    python -m mla_latent_kv_09_amd.profile_summary counters DB [DB ...] [--regex R]
+    python -m mla_latent_kv_09_amd.profile_summary traffic --fetch DB --write DB
+            --calib-fetch DB --calib-write DB --calib-mib N --regex R
+
+`trace` lists per-kernel dispatch count and duration statistics from a
+`--kernel-trace` run; `counters` lists per-kernel mean counter values per
+dispatch from `--pmc` runs; `traffic` turns FETCH_SIZE / WRITE_SIZE (KiB per
+dispatch) into HBM bytes per dispatch, each scaled by what the same counter
+reads for a plain copy of known size.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import glob
+import json
+import os
+import re
+import sqlite3
+import statistics
+
+
+def _db(path: str) -> str:
+    if os.path.isdir(path):
+        found = glob.glob(os.path.join(path, "**", "*_results.db"), recursive=True)
+        if not found:
+            raise SystemExit(f"no *_results.db under {path}")
+        return found[0]
+    return path
+
+
+def _short(name: str) -> str:
+    name = re.sub(r"\(anonymous namespace\)::", "", name)
+    return name if len(name) <= 70 else name[:67] + "..."
+
+
+def kernel_durations(path: str, regex: str = "."):
+    con = sqlite3.connect(_db(path))
+    out = collections.defaultdict(list)
+    for name, dur in con.execute("select name, duration from kernels"):
+        if re.search(regex, name):
+            out[name].append(dur / 1000.0)  # ns -> us
+    return out
+
+
+def counter_means(paths, regex: str = "."):
+    out = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in paths:
+        con = sqlite3.connect(_db(path))
+        for name, counter, value in con.execute(
+                "select name, counter_name, counter_value from pmc_events"):
+            if re.search(regex, name):
+                out[name][counter].append(value)
+    return {k: {c: statistics.fmean(v) for c, v in d.items()} for k, d in out.items()}
+
+
+def cmd_trace(args):
+    d = kernel_durations(args.db, args.regex)
+    print("| kernel | dispatches | mean us | median us | min us | max us |")
+    print("|---|---|---|---|---|---|")
+    for name, v in sorted(d.items(), key=lambda kv: -sum(kv[1])):
+        print(f"| `{_short(name)}` | {len(v)} | {statistics.fmean(v):.2f} | "
+              f"{statistics.median(v):.2f} | {min(v):.2f} | {max(v):.2f} |")
+
+
+def cmd_counters(args):
+    d = counter_means(args.db, args.regex)
+    counters = sorted({c for v in d.values() for c in v})
+    print("| kernel | " + " | ".join(counters) + " |")
+    print("|---|" + "---|" * len(counters))
+    for name, v in sorted(d.items()):
+        print(f"| `{_short(name)}` | " + " | ".join(f"{v.get(c, float('nan')):.1f}" for c in counters) + " |")
+
+
+def cmd_traffic(args):
+    mib_kib = args.calib_mib * 1024.0
+    cf = counter_means([args.calib_fetch], args.calib_regex)
+    cw = counter_means([args.calib_write], args.calib_regex)
+    fetch_copy = max(v["FETCH_SIZE"] for v in cf.values() if "FETCH_SIZE" in v)
+    write_copy = max(v["WRITE_SIZE"] for v in cw.values() if "WRITE_SIZE" in v)
+    f_scale = mib_kib / fetch_copy
+    w_scale = mib_kib / write_copy
+    fk = counter_means([args.fetch], args.regex)
+    wk = counter_means([args.write], args.regex)
+    rows = {}
+    for name in sorted(set(fk) | set(wk)):
+        fetch = fk.get(name, {}).get("FETCH_SIZE", float("nan")) * f_scale * 1024
+        write = wk.get(name, {}).get("WRITE_SIZE", float("nan")) * w_scale * 1024
+        rows[name] = {"fetch_bytes": fetch, "write_bytes": write, "bytes_per_launch": fetch + write}
+    print(json.dumps({"fetch_scale": f_scale, "write_scale": w_scale,
+                      "copy_fetch_kib": fetch_copy, "copy_write_kib": write_copy,
+                      "kernels": rows}, indent=1))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("trace")
+    t.add_argument("db")
+    t.add_argument("--regex", default=".")
+    c = sub.add_parser("counters")
+    c.add_argument("db", nargs="+")
+    c.add_argument("--regex", default=".")
+    f = sub.add_parser("traffic")
+    f.add_argument("--fetch", required=True)
+    f.add_argument("--write", required=True)
+    f.add_argument("--calib-fetch", required=True)
+    f.add_argument("--calib-write", required=True)
+    f.add_argument("--calib-mib", type=float, required=True)
+    f.add_argument("--calib-regex", default="copyBuffer")
+    f.add_argument("--regex", default=".")
+    args = ap.parse_args()
+    {"trace": cmd_trace, "counters": cmd_counters, "traffic": cmd_traffic}[args.cmd](args)
+
+
+if __name__ == "__main__":
+    main()
