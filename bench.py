@@ -7,8 +7,10 @@ A step is the whole hot path over one batch of synthetic input already resident
 in HBM: mla_absorb_q -> mla_decode_paged -> mla_combine -> mla_up_v, all on the
 current HIP stream, captured once as a HIP graph and replayed (--no-graph
 launches the four calls eagerly).  Before every timed step a 1 GiB buffer is
-rewritten so the L2 and the 256 MB Infinity Cache hold nothing of the step's
-working set (a real decode step reads a different layer's cache every time).
+read (a max-reduction) so the L2 and the 256 MB Infinity Cache hold nothing of the
+step's working set (a real decode step reads a different layer's cache every
+time).  The flush only reads: a flush that writes leaves up to 256 MB of dirty
+lines whose write-back then competes with the step's own reads.
 Each step is bracketed by HIP events; the reported time is the median over the
 K timed steps.  Per-kernel times (and the decode kernel's time in the roofline
 object) come from a second pass of K eager steps with events between the calls.
@@ -38,7 +40,9 @@ HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 FP32_PEAK_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode.json")
-DECODE_SRC = os.path.join(ROOT, "mla_latent_kv_09_amd", "csrc", "decode_mfma.hip")
+CSRC = os.path.join(ROOT, "mla_latent_kv_09_amd", "csrc")
+KERNEL_SRC = {"decode_pair_kernel": "decode_pair.hip", "decode_mfma_kernel": "decode_mfma.hip",
+              "decode_generic_kernel": "kernels_generic.hip"}
 
 
 def algorithmic_work(cfg, seq_lens, q_lens):
@@ -69,14 +73,17 @@ def source_hash(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(workload, splits):
-    """HBM bytes per decode launch from committed rocprofv3 counters, if still current."""
+def measured_traffic(kernel, workload, splits):
+    """HBM bytes per decode launch from committed rocprofv3 counters, if they were taken
+    on this kernel, its current source, this workload and this split count."""
     try:
         with open(TRAFFIC_FILE) as f:
             rec = json.load(f)
     except (OSError, ValueError):
         return None
-    if rec.get("kernel_source_sha256_16") != source_hash(DECODE_SRC):
+    if rec.get("kernel") != kernel:
+        return None
+    if rec.get("kernel_source_sha256_16") != source_hash(os.path.join(CSRC, KERNEL_SRC[kernel])):
         return None
     if rec.get("workload") != workload or rec.get("num_splits") != splits:
         return None
@@ -145,7 +152,11 @@ def main():
     d = harness.to_device(w)
     step = harness.make_step(w, d, args.splits)
     S = step.num_splits
-    flush = None if args.no_flush else torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    flush_buf = None if args.no_flush else torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+
+    def flush():
+        if flush_buf is not None:
+            flush_buf.max()
     stream = torch.cuda.current_stream()
 
     def one_step(ev=None):
@@ -163,8 +174,7 @@ def main():
         ev[4].record(stream)
 
     for _ in range(args.warmup):
-        if flush is not None:
-            flush.add_(1.0)
+        flush()
         one_step()
     torch.cuda.synchronize()
 
@@ -173,8 +183,7 @@ def main():
     # launches to be queued, so the events bracket kernel execution).
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     for k in range(args.steps):
-        if flush is not None:
-            flush.add_(1.0)
+        flush()
         one_step(events[k])
     torch.cuda.synchronize()
     dec_ms = [e[1].elapsed_time(e[2]) for e in events]
@@ -194,8 +203,7 @@ def main():
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for k in range(args.steps):
-        if flush is not None:
-            flush.add_(1.0)
+        flush()
         ev_step[k][0].record(stream)
         if graph is not None:
             graph.replay()
@@ -217,7 +225,8 @@ def main():
     peak_f = BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else FP32_PEAK_TFLOPS
     t_hbm = kv_bytes / (HBM_PEAK_GBPS * 1e9)
     t_mfma = att / (peak_f * 1e12)
-    traffic = measured_traffic(cfg.name, S)
+    kernel = decode_kernel_name(cfg)
+    traffic = measured_traffic(kernel, cfg.name, S)
     if t_hbm >= t_mfma:
         achieved = kv_bytes / (dec * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -226,8 +235,7 @@ def main():
         achieved = att / (dec * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": peak_f, "unit": "TFLOP/s",
                 "frac": achieved / peak_f, "traffic": traffic}
-    roof.update({"kernel": "decode_mfma_kernel" if mla_path_is_mfma(cfg) else "decode_generic_kernel",
-                 "kernel_ms": dec, "algorithmic_bytes": kv_bytes, "algorithmic_flops": att})
+    roof.update({"kernel": kernel, "kernel_ms": dec, "algorithmic_bytes": kv_bytes, "algorithmic_flops": att})
 
     out = {
         "metric": METRIC, "value": tflops, "unit": "TFLOP/s", "n_gpus": 1,
@@ -238,7 +246,7 @@ def main():
                    "d_c": cfg.d_c, "d_R": cfg.d_R, "groups": cfg.groups, "page_size": cfg.page_size,
                    "seq_len": cfg.seq_len, "seq_len_range": cfg.seq_len_range,
                    "total_q": int(w.total_q), "num_splits": S,
-                   "pages_per_split": step.pages_per_split, "cache_flushed": flush is not None,
+                   "pages_per_split": step.pages_per_split, "cache_flushed": flush_buf is not None,
                    "hip_graph": graph is not None},
         "latent_kv_gbps": kv_gbps, "latent_kv_frac_hbm_peak": kv_gbps / HBM_PEAK_GBPS,
         "tflops_frac_mfma_peak": tflops / peak_f, "seqs_per_s": seqs,
@@ -250,11 +258,15 @@ def main():
     print(json.dumps(out))
 
 
-def mla_path_is_mfma(cfg):
-    if os.environ.get("MLA_KV_DECODE_KERNEL") == "generic":
-        return False
-    return (cfg.dtype == "bf16" and cfg.heads == 128 and cfg.groups == 1 and cfg.d_c == 512
-            and cfg.d_R == 64 and cfg.page_size == 64)
+def decode_kernel_name(cfg):
+    """The decode kernel the library dispatches for this shape (same rule as the library:
+    MLA_KV_DECODE_KERNEL = generic / mfma / pair, default the mfma kernel where it applies)."""
+    mfma_shape = (cfg.dtype == "bf16" and cfg.heads == 128 and cfg.groups in (1, 2)
+                  and cfg.d_c == 512 and cfg.d_R == 64 and cfg.page_size == 64)
+    choice = os.environ.get("MLA_KV_DECODE_KERNEL", "")
+    if choice == "generic" or not mfma_shape:
+        return "decode_generic_kernel"
+    return "decode_pair_kernel" if choice == "pair" else "decode_mfma_kernel"
 
 
 if __name__ == "__main__":

@@ -56,13 +56,18 @@ template <int G> struct Shape {
 };
 static_assert(kLdsBytes <= 160 * 1024, "stages + q_R must fit the 160 KB LDS of a gfx950 CU");
 
-// Swizzles (16-byte chunk index XOR).  Latent part: token t's chunk c sits at slot
-// c ^ swz_c(t).  16 consecutive tokens x one chunk hit 16 distinct bank groups
-// (b128 score reads), and 8 aligned tokens x 2 aligned chunks do too (transposing
-// reads, 32 lanes per cycle).
-__device__ __forceinline__ int swz_c(int t) { return 2 * (t & 7) + ((t >> 3) & 1); }
-// RoPE part (8 chunks per token): 16 consecutive tokens x one chunk -> 16 groups.
-__device__ __forceinline__ int swz_r(int t) { return (t & 7) ^ ((t >> 3) & 1); }
+// Swizzles (16-byte chunk index XOR).  LDS serves a 16-byte-per-lane read 32 lanes at a
+// time out of one 512-byte bank row, and an 8-byte transposing read 32 lanes at a time
+// too, so a layout is conflict-free when the 32 lanes of each half-wave touch 32
+// distinct 16-byte (resp. 8-byte) slots of a 512-byte row.
+// Latent part: token t's chunk c sits at position c ^ swz_c(t), an XOR inside aligned
+// 32-chunk blocks.  A score read (16 consecutive tokens j x chunks c, c+1) then covers
+// all 32 slots (bit 0 from the chunk, bits 1-4 from the token), and so does a
+// transposing read (8 tokens x 2 chunks x 2 halves).
+__device__ __forceinline__ int swz_c(int t) { return 2 * (t & 15); }
+// RoPE part (8 chunks = 128 B per token, 4 tokens per 512-byte row): the XOR separates
+// the 4 tokens that share row slots, so 16 tokens x chunks c, c+1 are conflict-free.
+__device__ __forceinline__ int swz_r(int t) { return 2 * ((t >> 2) & 3); }
 // Rotated q_R (8 chunks per head): 16 consecutive heads x one chunk -> 16 groups.
 __device__ __forceinline__ uint32_t qr_slot(int h, int c) { return h * 128 + ((c ^ ((h >> 1) & 7)) << 4); }
 
@@ -105,7 +110,7 @@ __device__ __forceinline__ void dma16(const char* gptr, uint32_t lds) {
 // Issue this wave's share of one page into LDS stage `stage`: latent rows 8w..8w+7
 // and the RoPE rows of the same 8 tokens.  Rows at or past n_valid fetch row 0
 // instead (always valid), so no stale or uninitialised slot enters the MFMAs.
-// For row t = 8w + k the latent swizzle key is swz_c(t) = 2k + (w & 1).
+// For row t = 8w + k the latent swizzle key is swz_c(t) = 16 (w & 1) + 2k.
 // `lane_v` is the lane index passed through an empty asm each call, so the per-lane
 // offsets are recomputed here (two VALU ops each) instead of being hoisted out of
 // the page loop and kept live across it.
@@ -118,7 +123,7 @@ __device__ __forceinline__ void load_page(uint32_t smem_base, int stage, const c
   for (int k = 0; k < 8; ++k) {
     const int t = wave * 8 + k;
     const int src_t = t < n_valid ? t : 0;
-    const int key = 2 * k + (wave & 1);
+    const int key = 16 * (wave & 1) + 2 * k;
     dma16(page + src_t * kRowBytes + ((lane_v ^ key) << 4), c_base + t * 1024);
   }
   const int t = wave * 8 + (lane_v >> 3);
@@ -130,22 +135,25 @@ __device__ __forceinline__ void load_page(uint32_t smem_base, int stage, const c
 constexpr int kRing = 4;  // LDS fragments in flight per wave
 
 // Latent score-step fragment st = k * 4 + mb: A operand of S^T for tokens 16mb + j,
-// latent dims 32k + 8g .. +7.  The four token blocks alternate so that consecutive
-// MFMAs accumulate into different registers.  sb[i] = stage base + per-lane base
-// for k % 4 == i.
-__device__ __forceinline__ bf16x8 score_frag(const uint32_t* sb, int st) {
+// latent dims 32k + 8g .. +7 (chunk 4k + g).  The four token blocks alternate so that
+// consecutive MFMAs accumulate into different registers.  With key 2j the chunk sits
+// at position 32 (k / 8) + 4 ((k % 8) ^ (j / 2)) + (g ^ 2 (j % 2)): `lb` is the stage
+// base plus the per-lane row and low bits, `jx` = (j / 2) << 6, so each fragment costs
+// one xor-add and an immediate offset.
+__device__ __forceinline__ bf16x8 score_frag(uint32_t lb, uint32_t jx, int st) {
   const int mb = st % 4, k = st / 4;  // k < kQSteps of the instantiation
-  return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(sb[k & 3] + 16384 * mb +
-                                                                      256 * (k >> 2));
+  const uint32_t a = lb + (jx ^ static_cast<uint32_t>((k & 7) << 6));
+  return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(a + 16384 * mb + 512 * (k >> 3));
 }
 
-// Output-step fragment st = ks * 32 + nb: A operand of O^T for columns 16nb + j,
+// Output-step fragment st = ks * nC + nb: A operand of O^T for columns 16nb + j,
 // tokens 32ks + 4g + {0..3} and 32ks + 16 + 4g + {0..3}, via two transposing reads.
-// ob[i] = stage base + per-lane base for nb % 8 == i.
+// Column chunk 2nb + h of token tok sits at position 2 (nb ^ tok) + h: `lb` holds the
+// per-lane row, chunk half and in-chunk offset, `tx` = tok << 5.
 template <int kColBlocks>
-__device__ __forceinline__ bf16x8 out_frag(const uint32_t* ob, int st) {
+__device__ __forceinline__ bf16x8 out_frag(uint32_t lb, uint32_t tx, int st) {
   const int ks = st / kColBlocks, nb = st % kColBlocks;
-  const uint32_t a1 = ob[nb & 7] + 32768 * ks + 256 * (nb >> 3);
+  const uint32_t a1 = lb + (tx ^ static_cast<uint32_t>((nb & 15) << 5)) + 32768 * ks + 512 * (nb >> 4);
   const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lds_bf16x4(a1));
   const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(lds_bf16x4(a1 + 16384));
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -236,12 +244,12 @@ decode_mfma_kernel(DecodeArgs a) {
   for (int nb = 0; nb < kColBlocks; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // Per-lane LDS offsets inside a stage.  The swizzle keys depend only on the low
-  // four bits of the token index, so every address splits into a per-lane base
-  // plus a compile-time immediate:
-  //   score read  (token 16mb + j, chunk 4k + g):  base_s(k%4)  + 16384 mb + 256 (k/4)
-  //   RoPE read   (token 16mb + j, chunk 4k + g):  base_r(k)    + 2048 mb
+  // four bits of the token index, so every address is a per-lane base, one xor of a
+  // per-lane key with a compile-time constant, and a compile-time immediate:
+  //   score read  (token 16mb + j, chunk 4k + g):  base_s + (jx ^ 64 (k%8)) + 16384 mb + 512 (k/8)
+  //   RoPE read   (token 16mb + j, chunk 4k + g):  base_r(k) + 2048 mb
   //   output read (token 32ks + 4g + j/4 (+16), column 16nb + 4(j%4)):
-  //                                               base_o(nb%8) + 32768 ks (+16384) + 256 (nb/8)
+  //                           base_o + (tx ^ 32 (nb%16)) + 32768 ks (+16384) + 512 (nb/16)
   // The bases are recomputed from the lane index every page (a few VALU ops) rather
   // than kept in registers across the loop.
   const uint32_t smem_base = lds_addr(smem);
@@ -259,12 +267,8 @@ decode_mfma_kernel(DecodeArgs a) {
     const uint32_t st_base = smem_base + stage * kStageBytes;
     const int lv = static_cast<int>(opaque(static_cast<uint32_t>(lane)));
     const int lj = lv & 15, lg = lv >> 4;
-    uint32_t sb[4], ob[8];
-    {
-      const int sw = swz_c(lj);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sb[i] = st_base + grp_off + lj * 1024 + (((4 * i + lg) ^ sw) << 4);
-    }
+    const uint32_t sb = opaque(st_base + grp_off + lj * 1024 + ((lg ^ (2 * (lj & 1))) << 4));
+    const uint32_t sjx = opaque(static_cast<uint32_t>(lj >> 1) << 6);
 
     // ---- scores S^T for tokens mb*16 .. mb*16+15 of the page.  RoPE part first
     // (the q_R fragments are live only here), then the 64 latent (mb, k) steps in
@@ -294,11 +298,11 @@ decode_mfma_kernel(DecodeArgs a) {
       constexpr int kSteps = 4 * kQSteps;  // (mb, k) steps
       bf16x8 ring[kRing];
 #pragma unroll
-      for (int st = 0; st < kRing; ++st) ring[st] = score_frag(sb, st);
+      for (int st = 0; st < kRing; ++st) ring[st] = score_frag(sb, sjx, st);
 #pragma unroll
       for (int st = 0; st < kSteps; ++st) {
         const bf16x8 c = ring[st % kRing];
-        if (st + kRing < kSteps) ring[st % kRing] = score_frag(sb, st + kRing);
+        if (st + kRing < kSteps) ring[st % kRing] = score_frag(sb, sjx, st + kRing);
         const int mb = st % 4, k = st / 4;
         s[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c, q[k], s[mb], 0, 0, 0);
       }
@@ -343,23 +347,19 @@ decode_mfma_kernel(DecodeArgs a) {
                          s[2 * ks + 1][0], s[2 * ks + 1][1], s[2 * ks + 1][2], s[2 * ks + 1][3]);
 
     // ---- O^T[cols 16nb .. +15] += C^T . P^T, 64 (ks, nb) steps through the ring
-    {
-      const int tok = 4 * lg + (lj >> 2);
-      const int swo = swz_c(tok);
-      const int colb = 4 * (lj & 3);
-      const uint32_t rowb = st_base + grp_off + tok * 1024 + (colb & 7) * 2;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) ob[i] = rowb + (((2 * i + (colb >> 3)) ^ swo) << 4);
-    }
+    const int otok = 4 * lg + (lj >> 2);
+    const int colb = 4 * (lj & 3);
+    const uint32_t ob = opaque(st_base + grp_off + otok * 1024 + ((colb >> 3) << 4) + (colb & 7) * 2);
+    const uint32_t otx = opaque(static_cast<uint32_t>(otok) << 5);
     {
       constexpr int kSteps = 2 * kColBlocks;
       bf16x8 ring[kRing];
 #pragma unroll
-      for (int st = 0; st < kRing; ++st) ring[st] = out_frag<kColBlocks>(ob, st);
+      for (int st = 0; st < kRing; ++st) ring[st] = out_frag<kColBlocks>(ob, otx, st);
 #pragma unroll
       for (int st = 0; st < kSteps; ++st) {
         const bf16x8 ct = ring[st % kRing];
-        if (st + kRing < kSteps) ring[st % kRing] = out_frag<kColBlocks>(ob, st + kRing);
+        if (st + kRing < kSteps) ring[st % kRing] = out_frag<kColBlocks>(ob, otx, st + kRing);
         const int ks = st / kColBlocks, nb = st % kColBlocks;
         o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ct, pb[ks], o[nb], 0, 0, 0);
       }

@@ -113,9 +113,11 @@ def test_bitwise_repeatable():
 
 @pytest.mark.parametrize("lens,q_lens", [
     ((1,), (1,)), ((64,), (1,)), ((65,), (1,)), ((2,), (2,)), ((128, 129, 63), (1, 2, 1)),
+    ((31, 32, 33, 96, 97), (1, 1, 2, 1, 2)),
 ])
-def test_edge_lengths(lens, q_lens):
-    cfg = _small("dsv3_b16_l4096", batch=len(lens), seq_len=max(lens), heads=16)
+@pytest.mark.parametrize("heads", [16, 128])   # 16: generic kernel; 128: MFMA kernel
+def test_edge_lengths(lens, q_lens, heads):
+    cfg = _small("dsv3_b16_l4096", batch=len(lens), seq_len=max(lens), heads=heads)
     w = _with_lengths(cfg, lens, q_lens)
     step = run_step(w, num_splits=2)
     ref = oracle_for(w)
@@ -209,18 +211,21 @@ def test_projections_against_reference(T, d_cg):
     assert_parity(_f64(out), om.up_v_reference(o, w), what="up_v")
 
 
-@pytest.mark.parametrize("case", ["dsv3_small", "ragged_small", "long_small"])
-def test_mfma_decode_matches_generic_decode(case, monkeypatch):
-    """Both decode kernels on the same inputs: each within tolerance of the oracle and of each other."""
+@pytest.mark.parametrize("case", ["dsv3_small", "ragged_small", "long_small", "gla2_small"])
+def test_decode_kernels_agree(case, monkeypatch):
+    """The three decode kernels (wave-pair MFMA, one-wave-per-16-heads MFMA, generic) on
+    the same inputs: each within tolerance of the oracle and of the generic kernel."""
     cfg = SMALL_CASES[case]
     w = wl.make_workload(cfg)
     outs = {}
-    for kind in ("mfma", "generic"):
+    for kind in ("pair", "mfma", "generic"):
         monkeypatch.setenv("MLA_KV_DECODE_KERNEL", kind)
+        print(f"  kernel {kind}", flush=True)
         outs[kind] = _f64(run_step(w, num_splits=3).out)
     ref = oracle_for(w)["out"]
-    assert_parity(outs["mfma"], ref, what="mfma")
-    assert_parity(outs["generic"], ref, what="generic")
+    for kind in ("pair", "mfma", "generic"):
+        assert_parity(outs[kind], ref, what=kind)
+    assert_parity(outs["pair"], outs["generic"], what="pair vs generic")
     assert_parity(outs["mfma"], outs["generic"], what="mfma vs generic")
 
 
