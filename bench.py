@@ -41,7 +41,7 @@ BF16_PEAK_TFLOPS = 2500.0
 FP32_PEAK_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode.json")
 CSRC = os.path.join(ROOT, "mla_latent_kv_09_amd", "csrc")
-KERNEL_SRC = {"decode_pair_kernel": "decode_pair.hip", "decode_mfma_kernel": "decode_mfma.hip",
+KERNEL_SRC = {"decode_mfma_kernel": "decode_mfma.hip",
               "decode_generic_kernel": "kernels_generic.hip"}
 
 
@@ -260,13 +260,13 @@ def main():
 
 def decode_kernel_name(cfg):
     """The decode kernel the library dispatches for this shape (same rule as the library:
-    MLA_KV_DECODE_KERNEL = generic / mfma / pair, default the mfma kernel where it applies)."""
+    MLA_KV_DECODE_KERNEL = generic / mfma, default the mfma kernel where it applies)."""
     mfma_shape = (cfg.dtype == "bf16" and cfg.heads == 128 and cfg.groups in (1, 2)
                   and cfg.d_c == 512 and cfg.d_R == 64 and cfg.page_size == 64)
     choice = os.environ.get("MLA_KV_DECODE_KERNEL", "")
     if choice == "generic" or not mfma_shape:
         return "decode_generic_kernel"
-    return "decode_pair_kernel" if choice == "pair" else "decode_mfma_kernel"
+    return "decode_mfma_kernel"
 
 
 if __name__ == "__main__":

@@ -22,7 +22,11 @@
 //            score accumulators (no LDS round trip).
 // Pages: one 64-token page (72 KB) per stage, two stages in LDS (144 KB of 160 KB),
 // fetched with global_load_lds (16 B per lane) in a swizzled layout that keeps both
-// the b128 score reads and the transposing output reads free of bank conflicts.
+// the b128 score reads and the transposing output reads free of bank conflicts.  The
+// next page's nine copies per wave are spread through the score loop (issued
+// together they stall every wave's instruction issue behind the memory pipeline);
+// fragment rings keep 3 score and 6 output reads in flight per wave, the most the
+// 256-register budget of two waves per SIMD leaves room for.
 #include <math.h>
 
 #include "mla_device.h"
@@ -71,6 +75,22 @@ __device__ __forceinline__ int swz_r(int t) { return 2 * ((t >> 2) & 3); }
 // Rotated q_R (8 chunks per head): 16 consecutive heads x one chunk -> 16 groups.
 __device__ __forceinline__ uint32_t qr_slot(int h, int c) { return h * 128 + ((c ^ ((h >> 1) & 7)) << 4); }
 
+// Reductions over the four 16-lane rows of a wave (lanes j, j+16, j+32, j+48 hold the
+// same head): v_permlane16_swap / v_permlane32_swap exchange rows without lane-index
+// arithmetic; max and + are symmetric, so every lane of a head ends with the same value.
+__device__ __forceinline__ float rows_max(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // LDS byte offset of a pointer into a __shared__ array, and back.
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
@@ -93,43 +113,50 @@ __device__ __forceinline__ bf16x8 to_bf16x8(float x0, float x1, float x2, float 
                 static_cast<__bf16>(x6), static_cast<__bf16>(x7)};
 }
 
-// One 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4): lane i's 16
-// bytes land at LDS byte lds + 16 i.  Issued as inline asm on purpose: the
-// compiler then does not know that an LDS DMA is in flight, so it does not make
-// every later LDS read of the page being computed wait for the *next* page's copy
-// (it cannot prove they do not alias).  Completion is awaited explicitly with
-// s_waitcnt vmcnt(0) + a barrier before a stage is read; every wait the compiler
-// emits for its own loads only counts ops it knows about, which stays safe.
-__device__ __forceinline__ void dma16(const char* gptr, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+// One 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4) addressed as a
+// wave-uniform base (SGPR pair) plus a 32-bit per-lane byte offset: active lane i's 16
+// bytes land at LDS byte lds + 16 i.  Issued as inline asm on purpose: the compiler
+// then does not know that an LDS DMA is in flight, so it does not make every later LDS
+// read of the page being computed wait for the *next* page's copy (it cannot prove
+// they do not alias).  Completion is awaited explicitly with s_waitcnt vmcnt(0) + a
+// barrier before a stage is read; every wait the compiler emits for its own loads only
+// counts ops it knows about, which stays safe.
+__device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
-               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(gptr)
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(sbase)
                : "memory");
 }
 
-// Issue this wave's share of one page into LDS stage `stage`: latent rows 8w..8w+7
-// and the RoPE rows of the same 8 tokens.  Rows at or past n_valid fetch row 0
-// instead (always valid), so no stale or uninitialised slot enters the MFMAs.
-// For row t = 8w + k the latent swizzle key is swz_c(t) = 16 (w & 1) + 2k.
-// `lane_v` is the lane index passed through an empty asm each call, so the per-lane
-// offsets are recomputed here (two VALU ops each) instead of being hoisted out of
-// the page loop and kept live across it.
+// This wave's share of one page in LDS stage `c_base`: latent rows 8w .. 8w+7 (one
+// 1 KB copy each, `row` = 0..7) and the RoPE rows of the same 8 tokens (row 8).  Rows
+// at or past n_valid fetch row 0 instead (always valid), so no stale or uninitialised
+// slot enters the MFMAs.  For row t = 8w + k the latent swizzle key is
+// swz_c(t) = 16 (w & 1) + 2k.  The copies are spread through the score loop rather
+// than issued together: the memory pipeline takes 64 B per clock per CU, and nine
+// back-to-back 1 KB copies from every wave would stall each wave's issue for
+// thousands of cycles.
+__device__ __forceinline__ void load_row(uint32_t c_base, const char* page, int n_valid,
+                                         int wave, int lane, int row) {
+  if (row < 8) {
+    const int t = wave * 8 + row;
+    const int src_t = t < n_valid ? t : 0;
+    const int key = 16 * (wave & 1) + 2 * row;
+    dma16(page + src_t * kRowBytes, static_cast<uint32_t>((lane ^ key) << 4), c_base + t * 1024);
+  } else {
+    const int t = wave * 8 + (lane >> 3);
+    const int src_t = t < n_valid ? t : 0;
+    dma16(page, static_cast<uint32_t>(src_t * kRowBytes + kDc * 2 + (((lane & 7) ^ swz_r(t)) << 4)),
+          c_base + kCBytes + wave * 1024);
+  }
+}
+
 __device__ __forceinline__ void load_page(uint32_t smem_base, int stage, const char* page,
                                           int n_valid, int wave, int lane_v) {
   asm volatile("" : "+v"(lane_v));
   const uint32_t c_base = smem_base + stage * kStageBytes;
-  const uint32_t r_base = c_base + kCBytes;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int t = wave * 8 + k;
-    const int src_t = t < n_valid ? t : 0;
-    const int key = 16 * (wave & 1) + 2 * k;
-    dma16(page + src_t * kRowBytes + ((lane_v ^ key) << 4), c_base + t * 1024);
-  }
-  const int t = wave * 8 + (lane_v >> 3);
-  const int src_t = t < n_valid ? t : 0;
-  dma16(page + src_t * kRowBytes + kDc * 2 + (((lane_v & 7) ^ swz_r(t)) << 4),
-        r_base + wave * 1024);
+  for (int row = 0; row < 9; ++row) load_row(c_base, page, n_valid, wave, lane_v, row);
 }
 
 constexpr int kRing = 4;  // LDS fragments in flight per wave
@@ -191,6 +218,7 @@ decode_mfma_kernel(DecodeArgs a) {
   auto fetch_ids = [&](int chunk) {
     const int idx = chunk * 64 + lane;
     pid_v = idx < n_split_pages ? ptab[page0 + idx] : 0;
+    asm volatile("" : "+v"(pid_v));  // wait for the load here, on this rarely taken path
   };
   auto page_ptr = [&](int i) {  // i = page index within the split (wave-uniform)
     const int id = clamp_page(__builtin_amdgcn_readlane(pid_v, i & 63), a.num_pool_pages);
@@ -258,12 +286,17 @@ decode_mfma_kernel(DecodeArgs a) {
     const int n_valid = min(kTok, w.k1 - j0);
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's page loads have landed
     __syncthreads();                     // ... and every wave's; the other stage is free again
+    // The next page's copy is issued from inside the score loop below.
     const int j_next = j0 + kTok;
-    if (j_next < w.k1) {
+    const bool has_next = j_next < w.k1;
+    const char* next_page = kv;
+    const int next_valid = min(kTok, w.k1 - j_next);
+    if (has_next) {
       const int i_next = (j_next - w.k0) / kTok;
       if ((i_next & 63) == 0) fetch_ids(i_next >> 6);
-      load_page(smem_base, stage ^ 1, page_ptr(i_next), min(kTok, w.k1 - j_next), wave, lane);
+      next_page = page_ptr(i_next);
     }
+    const uint32_t next_base = smem_base + (stage ^ 1) * kStageBytes;
     const uint32_t st_base = smem_base + stage * kStageBytes;
     const int lv = static_cast<int>(opaque(static_cast<uint32_t>(lane)));
     const int lj = lv & 15, lg = lv >> 4;
@@ -296,15 +329,21 @@ decode_mfma_kernel(DecodeArgs a) {
     }
     {
       constexpr int kSteps = 4 * kQSteps;  // (mb, k) steps
-      bf16x8 ring[kRing];
+      constexpr int kSRing = 3;
+      bf16x8 ring[kSRing];
 #pragma unroll
-      for (int st = 0; st < kRing; ++st) ring[st] = score_frag(sb, sjx, st);
+      for (int st = 0; st < kSRing; ++st) ring[st] = score_frag(sb, sjx, st);
+      constexpr int kRowEvery = kSteps / 8;  // one page-row copy every kRowEvery steps
 #pragma unroll
       for (int st = 0; st < kSteps; ++st) {
-        const bf16x8 c = ring[st % kRing];
-        if (st + kRing < kSteps) ring[st % kRing] = score_frag(sb, sjx, st + kRing);
+        const bf16x8 c = ring[st % kSRing];
+        if (st + kSRing < kSteps) ring[st % kSRing] = score_frag(sb, sjx, st + kSRing);
         const int mb = st % 4, k = st / 4;
         s[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c, q[k], s[mb], 0, 0, 0);
+        if (st % kRowEvery == kRowEvery / 2 && has_next)
+          load_row(next_base, next_page, next_valid, wave, static_cast<int>(opaque(lane)), st / kRowEvery);
+        if (st == kSteps / 2 + 1 && has_next)
+          load_row(next_base, next_page, next_valid, wave, static_cast<int>(opaque(lane)), 8);
       }
     }
 
@@ -319,8 +358,7 @@ decode_mfma_kernel(DecodeArgs a) {
         s[mb][i] = x;
         mx = fmaxf(mx, x);
       }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    mx = rows_max(mx);
     const float m_new = fmaxf(m_run, mx);
     const float alpha = m_run == m_new ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
     float psum = 0.f;
@@ -353,23 +391,30 @@ decode_mfma_kernel(DecodeArgs a) {
     const uint32_t otx = opaque(static_cast<uint32_t>(otok) << 5);
     {
       constexpr int kSteps = 2 * kColBlocks;
-      bf16x8 ring[kRing];
+      constexpr int kORing = 6;
+      bf16x8 ring[kORing];
 #pragma unroll
-      for (int st = 0; st < kRing; ++st) ring[st] = out_frag<kColBlocks>(ob, otx, st);
+      for (int st = 0; st < kORing; ++st) ring[st] = out_frag<kColBlocks>(ob, otx, st);
 #pragma unroll
       for (int st = 0; st < kSteps; ++st) {
-        const bf16x8 ct = ring[st % kRing];
-        if (st + kRing < kSteps) ring[st % kRing] = out_frag<kColBlocks>(ob, otx, st + kRing);
+        const bf16x8 ct = ring[st % kORing];
+        if (st + kORing < kSteps) ring[st % kORing] = out_frag<kColBlocks>(ob, otx, st + kORing);
         const int ks = st / kColBlocks, nb = st % kColBlocks;
         o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ct, pb[ks], o[nb], 0, 0, 0);
+      }
+      // Keep kORing fragments (2 transposing reads each) in flight.
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * kORing, 0);
+#pragma unroll
+      for (int st = 0; st < kSteps; ++st) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (st + kORing < kSteps) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
       }
     }
     stage ^= 1;
   }
 
   // ---- finalize: normalise and write this split's partial output and LSE
-  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
+  const float l_tot = rows_sum(l_run);
   const float inv = 1.f / l_tot;
 #pragma unroll
   for (int nb = 0; nb < kColBlocks; ++nb)

@@ -32,16 +32,13 @@ int check_heads(int heads, int groups, int d_c) {
 int launch_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH; }
 
 // Decode kernel selection: MLA_KV_DECODE_KERNEL = "generic" forces the shape-generic
-// kernel, "mfma" (one wave per 16 heads) or "pair" (wave pairs splitting the score
-// contraction) require that MFMA kernel (unsupported shapes then fail with
-// MLA_ERR_UNSUPPORTED); anything else picks the one-wave-per-16-heads MFMA kernel
-// whenever the shape has one.
-enum class DecodeKernel { kAuto, kGeneric, kMfma, kPair };
+// kernel, "mfma" requires the MFMA kernel (unsupported shapes then fail with
+// MLA_ERR_UNSUPPORTED), anything else picks the MFMA kernel whenever the shape has one.
+enum class DecodeKernel { kAuto, kGeneric, kMfma };
 DecodeKernel decode_kernel_choice() {
   const char* v = getenv("MLA_KV_DECODE_KERNEL");
   if (v != nullptr && strcmp(v, "generic") == 0) return DecodeKernel::kGeneric;
   if (v != nullptr && strcmp(v, "mfma") == 0) return DecodeKernel::kMfma;
-  if (v != nullptr && strcmp(v, "pair") == 0) return DecodeKernel::kPair;
   return DecodeKernel::kAuto;
 }
 
@@ -151,10 +148,7 @@ int mla_decode_paged(const void* q_abs, const void* q_r, const void* kv_cache,
   const DecodeKernel choice = decode_kernel_choice();
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const bool mfma_ok = mla::decode_mfma_supported(a, bf16);
-  const bool pair_ok = mla::decode_pair_supported(a, bf16);
   if (choice == DecodeKernel::kMfma && !mfma_ok) return MLA_ERR_UNSUPPORTED;
-  if (choice == DecodeKernel::kPair && !pair_ok) return MLA_ERR_UNSUPPORTED;
-  if (choice == DecodeKernel::kPair) return launch_status(mla::launch_decode_pair(a, s));
   if (mfma_ok && choice != DecodeKernel::kGeneric) return launch_status(mla::launch_decode_mfma(a, s));
   return launch_status(mla::launch_decode_generic(a, bf16, s));
 }

@@ -44,9 +44,6 @@ namespace mla {
 // MFMA split-KV decode: bf16, 128 heads, d_c 512, d_R 64, one latent group.
 bool decode_mfma_supported(const DecodeArgs& a, bool bf16);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s);
-// MFMA split-KV decode with wave pairs splitting the score contraction (same shapes).
-bool decode_pair_supported(const DecodeArgs& a, bool bf16);
-hipError_t launch_decode_pair(const DecodeArgs& a, hipStream_t s);
 }  // namespace mla
 
 namespace mla {

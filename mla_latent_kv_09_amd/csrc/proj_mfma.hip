@@ -26,6 +26,21 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
 // lane (n = d0 + l%16, k = 8*(l/16) + e) reads 16 contiguous bytes of row d, so
 // the wave's 16 x d_cg weight slice goes straight from HBM into registers (once).
 // A operand = o_latent[t][h][c], 16 bytes per lane, one M-block of 16 rows at a time.
+// All loads of an M-block (the wave's weight slice and the block's activation rows)
+// are issued before the first MFMA, so the kernel costs one memory round trip per
+// block rather than one per K-step.
+template <int kSteps>
+__device__ __forceinline__ void load_rows(const uint16_t* __restrict__ base, size_t row_stride,
+                                          int row, int n_rows, bf16x8 (&a)[kSteps]) {
+  const bool ok = row < n_rows;
+  const uint16_t* p = base + static_cast<size_t>(ok ? row : 0) * row_stride;
+#pragma unroll
+  for (int k = 0; k < kSteps; ++k) {
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(p + 32 * k);
+    a[k] = ok ? v : bf16x8{};
+  }
+}
+
 template <int kSteps>  // d_cg / 32
 __global__ void __launch_bounds__(64)
 up_v_mfma_kernel(const uint16_t* __restrict__ o_lat, const uint16_t* __restrict__ w_uv,
@@ -34,25 +49,20 @@ up_v_mfma_kernel(const uint16_t* __restrict__ o_lat, const uint16_t* __restrict_
   const int h = blockIdx.y;
   const int d0 = blockIdx.x * 16;
   const int lane = threadIdx.x, g = lane >> 4, j = lane & 15;
+  // A operand rows t0 + j of o_latent[t][h][:]; lane holds columns 32k + 8g .. +7.
+  const uint16_t* abase = o_lat + static_cast<size_t>(h) * d_cg + 8 * g;
+  const size_t astride = static_cast<size_t>(H) * d_cg;
+  bf16x8 a[kSteps];
+  load_rows<kSteps>(abase, astride, j, T, a);
   const uint16_t* wrow = w_uv + (static_cast<size_t>(h) * d_hc + d0 + j) * d_cg + 8 * g;
   bf16x8 b[kSteps];
 #pragma unroll
   for (int k = 0; k < kSteps; ++k) b[k] = *reinterpret_cast<const bf16x8*>(wrow + 32 * k);
   for (int t0 = 0; t0 < T; t0 += 16) {
-    const int ta = t0 + j;  // A-operand row of this lane
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (ta < T) {
-      const uint16_t* arow = o_lat + (static_cast<size_t>(ta) * H + h) * d_cg + 8 * g;
 #pragma unroll
-      for (int k = 0; k < kSteps; ++k) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(arow + 32 * k);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[k], acc, 0, 0, 0);
-      }
-    } else {
-      const bf16x8 z = {};
-#pragma unroll
-      for (int k = 0; k < kSteps; ++k) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(z, b[k], acc, 0, 0, 0);
-    }
+    for (int k = 0; k < kSteps; ++k) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[k], b[k], acc, 0, 0, 0);
+    if (t0 + 16 < T) load_rows<kSteps>(abase, astride, t0 + 16 + j, T, a);
     // D layout: lane holds rows t0 + 4g + i, column d0 + j.
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -81,6 +91,12 @@ absorb_mfma_kernel(const uint16_t* __restrict__ q_c, const uint16_t* __restrict_
   const int c0 = blockIdx.x * kAbsCols;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, j = lane & 15;
+  // The first block's query rows are requested before the weight tile, so both
+  // round trips overlap.
+  const uint16_t* abase = q_c + static_cast<size_t>(h) * d_hc + 8 * g;
+  const size_t astride = static_cast<size_t>(H) * d_hc;
+  bf16x8 a[kSteps];
+  load_rows<kSteps>(abase, astride, j, T, a);
   // Stage the tile: thread -> (row d = tid/8 + 32r, chunk tid%8 of 8 columns).
   const uint16_t* wsrc = w_uk + static_cast<size_t>(h) * d_hc * d_cg + c0;
 #pragma unroll
@@ -106,19 +122,10 @@ absorb_mfma_kernel(const uint16_t* __restrict__ q_c, const uint16_t* __restrict_
   }
   const int cout = c0 + 16 * wave + j;
   for (int t0 = 0; t0 < T; t0 += 16) {
-    const int ta = t0 + j;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    bf16x8 a[kSteps];
-    if (ta < T) {
-      const uint16_t* arow = q_c + (static_cast<size_t>(ta) * H + h) * d_hc + 8 * g;
-#pragma unroll
-      for (int k = 0; k < kSteps; ++k) a[k] = *reinterpret_cast<const bf16x8*>(arow + 32 * k);
-    } else {
-#pragma unroll
-      for (int k = 0; k < kSteps; ++k) a[k] = bf16x8{};
-    }
 #pragma unroll
     for (int k = 0; k < kSteps; ++k) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[k], b[k], acc, 0, 0, 0);
+    if (t0 + 16 < T) load_rows<kSteps>(abase, astride, t0 + 16 + j, T, a);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = t0 + 4 * g + i;
