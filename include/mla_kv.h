@@ -119,9 +119,13 @@ int mla_rope_table(float* cos_out, float* sin_out, int max_pos, int d_R, double 
  *   rope_cos, rope_sin  [rope_max_pos, d_R/2] float32 from mla_rope_table, or
  *               both NULL for no rotation.  Query i of sequence b sits at
  *               position seq_lens[b] - q_len_b + i (clamped into the table).
- * Outputs (caller-allocated workspace, float32)
- *   o_part      [T, H, num_splits, d_cg]: split s's softmax-normalised output
- *   lse_part    [T, H, num_splits]: split s's natural-log log-sum-exp of the
+ * Outputs (caller-allocated workspace)
+ *   o_part      [T, H, num_splits, d_cg] in the storage type (bfloat16 for
+ *               MLA_DTYPE_BF16, float32 for MLA_DTYPE_FP32): split s's
+ *               softmax-normalised output, accumulated in float32 and rounded
+ *               once on the way out (a normalised average of latent rows, so it
+ *               cannot exceed the cache's own range)
+ *   lse_part    [T, H, num_splits] float32: split s's natural-log log-sum-exp of the
  *               scaled scores; -INFINITY for an empty split, whose o_part rows
  *               are then left unwritten (mla_combine never reads them)
  * Split plan: sequence b has n_b = ceil(seq_lens[b] / page_size) pages, cut into
@@ -135,7 +139,7 @@ int mla_rope_table(float* cos_out, float* sin_out, int max_pos, int d_R, double 
 int mla_decode_paged(const void* q_abs, const void* q_r, const void* kv_cache,
                      const int32_t* page_table, const int32_t* seq_lens, const int32_t* cu_q,
                      const float* rope_cos, const float* rope_sin, int rope_max_pos,
-                     float* o_part, float* lse_part,
+                     void* o_part, float* lse_part,
                      int batch, int total_q, int max_pages_per_seq, int num_pool_pages,
                      int heads, int groups, int d_hc, int d_c, int d_R, int page_size,
                      int num_splits, int pages_per_split, float softmax_scale, int causal,
@@ -147,11 +151,12 @@ int mla_decode_paged(const void* q_abs, const void* q_r, const void* kv_cache,
  *   o_latent = sum_s w_s o_part[s] / sum_s w_s,  lse = M + log(sum_s w_s).
  * A row whose splits are all empty gets o_latent = 0 and lse = -INFINITY.
  *
- *   o_part   [T, H, num_splits, d_cg] float32, lse_part [T, H, num_splits] float32
+ *   o_part   [T, H, num_splits, d_cg] dtype (as written by mla_decode_paged),
+ *   lse_part [T, H, num_splits] float32; the merge itself runs in float32
  *   o_latent [T, H, d_cg] dtype output
  *   lse_out  [T, H] float32 output, or NULL
  */
-int mla_combine(const float* o_part, const float* lse_part, void* o_latent, float* lse_out,
+int mla_combine(const void* o_part, const float* lse_part, void* o_latent, float* lse_out,
                 int total_q, int heads, int groups, int d_c, int num_splits,
                 int dtype, void* stream);
 
@@ -167,8 +172,10 @@ int mla_up_v(const void* o_latent, const void* w_uv, void* out,
              int total_q, int heads, int groups, int d_hc, int d_c,
              int dtype, void* stream);
 
-/* Bytes of the o_part + lse_part workspace mla_decode_paged needs (0 on bad sizes). */
-size_t mla_decode_workspace_bytes(int total_q, int heads, int groups, int d_c, int num_splits);
+/* Bytes of the o_part + lse_part workspace mla_decode_paged needs for this dtype
+ * (0 on bad sizes or dtype): T*H*num_splits*(d_cg*elem + 4), elem = 2 for bf16. */
+size_t mla_decode_workspace_bytes(int total_q, int heads, int groups, int d_c, int num_splits,
+                                  int dtype);
 
 /* Static text for a status code (never NULL). */
 const char* mla_status_string(int status);

@@ -203,7 +203,7 @@ decode_mfma_kernel(DecodeArgs a) {
   const QueryWork w = query_work(a.cu_q, a.seq_lens, a.batch, t, split, S,
                                  a.pages_per_split, kTok, a.max_pages, a.causal);
   const size_t row = (static_cast<size_t>(t) * kHeads + head) * S + split;
-  float* o_out = a.o_part + row * kDcg;
+  __bf16* o_out = static_cast<__bf16*>(a.o_part) + row * kDcg;  // bf16 partials
   if (w.k0 >= w.k1) {  // empty split: only the LSE is written
     if (g == 0) a.lse_part[row] = -INFINITY;
     return;
@@ -418,7 +418,12 @@ decode_mfma_kernel(DecodeArgs a) {
   const float inv = 1.f / l_tot;
 #pragma unroll
   for (int nb = 0; nb < kColBlocks; ++nb)
-    *reinterpret_cast<f32x4*>(o_out + nb * 16 + 4 * g) = o[nb] * inv;
+  {
+    const f32x4 v = o[nb] * inv;
+    *reinterpret_cast<bf16x4*>(o_out + nb * 16 + 4 * g) =
+        bf16x4{static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]), static_cast<__bf16>(v[2]),
+               static_cast<__bf16>(v[3])};
+  }
   if (g == 0) a.lse_part[row] = (m_run + __log2f(l_tot)) * kLn2;
 }
 

@@ -111,7 +111,7 @@ __global__ void __launch_bounds__(kThreads) decode_generic_kernel(DecodeArgs a) 
   const QueryWork w = query_work(a.cu_q, a.seq_lens, a.batch, t, split, S,
                                  a.pages_per_split, a.page_size, a.max_pages, a.causal);
   const size_t row = (static_cast<size_t>(t) * H + h) * S + split;
-  float* o_out = a.o_part + row * d_cg;
+  T* o_out = static_cast<T*>(a.o_part) + row * d_cg;
   if (w.k0 >= w.k1) {  // empty split: only the LSE is written
     if (tid == 0) a.lse_part[row] = -INFINITY;
     return;
@@ -179,7 +179,7 @@ __global__ void __launch_bounds__(kThreads) decode_generic_kernel(DecodeArgs a) 
 #pragma unroll
   for (int k = 0; k < kColsPerThread; ++k) {
     const int c = tid + k * kThreads;
-    if (c < d_cg) o_out[c] = acc[k] * inv;
+    if (c < d_cg) store_elem(o_out, c, acc[k] * inv);
   }
   if (tid == 0) a.lse_part[row] = (m + log2f(l)) * kLn2;
 }
@@ -187,7 +187,7 @@ __global__ void __launch_bounds__(kThreads) decode_generic_kernel(DecodeArgs a) 
 // One block per (t, h): merge num_splits partials by their log-sum-exp.
 template <typename T>
 __global__ void __launch_bounds__(kThreads)
-combine_kernel(const float* __restrict__ o_part, const float* __restrict__ lse_part,
+combine_kernel(const T* __restrict__ o_part, const float* __restrict__ lse_part,
                T* __restrict__ o_lat, float* __restrict__ lse_out, int d_cg, int S) {
   constexpr int kMaxSplits = 256;
   __shared__ float w_s[kMaxSplits];
@@ -226,56 +226,73 @@ combine_kernel(const float* __restrict__ o_part, const float* __restrict__ lse_p
     float acc = 0.f;
     for (int s = 0; s < S; ++s) {
       const float ww = w_s[s];
-      if (ww != 0.f) acc = fmaf(ww, o_part[(r * S + s) * d_cg + c], acc);
+      if (ww != 0.f) acc = fmaf(ww, load_elem(o_part, (r * S + s) * d_cg + c), acc);
     }
     store_elem(o_lat, r * d_cg + c, acc * inv);
   }
   if (tid == 0 && lse_out != nullptr) lse_out[r] = M == -INFINITY ? -INFINITY : M + logf(sum);
 }
 
-// One wave per (t, h) row, four rows per block, for latent widths 256 and 512:
-// each lane owns kDcg/64 consecutive-by-4 columns and streams the non-empty
-// splits' partials with 16-byte loads, four splits per iteration.
+// Four consecutive partials as float32 (8-byte bf16 or 16-byte fp32 load).
+__device__ __forceinline__ float __attribute__((ext_vector_type(4))) load4(const float* p) {
+  return *reinterpret_cast<const float __attribute__((ext_vector_type(4)))*>(p);
+}
+__device__ __forceinline__ float __attribute__((ext_vector_type(4))) load4(const uint16_t* p) {
+  const uint2 u = *reinterpret_cast<const uint2*>(p);
+  return {__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+          __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+}
+
+// Vectorised combine for d_cg in {256, 512}: one wave per (t, h) row, float4 per lane.
+// The partials of up to 16 splits are requested together, before the log-sum-exp
+// reduction, so a row costs about one memory round trip rather than one per group of
+// splits.  Splits with LSE = -inf (no keys) get weight 0 and their partials -- never
+// written -- are not used.
 template <typename T, int kDcg>
 __global__ void __launch_bounds__(kThreads)
-combine_vec_kernel(const float* __restrict__ o_part, const float* __restrict__ lse_part,
+combine_vec_kernel(const T* __restrict__ o_part, const float* __restrict__ lse_part,
                    T* __restrict__ o_lat, float* __restrict__ lse_out, int rows, int S) {
   constexpr int kVec = kDcg / 256;  // float4 groups per lane
+  constexpr int kChunk = 16;        // splits in flight per wave
   typedef float f32x4 __attribute__((ext_vector_type(4)));
   const int lane = threadIdx.x & 63;
   const size_t r = static_cast<size_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
   if (r >= static_cast<size_t>(rows)) return;
   const float* lse = lse_part + r * S;
-  float mx = -INFINITY;
-  for (int s = lane; s < S; s += 64) mx = fmaxf(mx, lse[s]);
+  const T* base = o_part + r * S * kDcg + 4 * lane;
+  auto load_chunk = [&](int s0, f32x4 (&x)[kChunk][kVec]) {
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      const int s = min(s0 + u, S - 1);  // in bounds; splits past S get weight 0
+#pragma unroll
+      for (int v = 0; v < kVec; ++v) x[u][v] = load4(base + s * kDcg + 256 * v);
+    }
+  };
+  // Lane s holds the LSE of split s (s < 64): loaded before the partials so that its
+  // wait does not also wait for them, and broadcast with readlane below.
+  const float l_lane = lane < S ? lse[lane] : -INFINITY;
+  f32x4 x[kChunk][kVec];
+  load_chunk(0, x);
+  float mx = l_lane;
+  for (int s = lane + 64; s < S; s += 64) mx = fmaxf(mx, lse[s]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-  float sum = 0.f;
-  if (mx != -INFINITY)
-    for (int s = lane; s < S; s += 64) sum += expf(lse[s] - mx);
-  sum = wave_sum(sum);
   f32x4 acc[kVec];
 #pragma unroll
   for (int v = 0; v < kVec; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (mx != -INFINITY) {
-    const float* base = o_part + r * S * kDcg + 4 * lane;
-    for (int s0 = 0; s0 < S; s0 += 4) {
-      float wt[4];
-      f32x4 x[4][kVec];
+  float sum = 0.f;
+  for (int s0 = 0; s0 < S; s0 += kChunk) {
+    if (s0 > 0) load_chunk(s0, x);
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int s = s0 + u;
-        const float l = s < S ? lse[s] : -INFINITY;
-        wt[u] = l == -INFINITY ? 0.f : expf(l - mx);
+    for (int u = 0; u < kChunk; ++u) {
+      const int s = s0 + u;
+      float l = -INFINITY;
+      if (s < S) l = s < 64 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_lane), s)) : lse[s];
+      const float wt = (l == -INFINITY || mx == -INFINITY) ? 0.f : expf(l - mx);
+      sum += wt;
 #pragma unroll
-        for (int v = 0; v < kVec; ++v)
-          x[u][v] = wt[u] != 0.f ? *reinterpret_cast<const f32x4*>(base + s * kDcg + 256 * v)
-                                 : f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int v = 0; v < kVec; ++v) acc[v] += wt[u] * x[u][v];
+      for (int v = 0; v < kVec; ++v)
+        if (wt != 0.f) acc[v] += wt * x[u][v];
     }
   }
   const float inv = mx == -INFINITY ? 0.f : 1.f / sum;
@@ -339,32 +356,34 @@ hipError_t launch_decode_generic(const DecodeArgs& a, bool bf16, hipStream_t s) 
   return hipGetLastError();
 }
 
-hipError_t launch_combine(const float* o_part, const float* lse_part, void* o_lat, float* lse_out,
+hipError_t launch_combine(const void* o_part_v, const float* lse_part, void* o_lat, float* lse_out,
                           int T, int H, int d_cg, int S, bool bf16, hipStream_t s) {
   const int rows = T * H;
+  const auto* op16 = static_cast<const uint16_t*>(o_part_v);
+  const auto* op32 = static_cast<const float*>(o_part_v);
   if (d_cg == 512 || d_cg == 256) {
     const dim3 vgrid((rows + 3) / 4);
     if (bf16) {
       auto* o = static_cast<uint16_t*>(o_lat);
       if (d_cg == 512)
-        combine_vec_kernel<uint16_t, 512><<<vgrid, kThreads, 0, s>>>(o_part, lse_part, o, lse_out, rows, S);
+        combine_vec_kernel<uint16_t, 512><<<vgrid, kThreads, 0, s>>>(op16, lse_part, o, lse_out, rows, S);
       else
-        combine_vec_kernel<uint16_t, 256><<<vgrid, kThreads, 0, s>>>(o_part, lse_part, o, lse_out, rows, S);
+        combine_vec_kernel<uint16_t, 256><<<vgrid, kThreads, 0, s>>>(op16, lse_part, o, lse_out, rows, S);
     } else {
       auto* o = static_cast<float*>(o_lat);
       if (d_cg == 512)
-        combine_vec_kernel<float, 512><<<vgrid, kThreads, 0, s>>>(o_part, lse_part, o, lse_out, rows, S);
+        combine_vec_kernel<float, 512><<<vgrid, kThreads, 0, s>>>(op32, lse_part, o, lse_out, rows, S);
       else
-        combine_vec_kernel<float, 256><<<vgrid, kThreads, 0, s>>>(o_part, lse_part, o, lse_out, rows, S);
+        combine_vec_kernel<float, 256><<<vgrid, kThreads, 0, s>>>(op32, lse_part, o, lse_out, rows, S);
     }
     return hipGetLastError();
   }
   const dim3 grid(static_cast<unsigned>(T) * H);
   if (bf16)
-    combine_kernel<uint16_t><<<grid, kThreads, 0, s>>>(o_part, lse_part, static_cast<uint16_t*>(o_lat),
+    combine_kernel<uint16_t><<<grid, kThreads, 0, s>>>(op16, lse_part, static_cast<uint16_t*>(o_lat),
                                                        lse_out, d_cg, S);
   else
-    combine_kernel<float><<<grid, kThreads, 0, s>>>(o_part, lse_part, static_cast<float*>(o_lat),
+    combine_kernel<float><<<grid, kThreads, 0, s>>>(op32, lse_part, static_cast<float*>(o_lat),
                                                     lse_out, d_cg, S);
   return hipGetLastError();
 }

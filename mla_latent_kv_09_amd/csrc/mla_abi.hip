@@ -61,10 +61,13 @@ const char* mla_status_string(int status) {
   }
 }
 
-size_t mla_decode_workspace_bytes(int total_q, int heads, int groups, int d_c, int num_splits) {
+size_t mla_decode_workspace_bytes(int total_q, int heads, int groups, int d_c, int num_splits,
+                                  int dtype) {
   if (total_q < 0 || num_splits <= 0 || check_heads(heads, groups, d_c) != MLA_OK) return 0;
+  if (check_dtype(dtype) != MLA_OK) return 0;
+  const size_t elem = dtype == MLA_DTYPE_BF16 ? 2 : 4;
   const size_t rows = static_cast<size_t>(total_q) * heads * num_splits;
-  return rows * (static_cast<size_t>(d_c / groups) + 1) * sizeof(float);
+  return rows * (static_cast<size_t>(d_c / groups) * elem + sizeof(float));
 }
 
 int mla_absorb_q(const void* q_c, const void* w_uk, void* q_abs, int total_q, int heads, int groups,
@@ -97,7 +100,7 @@ int mla_rope_table(float* cos_out, float* sin_out, int max_pos, int d_R, double 
 int mla_decode_paged(const void* q_abs, const void* q_r, const void* kv_cache,
                      const int32_t* page_table, const int32_t* seq_lens, const int32_t* cu_q,
                      const float* rope_cos, const float* rope_sin, int rope_max_pos,
-                     float* o_part, float* lse_part, int batch, int total_q, int max_pages_per_seq,
+                     void* o_part, float* lse_part, int batch, int total_q, int max_pages_per_seq,
                      int num_pool_pages, int heads, int groups, int d_hc, int d_c, int d_R,
                      int page_size, int num_splits, int pages_per_split, float softmax_scale,
                      int causal, int dtype, void* stream) {
@@ -153,7 +156,7 @@ int mla_decode_paged(const void* q_abs, const void* q_r, const void* kv_cache,
   return launch_status(mla::launch_decode_generic(a, bf16, s));
 }
 
-int mla_combine(const float* o_part, const float* lse_part, void* o_latent, float* lse_out,
+int mla_combine(const void* o_part, const float* lse_part, void* o_latent, float* lse_out,
                 int total_q, int heads, int groups, int d_c, int num_splits, int dtype,
                 void* stream) {
   int st = check_dtype(dtype);

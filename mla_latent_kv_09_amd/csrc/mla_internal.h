@@ -17,7 +17,7 @@ struct DecodeArgs {
   const float* rope_cos;
   const float* rope_sin;
   int rope_max_pos;
-  float* o_part;
+  void* o_part;      // [T, H, S, d_cg] in the storage type (bf16 or fp32)
   float* lse_part;
   int batch, total_q, max_pages, num_pool_pages;
   int heads, groups, d_c, d_R, page_size, num_splits, pages_per_split;
@@ -33,7 +33,7 @@ hipError_t launch_up_v_generic(const void* o_lat, const void* w_uv, void* out, i
 hipError_t launch_decode_generic(const DecodeArgs& a, bool bf16, hipStream_t s);
 
 // Combine and RoPE table (one implementation each).
-hipError_t launch_combine(const float* o_part, const float* lse_part, void* o_lat, float* lse_out,
+hipError_t launch_combine(const void* o_part, const float* lse_part, void* o_lat, float* lse_out,
                           int T, int H, int d_cg, int S, bool bf16, hipStream_t s);
 hipError_t launch_rope_table(float* cos_out, float* sin_out, int max_pos, int d_R, double base,
                              hipStream_t s);

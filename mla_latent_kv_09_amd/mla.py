@@ -50,7 +50,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_decode_paged.argtypes = ([P] * 8 + [I] + [P] * 2 + [I] * 12 + [F, I, I, P])
     lib.mla_combine.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
     lib.mla_up_v.argtypes = [P, P, P, I, I, I, I, I, I, P]
-    lib.mla_decode_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.mla_decode_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.mla_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.mla_status_string.argtypes = [I]
     lib.mla_status_string.restype = ctypes.c_char_p
@@ -121,9 +121,11 @@ def rope_table(max_pos: int, d_R: int, base: float = 10000.0, *, device="cuda", 
     return cos, sin
 
 
-def workspace(total_q: int, heads: int, d_cg: int, num_splits: int, device="cuda"):
-    """Allocate the (o_part, lse_part) split workspace."""
-    o_part = torch.empty((total_q, heads, num_splits, d_cg), dtype=torch.float32, device=device)
+def workspace(total_q: int, heads: int, d_cg: int, num_splits: int, device="cuda",
+              dtype=torch.bfloat16):
+    """Allocate the (o_part, lse_part) split workspace: o_part in the storage dtype,
+    lse_part in float32."""
+    o_part = torch.empty((total_q, heads, num_splits, d_cg), dtype=dtype, device=device)
     lse_part = torch.empty((total_q, heads, num_splits), dtype=torch.float32, device=device)
     return o_part, lse_part
 
@@ -142,7 +144,7 @@ def decode_paged(q_abs, q_r, kv_cache, page_table, seq_lens, cu_q, o_part, lse_p
     if o_part.shape != (T, H, S, d_cg) or lse_part.shape != (T, H, S):
         raise ValueError("o_part must be [T,H,S,d_c/G] and lse_part [T,H,S]")
     for t, dt in ((page_table, torch.int32), (seq_lens, torch.int32), (cu_q, torch.int32),
-                  (o_part, torch.float32), (lse_part, torch.float32)):
+                  (o_part, q_abs.dtype), (lse_part, torch.float32)):
         if t.dtype != dt:
             raise TypeError(f"expected {dt}, got {t.dtype}")
     if seq_lens.shape != (B,) or cu_q.shape != (B + 1,):
@@ -165,6 +167,8 @@ def combine(o_part, lse_part, o_latent=None, lse_out=None, *, dtype=torch.bfloat
     T, H, S, d_cg = o_part.shape
     if o_latent is None:
         o_latent = torch.empty((T, H, d_cg), dtype=dtype, device=o_part.device)
+    if o_part.dtype != o_latent.dtype or lse_part.dtype != torch.float32:
+        raise TypeError("o_part must share o_latent's dtype and lse_part must be float32")
     _dev(o_part, lse_part, o_latent, lse_out)
     _check("mla_combine", load().mla_combine(
         _ptr(o_part), _ptr(lse_part), _ptr(o_latent), _ptr(lse_out), T, H, 1, d_cg, S,
@@ -220,7 +224,7 @@ class DecodeStep:
         self.num_splits = num_splits
         dev = q_c.device
         self.q_abs = torch.empty((T, H, d_cg), dtype=q_c.dtype, device=dev)
-        self.o_part, self.lse_part = workspace(T, H, d_cg, num_splits, dev)
+        self.o_part, self.lse_part = workspace(T, H, d_cg, num_splits, dev, q_c.dtype)
         self.o_latent = torch.empty((T, H, d_cg), dtype=q_c.dtype, device=dev)
         self.lse = torch.empty((T, H), dtype=torch.float32, device=dev)
         self.out = torch.empty((T, H, d_hc), dtype=q_c.dtype, device=dev)

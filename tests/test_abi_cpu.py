@@ -54,10 +54,14 @@ def test_status_strings(lib):
 
 
 def test_workspace_bytes(lib):
-    assert lib.mla_decode_workspace_bytes(16, 128, 1, 512, 16) == 16 * 128 * 16 * 513 * 4
-    assert lib.mla_decode_workspace_bytes(32, 128, 2, 512, 8) == 32 * 128 * 8 * 257 * 4
-    assert lib.mla_decode_workspace_bytes(16, 128, 3, 512, 16) == 0      # 128 % 3 != 0
-    assert lib.mla_decode_workspace_bytes(16, 128, 1, 512, 0) == 0
+    bf16, fp32 = 0, 1
+    # o_part rows in the storage type plus one float32 LSE per row.
+    assert lib.mla_decode_workspace_bytes(16, 128, 1, 512, 16, bf16) == 16 * 128 * 16 * (512 * 2 + 4)
+    assert lib.mla_decode_workspace_bytes(32, 128, 2, 512, 8, bf16) == 32 * 128 * 8 * (256 * 2 + 4)
+    assert lib.mla_decode_workspace_bytes(16, 128, 1, 512, 16, fp32) == 16 * 128 * 16 * (512 * 4 + 4)
+    assert lib.mla_decode_workspace_bytes(16, 128, 3, 512, 16, bf16) == 0  # 128 % 3 != 0
+    assert lib.mla_decode_workspace_bytes(16, 128, 1, 512, 0, bf16) == 0
+    assert lib.mla_decode_workspace_bytes(16, 128, 1, 512, 16, 7) == 0     # unknown dtype
 
 
 # -------------------------------------------------------------- absorb / up_v
