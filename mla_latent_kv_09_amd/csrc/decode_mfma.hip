@@ -11,6 +11,12 @@
 // (nxmr.cn/news/151634 §1: the 512-d latent plus the 64-d shared RoPE key is all a
 // token stores).  Softmax statistics are fp32 (online, one page at a time).
 //
+// Softmax reference: the exponentials of a page are taken against a per-head
+// reference m that only moves when a page's maximum exceeds it by more than kSlack
+// (log2 units), so p <= 2^kSlack and the running output is rescaled only on those
+// rare moves.  Output and log-sum-exp are normalised against the same m at the end,
+// so the result is the same softmax.
+//
 // Work layout (workgroup = 8 waves, two per SIMD):
 //   wave w owns heads 16w .. 16w+15; lane l owns head 16w + l%16, and the four
 //   lanes l%16 + 16g (g = 0..3) split that head's keys (scores) and latent
@@ -52,6 +58,7 @@ constexpr int kRBytes = kTok * kDr * 2;  // 8 KB RoPE part
 constexpr int kStageBytes = kCBytes + kRBytes;
 constexpr int kQrOff = 2 * kStageBytes;   // rotated q_R of all heads lives after the two stages
 constexpr int kLdsBytes = kQrOff + kHeads * kDr * 2;
+constexpr float kSlack = 8.f;             // softmax reference slack, log2 units
 template <int G> struct Shape {
   static constexpr int kDcg = kDc / G;        // latent columns seen by one head
   static constexpr int kQSteps = kDcg / 32;   // latent K-steps of 32 dims (+2 RoPE steps)
@@ -265,8 +272,8 @@ decode_mfma_kernel(DecodeArgs a) {
   }
 
   const float scale_log2 = a.scale * kLog2e;
-  float m_run = -INFINITY;   // running max of scaled scores (log2 units), same in the 4 lanes of a head
-  float l_run = 0.f;         // this lane's share of the running sum
+  float m_ref = -INFINITY;   // softmax reference of this lane's head (log2 units), same in its 4 lanes
+  float l_run = 0.f;         // this lane's share of the running sum against m_ref
   f32x4 o[kColBlocks];       // O^T block nb: columns 16nb + 4g .. +3 of this lane's head
 #pragma unroll
   for (int nb = 0; nb < kColBlocks; ++nb) o[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -359,8 +366,10 @@ decode_mfma_kernel(DecodeArgs a) {
         mx = fmaxf(mx, x);
       }
     mx = rows_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float alpha = m_run == m_new ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+    const float m_old = m_ref;
+    const bool grow = mx > m_old + kSlack;   // always true on the first page
+    const float m_new = grow ? mx : m_old;
+    const float alpha = __builtin_amdgcn_exp2f(m_old - m_new);  // 0 on the first page
     float psum = 0.f;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
@@ -371,8 +380,10 @@ decode_mfma_kernel(DecodeArgs a) {
         psum += p;
       }
     l_run = l_run * alpha + psum;
-    m_run = m_new;
-    if (__any(alpha != 1.f)) {
+    m_ref = m_new;
+    // The output only needs rescaling when a reference that was already in use moves
+    // (before the first page it is still zero).
+    if (__any(grow && m_old != -INFINITY)) {
 #pragma unroll
       for (int nb = 0; nb < kColBlocks; ++nb) o[nb] *= alpha;
     }
@@ -424,7 +435,7 @@ decode_mfma_kernel(DecodeArgs a) {
         bf16x4{static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]), static_cast<__bf16>(v[2]),
                static_cast<__bf16>(v[3])};
   }
-  if (g == 0) a.lse_part[row] = (m_run + __log2f(l_tot)) * kLn2;
+  if (g == 0) a.lse_part[row] = (m_ref + __log2f(l_tot)) * kLn2;
 }
 
 }  // namespace

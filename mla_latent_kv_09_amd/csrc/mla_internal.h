@@ -41,7 +41,7 @@ hipError_t launch_rope_table(float* cos_out, float* sin_out, int max_pos, int d_
 }  // namespace mla
 
 namespace mla {
-// MFMA split-KV decode: bf16, 128 heads, d_c 512, d_R 64, one latent group.
+// MFMA split-KV decode: bf16, 128 heads, d_c 512, d_R 64, one or two latent groups.
 bool decode_mfma_supported(const DecodeArgs& a, bool bf16);
 hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s);
 }  // namespace mla

@@ -10,6 +10,7 @@ has not been built.
 from __future__ import annotations
 
 import ctypes
+import heapq
 import math
 import os
 from typing import Optional
@@ -191,18 +192,52 @@ def up_v(o_latent, w_uv, out=None, *, groups: int = 1, stream=None):
     return out
 
 
+# Cost of one split in units of one page (streaming 72 KB and computing 128 heads
+# over it): a fixed part for the prologue (queries fetched, first page in flight) and
+# the epilogue (bf16 partial written, 128 KB), measured at about 2.5 pages on MI355X,
+# plus one unit per page.  A split with no keys exits at once.
+SPLIT_OVERHEAD_PAGES = 2.5
+EMPTY_SPLIT_PAGES = 0.2
+
+
+def plan_makespan(pages, q_lens, pages_per_split: int, cu_count: int = 256) -> float:
+    """Finish time, in page units, of the decode grid under the cost model above when
+    the dispatcher hands workgroups to the first free CU in launch order (query token
+    fastest, split slowest), one workgroup per CU at a time."""
+    n_splits = max(math.ceil(p / pages_per_split) for p in pages)
+    free = [0.0] * cu_count
+    for y in range(n_splits):
+        for p, n in zip(pages, q_lens):
+            work = min(pages_per_split, p - y * pages_per_split)
+            cost = SPLIT_OVERHEAD_PAGES + work if work > 0 else EMPTY_SPLIT_PAGES
+            for _ in range(n):
+                heapq.heapreplace(free, free[0] + cost)
+    return max(free)
+
+
 def split_plan(seq_lens_host, q_lens_host, cu_count: int = 256):
-    """(num_splits, pages_per_split) for a batch: about one workgroup per CU when
-    all sequences have about the same length, four per CU when they differ (long
-    sequences are cut finer so the dispatcher can balance), never fewer than 4
-    pages per split (a split pays a fixed prologue and epilogue)."""
+    """(num_splits, pages_per_split) for a batch: the split length whose grid finishes
+    first under plan_makespan's model, among at most 256 splits per sequence.  The
+    candidates are the shortest split lengths for each split count of the longest
+    sequence and the lengths that give k workgroups per CU for small k; a tie goes
+    to the fewer workgroups (less partial output to merge)."""
     pages = [max(1, math.ceil(int(L) / PAGE_SIZE)) for L in seq_lens_host]
     q = [int(x) for x in q_lens_host]
+    max_p = max(pages)
     total = sum(p * n for p, n in zip(pages, q))
-    ragged = max(pages) > 1.25 * min(pages)
-    pps = max(4, math.ceil(total / (cu_count * (4 if ragged else 1))))
-    num_splits = max(1, min(256, max(math.ceil(p / pps) for p in pages)))
-    return num_splits, pps
+    cands = {math.ceil(max_p / s) for s in range(1, min(256, max_p) + 1)}
+    cands |= {max(1, math.ceil(total / (cu_count * k))) for k in range(1, 17)}
+    cands = sorted(c for c in cands if math.ceil(max_p / c) <= 256)
+    if len(cands) > 96:  # keep the evaluation cheap: the longest splits plus a spread
+        cands = sorted(set(cands[-64:]) | set(cands[:: max(1, len(cands) // 32)]))
+    best = None
+    for pps in cands:
+        n_wg = sum(n * math.ceil(p / pps) for p, n in zip(pages, q))
+        key = (plan_makespan(pages, q, pps, cu_count), n_wg)
+        if best is None or key < best[0]:
+            best = (key, pps)
+    pps = best[1]
+    return max(1, math.ceil(max_p / pps)), pps
 
 
 class DecodeStep:

@@ -230,6 +230,55 @@ def test_decode_kernels_agree(case, monkeypatch):
         assert_parity(outs[kind], outs["generic"], what=f"{kind} vs generic")
 
 
+@pytest.mark.parametrize("kind", ["mfma", "generic"])
+@pytest.mark.parametrize("case,mode", [("dsv3_small", "grow"), ("dsv3_small", "flood"),
+                                       ("dsv3_small", "shrink"), ("gla2_small", "grow"),
+                                       ("gla2_small", "flood")])
+def test_softmax_reference_moves(kind, case, mode, monkeypatch):
+    """Pages 2.. of every sequence rewritten (exactly, in bf16), one split per sequence.
+    grow:   rows scaled by 4; the later pages' score maxima (std ~1.4 -> ~5.8 log2
+            units) exceed the first page's by more than the kernels' softmax reference
+            slack (8 log2 units) for most heads, so the running output is rescaled
+            mid-split.
+    flood:  every row replaced by one row scaled by 512; heads that score it positive
+            see their reference jump by hundreds of log2 units (the rescale factor
+            underflows to zero) and a softmax spread evenly over identical rows, so the
+            output is that row exactly; the other heads keep the first pages.
+    shrink: rows scaled by 1/64; the first pages keep the reference for the whole split.
+    Scaled rows scale the rounding error of a score with them, so W_UK is a selection
+    matrix (q_abs = q_c on the first d_hc latent columns, exact in bf16) and RoPE is
+    off (a rotated q_R is rounded to bf16): the scores then differ from the oracle's
+    by fp32 accumulation only, and the comparison tests the kernels' softmax."""
+    w = wl.make_workload(SMALL_CASES[case])
+    H, d_hc, d_cg = w.w_uk.shape
+    w.w_uk = np.zeros_like(w.w_uk)
+    w.w_uk[:, np.arange(d_hc), np.arange(d_hc)] = 1.0
+    ps = w.cfg.page_size
+    for b in range(len(w.seq_lens)):
+        L = int(w.seq_lens[b])
+        n_pages = (L + ps - 1) // ps
+        if n_pages < 3:
+            continue
+        first = wl.bf16_bits_to_f32(w.pool[w.page_table[b, 2], 0]).copy()
+        for k in range(2, n_pages):
+            pg = w.page_table[b, k]
+            n = min(ps, L - k * ps)             # rows past the sequence end stay NaN
+            x = wl.bf16_bits_to_f32(w.pool[pg, :n])
+            if mode == "grow":
+                x = x * np.float32(4.0)
+            elif mode == "shrink":
+                x = x * np.float32(1.0 / 64.0)
+            else:
+                x = np.broadcast_to(first * np.float32(512.0), x.shape)
+            w.pool[pg, :n] = wl.bf16_bits(x)
+    monkeypatch.setenv("MLA_KV_DECODE_KERNEL", kind)
+    print(f"case {case} mode {mode} kernel {kind}", flush=True)
+    step = run_step(w, num_splits=1, rope=False)
+    ref = oracle_for(w, rope=False)
+    assert_parity(_f64(step.o_latent), ref["o_latent"], what="o_latent")
+    assert_parity(_f64(step.out), ref["out"])
+
+
 def test_combine_ignores_unwritten_empty_splits():
     """Empty splits leave their o_part rows unwritten; NaN there must not reach the output."""
     w = wl.make_workload(_small("ragged_b64", batch=4, seq_len_range=(10, 300)))

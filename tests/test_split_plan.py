@@ -1,0 +1,64 @@
+"""Host-side split planning (CPU only): coverage, the split-count limit, one workgroup
+per CU on uniform batches, and the dispatch model it optimises."""
+import math
+
+import numpy as np
+import pytest
+
+from mla_latent_kv_09_amd import mla
+from mla_latent_kv_09_amd import workloads as wl
+
+
+def _lens(cfg):
+    if cfg.seq_len_range is not None:
+        lo, hi = cfg.seq_len_range
+        L = wl._rng(cfg.seed, "lengths").integers(lo, hi + 1, size=cfg.batch)
+    else:
+        L = np.full(cfg.batch, cfg.seq_len)
+    q = np.full(cfg.batch, cfg.q_len)
+    if cfg.q_len_mix:
+        q = np.ones(cfg.batch, dtype=np.int64)
+        q[wl._rng(cfg.seed, "q_lens").permutation(cfg.batch)[: cfg.batch // 2]] = 2
+    return [int(x) for x in L], [int(x) for x in q]
+
+
+@pytest.mark.parametrize("name", ["dsv3_b16_l4096", "long_b16_l65536", "ragged_b64",
+                                  "gla2_b32_l16384"])
+def test_plan_covers_every_page_within_the_split_limit(name):
+    L, q = _lens(wl.CONFIGS[name])
+    S, pps = mla.split_plan(L, q)
+    pages = [math.ceil(x / mla.PAGE_SIZE) for x in L]
+    assert 1 <= S <= 256 and pps >= 1
+    assert S * pps >= max(pages)               # the last split never has to take extra pages
+    assert (S - 1) * pps < max(pages)          # and no split is empty for the longest sequence
+
+
+@pytest.mark.parametrize("name,expect", [("dsv3_b16_l4096", (16, 4)), ("long_b16_l65536", (16, 64)),
+                                         ("gla2_b32_l16384", (8, 32))])
+def test_uniform_batches_get_one_workgroup_per_cu(name, expect):
+    L, q = _lens(wl.CONFIGS[name])
+    S, pps = mla.split_plan(L, q)
+    assert (S, pps) == expect
+    assert sum(n * S for n in q) == 256
+
+
+def test_makespan_model_by_hand():
+    # 4 CUs, 2 sequences of 8 pages, q_len 1: splits of 4 pages -> 4 workgroups, one each.
+    assert mla.plan_makespan([8, 8], [1, 1], 4, cu_count=4) == pytest.approx(
+        mla.SPLIT_OVERHEAD_PAGES + 4)
+    # 3 CUs: the fourth workgroup queues behind the first to finish.
+    assert mla.plan_makespan([8, 8], [1, 1], 4, cu_count=3) == pytest.approx(
+        2 * (mla.SPLIT_OVERHEAD_PAGES + 4))
+    # an empty split (short sequence past its pages) costs only the early exit
+    assert mla.plan_makespan([8, 1], [1, 1], 4, cu_count=8) == pytest.approx(
+        mla.SPLIT_OVERHEAD_PAGES + 4)
+
+
+def test_ragged_plan_no_worse_than_any_candidate_length():
+    L, q = _lens(wl.CONFIGS["ragged_b64"])
+    pages = [math.ceil(x / mla.PAGE_SIZE) for x in L]
+    S, pps = mla.split_plan(L, q)
+    best = mla.plan_makespan(pages, q, pps)
+    for other in (4, 8, 16, 24, 28, 32, 48, 64, 128):
+        if math.ceil(max(pages) / other) <= 256:
+            assert best <= mla.plan_makespan(pages, q, other) + 1e-9
