@@ -21,6 +21,20 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
 
+// Workgroup -> (x, head) for a 1-D launch of nx * n_heads workgroups.  The dispatcher
+// deals workgroups to the 8 XCDs of the chip in turn (id mod 8), and every XCD has its
+// own L2; the nx workgroups of one head read the same activation rows, so they are
+// placed on one XCD (ids with the same residue mod 8, consecutive in that XCD's order)
+// and the rows come from HBM once instead of once per XCD.  Head counts that are not a
+// multiple of 8 keep the plain order.
+struct HeadTile { int x, head; };
+__device__ __forceinline__ HeadTile head_tile(int nx, int n_heads) {
+  const int L = blockIdx.x;
+  if (n_heads % 8 != 0) return {L % nx, L / nx};
+  const int r = L >> 3;
+  return {r % nx, (r / nx) * 8 + (L & 7)};
+}
+
 // ---------------------------------------------------------------- up_v
 // One wave per (head h, 16 output dims d0..d0+15).  B operand = W_UV[h][d][c]:
 // lane (n = d0 + l%16, k = 8*(l/16) + e) reads 16 contiguous bytes of row d, so
@@ -46,8 +60,9 @@ __global__ void __launch_bounds__(64)
 up_v_mfma_kernel(const uint16_t* __restrict__ o_lat, const uint16_t* __restrict__ w_uv,
                  uint16_t* __restrict__ out, int T, int H, int d_hc) {
   constexpr int d_cg = kSteps * 32;
-  const int h = blockIdx.y;
-  const int d0 = blockIdx.x * 16;
+  const HeadTile ht = head_tile(d_hc / 16, H);
+  const int h = ht.head;
+  const int d0 = ht.x * 16;
   const int lane = threadIdx.x, g = lane >> 4, j = lane & 15;
   // A operand rows t0 + j of o_latent[t][h][:]; lane holds columns 32k + 8g .. +7.
   const uint16_t* abase = o_lat + static_cast<size_t>(h) * d_cg + 8 * g;
@@ -87,8 +102,9 @@ absorb_mfma_kernel(const uint16_t* __restrict__ q_c, const uint16_t* __restrict_
                    uint16_t* __restrict__ q_abs, int T, int H, int d_cg) {
   constexpr int d_hc = kSteps * 32;
   __shared__ __attribute__((aligned(16))) char tile[d_hc * kAbsRowBytes];
-  const int h = blockIdx.y;
-  const int c0 = blockIdx.x * kAbsCols;
+  const HeadTile ht = head_tile(d_cg / kAbsCols, H);
+  const int h = ht.head;
+  const int c0 = ht.x * kAbsCols;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, j = lane & 15;
   // The first block's query rows are requested before the weight tile, so both
@@ -146,7 +162,7 @@ bool absorb_mfma_supported(int d_hc, int d_cg, bool bf16) {
 
 hipError_t launch_up_v_mfma(const void* o_lat, const void* w_uv, void* out, int T, int H, int d_hc,
                             int d_cg, hipStream_t s) {
-  const dim3 grid(d_hc / 16, H);
+  const dim3 grid((d_hc / 16) * H);
   const auto* o = static_cast<const uint16_t*>(o_lat);
   const auto* wt = static_cast<const uint16_t*>(w_uv);
   auto* dst = static_cast<uint16_t*>(out);
@@ -160,7 +176,7 @@ hipError_t launch_up_v_mfma(const void* o_lat, const void* w_uv, void* out, int 
 hipError_t launch_absorb_mfma(const void* q_c, const void* w_uk, void* q_abs, int T, int H,
                               int d_hc, int d_cg, hipStream_t s) {
   (void)d_hc;
-  const dim3 grid(d_cg / kAbsCols, H);
+  const dim3 grid((d_cg / kAbsCols) * H);
   absorb_mfma_kernel<4><<<grid, 256, 0, s>>>(static_cast<const uint16_t*>(q_c),
                                              static_cast<const uint16_t*>(w_uk),
                                              static_cast<uint16_t*>(q_abs), T, H, d_cg);
