@@ -30,7 +30,8 @@
  *   failure of a vectorized gather, P3 §5).
  * - dtype selects the storage type of the non-float32 tensors: MLA_DTYPE_BF16
  *   (bfloat16 storage and MFMA operands, fp32 accumulation) or MLA_DTYPE_FP32.
- *   Softmax state, split partials and the log-sum-exp are always float32.
+ *   Softmax state and the log-sum-exp are always float32; split partial outputs
+ *   are kept in the storage type (see mla_decode_paged).
  * - Indices: T = total query tokens of the batch (queries of all sequences
  *   packed back to back), H = heads, G = latent groups (1 = MLA; >1 = grouped
  *   latent attention, P1 §1), d_cg = d_c / G.  Head h belongs to group
@@ -134,7 +135,7 @@ int mla_rope_table(float* cos_out, float* sin_out, int max_pos, int d_R, double 
  * split (s = num_splits - 1) runs to the end of the sequence, so no key is ever
  * dropped whatever the two numbers are.  With causal != 0 query i sees keys
  * j <= its position; otherwise all keys.  softmax_scale <= 0 selects
- * 1/sqrt(d_hc + d_R).
+ * 1/sqrt(d_hc + d_R).  total_q * num_splits above 2^31 - 1 is MLA_ERR_UNSUPPORTED.
  */
 int mla_decode_paged(const void* q_abs, const void* q_r, const void* kv_cache,
                      const int32_t* page_table, const int32_t* seq_lens, const int32_t* cu_q,

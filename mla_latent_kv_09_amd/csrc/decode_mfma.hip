@@ -199,7 +199,11 @@ decode_mfma_kernel(DecodeArgs a) {
   using Sh = Shape<G>;
   constexpr int kDcg = Sh::kDcg, kQSteps = Sh::kQSteps, kColBlocks = Sh::kColBlocks;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int t = blockIdx.x, split = blockIdx.y;
+  // 1-D grid in split-fastest order: workgroup L = t * S + split.  The dispatcher deals
+  // workgroups to the 8 XCDs in turn (L mod 8), so the splits of one token spread over
+  // the XCDs, and a batch whose sequences differ in length loads every XCD alike.
+  const int t = static_cast<int>(blockIdx.x) / a.num_splits;
+  const int split = static_cast<int>(blockIdx.x) - t * a.num_splits;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
   const int g = lane >> 4, j = lane & 15;   // 16-lane group, position in group
@@ -454,7 +458,7 @@ hipError_t launch_decode_mfma_g(const DecodeArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const dim3 grid(a.total_q, a.num_splits);
+  const dim3 grid(a.total_q * a.num_splits);
   decode_mfma_kernel<G><<<grid, kThreads, kLdsBytes, s>>>(a);
   return hipGetLastError();
 }

@@ -111,6 +111,7 @@ int mla_decode_paged(const void* q_abs, const void* q_r, const void* kv_cache,
     return MLA_ERR_DIM;
   if ((st = check_heads(heads, groups, d_c)) != MLA_OK) return st;
   if (page_size != MLA_PAGE_SIZE || num_splits > kMaxSplits) return MLA_ERR_UNSUPPORTED;
+  if (static_cast<long long>(total_q) * num_splits > INT32_MAX) return MLA_ERR_UNSUPPORTED;
   if (d_c / groups > kMaxGenericCols || d_R > kMaxGenericRope) return MLA_ERR_UNSUPPORTED;
   if ((rope_cos == nullptr) != (rope_sin == nullptr)) return MLA_ERR_NULL;
   if (rope_cos != nullptr && rope_max_pos <= 0) return MLA_ERR_DIM;

@@ -198,21 +198,27 @@ def up_v(o_latent, w_uv, out=None, *, groups: int = 1, stream=None):
 # plus one unit per page.  A split with no keys exits at once.
 SPLIT_OVERHEAD_PAGES = 2.5
 EMPTY_SPLIT_PAGES = 0.2
+XCDS = 8
 
 
 def plan_makespan(pages, q_lens, pages_per_split: int, cu_count: int = 256) -> float:
-    """Finish time, in page units, of the decode grid under the cost model above when
-    the dispatcher hands workgroups to the first free CU in launch order (query token
-    fastest, split slowest), one workgroup per CU at a time."""
+    """Finish time, in page units, of the decode grid under the cost model above.  The
+    grid is launched in split-fastest order (workgroup L = token * S + split); the
+    dispatcher deals workgroup L to XCD L mod 8, and each XCD hands its workgroups to
+    the first of its CUs to come free, one workgroup per CU at a time."""
     n_splits = max(math.ceil(p / pages_per_split) for p in pages)
-    free = [0.0] * cu_count
-    for y in range(n_splits):
-        for p, n in zip(pages, q_lens):
-            work = min(pages_per_split, p - y * pages_per_split)
-            cost = SPLIT_OVERHEAD_PAGES + work if work > 0 else EMPTY_SPLIT_PAGES
-            for _ in range(n):
-                heapq.heapreplace(free, free[0] + cost)
-    return max(free)
+    per_xcd = max(1, cu_count // XCDS)
+    free = [[0.0] * per_xcd for _ in range(XCDS)]
+    wg = 0
+    for p, n in zip(pages, q_lens):
+        for _ in range(n):
+            for y in range(n_splits):
+                work = min(pages_per_split, p - y * pages_per_split)
+                cost = SPLIT_OVERHEAD_PAGES + work if work > 0 else EMPTY_SPLIT_PAGES
+                f = free[wg % XCDS]
+                heapq.heapreplace(f, f[0] + cost)
+                wg += 1
+    return max(max(f) for f in free)
 
 
 def split_plan(seq_lens_host, q_lens_host, cu_count: int = 256):

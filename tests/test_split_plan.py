@@ -43,15 +43,20 @@ def test_uniform_batches_get_one_workgroup_per_cu(name, expect):
 
 
 def test_makespan_model_by_hand():
-    # 4 CUs, 2 sequences of 8 pages, q_len 1: splits of 4 pages -> 4 workgroups, one each.
-    assert mla.plan_makespan([8, 8], [1, 1], 4, cu_count=4) == pytest.approx(
-        mla.SPLIT_OVERHEAD_PAGES + 4)
-    # 3 CUs: the fourth workgroup queues behind the first to finish.
-    assert mla.plan_makespan([8, 8], [1, 1], 4, cu_count=3) == pytest.approx(
-        2 * (mla.SPLIT_OVERHEAD_PAGES + 4))
+    one = mla.SPLIT_OVERHEAD_PAGES + 4
+    # 8 CUs = one per XCD.  Two sequences of 8 pages, splits of 4 pages: workgroups
+    # 0..3 go to XCDs 0..3 and run side by side.
+    assert mla.plan_makespan([8, 8], [1, 1], 4, cu_count=8) == pytest.approx(one)
+    # nine splits of one sequence: workgroup 8 is dealt to XCD 0 again and queues there
+    # although the other seven XCDs are idle.
+    assert mla.plan_makespan([36], [1], 4, cu_count=8) == pytest.approx(2 * one)
+    # with two CUs per XCD it runs next to workgroup 0 instead
+    assert mla.plan_makespan([36], [1], 4, cu_count=16) == pytest.approx(one)
     # an empty split (short sequence past its pages) costs only the early exit
-    assert mla.plan_makespan([8, 1], [1, 1], 4, cu_count=8) == pytest.approx(
-        mla.SPLIT_OVERHEAD_PAGES + 4)
+    assert mla.plan_makespan([8, 1], [1, 1], 4, cu_count=8) == pytest.approx(one)
+    # a query length of 2 runs the sequence's splits once per query token
+    assert mla.plan_makespan([8], [2], 4, cu_count=8) == pytest.approx(one)
+    assert mla.plan_makespan([4] * 9, [1] * 9, 4, cu_count=8) == pytest.approx(2 * one)
 
 
 def test_ragged_plan_no_worse_than_any_candidate_length():
