@@ -228,6 +228,26 @@ def mla_decode(q_c, q_r, latents, w_uk, w_uv, cu_q, *, groups=1, d_c=None,
     return {"out": out, "o_latent": o_lat, "lse": lse}
 
 
+def merge_splits(o_parts, lses):
+    """Log-sum-exp merge of split-KV partial results (P3 §5: the split partials are
+    combined by a separate step).  o_parts [..., S, d] holds each split's softmax-
+    normalised output over its own keys and lses [..., S] the natural-log log-sum-exp of
+    its scaled scores; a split with lse = -inf holds no keys and its partial never
+    enters (it may be unwritten).  With M = max_s lse_s and w_s = exp(lse_s - M):
+    out = sum_s w_s o_s / sum_s w_s, lse = M + log sum_s w_s.  A row with no keys at
+    all gives out = 0 and lse = -inf.  float64."""
+    o = np.asarray(o_parts, np.float64)
+    lse = np.asarray(lses, np.float64)
+    empty = np.isneginf(lse)
+    m = np.max(lse, axis=-1)
+    has = ~np.isneginf(m)
+    w = np.where(empty, 0.0, np.exp(lse - np.where(has, m, 0.0)[..., None]))
+    z = w.sum(axis=-1)
+    o = np.where(empty[..., None], 0.0, o)
+    out = np.einsum("...s,...sd->...d", w, o) / np.where(has, z, 1.0)[..., None]
+    return out, np.where(has, m + np.log(np.where(has, z, 1.0)), -np.inf)
+
+
 def absorb_reference(q_c, w_uk):
     """q_abs[t,h,:] = q_c[t,h,:] @ W_UK[h]  (P3 §4 path B, first product), float64."""
     q_c = np.asarray(q_c, np.float64)

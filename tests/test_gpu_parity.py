@@ -279,6 +279,38 @@ def test_softmax_reference_moves(kind, case, mode, monkeypatch):
     assert_parity(_f64(step.out), ref["out"])
 
 
+@pytest.mark.parametrize("T,d_cg,S,dt", [(37, 512, 16, "bf16"), (9, 256, 70, "bf16"),
+                                         (5, 512, 3, "fp32")])
+def test_combine_against_oracle_merge(T, d_cg, S, dt):
+    """mla_combine alone on synthetic partials: a third of the splits empty (LSE = -inf,
+    partials NaN), one token with no keys at all, and split counts past one wave's 64
+    lanes; o_latent and the LSE against the oracle's fp64 merge."""
+    H = 128 if dt == "bf16" else 16
+    rng = np.random.default_rng(T * 1000 + S)
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    o_part = rng.standard_normal((T, H, S, d_cg)).astype(np.float32)
+    if dt == "bf16":
+        o_part = wl.round_bf16(o_part)
+    lse = (rng.standard_normal((T, H, S)) * 3).astype(np.float32)
+    empty = rng.random((T, H, S)) < 1 / 3
+    empty[0] = True
+    lse[empty] = -np.inf
+    o_part[empty] = np.nan
+    op = torch.from_numpy(o_part).to("cuda").to(tdt)
+    lp = torch.from_numpy(lse).to("cuda")
+    lse_out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    o_lat = mla.combine(op, lp, lse_out=lse_out, dtype=tdt)
+    torch.cuda.synchronize()
+    ref_o, ref_l = om.merge_splits(o_part, lse)
+    assert_parity(_f64(o_lat), ref_o, tol=NORM_TOL if dt == "bf16" else 1e-6,
+                  cos_tol=COS_TOL if dt == "bf16" else 0.9999999, what="o_latent")
+    got_l = _f64(lse_out)
+    assert np.array_equal(np.isneginf(got_l), np.isneginf(ref_l))
+    fin = np.isfinite(ref_l)
+    assert np.max(np.abs(got_l[fin] - ref_l[fin])) < 1e-4
+    assert torch.all(o_lat[0] == 0)
+
+
 def test_combine_ignores_unwritten_empty_splits():
     """Empty splits leave their o_part rows unwritten; NaN there must not reach the output."""
     w = wl.make_workload(_small("ragged_b64", batch=4, seq_len_range=(10, 300)))

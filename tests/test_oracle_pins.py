@@ -341,3 +341,35 @@ def test_projection_references_match_scalar_sums():
     c = rng.standard_normal((4, 7))
     naive = om.naive_scores(q[1, 1], np.zeros(2), c, np.zeros((4, 2)), w[1], 1.0)
     assert np.allclose(c @ qa[1, 1], naive, rtol=1e-12, atol=1e-12)
+
+
+def test_merge_of_key_chunks_equals_attention_over_all_keys():
+    """The split merge is pinned to the oracle's own softmax over all keys: attention over
+    each chunk of the keys separately (no causal mask, no RoPE, so a chunk's scores are
+    the same as in the whole), merged by lse, equals attention over all keys.  One chunk
+    is empty (lse = -inf, partial NaN: it must not enter)."""
+    rng = np.random.default_rng(5)
+    H, d_hc, d_c, d_R, L = 4, 8, 16, 4, 23
+    q_c = rng.standard_normal((1, H, d_hc))
+    q_r = rng.standard_normal((1, H, d_R))
+    rows = rng.standard_normal((L, d_c + d_R))
+    w_uk = rng.standard_normal((H, d_hc, d_c)) / 4
+    w_uv = rng.standard_normal((H, d_hc, d_c)) / 4
+    cu = np.array([0, 1])
+    full = om.mla_decode(q_c, q_r, [rows], w_uk, w_uv, cu, causal=False)
+    bounds = [0, 5, 5, 12, 23]                      # chunk [5, 5) is empty
+    parts, lses = [], []
+    for a, b in zip(bounds, bounds[1:]):
+        if a == b:
+            parts.append(np.full((1, H, d_c), np.nan))
+            lses.append(np.full((1, H), -np.inf))
+            continue
+        r = om.mla_decode(q_c, q_r, [rows[a:b]], w_uk, w_uv, cu, causal=False)
+        parts.append(r["o_latent"])
+        lses.append(r["lse"])
+    o, lse = om.merge_splits(np.stack(parts, axis=2), np.stack(lses, axis=2))
+    assert np.allclose(o, full["o_latent"], rtol=0, atol=1e-12)
+    assert np.allclose(lse, full["lse"], rtol=0, atol=1e-12)
+    # no keys anywhere: zero output, -inf lse
+    o0, l0 = om.merge_splits(np.full((2, 3, 5), np.nan), np.full((2, 3), -np.inf))
+    assert np.all(o0 == 0) and np.all(np.isneginf(l0))
