@@ -358,18 +358,22 @@ decode_mfma_kernel(DecodeArgs a) {
       }
     }
 
-    // ---- online softmax.  s[mb][i] is the score of token mb*16 + 4g + i.
+    // ---- online softmax.  s[mb][i] is the raw score of token mb*16 + 4g + i; only the
+    // last page of a split can be partial, so the mask is skipped on full pages, and the
+    // scale is applied in the exponent (it is positive, so it commutes with the max).
+    if (n_valid < kTok) {
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (mb * 16 + 4 * g + i >= n_valid) s[mb][i] = -INFINITY;
+    }
     float mx = -INFINITY;
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int tok = mb * 16 + 4 * g + i;
-        const float x = tok < n_valid ? s[mb][i] * scale_log2 : -INFINITY;
-        s[mb][i] = x;
-        mx = fmaxf(mx, x);
-      }
-    mx = rows_max(mx);
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[mb][i]);
+    mx = rows_max(mx) * scale_log2;
     const float m_old = m_ref;
     const bool grow = mx > m_old + kSlack;   // always true on the first page
     const float m_new = grow ? mx : m_old;
@@ -379,7 +383,7 @@ decode_mfma_kernel(DecodeArgs a) {
     for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = __builtin_amdgcn_exp2f(s[mb][i] - m_new);
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[mb][i], scale_log2, -m_new));
         s[mb][i] = p;
         psum += p;
       }
