@@ -1,19 +1,26 @@
 """Benchmark of one absorbed-MLA decode step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--splits S]
-                    [--no-cpu-baseline] [--no-flush]
+                    [--no-cpu-baseline] [--flush] [--no-graph]
 
 A step is the whole hot path over one batch of synthetic input already resident
 in HBM: mla_absorb_q -> mla_decode_paged -> mla_combine -> mla_up_v, all on the
-current HIP stream, captured once as a HIP graph and replayed (--no-graph
-launches the four calls eagerly).  Before every timed step a 1 GiB buffer is
-read (a max-reduction) so the L2 and the 256 MB Infinity Cache hold nothing of the
-step's working set (a real decode step reads a different layer's cache every
-time).  The flush only reads: a flush that writes leaves up to 256 MB of dirty
-lines whose write-back then competes with the step's own reads.
-Each step is bracketed by HIP events; the reported time is the median over the
-K timed steps.  Per-kernel times (and the decode kernel's time in the roofline
-object) come from a second pass of K eager steps with events between the calls.
+current HIP stream.
+
+Timing (default).  The step's inputs, outputs and workspace exist in n copies (n >= 2,
+enough that n steps read more than twice the 256 MB Infinity Cache), used in turn,
+so a step never finds its cache pages, weights or queries in L2 or the MALL: every
+step starts from HBM, as a decode step that reads another layer's cache does.  After
+W warmup steps over every copy, exactly K steps run back to back over the copies
+(HIP graphs of up to 8 steps, replayed) in one region between two synchronizations
+and two HIP events; the step time is that region's time / K.  Back-to-back replay is
+how a serving loop runs the step; timing each step alone between two events would
+add the event and graph-launch latency (about 10 us here) to every step.  Per-call
+times (and the decode kernel's time in the roofline object) are measured the same
+way, each call alone back to back over the copies (median of 5 runs of about K
+calls), and agree with rocprofv3's kernel durations.  --no-graph launches the same
+sequences eagerly.  --flush keeps the earlier method: one copy, a 1 GiB read-only
+cache flush before every step, each step between its own events.
 
 Prints one JSON line.  `value` is the algorithmic TFLOP/s of the whole step
 (attention flops of the absorbed method plus the two projections, divided by the
@@ -37,6 +44,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MLA decode attention TFLOP/s + latent-KV GB/s (% MI355X roofline), seqs/s"
 HEADLINE = "dsv3_b16_l4096"
 HBM_PEAK_GBPS = 8000.0
+MALL_BYTES = 256 << 20  # Infinity Cache of one MI355X
 BF16_PEAK_TFLOPS = 2500.0
 FP32_PEAK_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode.json")
@@ -121,16 +129,73 @@ def cpu_baseline(w, att_flops_full, budget_s=20.0):
     }
 
 
+def flush_timing(args, w, torch, harness, stream, names):
+    """The earlier method, kept for comparison (--flush): one input copy, a 1 GiB
+    read-only flush before every step, events around each step and between the calls
+    of a second pass."""
+    d = harness.to_device(w)
+    step = harness.make_step(w, d, args.splits)
+    flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+
+    def one_step(ev=None):
+        if ev is None:
+            step()
+            return
+        ev[0].record(stream)
+        step.absorb()
+        ev[1].record(stream)
+        step.attend()
+        ev[2].record(stream)
+        step.merge()
+        ev[3].record(stream)
+        step.project()
+        ev[4].record(stream)
+
+    for _ in range(args.warmup):
+        flush_buf.max()
+        one_step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        flush_buf.max()
+        one_step(events[k])
+    torch.cuda.synchronize()
+    parts = {name: statistics.median([e[i].elapsed_time(e[i + 1]) for e in events])
+             for i, name in enumerate(names)}
+    graph = None
+    if not args.no_graph:
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+    ev_step = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+    wall0 = time.perf_counter()
+    for k in range(args.steps):
+        flush_buf.max()
+        ev_step[k][0].record(stream)
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
+        ev_step[k][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = statistics.median(e[0].elapsed_time(e[1]) for e in ev_step)
+    return ms, parts, parts["decode_paged"], step.num_splits, step, wall, graph is not None
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=HEADLINE)
     ap.add_argument("--splits", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-flush", action="store_true")
-    ap.add_argument("--no-graph", action="store_true", help="launch the four calls eagerly")
+    ap.add_argument("--flush", action="store_true",
+                    help="one input copy and a 1 GiB read-only cache flush before every step, "
+                         "each step timed alone (the earlier method) instead of rotating copies")
+    ap.add_argument("--no-graph", action="store_true", help="launch the calls eagerly")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the decode path is built "
@@ -149,73 +214,83 @@ def main():
 
     cfg = wl.CONFIGS[args.config]
     w = wl.make_workload(cfg)
-    d = harness.to_device(w)
-    step = harness.make_step(w, d, args.splits)
-    S = step.num_splits
-    flush_buf = None if args.no_flush else torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-
-    def flush():
-        if flush_buf is not None:
-            flush_buf.max()
-    stream = torch.cuda.current_stream()
-
-    def one_step(ev=None):
-        if ev is None:
-            step()
-            return
-        ev[0].record(stream)
-        step.absorb()
-        ev[1].record(stream)
-        step.attend()
-        ev[2].record(stream)
-        step.merge()
-        ev[3].record(stream)
-        step.project()
-        ev[4].record(stream)
-
-    for _ in range(args.warmup):
-        flush()
-        one_step()
-    torch.cuda.synchronize()
-
-    # Per-kernel times: the four calls issued one by one with events between them
-    # (the flush before each step keeps the GPU busy long enough for all four
-    # launches to be queued, so the events bracket kernel execution).
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    for k in range(args.steps):
-        flush()
-        one_step(events[k])
-    torch.cuda.synchronize()
-    dec_ms = [e[1].elapsed_time(e[2]) for e in events]
-    parts = {name: statistics.median([e[i].elapsed_time(e[i + 1]) for e in events])
-             for i, name in enumerate(["absorb_q", "decode_paged", "combine", "up_v"])}
-    dec = statistics.median(dec_ms)
-
-    # Step time: the four calls captured once as a HIP graph and replayed, so the
-    # host's per-call launch cost does not sit between the kernels.
-    graph = None
-    if not args.no_graph:
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
-        torch.cuda.synchronize()
-    ev_step = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    for k in range(args.steps):
-        flush()
-        ev_step[k][0].record(stream)
-        if graph is not None:
-            graph.replay()
-        else:
-            step()
-        ev_step[k][1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    step_ms = [e[0].elapsed_time(e[1]) for e in ev_step]
-    ms = statistics.median(step_ms)
-
     att, proj, kv_bytes, w_bytes = algorithmic_work(cfg, w.seq_lens, w.q_lens)
+    stream = torch.cuda.current_stream()
+    names = ["absorb_q", "decode_paged", "combine", "up_v"]
+
+    if not args.flush:
+        # Rotation: n_copies independent device copies of the step's inputs, outputs and
+        # workspace, used in turn, so every step reads data that the steps since its
+        # copy's last use (together more than twice the 256 MB Infinity Cache) have
+        # evicted from L2 and MALL: each step starts from HBM.  Steps and calls are
+        # timed back to back inside HIP graphs, as a serving loop runs them.
+        n_copies = max(2, min(8, math.ceil(2 * MALL_BYTES / (kv_bytes + w_bytes))))
+        steps = [harness.make_step(w, harness.to_device(w), args.splits) for _ in range(n_copies)]
+        step = steps[0]
+        S = step.num_splits
+        per_graph = n_copies * max(1, math.ceil(8 / n_copies))  # calls captured per graph
+
+        def graph_of(calls):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for c in calls:
+                    c()
+            g.replay()
+            torch.cuda.synchronize()
+            return g
+
+        def runner(calls):
+            """A callable that issues `calls` once: a graph replay, or eager launches."""
+            if args.no_graph:
+                return lambda: [c() for c in calls]
+            return graph_of(calls).replay
+
+        def timed(run, reps):
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(reps):
+                run()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1)
+
+        for _ in range(max(1, args.warmup)):
+            for st in steps:
+                st()
+        torch.cuda.synchronize()
+        # Per-call times: each call alone, back to back over the rotated copies (median of
+        # 5 runs of about K calls).
+        reps = max(1, math.ceil(args.steps / per_graph))
+        parts = {}
+        for name, attr in zip(names, ["absorb", "attend", "merge", "project"]):
+            run = runner([getattr(steps[i % n_copies], attr) for i in range(per_graph)])
+            parts[name] = statistics.median(timed(run, reps) / (reps * per_graph) for _ in range(5))
+            del run
+        dec = parts["decode_paged"]
+        # Step time: exactly K whole steps back to back over the rotated copies, one timed
+        # region between two synchronizations.
+        full, rest = divmod(args.steps, per_graph)
+        run_full = runner([steps[i % n_copies] for i in range(per_graph)]) if full else None
+        run_rest = runner([steps[i % n_copies] for i in range(rest)]) if rest else None
+
+        def k_steps():
+            for _ in range(full):
+                run_full()
+            if run_rest is not None:
+                run_rest()
+
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        ms = timed(k_steps, 1) / args.steps
+        wall = time.perf_counter() - wall0
+        timing = {"method": "rotate", "copies": n_copies, "steps_per_graph": per_graph}
+        graph_used = not args.no_graph
+    else:
+        ms, parts, dec, S, step, wall, graph_used = flush_timing(args, w, torch, harness, stream, names)
+        timing = {"method": "flush"}
+
     flops = att + proj
     tflops = flops / (ms * 1e-3) / 1e12
     kv_gbps = kv_bytes / (ms * 1e-3) / 1e9
@@ -246,8 +321,8 @@ def main():
                    "d_c": cfg.d_c, "d_R": cfg.d_R, "groups": cfg.groups, "page_size": cfg.page_size,
                    "seq_len": cfg.seq_len, "seq_len_range": cfg.seq_len_range,
                    "total_q": int(w.total_q), "num_splits": S,
-                   "pages_per_split": step.pages_per_split, "cache_flushed": flush_buf is not None,
-                   "hip_graph": graph is not None},
+                   "pages_per_split": step.pages_per_split, "timing": timing,
+                   "hip_graph": graph_used},
         "latent_kv_gbps": kv_gbps, "latent_kv_frac_hbm_peak": kv_gbps / HBM_PEAK_GBPS,
         "tflops_frac_mfma_peak": tflops / peak_f, "seqs_per_s": seqs,
         "kernel_ms": parts, "wall_s_timed_region": wall,
