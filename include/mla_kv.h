@@ -136,6 +136,14 @@ int mla_rope_table(float* cos_out, float* sin_out, int max_pos, int d_R, double 
  * dropped whatever the two numbers are.  With causal != 0 query i sees keys
  * j <= its position; otherwise all keys.  softmax_scale <= 0 selects
  * 1/sqrt(d_hc + d_R).  total_q * num_splits above 2^31 - 1 is MLA_ERR_UNSUPPORTED.
+ * Work split (no effect on the results beyond rounding order): with bf16 storage, 128
+ * heads, d_c 512 and d_R 64 the MFMA kernel runs one workgroup of 128 heads per
+ * (token, split), or, with one latent group and 2 * total_q * num_splits at most the
+ * device's compute-unit count, two workgroups of 64 heads each.  The environment
+ * variable MLA_KV_DECODE_KERNEL overrides the choice: "generic" (the shape-generic
+ * kernel), "mfma" (MFMA kernel, automatic head split), "mfma128" / "mfma64" (MFMA
+ * kernel with the given heads per workgroup); an MFMA choice the shape does not
+ * support returns MLA_ERR_UNSUPPORTED.
  */
 int mla_decode_paged(const void* q_abs, const void* q_r, const void* kv_cache,
                      const int32_t* page_table, const int32_t* seq_lens, const int32_t* cu_q,

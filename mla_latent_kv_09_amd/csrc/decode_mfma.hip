@@ -168,14 +168,13 @@ __device__ __forceinline__ void load_page(uint32_t smem_base, int stage, const c
 
 constexpr int kRing = 4;  // LDS fragments in flight per wave
 
-// Latent score-step fragment st = k * 4 + mb: A operand of S^T for tokens 16mb + j,
-// latent dims 32k + 8g .. +7 (chunk 4k + g).  The four token blocks alternate so that
+// Latent score fragment (mb, k): A operand of S^T for tokens 16mb + j, latent dims
+// 32k + 8g .. +7 (chunk 4k + g).  The token blocks alternate in the step order so that
 // consecutive MFMAs accumulate into different registers.  With key 2j the chunk sits
 // at position 32 (k / 8) + 4 ((k % 8) ^ (j / 2)) + (g ^ 2 (j % 2)): `lb` is the stage
 // base plus the per-lane row and low bits, `jx` = (j / 2) << 6, so each fragment costs
 // one xor-add and an immediate offset.
-__device__ __forceinline__ bf16x8 score_frag(uint32_t lb, uint32_t jx, int st) {
-  const int mb = st % 4, k = st / 4;  // k < kQSteps of the instantiation
+__device__ __forceinline__ bf16x8 score_frag(uint32_t lb, uint32_t jx, int mb, int k) {
   const uint32_t a = lb + (jx ^ static_cast<uint32_t>((k & 7) << 6));
   return *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(a + 16384 * mb + 512 * (k >> 3));
 }
@@ -193,30 +192,58 @@ __device__ __forceinline__ bf16x8 out_frag(uint32_t lb, uint32_t tx, int st) {
   return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
-template <int G>
+// HS = 1: one workgroup per (token, split) covers all 128 heads; wave w owns heads
+// 16w .. 16w+15 over all 64 tokens of each page.
+// HS = 2 (one latent group only): two workgroups per (token, split), 64 heads each, so
+// a batch with few (token, split) pairs still fills the device with half as many
+// split partials to write and merge.  Wave w owns heads 16 (w % 4) .. +15 of its half
+// over tokens 32 (w / 4) .. +31 of each page; waves w and w + 4 (one SIMD) keep their
+// own softmax state and merge it through LDS at the end.  Both halves of a pair stream
+// the same pages, and run side by side on one XCD, so the second read of a page is
+// served by that XCD's L2.
+template <int G, int HS>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 decode_mfma_kernel(DecodeArgs a) {
+  static_assert(HS == 1 || (HS == 2 && G == 1), "head split only for one latent group");
   using Sh = Shape<G>;
   constexpr int kDcg = Sh::kDcg, kQSteps = Sh::kQSteps, kColBlocks = Sh::kColBlocks;
+  constexpr int kMB = 4 / HS;           // 16-token score blocks per wave and page
+  constexpr int kHeadsWG = kHeads / HS;  // heads of one workgroup
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  // 1-D grid in split-fastest order: workgroup L = t * S + split.  The dispatcher deals
+  const int S = a.num_splits;
+  // 1-D grid in split-fastest order over pairs P = t * S + split.  The dispatcher deals
   // workgroups to the 8 XCDs in turn (L mod 8), so the splits of one token spread over
-  // the XCDs, and a batch whose sequences differ in length loads every XCD alike.
-  const int t = static_cast<int>(blockIdx.x) / a.num_splits;
-  const int split = static_cast<int>(blockIdx.x) - t * a.num_splits;
+  // the XCDs, and a batch whose sequences differ in length loads every XCD alike.  With
+  // HS = 2, blocks of 8 pairs take 16 consecutive workgroups: half h2 of pair 8k + i is
+  // workgroup 16k + 8 h2 + i (in a last block of r < 8 pairs, 16k + r h2 + i), so the
+  // two halves of a pair land on the same XCD.
+  int t, split, h2 = 0;
+  if constexpr (HS == 1) {
+    t = static_cast<int>(blockIdx.x) / S;
+    split = static_cast<int>(blockIdx.x) - t * S;
+  } else {
+    const int L = static_cast<int>(blockIdx.x), kb = L >> 4, base = kb * 8;
+    const int r = min(8, a.total_q * S - base), off = L - 16 * kb;
+    const int pair = base + off % r;
+    h2 = off / r;
+    t = pair / S;
+    split = pair - t * S;
+  }
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
   const int g = lane >> 4, j = lane & 15;   // 16-lane group, position in group
-  const int head = wave * 16 + j;
+  const int hb = HS == 1 ? wave : (wave & 3);  // 16-head block within the workgroup
+  const int th = HS == 1 ? 0 : (wave >> 2);    // token half of each page (HS = 2)
+  const int hl = hb * 16 + j;                  // head within the workgroup
+  const int head = h2 * kHeadsWG + hl;
   const int grp = wave / Sh::kWavesPerGroup;             // latent group of this wave
   const uint32_t grp_off = static_cast<uint32_t>(grp) * kDcg * 2;  // its columns in a token row
-  const int S = a.num_splits;
   const QueryWork w = query_work(a.cu_q, a.seq_lens, a.batch, t, split, S,
                                  a.pages_per_split, kTok, a.max_pages, a.causal);
   const size_t row = (static_cast<size_t>(t) * kHeads + head) * S + split;
   __bf16* o_out = static_cast<__bf16*>(a.o_part) + row * kDcg;  // bf16 partials
   if (w.k0 >= w.k1) {  // empty split: only the LSE is written
-    if (g == 0) a.lse_part[row] = -INFINITY;
+    if (g == 0 && th == 0) a.lse_part[row] = -INFINITY;
     return;
   }
   const char* kv = static_cast<const char*>(a.kv);
@@ -243,13 +270,16 @@ decode_mfma_kernel(DecodeArgs a) {
 
   // Q fragments: B operand of S^T = C . Q^T.  K-step k covers latent dims 32k .. 32k+31;
   // this lane holds dims 32k + 8g .. +7 of its head.  The RoPE half of the query is
-  // rotated here in fp32 and parked, as bf16, in LDS (read back twice per page).
+  // rotated here in fp32 and parked, as bf16, in LDS (read back twice per page; with
+  // HS = 2 the token-half-0 wave of a head block writes it for both).
   bf16x8 q[kQSteps];  // latent part of the query
   {
     const uint16_t* qa = static_cast<const uint16_t*>(a.q_abs) +
                          (static_cast<size_t>(t) * kHeads + head) * kDcg + g * 8;
 #pragma unroll
     for (int k = 0; k < kQSteps; ++k) q[k] = *reinterpret_cast<const bf16x8*>(qa + 32 * k);
+  }
+  if (th == 0) {
     const uint16_t* qr = static_cast<const uint16_t*>(a.q_r) +
                          (static_cast<size_t>(t) * kHeads + head) * kDr + g * 8;
     const int p = min(max(w.pos, 0), max(a.rope_max_pos - 1, 0));
@@ -270,7 +300,7 @@ decode_mfma_kernel(DecodeArgs a) {
         }
       }
       *(__attribute__((address_space(3))) bf16x8*)(uintptr_t)(lds_addr(smem) + kQrOff +
-                                                             qr_slot(head, 4 * k + g)) =
+                                                             qr_slot(hl, 4 * k + g)) =
           to_bf16x8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
     }
   }
@@ -289,9 +319,12 @@ decode_mfma_kernel(DecodeArgs a) {
   //   RoPE read   (token 16mb + j, chunk 4k + g):  base_r(k) + 2048 mb
   //   output read (token 32ks + 4g + j/4 (+16), column 16nb + 4(j%4)):
   //                           base_o + (tx ^ 32 (nb%16)) + 32768 ks (+16384) + 512 (nb/16)
-  // The bases are recomputed from the lane index every page (a few VALU ops) rather
-  // than kept in registers across the loop.
+  // (with HS = 2 the token half th moves every base by 32 tokens: mb = 2 th + 0..1,
+  // ks = th).  The bases are recomputed from the lane index every page (a few VALU ops)
+  // rather than kept in registers across the loop.
   const uint32_t smem_base = lds_addr(smem);
+  const uint32_t half_c = static_cast<uint32_t>(th) * 32768;  // 32 tokens of latent rows
+  const uint32_t half_r = static_cast<uint32_t>(th) * 4096;   // 32 tokens of RoPE rows
   int stage = 0;
   for (; j0 < w.k1; j0 += kTok) {
     const int n_valid = min(kTok, w.k1 - j0);
@@ -311,25 +344,25 @@ decode_mfma_kernel(DecodeArgs a) {
     const uint32_t st_base = smem_base + stage * kStageBytes;
     const int lv = static_cast<int>(opaque(static_cast<uint32_t>(lane)));
     const int lj = lv & 15, lg = lv >> 4;
-    const uint32_t sb = opaque(st_base + grp_off + lj * 1024 + ((lg ^ (2 * (lj & 1))) << 4));
+    const uint32_t sb = opaque(st_base + half_c + grp_off + lj * 1024 + ((lg ^ (2 * (lj & 1))) << 4));
     const uint32_t sjx = opaque(static_cast<uint32_t>(lj >> 1) << 6);
 
     // ---- scores S^T for tokens mb*16 .. mb*16+15 of the page.  RoPE part first
-    // (the q_R fragments are live only here), then the 64 latent (mb, k) steps in
-    // order through a ring of kRing prefetched LDS fragments.
-    f32x4 s[4];
+    // (the q_R fragments are live only here), then the (mb, k) latent steps in order
+    // through a ring of prefetched LDS fragments.
+    f32x4 s[kMB];
     {
       const int swr = swz_r(lj);
-      const uint32_t rb0 = st_base + kCBytes + lj * 128 + (((lg) ^ swr) << 4);
-      const uint32_t rb1 = st_base + kCBytes + lj * 128 + (((4 + lg) ^ swr) << 4);
-      const uint32_t qr_head = smem_base + kQrOff + (wave * 16 + lj) * 128;
+      const uint32_t rb0 = st_base + half_r + kCBytes + lj * 128 + (((lg) ^ swr) << 4);
+      const uint32_t rb1 = st_base + half_r + kCBytes + lj * 128 + (((4 + lg) ^ swr) << 4);
+      const uint32_t qr_head = smem_base + kQrOff + (hb * 16 + lj) * 128;
       const int swq = (lj >> 1) & 7;
       const uint32_t qr_addr0 = qr_head + ((lg ^ swq) << 4);
       const uint32_t qr_addr1 = qr_head + (((4 + lg) ^ swq) << 4);
       const bf16x8 qr0 = *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(qr_addr0);
       const bf16x8 qr1 = *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(qr_addr1);
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
+      for (int mb = 0; mb < kMB; ++mb) {
         const bf16x8 c0 = *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(
             rb0 + 2048 * mb);
         const bf16x8 c1 = *(const __attribute__((address_space(3))) bf16x8*)(uintptr_t)(
@@ -339,17 +372,18 @@ decode_mfma_kernel(DecodeArgs a) {
       }
     }
     {
-      constexpr int kSteps = 4 * kQSteps;  // (mb, k) steps
+      constexpr int kSteps = kMB * kQSteps;  // (mb, k) steps
       constexpr int kSRing = 3;
       bf16x8 ring[kSRing];
 #pragma unroll
-      for (int st = 0; st < kSRing; ++st) ring[st] = score_frag(sb, sjx, st);
+      for (int st = 0; st < kSRing; ++st) ring[st] = score_frag(sb, sjx, st % kMB, st / kMB);
       constexpr int kRowEvery = kSteps / 8;  // one page-row copy every kRowEvery steps
 #pragma unroll
       for (int st = 0; st < kSteps; ++st) {
         const bf16x8 c = ring[st % kSRing];
-        if (st + kSRing < kSteps) ring[st % kSRing] = score_frag(sb, sjx, st + kSRing);
-        const int mb = st % 4, k = st / 4;
+        if (st + kSRing < kSteps)
+          ring[st % kSRing] = score_frag(sb, sjx, (st + kSRing) % kMB, (st + kSRing) / kMB);
+        const int mb = st % kMB, k = st / kMB;
         s[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(c, q[k], s[mb], 0, 0, 0);
         if (st % kRowEvery == kRowEvery / 2 && has_next)
           load_row(next_base, next_page, next_valid, wave, static_cast<int>(opaque(lane)), st / kRowEvery);
@@ -358,32 +392,37 @@ decode_mfma_kernel(DecodeArgs a) {
       }
     }
 
-    // ---- online softmax.  s[mb][i] is the raw score of token mb*16 + 4g + i; only the
-    // last page of a split can be partial, so the mask is skipped on full pages, and the
-    // scale is applied in the exponent (it is positive, so it commutes with the max).
+    // ---- online softmax.  s[mb][i] is the raw score of token 32th + mb*16 + 4g + i; only
+    // the last page of a split can be partial, so the mask is skipped on full pages, and
+    // the scale is applied in the exponent (it is positive, so it commutes with the max).
     if (n_valid < kTok) {
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (mb * 16 + 4 * g + i >= n_valid) s[mb][i] = -INFINITY;
+          if (32 * th + mb * 16 + 4 * g + i >= n_valid) s[mb][i] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[mb][i]);
     mx = rows_max(mx) * scale_log2;
     const float m_old = m_ref;
-    const bool grow = mx > m_old + kSlack;   // always true on the first page
+    const bool grow = mx > m_old + kSlack;   // always true on a first page with a valid key
     const float m_new = grow ? mx : m_old;
-    const float alpha = __builtin_amdgcn_exp2f(m_old - m_new);  // 0 on the first page
+    // With HS = 2 the second token half of a split's only (partial) page can hold no
+    // valid key: the reference then stays -inf and is subtracted as 0, which keeps
+    // every exponential at 0 instead of NaN.  (Token 0 of a page is always valid, so
+    // with HS = 1 the first page already sets a finite reference.)
+    const float m_sub = (HS == 2 && m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_old - m_sub);  // 0 before the first valid key
     float psum = 0.f;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int mb = 0; mb < kMB; ++mb)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[mb][i], scale_log2, -m_new));
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[mb][i], scale_log2, -m_sub));
         s[mb][i] = p;
         psum += p;
       }
@@ -397,19 +436,22 @@ decode_mfma_kernel(DecodeArgs a) {
     }
 
     // ---- P^T operands: K-step ks covers tokens 32ks + 4g + {0..3} and 32ks + 16 + 4g + {0..3}
-    bf16x8 pb[2];
+    // (with HS = 2 the one K-step of token half th)
+    constexpr int kKS = kMB / 2;
+    bf16x8 pb[kKS];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
+    for (int ks = 0; ks < kKS; ++ks)
       pb[ks] = to_bf16x8(s[2 * ks][0], s[2 * ks][1], s[2 * ks][2], s[2 * ks][3],
                          s[2 * ks + 1][0], s[2 * ks + 1][1], s[2 * ks + 1][2], s[2 * ks + 1][3]);
 
-    // ---- O^T[cols 16nb .. +15] += C^T . P^T, 64 (ks, nb) steps through the ring
+    // ---- O^T[cols 16nb .. +15] += C^T . P^T, (ks, nb) steps through the ring
     const int otok = 4 * lg + (lj >> 2);
     const int colb = 4 * (lj & 3);
-    const uint32_t ob = opaque(st_base + grp_off + otok * 1024 + ((colb >> 3) << 4) + (colb & 7) * 2);
+    const uint32_t ob =
+        opaque(st_base + half_c + grp_off + otok * 1024 + ((colb >> 3) << 4) + (colb & 7) * 2);
     const uint32_t otx = opaque(static_cast<uint32_t>(otok) << 5);
     {
-      constexpr int kSteps = 2 * kColBlocks;
+      constexpr int kSteps = kKS * kColBlocks;
       constexpr int kORing = 6;
       bf16x8 ring[kORing];
 #pragma unroll
@@ -434,16 +476,62 @@ decode_mfma_kernel(DecodeArgs a) {
 
   // ---- finalize: normalise and write this split's partial output and LSE
   const float l_tot = rows_sum(l_run);
-  const float inv = 1.f / l_tot;
+  if constexpr (HS == 1) {
+    const float inv = 1.f / l_tot;
 #pragma unroll
-  for (int nb = 0; nb < kColBlocks; ++nb)
-  {
-    const f32x4 v = o[nb] * inv;
-    *reinterpret_cast<bf16x4*>(o_out + nb * 16 + 4 * g) =
-        bf16x4{static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]), static_cast<__bf16>(v[2]),
-               static_cast<__bf16>(v[3])};
+    for (int nb = 0; nb < kColBlocks; ++nb) {
+      const f32x4 v = o[nb] * inv;
+      *reinterpret_cast<bf16x4*>(o_out + nb * 16 + 4 * g) =
+          bf16x4{static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]), static_cast<__bf16>(v[2]),
+                 static_cast<__bf16>(v[3])};
+    }
+    if (g == 0) a.lse_part[row] = (m_ref + __log2f(l_tot)) * kLn2;
+  } else {
+    // Merge the two token halves of each head: wave w keeps output columns
+    // 256 th .. +255 and hands the other half, with its (m, l), to its partner w ^ 4
+    // through LDS (the stages are free once every wave has finished the last page).
+    // Lane-linear 16-byte slots: conflict-free.
+    constexpr int kHalf = kColBlocks / 2;
+    const uint32_t xo_mine = smem_base + static_cast<uint32_t>(wave) * (kHalf * 1024) + lane * 16;
+    const uint32_t xo_part = smem_base + static_cast<uint32_t>(wave ^ 4) * (kHalf * 1024) + lane * 16;
+    const uint32_t ml_mine = smem_base + kWaves * kHalf * 1024 + (wave * 64 + lane) * 8;
+    const uint32_t ml_part = smem_base + kWaves * kHalf * 1024 + ((wave ^ 4) * 64 + lane) * 8;
+    typedef __attribute__((address_space(3))) f32x4 lds_f32x4_t;
+    typedef __attribute__((address_space(3))) float lds_f32_t;
+    __syncthreads();  // every wave is done with the stages
+    if (th == 0) {
+#pragma unroll
+      for (int i = 0; i < kHalf; ++i) *(lds_f32x4_t*)(uintptr_t)(xo_mine + i * 1024) = o[kHalf + i];
+    } else {
+#pragma unroll
+      for (int i = 0; i < kHalf; ++i) *(lds_f32x4_t*)(uintptr_t)(xo_mine + i * 1024) = o[i];
+    }
+    *(lds_f32_t*)(uintptr_t)(ml_mine) = m_ref;
+    *(lds_f32_t*)(uintptr_t)(ml_mine + 4) = l_tot;
+    __syncthreads();
+    const float m_p = *(lds_f32_t*)(uintptr_t)(ml_part);
+    const float l_p = *(lds_f32_t*)(uintptr_t)(ml_part + 4);
+    const float m = fmaxf(m_ref, m_p);  // finite: token 0 of every page is in half 0
+    const float a_me = __builtin_amdgcn_exp2f(m_ref - m), a_p = __builtin_amdgcn_exp2f(m_p - m);
+    const float l = l_tot * a_me + l_p * a_p;
+    const float inv = 1.f / l;
+    const float w_me = a_me * inv, w_p = a_p * inv;
+    auto emit = [&](int nb, const f32x4& mine, uint32_t slot) {
+      const f32x4 other = *(lds_f32x4_t*)(uintptr_t)(slot);
+      const f32x4 v = mine * w_me + other * w_p;
+      *reinterpret_cast<bf16x4*>(o_out + nb * 16 + 4 * g) =
+          bf16x4{static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]), static_cast<__bf16>(v[2]),
+                 static_cast<__bf16>(v[3])};
+    };
+    if (th == 0) {
+#pragma unroll
+      for (int i = 0; i < kHalf; ++i) emit(i, o[i], xo_part + i * 1024);
+      if (g == 0) a.lse_part[row] = (m + __log2f(l)) * kLn2;
+    } else {
+#pragma unroll
+      for (int i = 0; i < kHalf; ++i) emit(kHalf + i, o[kHalf + i], xo_part + i * 1024);
+    }
   }
-  if (g == 0) a.lse_part[row] = (m_ref + __log2f(l_tot)) * kLn2;
 }
 
 }  // namespace
@@ -453,22 +541,29 @@ bool decode_mfma_supported(const DecodeArgs& a, bool bf16) {
          a.d_R == kDr && a.page_size == kTok;
 }
 
-template <int G>
-hipError_t launch_decode_mfma_g(const DecodeArgs& a, hipStream_t s) {
+template <int G, int HS>
+hipError_t launch_decode_mfma_k(const DecodeArgs& a, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_mfma_kernel<G>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_mfma_kernel<G, HS>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const dim3 grid(a.total_q * a.num_splits);
-  decode_mfma_kernel<G><<<grid, kThreads, kLdsBytes, s>>>(a);
+  const dim3 grid(a.total_q * a.num_splits * HS);
+  decode_mfma_kernel<G, HS><<<grid, kThreads, kLdsBytes, s>>>(a);
   return hipGetLastError();
 }
 
-hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s) {
-  return a.groups == 2 ? launch_decode_mfma_g<2>(a, s) : launch_decode_mfma_g<1>(a, s);
+int decode_mfma_head_split(const DecodeArgs& a, int cu_count) {
+  if (a.groups != 1) return 1;
+  if (a.head_split == 1 || a.head_split == 2) return a.head_split;
+  return 2LL * a.total_q * a.num_splits <= cu_count ? 2 : 1;
+}
+
+hipError_t launch_decode_mfma(const DecodeArgs& a, int head_split, hipStream_t s) {
+  if (a.groups == 2) return launch_decode_mfma_k<2, 1>(a, s);
+  return head_split == 2 ? launch_decode_mfma_k<1, 2>(a, s) : launch_decode_mfma_k<1, 1>(a, s);
 }
 
 }  // namespace mla

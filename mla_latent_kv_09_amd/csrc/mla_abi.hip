@@ -33,13 +33,33 @@ int launch_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_LAUN
 
 // Decode kernel selection: MLA_KV_DECODE_KERNEL = "generic" forces the shape-generic
 // kernel, "mfma" requires the MFMA kernel (unsupported shapes then fail with
-// MLA_ERR_UNSUPPORTED), anything else picks the MFMA kernel whenever the shape has one.
-enum class DecodeKernel { kAuto, kGeneric, kMfma };
+// MLA_ERR_UNSUPPORTED) with the head split chosen from the grid size, "mfma128" and
+// "mfma64" require it with one workgroup of 128 heads, resp. two of 64 heads (one
+// latent group only), per (token, split); anything else picks the MFMA kernel whenever
+// the shape has one.
+enum class DecodeKernel { kAuto, kGeneric, kMfma, kMfma128, kMfma64 };
 DecodeKernel decode_kernel_choice() {
   const char* v = getenv("MLA_KV_DECODE_KERNEL");
-  if (v != nullptr && strcmp(v, "generic") == 0) return DecodeKernel::kGeneric;
-  if (v != nullptr && strcmp(v, "mfma") == 0) return DecodeKernel::kMfma;
+  if (v == nullptr) return DecodeKernel::kAuto;
+  if (strcmp(v, "generic") == 0) return DecodeKernel::kGeneric;
+  if (strcmp(v, "mfma") == 0) return DecodeKernel::kMfma;
+  if (strcmp(v, "mfma128") == 0) return DecodeKernel::kMfma128;
+  if (strcmp(v, "mfma64") == 0) return DecodeKernel::kMfma64;
   return DecodeKernel::kAuto;
+}
+
+// Compute units of the current device, looked up once per device (0 if unknown).
+int cu_count_of_current_device() {
+  constexpr int kMaxDevices = 64;
+  static int cached[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    cached[dev] = n;
+  }
+  return cached[dev];
 }
 
 }  // namespace
@@ -152,8 +172,16 @@ int mla_decode_paged(const void* q_abs, const void* q_r, const void* kv_cache,
   const DecodeKernel choice = decode_kernel_choice();
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const bool mfma_ok = mla::decode_mfma_supported(a, bf16);
-  if (choice == DecodeKernel::kMfma && !mfma_ok) return MLA_ERR_UNSUPPORTED;
-  if (mfma_ok && choice != DecodeKernel::kGeneric) return launch_status(mla::launch_decode_mfma(a, s));
+  const bool mfma_required = choice == DecodeKernel::kMfma || choice == DecodeKernel::kMfma128 ||
+                             choice == DecodeKernel::kMfma64;
+  if (mfma_required && !mfma_ok) return MLA_ERR_UNSUPPORTED;
+  if (choice == DecodeKernel::kMfma64 && groups != 1) return MLA_ERR_UNSUPPORTED;
+  if (mfma_ok && choice != DecodeKernel::kGeneric) {
+    a.head_split = choice == DecodeKernel::kMfma128 ? 1 : choice == DecodeKernel::kMfma64 ? 2 : 0;
+    const int hs = mla::decode_mfma_head_split(a, cu_count_of_current_device());
+    if (static_cast<long long>(total_q) * num_splits * hs > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+    return launch_status(mla::launch_decode_mfma(a, hs, s));
+  }
   return launch_status(mla::launch_decode_generic(a, bf16, s));
 }
 

@@ -23,6 +23,7 @@ struct DecodeArgs {
   int heads, groups, d_c, d_R, page_size, num_splits, pages_per_split;
   float scale;
   int causal;
+  int head_split;    // MFMA decode, one latent group: 0 = chosen from the grid size, 1 or 2
 };
 
 // Generic kernels: any (d_cg <= 1024, d_R <= 256), bf16 or fp32 storage.
@@ -42,8 +43,13 @@ hipError_t launch_rope_table(float* cos_out, float* sin_out, int max_pos, int d_
 
 namespace mla {
 // MFMA split-KV decode: bf16, 128 heads, d_c 512, d_R 64, one or two latent groups.
+// With one latent group the heads of a (token, split) pair are either covered by one
+// workgroup (head split 1) or by two of 64 heads each (head split 2, the default when
+// 2 * total_q * num_splits <= cu_count, i.e. when one workgroup per pair would leave
+// compute units idle).
 bool decode_mfma_supported(const DecodeArgs& a, bool bf16);
-hipError_t launch_decode_mfma(const DecodeArgs& a, hipStream_t s);
+int decode_mfma_head_split(const DecodeArgs& a, int cu_count);
+hipError_t launch_decode_mfma(const DecodeArgs& a, int head_split, hipStream_t s);
 }  // namespace mla
 
 namespace mla {

@@ -221,12 +221,31 @@ def plan_makespan(pages, q_lens, pages_per_split: int, cu_count: int = 256) -> f
     return max(max(f) for f in free)
 
 
-def split_plan(seq_lens_host, q_lens_host, cu_count: int = 256):
+# Longest split (pages) for which two 64-head workgroups per (token, split) pay off: the
+# half-head workgroups run a page at about 0.66 of a full page's time, so twice the
+# pages cost about 1.3x; in exchange the split count halves, which halves the partial
+# output the decode writes and the merge reads.  Measured on 4096-key sequences at
+# batch 16 (4 pages per full-head split): 58.1 against 61.4 us per step; at 1024
+# pages per sequence (64 per split) the head split loses (383 against 348 us).
+HEAD_SPLIT_MAX_PAGES = 6
+
+
+def head_split(total_q: int, num_splits: int, groups: int, cu_count: int = 256) -> int:
+    """Workgroups per (token, split) pair of the MFMA decode kernel: 2 (64 heads each)
+    for one latent group when 2 * total_q * num_splits <= cu_count, else 1 (128 heads).
+    The library applies the same rule to the device's compute-unit count."""
+    return 2 if groups == 1 and 2 * total_q * num_splits <= cu_count else 1
+
+
+def split_plan(seq_lens_host, q_lens_host, cu_count: int = 256, groups: int = 1):
     """(num_splits, pages_per_split) for a batch: the split length whose grid finishes
     first under plan_makespan's model, among at most 256 splits per sequence.  The
     candidates are the shortest split lengths for each split count of the longest
     sequence and the lengths that give k workgroups per CU for small k; a tie goes
-    to the fewer workgroups (less partial output to merge)."""
+    to the fewer workgroups (less partial output to merge).  With one latent group, a
+    plan of at most HEAD_SPLIT_MAX_PAGES pages per split is then doubled in length
+    when the halved split count lets the kernel run two 64-head workgroups per
+    (token, split) (head_split)."""
     pages = [max(1, math.ceil(int(L) / PAGE_SIZE)) for L in seq_lens_host]
     q = [int(x) for x in q_lens_host]
     max_p = max(pages)
@@ -243,7 +262,13 @@ def split_plan(seq_lens_host, q_lens_host, cu_count: int = 256):
         if best is None or key < best[0]:
             best = (key, pps)
     pps = best[1]
-    return max(1, math.ceil(max_p / pps)), pps
+    S = max(1, math.ceil(max_p / pps))
+    if groups == 1 and S >= 2 and pps <= HEAD_SPLIT_MAX_PAGES:
+        pps2 = 2 * pps
+        S2 = max(1, math.ceil(max_p / pps2))
+        if head_split(sum(q), S2, groups, cu_count) == 2:
+            return S2, pps2
+    return S, pps
 
 
 class DecodeStep:
@@ -259,7 +284,8 @@ class DecodeStep:
         if num_splits is None:
             lens = seq_lens_host if seq_lens_host is not None else seq_lens.cpu().tolist()
             cu = cu_q.cpu().tolist()
-            num_splits, self.pages_per_split = split_plan(lens, [b - a for a, b in zip(cu, cu[1:])])
+            num_splits, self.pages_per_split = split_plan(lens, [b - a for a, b in zip(cu, cu[1:])],
+                                                          groups=groups)
         else:
             self.pages_per_split = 0
         self.num_splits = num_splits

@@ -33,13 +33,50 @@ def test_plan_covers_every_page_within_the_split_limit(name):
     assert (S - 1) * pps < max(pages)          # and no split is empty for the longest sequence
 
 
-@pytest.mark.parametrize("name,expect", [("dsv3_b16_l4096", (16, 4)), ("long_b16_l65536", (16, 64)),
-                                         ("gla2_b32_l16384", (8, 32))])
-def test_uniform_batches_get_one_workgroup_per_cu(name, expect):
-    L, q = _lens(wl.CONFIGS[name])
-    S, pps = mla.split_plan(L, q)
+@pytest.mark.parametrize("name,expect,hs", [("dsv3_b16_l4096", (8, 8), 2),
+                                            ("long_b16_l65536", (16, 64), 1),
+                                            ("gla2_b32_l16384", (8, 32), 1)])
+def test_uniform_batches_get_one_workgroup_per_cu(name, expect, hs):
+    """16 x 4096 keys: 16 splits of 4 pages would fill the 256 CUs, and that short a
+    split is doubled so two 64-head workgroups per (token, split) fill them instead."""
+    cfg = wl.CONFIGS[name]
+    L, q = _lens(cfg)
+    S, pps = mla.split_plan(L, q, groups=cfg.groups)
     assert (S, pps) == expect
-    assert sum(n * S for n in q) == 256
+    T = sum(q)
+    assert mla.head_split(T, S, cfg.groups) == hs
+    assert T * S * hs == 256
+
+
+def test_head_split_rule():
+    # one latent group: two workgroups per pair while the doubled grid fits the CUs
+    assert mla.head_split(16, 8, 1) == 2
+    assert mla.head_split(16, 9, 1) == 1
+    assert mla.head_split(1, 128, 1) == 2 and mla.head_split(1, 129, 1) == 1
+    assert mla.head_split(16, 8, 1, cu_count=128) == 1
+    # two latent groups: never
+    assert mla.head_split(1, 1, 2) == 1
+
+
+@pytest.mark.parametrize("B,L,groups", [(16, 2048, 1), (16, 4096, 1), (32, 4096, 1), (16, 4096, 2),
+                                        (4, 1000, 1), (64, 300, 1)])
+def test_head_split_only_doubles_short_splits(B, L, groups):
+    """The head split doubles a plan's split length only when that length is at most
+    HEAD_SPLIT_MAX_PAGES and the halved split count then gets two workgroups per pair;
+    otherwise the plan is the one-workgroup plan.  Either way every page is covered."""
+    lens, q = [L] * B, [1] * B
+    S, pps = mla.split_plan(lens, q, groups=groups)
+    S1, pps1 = mla.split_plan(lens, q, groups=2)      # the plan without a head split
+    pages = math.ceil(L / mla.PAGE_SIZE)
+    assert S * pps >= pages and (S - 1) * pps < pages
+    if groups == 2:
+        assert mla.head_split(B, S, groups) == 1
+    elif (S, pps) != (S1, pps1):
+        assert pps == 2 * pps1 and pps1 <= mla.HEAD_SPLIT_MAX_PAGES
+        assert mla.head_split(B, S, groups) == 2
+    else:
+        assert pps1 > mla.HEAD_SPLIT_MAX_PAGES or S1 == 1 or mla.head_split(
+            B, math.ceil(pages / (2 * pps1)), groups) == 1 or mla.head_split(B, S, groups) == 2
 
 
 def test_makespan_model_by_hand():
