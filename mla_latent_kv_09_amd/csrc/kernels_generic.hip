@@ -233,56 +233,76 @@ combine_kernel(const T* __restrict__ o_part, const float* __restrict__ lse_part,
   if (tid == 0 && lse_out != nullptr) lse_out[r] = M == -INFINITY ? -INFINITY : M + logf(sum);
 }
 
-// Four consecutive partials as float32 (8-byte bf16 or 16-byte fp32 load).
-__device__ __forceinline__ float __attribute__((ext_vector_type(4))) load4(const float* p) {
-  return *reinterpret_cast<const float __attribute__((ext_vector_type(4)))*>(p);
+// Vectorised combine for d_cg in {256, 512}: one wave per (t, h) row; lane l owns
+// columns kE l .. kE l + kE - 1 (kE = d_cg / 64), read as kW 32-bit words per split
+// (16 B for bf16 rows of 512).  The partials of up to kChunk splits (at most 128 words
+// per lane) are requested together, before the log-sum-exp reduction, so a row of up
+// to kChunk splits costs about one memory round trip; the launch picks the smallest
+// chunk that covers the split count, which keeps the register count, and so the
+// number of rows in flight per CU, as high as the split count allows.  Splits with LSE = -inf (no keys)
+// get weight 0 and their partials -- never written -- are not used.
+template <typename T, int kW>
+__device__ __forceinline__ void load_words(const T* p, uint32_t (&x)[kW]) {
+  static_assert(kW == 2 || kW % 4 == 0, "8- or 16-byte pieces");
+  if constexpr (kW == 2) {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    x[0] = v.x;
+    x[1] = v.y;
+  } else {
+#pragma unroll
+    for (int i = 0; i < kW / 4; ++i) {
+      const uint4 v = reinterpret_cast<const uint4*>(p)[i];
+      x[4 * i] = v.x;
+      x[4 * i + 1] = v.y;
+      x[4 * i + 2] = v.z;
+      x[4 * i + 3] = v.w;
+    }
+  }
 }
-__device__ __forceinline__ float __attribute__((ext_vector_type(4))) load4(const uint16_t* p) {
-  const uint2 u = *reinterpret_cast<const uint2*>(p);
-  return {__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-          __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u)};
+// Element e of a lane's piece, widened to float.
+template <typename T>
+__device__ __forceinline__ float word_elem(const uint32_t* x, int e) {
+  if constexpr (sizeof(T) == 2)
+    return __uint_as_float((e & 1) ? (x[e >> 1] & 0xffff0000u) : (x[e >> 1] << 16));
+  else
+    return __uint_as_float(x[e]);
 }
 
-// Vectorised combine for d_cg in {256, 512}: one wave per (t, h) row, float4 per lane.
-// The partials of up to 16 splits are requested together, before the log-sum-exp
-// reduction, so a row costs about one memory round trip rather than one per group of
-// splits.  Splits with LSE = -inf (no keys) get weight 0 and their partials -- never
-// written -- are not used.
 template <typename T, int kDcg>
+constexpr int combine_max_chunk() { return 128 / (kDcg / 64 * static_cast<int>(sizeof(T)) / 4); }
+
+template <typename T, int kDcg, int kChunk>
 __global__ void __launch_bounds__(kThreads)
 combine_vec_kernel(const T* __restrict__ o_part, const float* __restrict__ lse_part,
                    T* __restrict__ o_lat, float* __restrict__ lse_out, int rows, int S) {
-  constexpr int kVec = kDcg / 256;  // float4 groups per lane
-  constexpr int kChunk = 16;        // splits in flight per wave
-  typedef float f32x4 __attribute__((ext_vector_type(4)));
+  constexpr int kE = kDcg / 64;                                  // columns per lane
+  constexpr int kW = kE * static_cast<int>(sizeof(T)) / 4;       // words per lane and split
+  static_assert(kChunk * kW <= 128, "at most 128 words of partials per lane");
   const int lane = threadIdx.x & 63;
   const size_t r = static_cast<size_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
   if (r >= static_cast<size_t>(rows)) return;
   const float* lse = lse_part + r * S;
-  const T* base = o_part + r * S * kDcg + 4 * lane;
-  auto load_chunk = [&](int s0, f32x4 (&x)[kChunk][kVec]) {
-#pragma unroll
-    for (int u = 0; u < kChunk; ++u) {
-      const int s = min(s0 + u, S - 1);  // in bounds; splits past S get weight 0
-#pragma unroll
-      for (int v = 0; v < kVec; ++v) x[u][v] = load4(base + s * kDcg + 256 * v);
-    }
-  };
+  const T* base = o_part + r * S * kDcg + kE * lane;
   // Lane s holds the LSE of split s (s < 64): loaded before the partials so that its
   // wait does not also wait for them, and broadcast with readlane below.
   const float l_lane = lane < S ? lse[lane] : -INFINITY;
-  f32x4 x[kChunk][kVec];
-  load_chunk(0, x);
+  uint32_t x[kChunk][kW];
+  auto load_chunk = [&](int s0) {
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u)
+      if (s0 + u < S) load_words<T, kW>(base + static_cast<size_t>(s0 + u) * kDcg, x[u]);
+  };
+  load_chunk(0);
   float mx = l_lane;
   for (int s = lane + 64; s < S; s += 64) mx = fmaxf(mx, lse[s]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-  f32x4 acc[kVec];
+  float acc[kE];
 #pragma unroll
-  for (int v = 0; v < kVec; ++v) acc[v] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int e = 0; e < kE; ++e) acc[e] = 0.f;
   float sum = 0.f;
   for (int s0 = 0; s0 < S; s0 += kChunk) {
-    if (s0 > 0) load_chunk(s0, x);
+    if (s0 > 0) load_chunk(s0);
 #pragma unroll
     for (int u = 0; u < kChunk; ++u) {
       const int s = s0 + u;
@@ -290,16 +310,31 @@ combine_vec_kernel(const T* __restrict__ o_part, const float* __restrict__ lse_p
       if (s < S) l = s < 64 ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_lane), s)) : lse[s];
       const float wt = (l == -INFINITY || mx == -INFINITY) ? 0.f : expf(l - mx);
       sum += wt;
+      if (wt != 0.f) {
 #pragma unroll
-      for (int v = 0; v < kVec; ++v)
-        if (wt != 0.f) acc[v] += wt * x[u][v];
+        for (int e = 0; e < kE; ++e) acc[e] += wt * word_elem<T>(x[u], e);
+      }
     }
   }
   const float inv = mx == -INFINITY ? 0.f : 1.f / sum;
+  uint32_t y[kW];
+  if constexpr (sizeof(T) == 2) {
 #pragma unroll
-  for (int v = 0; v < kVec; ++v)
+    for (int w = 0; w < kW; ++w)
+      y[w] = static_cast<uint32_t>(f32_to_bf16(acc[2 * w] * inv)) |
+             (static_cast<uint32_t>(f32_to_bf16(acc[2 * w + 1] * inv)) << 16);
+  } else {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) store_elem(o_lat, r * kDcg + 256 * v + 4 * lane + e, acc[v][e] * inv);
+    for (int w = 0; w < kW; ++w) y[w] = __float_as_uint(acc[w] * inv);
+  }
+  T* dst = o_lat + r * kDcg + kE * lane;
+  if constexpr (kW == 2) {
+    *reinterpret_cast<uint2*>(dst) = uint2{y[0], y[1]};
+  } else {
+#pragma unroll
+    for (int i = 0; i < kW / 4; ++i)
+      reinterpret_cast<uint4*>(dst)[i] = uint4{y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]};
+  }
   if (lane == 0 && lse_out != nullptr) lse_out[r] = mx == -INFINITY ? -INFINITY : mx + logf(sum);
 }
 
@@ -356,27 +391,34 @@ hipError_t launch_decode_generic(const DecodeArgs& a, bool bf16, hipStream_t s) 
   return hipGetLastError();
 }
 
+template <typename T, int kDcg>
+hipError_t launch_combine_vec(const T* o_part, const float* lse_part, T* o_lat, float* lse_out,
+                              int rows, int S, hipStream_t s) {
+  constexpr int kMax = combine_max_chunk<T, kDcg>();
+  const dim3 grid((rows + 3) / 4);
+  if (S <= 8)
+    combine_vec_kernel<T, kDcg, 8><<<grid, kThreads, 0, s>>>(o_part, lse_part, o_lat, lse_out, rows, S);
+  else if (S <= 16 || kMax == 16)
+    combine_vec_kernel<T, kDcg, 16><<<grid, kThreads, 0, s>>>(o_part, lse_part, o_lat, lse_out, rows, S);
+  else
+    combine_vec_kernel<T, kDcg, kMax><<<grid, kThreads, 0, s>>>(o_part, lse_part, o_lat, lse_out, rows, S);
+  return hipGetLastError();
+}
+
 hipError_t launch_combine(const void* o_part_v, const float* lse_part, void* o_lat, float* lse_out,
                           int T, int H, int d_cg, int S, bool bf16, hipStream_t s) {
   const int rows = T * H;
   const auto* op16 = static_cast<const uint16_t*>(o_part_v);
   const auto* op32 = static_cast<const float*>(o_part_v);
   if (d_cg == 512 || d_cg == 256) {
-    const dim3 vgrid((rows + 3) / 4);
     if (bf16) {
       auto* o = static_cast<uint16_t*>(o_lat);
-      if (d_cg == 512)
-        combine_vec_kernel<uint16_t, 512><<<vgrid, kThreads, 0, s>>>(op16, lse_part, o, lse_out, rows, S);
-      else
-        combine_vec_kernel<uint16_t, 256><<<vgrid, kThreads, 0, s>>>(op16, lse_part, o, lse_out, rows, S);
-    } else {
-      auto* o = static_cast<float*>(o_lat);
-      if (d_cg == 512)
-        combine_vec_kernel<float, 512><<<vgrid, kThreads, 0, s>>>(op32, lse_part, o, lse_out, rows, S);
-      else
-        combine_vec_kernel<float, 256><<<vgrid, kThreads, 0, s>>>(op32, lse_part, o, lse_out, rows, S);
+      return d_cg == 512 ? launch_combine_vec<uint16_t, 512>(op16, lse_part, o, lse_out, rows, S, s)
+                         : launch_combine_vec<uint16_t, 256>(op16, lse_part, o, lse_out, rows, S, s);
     }
-    return hipGetLastError();
+    auto* o = static_cast<float*>(o_lat);
+    return d_cg == 512 ? launch_combine_vec<float, 512>(op32, lse_part, o, lse_out, rows, S, s)
+                       : launch_combine_vec<float, 256>(op32, lse_part, o, lse_out, rows, S, s);
   }
   const dim3 grid(static_cast<unsigned>(T) * H);
   if (bf16)
