@@ -25,7 +25,10 @@ cache flush before every step, each step between its own events.
 Prints one JSON line.  `value` is the algorithmic TFLOP/s of the whole step
 (attention flops of the absorbed method plus the two projections, divided by the
 step time); the line also carries latent-KV GB/s, sequences/s, the roofline
-object of the dominant kernel (the split-KV decode) and the CPU oracle baseline.
+object of the dominant kernel (the split-KV decode), the roofline fractions of the
+attention calls (decode + combine) and of the whole step against the nominal 8 TB/s
+and against a measured 1 GiB device copy (`roofline_path`), and the CPU oracle
+baseline.
 """
 from __future__ import annotations
 
@@ -184,6 +187,43 @@ def flush_timing(args, w, torch, harness, stream, names):
     return ms, parts, parts["decode_paged"], step.num_splits, step, wall, graph is not None
 
 
+def measure_copy_gbps(torch, stream, mib=1024, reps=5):
+    """Achievable HBM streaming rate on this GPU: a 1 GiB device-to-device copy (read +
+    write bytes / time), median of `reps`, the same bytes counted both ways."""
+    src = torch.empty(mib << 20, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    del src, dst
+    return 2 * (mib << 20) / (statistics.median(times) * 1e-3) / 1e9
+
+
+def path_roofline(att, proj, kv_bytes, w_bytes, parts, step_ms, peak_tflops, copy_gbps):
+    """Roofline fractions of the attention calls (decode + combine) and of the whole step
+    (all four calls): the binding roof's time, max(bytes / bandwidth, flops / peak), over the
+    measured time, against the nominal 8 TB/s and against the measured copy rate."""
+    def frac(flops, nbytes, ms, gbps):
+        t_roof = max(nbytes / (gbps * 1e9), flops / (peak_tflops * 1e12))
+        return t_roof / (ms * 1e-3)
+    att_ms = parts["decode_paged"] + parts["combine"]
+    return {
+        "hbm_copy_gbps": copy_gbps,
+        "attention": {"ms": att_ms, "frac": frac(att, kv_bytes, att_ms, HBM_PEAK_GBPS),
+                      "frac_of_copy_bw": frac(att, kv_bytes, att_ms, copy_gbps)},
+        "step": {"ms": step_ms, "frac": frac(att + proj, kv_bytes + w_bytes, step_ms, HBM_PEAK_GBPS),
+                 "frac_of_copy_bw": frac(att + proj, kv_bytes + w_bytes, step_ms, copy_gbps)},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -291,6 +331,7 @@ def main():
         ms, parts, dec, S, step, wall, graph_used = flush_timing(args, w, torch, harness, stream, names)
         timing = {"method": "flush"}
 
+    copy_gbps = measure_copy_gbps(torch, stream)
     flops = att + proj
     tflops = flops / (ms * 1e-3) / 1e12
     kv_gbps = kv_bytes / (ms * 1e-3) / 1e9
@@ -325,6 +366,7 @@ def main():
                    "hip_graph": graph_used},
         "latent_kv_gbps": kv_gbps, "latent_kv_frac_hbm_peak": kv_gbps / HBM_PEAK_GBPS,
         "tflops_frac_mfma_peak": tflops / peak_f, "seqs_per_s": seqs,
+        "roofline_path": path_roofline(att, proj, kv_bytes, w_bytes, parts, ms, peak_f, copy_gbps),
         "kernel_ms": parts, "wall_s_timed_region": wall,
         "roofline": roof,
     }
