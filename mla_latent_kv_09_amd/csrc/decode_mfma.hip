@@ -1,13 +1,15 @@
-// Split-KV absorbed-MLA decode on bf16 MFMA (gfx950), 128 query rows per workgroup.
-// Instantiated for one latent group (MLA: every head sees the 512-d latent) and for
-// two groups (grouped latent attention, www.hotelren.com/news/5324130 §1: heads
+// Split-KV absorbed-MLA decode on bf16 MFMA (gfx950), 128 (or 64) query rows per
+// workgroup.  Instantiated for one latent group (MLA: every head sees the 512-d latent)
+// and for two groups (grouped latent attention, www.hotelren.com/news/5324130 §1: heads
 // 0-63 see latent columns 0-255, heads 64-127 columns 256-511, all share k_R).
 //
 // Computes, for one query token t and one split of its sequence's pages, the
 // softmax-normalised latent output and log-sum-exp of
 //     s_j = scale * (q_abs . c_KV[j] + RoPE(q_R) . k_R[j])          (nxmr.cn/news/151634 §4)
-// over the split's keys, for all H = 128 heads at once, so every streamed latent
-// page is read from HBM once per (token, split) and shared by all heads
+// over the split's keys, for all H = 128 heads at once (or, with the head split HS = 2
+// below, for 64 heads in each of two workgroups that run side by side on one XCD), so
+// every streamed latent page is read from HBM once per (token, split) and shared by all
+// heads
 // (nxmr.cn/news/151634 §1: the 512-d latent plus the 64-d shared RoPE key is all a
 // token stores).  Softmax statistics are fp32 (online, one page at a time).
 //
@@ -17,7 +19,7 @@
 // rare moves.  Output and log-sum-exp are normalised against the same m at the end,
 // so the result is the same softmax.
 //
-// Work layout (workgroup = 8 waves, two per SIMD):
+// Work layout (workgroup = 8 waves, two per SIMD; HS = 1):
 //   wave w owns heads 16w .. 16w+15; lane l owns head 16w + l%16, and the four
 //   lanes l%16 + 16g (g = 0..3) split that head's keys (scores) and latent
 //   columns (output) between them.
