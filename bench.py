@@ -1,6 +1,7 @@
 """Benchmark of one absorbed-MLA decode step on one MI355X.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--splits S]
+                    [--pages-per-split P]
                     [--no-cpu-baseline] [--flush] [--no-graph]
 
 A step is the whole hot path over one batch of synthetic input already resident
@@ -137,7 +138,7 @@ def flush_timing(args, w, torch, harness, stream, names):
     read-only flush before every step, events around each step and between the calls
     of a second pass."""
     d = harness.to_device(w)
-    step = harness.make_step(w, d, args.splits)
+    step = harness.make_step(w, d, args.splits, args.pages_per_split)
     flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
 
     def one_step(ev=None):
@@ -230,7 +231,11 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", default=HEADLINE)
-    ap.add_argument("--splits", type=int, default=None)
+    ap.add_argument("--splits", type=int, default=None,
+                    help="split count instead of the planner's (each sequence cut into S equal "
+                         "parts unless --pages-per-split is given)")
+    ap.add_argument("--pages-per-split", type=int, default=0,
+                    help="with --splits: fixed split length in pages")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--flush", action="store_true",
                     help="one input copy and a 1 GiB read-only cache flush before every step, "
@@ -265,7 +270,8 @@ def main():
         # evicted from L2 and MALL: each step starts from HBM.  Steps and calls are
         # timed back to back inside HIP graphs, as a serving loop runs them.
         n_copies = max(2, min(8, math.ceil(2 * MALL_BYTES / (kv_bytes + w_bytes))))
-        steps = [harness.make_step(w, harness.to_device(w), args.splits) for _ in range(n_copies)]
+        steps = [harness.make_step(w, harness.to_device(w), args.splits, args.pages_per_split)
+                 for _ in range(n_copies)]
         step = steps[0]
         S = step.num_splits
         per_graph = n_copies * max(1, math.ceil(8 / n_copies))  # calls captured per graph

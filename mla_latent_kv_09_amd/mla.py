@@ -275,7 +275,7 @@ class DecodeStep:
     """The four calls of one decode step over preallocated buffers (no allocation per call)."""
 
     def __init__(self, *, q_c, q_r, w_uk, w_uv, kv_cache, page_table, seq_lens, cu_q, groups=1,
-                 num_splits=None, rope=None, causal=True, seq_lens_host=None):
+                 num_splits=None, rope=None, causal=True, seq_lens_host=None, pages_per_split=0):
         self.q_c, self.q_r, self.w_uk, self.w_uv = q_c, q_r, w_uk, w_uv
         self.kv, self.page_table, self.seq_lens, self.cu_q = kv_cache, page_table, seq_lens, cu_q
         self.groups, self.rope, self.causal = groups, rope, causal
@@ -287,7 +287,7 @@ class DecodeStep:
             num_splits, self.pages_per_split = split_plan(lens, [b - a for a, b in zip(cu, cu[1:])],
                                                           groups=groups)
         else:
-            self.pages_per_split = 0
+            self.pages_per_split = int(pages_per_split)
         self.num_splits = num_splits
         dev = q_c.device
         self.q_abs = torch.empty((T, H, d_cg), dtype=q_c.dtype, device=dev)

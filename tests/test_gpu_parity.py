@@ -162,8 +162,14 @@ def _with_lengths(cfg, lens, q_lens):
                        latents=latents, w_uk=w.w_uk, w_uv=w.w_uv, page_table=pt, pool=pool)
 
 
-def test_empty_sequence_gives_zero_and_minus_inf():
-    cfg = _small("dsv3_b16_l4096", batch=2, heads=16, seq_len=100)
+@pytest.mark.parametrize("heads,kind", [(16, None), (128, "mfma128"), (128, "mfma64")])
+def test_empty_sequence_gives_zero_and_minus_inf(heads, kind, monkeypatch):
+    """A sequence with no keys: output 0 and LSE -inf on every head, from the generic
+    kernel and from both head splits of the MFMA kernel (where both workgroups of an
+    empty pair leave through the early exit)."""
+    if kind is not None:
+        monkeypatch.setenv("MLA_KV_DECODE_KERNEL", kind)
+    cfg = _small("dsv3_b16_l4096", batch=2, heads=heads, seq_len=100)
     w = wl.make_workload(cfg)
     w.seq_lens[1] = 0                       # second sequence has no keys at all
     step = run_step(w, num_splits=2)
