@@ -315,6 +315,8 @@ def main():
             parts[name] = statistics.median(timed(run, reps) / (reps * per_graph) for _ in range(5))
             del run
         dec = parts["decode_paged"]
+        append = measure_append(args, w, torch, harness, mla, wl, steps, runner, timed, reps,
+                                per_graph)
         # Step time: exactly K whole steps back to back over the rotated copies, one timed
         # region between two synchronizations.
         full, rest = divmod(args.steps, per_graph)
@@ -336,6 +338,7 @@ def main():
     else:
         ms, parts, dec, S, step, wall, graph_used = flush_timing(args, w, torch, harness, stream, names)
         timing = {"method": "flush"}
+        append = None
 
     copy_gbps = measure_copy_gbps(torch, stream)
     flops = att + proj
@@ -376,9 +379,56 @@ def main():
         "kernel_ms": parts, "wall_s_timed_region": wall,
         "roofline": roof,
     }
+    if append is not None:
+        out["append_kv"] = append
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, att)
     print(json.dumps(out))
+
+
+def measure_append(args, w, torch, harness, mla, wl, steps, runner, timed, reps, per_graph):
+    """The latent-cache append (mla_append_kv, the call before the decode; not part of the
+    step): (1) this workload's T new rows per call, back to back over the rotated copies;
+    (2) a prefill-shaped bulk append that writes every slot of the first sequences (at
+    most 65536 rows; q_len = seq_len, so each sequence's rows 0 .. L-1), rotated over the
+    copies like the step, whose bytes (each row read once and written once: 2 (d_c + d_R)
+    elements) give the kernel's HBM roofline."""
+    cfg = w.cfg
+    elem = 2 if cfg.dtype == "bf16" else 4
+    n = len(steps)
+    new = wl.make_new_tokens(w)
+    tensors = [harness.new_tokens_to_device(w, new, st.kv.device) for st in steps]
+
+    def call(i):
+        st, (c, k) = steps[i % n], tensors[i % n]
+        return lambda: mla.append_kv(c, k, st.kv, st.page_table, st.seq_lens, st.cu_q, rope=st.rope)
+
+    run = runner([call(i) for i in range(per_graph)])
+    ms_t = statistics.median(timed(run, reps) / (reps * per_graph) for _ in range(5))
+    del run
+    res = {"rows": int(w.total_q), "ms": ms_t}
+    if cfg.seq_len is None:  # bulk case only for equal lengths
+        return res
+    L, B = int(cfg.seq_len), cfg.batch
+    nb = max(1, min(B, 65536 // L))  # whole sequences, at most 65536 rows
+    bulk = wl.make_new_tokens(w, rows=nb * L)
+    cu = torch.tensor([min(b, nb) * L for b in range(B + 1)], dtype=torch.int32,
+                      device=steps[0].kv.device)
+    bulk_t = [harness.new_tokens_to_device(w, bulk, st.kv.device) for st in steps]
+
+    def bulk_call(i):
+        st, (c, k) = steps[i % n], bulk_t[i % n]
+        return lambda: mla.append_kv(c, k, st.kv, st.page_table, st.seq_lens, cu, rope=st.rope)
+
+    run = runner([bulk_call(i) for i in range(n)])
+    bulk_reps = max(2, min(10, reps))
+    ms_b = statistics.median(timed(run, bulk_reps) / (bulk_reps * n) for _ in range(5))
+    del run, bulk_t
+    nbytes = 2 * nb * L * (cfg.d_c + cfg.d_R) * elem
+    gbps = nbytes / (ms_b * 1e-3) / 1e9
+    res["bulk"] = {"rows": nb * L, "ms": ms_b, "algorithmic_bytes": nbytes, "gbps": gbps,
+                   "frac_hbm_peak": gbps / HBM_PEAK_GBPS}
+    return res
 
 
 def decode_kernel_name(cfg):

@@ -11,8 +11,9 @@
  *   mla_combine       log-sum-exp merge of the splits -> o_latent
  *   mla_up_v          out[t,h,:] = W_UV[h] . o_latent[t,h,:]            (value up-projection)
  *
- * plus mla_rope_table (the fp32 cos/sin table the decode call reads) and
- * mla_status_string.
+ * plus mla_rope_table (the fp32 cos/sin table the decode call reads),
+ * mla_append_kv (writes the new tokens' latent rows, with their rotated RoPE keys,
+ * into the paged cache before the decode reads them) and mla_status_string.
  *
  * Sources, cited by page address and section:
  *   P3 = www.nxmr.cn/news/151634  (MLA operators: absorption, paged latent cache)
@@ -153,6 +154,40 @@ int mla_decode_paged(const void* q_abs, const void* q_r, const void* kv_cache,
                      int heads, int groups, int d_hc, int d_c, int d_R, int page_size,
                      int num_splits, int pages_per_split, float softmax_scale, int causal,
                      int dtype, void* stream);
+
+/*
+ * mla_append_kv -- write the latent-cache rows of a step's new tokens into their
+ * pages, the step just before mla_decode_paged reads them (P3 §1: what one token
+ * stores per layer is its latent c_KV followed by its decoupled RoPE key k_R, the
+ * part that carries its position; P3 §3: 64-token pages, RoPE computed in fp32;
+ * P3 §4: the fp32 table applied with fp32 multiply-adds).
+ *
+ * Inputs
+ *   c_kv_new    [T, d_c]  dtype   latent of each new token (packed rows, as the queries)
+ *   k_r_new     [T, d_R]  dtype   RoPE key of each new token, before rotation
+ *   page_table, seq_lens, cu_q    as in mla_decode_paged; seq_lens[b] already counts
+ *               the q_len_b new tokens, so new token i of sequence b (row cu_q[b] + i)
+ *               sits at pos = seq_lens[b] - q_len_b + i, the position its query is
+ *               rotated at
+ *   rope_cos, rope_sin  [rope_max_pos, d_R/2] float32 from mla_rope_table, or both NULL
+ *               for no rotation; positions past the table use its last row (as the decode)
+ * In/out
+ *   kv_cache    [num_pool_pages, page_size, d_c + d_R] dtype.  Slot pos % page_size of
+ *               page page_table[b][pos / page_size] becomes
+ *                 [c_kv_new[t] | RoPE(k_r_new[t], pos)],
+ *               the latent copied bit for bit and each key pair (x0, x1) = (k[2k], k[2k+1])
+ *               rotated in fp32 as y0 = x0 cos - x1 sin, y1 = x0 sin + x1 cos with the
+ *               table's (pos, k) entry, rounded once to dtype (the arithmetic the decode
+ *               applies to q_R).  No other slot is touched.
+ * d_c and d_R must be multiples of 8 (bf16) or 4 (fp32): MLA_ERR_UNSUPPORTED otherwise.
+ * Two new tokens that map to the same slot (overlapping page tables) race; a sequence
+ * with seq_lens[b] < q_len_b writes only its rows at positions >= 0.
+ */
+int mla_append_kv(const void* c_kv_new, const void* k_r_new, void* kv_cache,
+                  const int32_t* page_table, const int32_t* seq_lens, const int32_t* cu_q,
+                  const float* rope_cos, const float* rope_sin, int rope_max_pos,
+                  int batch, int total_q, int max_pages_per_seq, int num_pool_pages,
+                  int d_c, int d_R, int page_size, int dtype, void* stream);
 
 /*
  * mla_combine -- merge the split partials by their log-sum-exp:

@@ -185,6 +185,50 @@ int mla_decode_paged(const void* q_abs, const void* q_r, const void* kv_cache,
   return launch_status(mla::launch_decode_generic(a, bf16, s));
 }
 
+int mla_append_kv(const void* c_kv_new, const void* k_r_new, void* kv_cache,
+                  const int32_t* page_table, const int32_t* seq_lens, const int32_t* cu_q,
+                  const float* rope_cos, const float* rope_sin, int rope_max_pos, int batch,
+                  int total_q, int max_pages_per_seq, int num_pool_pages, int d_c, int d_R,
+                  int page_size, int dtype, void* stream) {
+  int st = check_dtype(dtype);
+  if (st != MLA_OK) return st;
+  if (total_q < 0 || batch <= 0 || d_c <= 0 || d_R <= 0 || (d_R & 1) || max_pages_per_seq <= 0 ||
+      num_pool_pages <= 0 || page_size <= 0)
+    return MLA_ERR_DIM;
+  if (page_size != MLA_PAGE_SIZE) return MLA_ERR_UNSUPPORTED;
+  const int piece = dtype == MLA_DTYPE_BF16 ? 8 : 4;  // elements per 16-byte piece
+  if (d_c % piece != 0 || d_R % piece != 0) return MLA_ERR_UNSUPPORTED;
+  if (static_cast<long long>(max_pages_per_seq) * page_size > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+  if (static_cast<long long>(total_q) * ((d_c + d_R) / piece) > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+  if ((rope_cos == nullptr) != (rope_sin == nullptr)) return MLA_ERR_NULL;
+  if (rope_cos != nullptr && rope_max_pos <= 0) return MLA_ERR_DIM;
+  if (total_q == 0) return MLA_OK;
+  if (!c_kv_new || !k_r_new || !kv_cache || !page_table || !seq_lens || !cu_q) return MLA_ERR_NULL;
+  const void* ptrs[] = {c_kv_new, k_r_new, kv_cache, page_table, seq_lens, cu_q};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MLA_ERR_ALIGN;
+  if (rope_cos && (!aligned16(rope_cos) || !aligned16(rope_sin))) return MLA_ERR_ALIGN;
+  mla::AppendArgs a{};
+  a.c_new = c_kv_new;
+  a.k_new = k_r_new;
+  a.kv = kv_cache;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.cu_q = cu_q;
+  a.rope_cos = rope_cos;
+  a.rope_sin = rope_sin;
+  a.rope_max_pos = rope_max_pos;
+  a.batch = batch;
+  a.total_q = total_q;
+  a.max_pages = max_pages_per_seq;
+  a.num_pool_pages = num_pool_pages;
+  a.d_c = d_c;
+  a.d_R = d_R;
+  a.page_size = page_size;
+  return launch_status(mla::launch_append_kv(a, dtype == MLA_DTYPE_BF16,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 int mla_combine(const void* o_part, const float* lse_part, void* o_latent, float* lse_out,
                 int total_q, int heads, int groups, int d_c, int num_splits, int dtype,
                 void* stream) {

@@ -26,6 +26,22 @@ struct DecodeArgs {
   int head_split;    // MFMA decode, one latent group: 0 = chosen from the grid size, 1 or 2
 };
 
+// Latent-cache append of the new tokens' rows (c_KV | RoPE(k_R, pos)).
+struct AppendArgs {
+  const void* c_new;   // [T, d_c] storage type
+  const void* k_new;   // [T, d_R] storage type, before rotation
+  void* kv;            // [num_pool_pages, page_size, d_c + d_R] storage type
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  const int32_t* cu_q;
+  const float* rope_cos;  // [rope_max_pos, d_R / 2] or NULL
+  const float* rope_sin;
+  int rope_max_pos;
+  int batch, total_q, max_pages, num_pool_pages;
+  int d_c, d_R, page_size;
+};
+hipError_t launch_append_kv(const AppendArgs& a, bool bf16, hipStream_t s);
+
 // Generic kernels: any (d_cg <= 1024, d_R <= 256), bf16 or fp32 storage.
 hipError_t launch_absorb_generic(const void* q_c, const void* w_uk, void* q_abs, int T, int H,
                                  int d_hc, int d_cg, bool bf16, hipStream_t s);

@@ -13,7 +13,7 @@ import numpy as np
 import torch
 
 from . import mla
-from .workloads import Workload
+from .workloads import NewTokens, Workload
 
 
 @dataclass
@@ -65,3 +65,9 @@ def make_step(w: Workload, d: DeviceWorkload, num_splits: Optional[int] = None,
                           groups=w.cfg.groups, num_splits=num_splits, rope=d.rope,
                           causal=w.cfg.causal, seq_lens_host=w.seq_lens.tolist(),
                           pages_per_split=pages_per_split)
+
+
+def new_tokens_to_device(w: Workload, new: NewTokens, device="cuda"):
+    """(c_kv_new, k_r_new) device tensors of the storage dtype for ``mla.append_kv``."""
+    dev = torch.device(device)
+    return _storage_tensor(w, new.c_kv, dev), _storage_tensor(w, new.k_r, dev)

@@ -24,7 +24,7 @@ DTYPE_FP32 = 1
 PAGE_SIZE = 64
 
 EXPORTED = ("mla_absorb_q", "mla_rope_table", "mla_decode_paged", "mla_combine", "mla_up_v",
-            "mla_decode_workspace_bytes", "mla_status_string")
+            "mla_append_kv", "mla_decode_workspace_bytes", "mla_status_string")
 
 _lib = None
 
@@ -51,11 +51,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_decode_paged.argtypes = ([P] * 8 + [I] + [P] * 2 + [I] * 12 + [F, I, I, P])
     lib.mla_combine.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
     lib.mla_up_v.argtypes = [P, P, P, I, I, I, I, I, I, P]
+    lib.mla_append_kv.argtypes = [P] * 8 + [I] * 9 + [P]
     lib.mla_decode_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.mla_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.mla_status_string.argtypes = [I]
     lib.mla_status_string.restype = ctypes.c_char_p
-    for name in ("mla_absorb_q", "mla_rope_table", "mla_decode_paged", "mla_combine", "mla_up_v"):
+    for name in ("mla_absorb_q", "mla_rope_table", "mla_decode_paged", "mla_combine", "mla_up_v",
+                 "mla_append_kv"):
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -161,6 +163,32 @@ def decode_paged(q_abs, q_r, kv_cache, page_table, seq_lens, cu_q, o_part, lse_p
         B, T, max_pages, P, H, groups, d_hc, d_cg * groups, d_R, ps, S, int(pages_per_split),
         float(softmax_scale),
         int(bool(causal)), _dtype_code(q_abs), _stream(stream)))
+
+
+def append_kv(c_kv_new, k_r_new, kv_cache, page_table, seq_lens, cu_q, *,
+              rope: Optional[tuple] = None, stream=None) -> None:
+    """Write the new tokens' rows [c_KV | RoPE(k_R, pos)] into their pages of kv_cache
+    (in place); c_kv_new [T, d_c], k_r_new [T, d_R], kv_cache [P, 64, d_c + d_R]."""
+    T, d_c = c_kv_new.shape
+    d_R = k_r_new.shape[1]
+    P, ps, width = kv_cache.shape
+    B, max_pages = page_table.shape
+    if k_r_new.shape[0] != T or width != d_c + d_R:
+        raise ValueError("inconsistent c_kv_new / k_r_new / kv_cache shapes")
+    if c_kv_new.dtype != kv_cache.dtype or k_r_new.dtype != kv_cache.dtype:
+        raise TypeError("c_kv_new, k_r_new and kv_cache must share the storage dtype")
+    for t in (page_table, seq_lens, cu_q):
+        if t.dtype != torch.int32:
+            raise TypeError(f"expected int32, got {t.dtype}")
+    if seq_lens.shape != (B,) or cu_q.shape != (B + 1,):
+        raise ValueError("seq_lens must be [B] and cu_q [B+1]")
+    cos, sin = rope if rope is not None else (None, None)
+    rope_max_pos = 0 if cos is None else cos.shape[0]
+    _dev(c_kv_new, k_r_new, kv_cache, page_table, seq_lens, cu_q, cos, sin)
+    _check("mla_append_kv", load().mla_append_kv(
+        _ptr(c_kv_new), _ptr(k_r_new), _ptr(kv_cache), _ptr(page_table), _ptr(seq_lens),
+        _ptr(cu_q), _ptr(cos), _ptr(sin), rope_max_pos, B, T, max_pages, P, d_c, d_R, ps,
+        _dtype_code(kv_cache), _stream(stream)))
 
 
 def combine(o_part, lse_part, o_latent=None, lse_out=None, *, dtype=torch.bfloat16, stream=None):

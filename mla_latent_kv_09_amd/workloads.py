@@ -24,6 +24,9 @@ Input recipe (the same for every consumer):
   page-table entries are -1.
 * Ragged batches draw L_b uniformly from an inclusive integer range and give
   query length 1 to a random half of the sequences and 2 to the rest.
+* Cache append inputs (``make_new_tokens``): one latent c_KV [d_c] and one unrotated
+  RoPE key k_R [d_R] per new token (T of them, one per query row), standard normal,
+  rounded like the rest.
 """
 from __future__ import annotations
 
@@ -41,7 +44,7 @@ BF16_NAN_BITS = 0x7FC0
 
 _STREAMS = {
     "q_c": 1, "q_r": 2, "latent": 3, "w_uk": 4, "w_uv": 5,
-    "pages": 6, "lengths": 7, "q_lens": 8,
+    "pages": 6, "lengths": 7, "q_lens": 8, "c_kv_new": 9, "k_r_new": 10,
 }
 
 
@@ -255,6 +258,26 @@ def make_workload(cfg: MLAConfig, *, seed: Optional[int] = None, nan_fill: bool 
                  latents=[], w_uk=w_uk, w_uv=w_uv, page_table=page_table, pool=pool)
     w.latents = PagedRows(w)
     return w
+
+@dataclass
+class NewTokens:
+    """The latent rows a decode step appends: one per new token (packed query row)."""
+
+    c_kv: np.ndarray            # float32 [T, d_c]   (values exact in the storage dtype)
+    k_r: np.ndarray             # float32 [T, d_R]   before rotation
+
+
+def make_new_tokens(w: Workload, *, seed: Optional[int] = None,
+                    rows: Optional[int] = None) -> NewTokens:
+    """Draw the new tokens' c_KV and (unrotated) k_R for workload ``w``: one per query
+    row, or ``rows`` of them."""
+    cfg = w.cfg
+    seed = cfg.seed if seed is None else seed
+    rnd = round_bf16 if cfg.dtype == "bf16" else (lambda a: a.astype(np.float32))
+    T = w.total_q if rows is None else int(rows)
+    return NewTokens(c_kv=rnd(_normal(_rng(seed, "c_kv_new"), (T, cfg.d_c))),
+                     k_r=rnd(_normal(_rng(seed, "k_r_new"), (T, cfg.d_R))))
+
 
 def gather_sequence(w: Workload, b: int) -> np.ndarray:
     """Read sequence b's rows back out of the paged pool (float32), for layout checks."""

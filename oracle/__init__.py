@@ -6,6 +6,8 @@ product library never does.
 from .mla_oracle import (  # noqa: F401
     absorb_reference,
     absorbed_scores,
+    append_rows,
+    append_to_pool,
     default_scale,
     latent_row_bytes,
     latent_row_elements,
@@ -13,6 +15,7 @@ from .mla_oracle import (  # noqa: F401
     mla_decode,
     mqa_row_elements,
     naive_scores,
+    new_token_positions,
     page_bytes,
     rope_angles,
     rope_rotate,

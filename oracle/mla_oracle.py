@@ -277,3 +277,56 @@ def softmax_rows(q_c, q_r, latent, w_uk_h, pos, *, rope_base=None, scale=None, c
     s = naive_scores(q_c, qr, rows[:n_vis, cols], rows[:n_vis, d_c:], w_uk_h, scale)
     e = np.exp(s - s.max())
     return e / e.sum()
+
+
+# --------------------------------------------------------------------------
+# Latent-cache append (P3 §1: what one token stores per layer is its latent c_KV and
+# its decoupled RoPE key, the key being the part that carries the token's position;
+# P3 §3: 64-token pages; P3 §3/§4: RoPE computed in fp32 -- here in float64)
+# --------------------------------------------------------------------------
+
+
+def new_token_positions(seq_lens, cu_q):
+    """Absolute position of every new token, int64 [T].
+
+    Sequence b owns packed rows cu_q[b] .. cu_q[b+1]-1; its length seq_lens[b] already
+    counts its q_len new tokens, so new token i sits at seq_lens[b] - q_len + i (the same
+    position its query is rotated at)."""
+    cu_q = np.asarray(cu_q, np.int64)
+    seq_lens = np.asarray(seq_lens, np.int64)
+    pos = np.empty(int(cu_q[-1]), np.int64)
+    for b in range(len(seq_lens)):
+        q0, q1 = int(cu_q[b]), int(cu_q[b + 1])
+        for i in range(q1 - q0):
+            pos[q0 + i] = seq_lens[b] - (q1 - q0) + i
+    return pos
+
+
+def append_rows(c_kv_new, k_r_new, seq_lens, cu_q, rope_base):
+    """Cache rows of the new tokens, float64 [T, d_c + d_R]: the latent unchanged, then
+    the RoPE key rotated at the token's own position (``rope_base=None``: unrotated)."""
+    c = np.asarray(c_kv_new, np.float64)
+    k = np.asarray(k_r_new, np.float64)
+    pos = new_token_positions(seq_lens, cu_q)
+    rows = np.empty((c.shape[0], c.shape[1] + k.shape[1]), np.float64)
+    for t in range(c.shape[0]):
+        rows[t, :c.shape[1]] = c[t]
+        rows[t, c.shape[1]:] = rope_rotate(k[t], int(pos[t]), rope_base)
+    return rows
+
+
+def append_to_pool(pool, page_table, seq_lens, cu_q, c_kv_new, k_r_new, rope_base,
+                   page_size=64):
+    """The paged pool after the append, float64 [P, page_size, d_c + d_R] (a copy).
+
+    Logical row ``pos`` of sequence b lives in physical page page_table[b][pos // page_size],
+    slot pos % page_size; every other slot keeps its content."""
+    out = np.array(pool, dtype=np.float64, copy=True)
+    rows = append_rows(c_kv_new, k_r_new, seq_lens, cu_q, rope_base)
+    pos = new_token_positions(seq_lens, cu_q)
+    cu_q = np.asarray(cu_q, np.int64)
+    for b in range(len(seq_lens)):
+        for t in range(int(cu_q[b]), int(cu_q[b + 1])):
+            page = int(page_table[b][int(pos[t]) // page_size])
+            out[page, int(pos[t]) % page_size] = rows[t]
+    return out

@@ -144,3 +144,30 @@ def test_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(mla, "_lib", None)
     with pytest.raises(RuntimeError, match="no CPU fallback"):
         mla.load(str(tmp_path / "missing.so"))
+
+
+# -------------------------------------------------------------- append
+
+def _append(lib, **kw):
+    a = dict(c=A, k=A, kv=A, pt=A, sl=A, cu=A, cos=None, sin=None, rmp=0, B=16, T=16, maxp=64,
+             pool=1024, d_c=512, d_R=64, ps=64, dt=0)
+    a.update(kw)
+    return lib.mla_append_kv(a["c"], a["k"], a["kv"], a["pt"], a["sl"], a["cu"], a["cos"], a["sin"],
+                             a["rmp"], a["B"], a["T"], a["maxp"], a["pool"], a["d_c"], a["d_R"],
+                             a["ps"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(c=None), NULL), (dict(k=None), NULL), (dict(kv=None), NULL), (dict(pt=None), NULL),
+    (dict(sl=None), NULL), (dict(cu=None), NULL), (dict(sin=A), NULL),
+    (dict(kv=MIS), ALIGN), (dict(k=MIS), ALIGN), (dict(cos=A, sin=MIS, rmp=10), ALIGN),
+    (dict(d_R=63, kv=None), DIM), (dict(d_c=0, kv=None), DIM), (dict(B=0, kv=None), DIM),
+    (dict(T=-1, kv=None), DIM), (dict(maxp=0, kv=None), DIM), (dict(pool=0, kv=None), DIM),
+    (dict(cos=A, sin=A, rmp=0, kv=None), DIM),
+    (dict(ps=16, kv=None), UNSUP), (dict(d_c=500, kv=None), UNSUP), (dict(d_R=6, kv=None), UNSUP),
+    (dict(d_R=6, dt=1, kv=None), UNSUP),
+    (dict(dt=5), DTYPE),
+    (dict(T=0, kv=None), OK),
+])
+def test_append_validation(lib, kw, code):
+    assert _append(lib, **kw) == code
