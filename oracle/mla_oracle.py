@@ -43,8 +43,9 @@ design notes):
 * W_UK and W_UV are both laid out [H, d_hc, d_c'] ("hdc" in P3 §4's einsum);
   the value head dimension equals d_hc (P3 §1: K/V are 128 heads x 128 dims).
   There is no output projection.
-* RoPE: k_R is stored already rotated (it "carries position", P3 §1; writing
-  the cache is outside the decode step).  The query's q_R is rotated at its
+* RoPE: k_R is stored already rotated (it "carries position", P3 §1); the
+  cache append (``append_rows`` / ``append_to_pool`` below) rotates a new
+  token's key at its own position, the position its query sits at.  The query's q_R is rotated at its
   absolute position with interleaved pairs (2k, 2k+1) and angle pos * theta_k,
   theta_k = base^(-2k/d_R).  ``rope_base=None`` means no rotation, which is the
   P3 §4 check script's setting.
