@@ -53,7 +53,7 @@ BF16_PEAK_TFLOPS = 2500.0
 FP32_PEAK_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode.json")
 CSRC = os.path.join(ROOT, "mla_latent_kv_09_amd", "csrc")
-KERNEL_SRC = {"decode_mfma_kernel": "decode_mfma.hip",
+KERNEL_SRC = {"decode_mfma_kernel": "decode_mfma.hip", "decode_m32_kernel": "decode_m32.hip",
               "decode_generic_kernel": "kernels_generic.hip"}
 
 
@@ -356,7 +356,7 @@ def main():
     peak_f = BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else FP32_PEAK_TFLOPS
     t_hbm = kv_bytes / (HBM_PEAK_GBPS * 1e9)
     t_mfma = att / (peak_f * 1e12)
-    kernel = decode_kernel_name(cfg)
+    kernel = decode_kernel_name(cfg, int(w.total_q), S, mla)
     traffic = measured_traffic(kernel, cfg.name, S)
     if t_hbm >= t_mfma:
         achieved = kv_bytes / (dec * 1e-3) / 1e9
@@ -437,14 +437,20 @@ def measure_append(args, w, torch, harness, mla, wl, steps, runner, timed, reps,
     return res
 
 
-def decode_kernel_name(cfg):
+def decode_kernel_name(cfg, total_q, num_splits, mla):
     """The decode kernel the library dispatches for this shape (same rule as the library:
-    MLA_KV_DECODE_KERNEL = generic / mfma, default the mfma kernel where it applies)."""
+    MLA_KV_DECODE_KERNEL = generic / mfma / mfma128 / mfma64 / mfma32; by default, for one
+    latent group, the 32x32x16 kernel when one workgroup per (token, split) fills the
+    device and the 16x16x32 kernel's 64-head split otherwise)."""
     mfma_shape = (cfg.dtype == "bf16" and cfg.heads == 128 and cfg.groups in (1, 2)
                   and cfg.d_c == 512 and cfg.d_R == 64 and cfg.page_size == 64)
     choice = os.environ.get("MLA_KV_DECODE_KERNEL", "")
     if choice == "generic" or not mfma_shape:
         return "decode_generic_kernel"
+    if cfg.groups != 1 or choice in ("mfma128", "mfma64"):
+        return "decode_mfma_kernel"
+    if choice == "mfma32" or mla.head_split(total_q, num_splits, cfg.groups) == 1:
+        return "decode_m32_kernel"
     return "decode_mfma_kernel"
 
 

@@ -1,0 +1,433 @@
+// Split-KV absorbed-MLA decode on the 32x32x16 bf16 MFMA (gfx950), one latent group:
+// one workgroup of four waves per (token, split), wave w owning heads 32w .. 32w+31
+// over all 64 tokens of every page.
+//
+// Computes, for one query token and one split of its sequence's pages, the
+// softmax-normalised latent output and log-sum-exp of
+//     s_j = scale * (q_abs . c_KV[j] + RoPE(q_R) . k_R[j])          (nxmr.cn/news/151634 §4)
+// over the split's keys, for all 128 heads at once, so every streamed latent page is
+// read from HBM once per (token, split) and shared by all heads (nxmr.cn/news/151634
+// §1: the 512-d latent plus the 64-d shared RoPE key is all a token stores).
+//
+// Why 32x32x16 with one wave per SIMD: one wave issuing v_mfma_f32_32x32x16_bf16
+// keeps the matrix pipe of its SIMD busy on its own (about 95 % of the bf16 peak with
+// two independent accumulators, measured), where the 16x16x32 form needs two waves in
+// the same phase to get there (one wave alone reaches 38-59 %).  Each 16-byte LDS
+// fragment also feeds twice the flops of a 16x16x32 step, halving LDS reads.  The
+// price is registers: the query (576 dims of 32 heads, 128 VGPRs plus the RoPE part
+// from LDS) stays in VGPRs and the output O^T[512 x 32 heads] (256 fp32 per lane)
+// needs the accumulator half of the 512-register file.
+//
+// Per page and wave:
+//   scores  S^T[64 tok x 32 heads] = C[64 x 576] . Q^T as two 32-token blocks of 36
+//           K-steps (4 RoPE + 32 latent); A = C from LDS (ds_read_b128), B = Q.
+//           Lane l then holds head l % 32 and 16 tokens per block:
+//           token 8 (r / 4) + 4 (l / 32) + r % 4 of accumulator element r.
+//   softmax fp32, per head, the two lane halves combined with v_permlane32_swap.
+//   output  O^T[cols x heads] += C^T . P^T over four 16-token K-steps.  The K order of a
+//           step is the order the score accumulators hold the tokens in (elements
+//           8q .. 8q+7 of block mb), so P^T is the score registers converted in place
+//           and the matching C^T fragment is two transposing reads of 4 tokens each.
+// Pages: one 64-token page (72 KB) per stage, two stages (144 KB) plus the rotated q_R
+// of all heads (16 KB) fill the 160 KB LDS.  Copies (global_load_lds, 16 B per lane)
+// of the next page are spread through the score loop.
+//
+// LDS layout of a stage: latent row t (1 KB) holds chunk c (8 dims) at 16-byte position
+// c ^ f(t), f(t) = (t[1:0] << 2) | t[3:2] | (t[4] << 4) (a bit permutation of t mod 32).
+// A score read (32 consecutive tokens, one chunk) then hits 32 distinct 16-byte slots of
+// a 512-byte bank row, and so does a transposing read (4 tokens x 4 chunks x 2 halves).
+// RoPE row t (128 B) holds chunk c at c ^ ((t >> 2) & 7); q_R of head n the same with n.
+#include <math.h>
+
+#include "mla_device.h"
+#include "mla_internal.h"
+
+namespace mla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8_t;
+
+constexpr int kWaves = 4;
+constexpr int kThreads = kWaves * 64;
+constexpr int kHeads = 128;
+constexpr int kTok = 64;
+constexpr int kDc = 512;
+constexpr int kDr = 64;
+constexpr int kRowBytes = (kDc + kDr) * 2;
+constexpr int kCBytes = kTok * kDc * 2;  // 64 KB latent part of a stage
+constexpr int kRBytes = kTok * kDr * 2;  // 8 KB RoPE part
+constexpr int kStageBytes = kCBytes + kRBytes;
+constexpr int kQrOff = 2 * kStageBytes;
+constexpr int kLdsBytes = kQrOff + kHeads * kDr * 2;
+constexpr int kQSteps = kDc / 16;        // 32 latent K-steps
+constexpr int kRSteps = kDr / 16;        // 4 RoPE K-steps
+constexpr int kColBlocks = kDc / 32;     // 16 output blocks of 32 columns
+constexpr float kJump = 64.f;            // reference restart threshold, log2 units
+static_assert(kLdsBytes <= 160 * 1024, "stages + q_R must fit the 160 KB LDS of a gfx950 CU");
+
+__device__ __forceinline__ uint32_t swz_f(int t) {
+  return static_cast<uint32_t>(((t & 3) << 2) | ((t >> 2) & 3) | (t & 16));
+}
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
+}
+__device__ __forceinline__ uint32_t opaque(uint32_t v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+__device__ __forceinline__ bf16x8 lds_read8(uint32_t a) { return *(const lds_bf16x8_t*)(uintptr_t)a; }
+__device__ __forceinline__ float halves_max(float x) {  // lanes l and l ^ 32
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+__device__ __forceinline__ bf16x8 to_bf16x8(float x0, float x1, float x2, float x3, float x4,
+                                            float x5, float x6, float x7) {
+  return bf16x8{static_cast<__bf16>(x0), static_cast<__bf16>(x1), static_cast<__bf16>(x2),
+                static_cast<__bf16>(x3), static_cast<__bf16>(x4), static_cast<__bf16>(x5),
+                static_cast<__bf16>(x6), static_cast<__bf16>(x7)};
+}
+
+// Score MFMAs in inline asm so that their accumulators stay in VGPRs (the compiler
+// puts the result of every MFMA builtin of this kernel in the accumulator registers,
+// which the 256 output values already fill).  Chained steps accumulate in place
+// (srcC = vdst, which the hardware forwards without wait states); the first step of a
+// chain takes srcC = 0, so no vector-ALU write precedes an MFMA read of the
+// accumulator.  Vector-ALU reads of the result wait behind mfma_results_ready().
+__device__ __forceinline__ void mfma32_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma32_acc(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+// Wait states between the last asm MFMA writing s0 / s1 and the first vector-ALU read
+// of them (the compiler inserts none for asm): 3 x s_nop 7 = 24, more than the
+// 32x32 MFMA's result latency requires.  The operands tie the pad after those MFMAs.
+__device__ __forceinline__ void mfma_results_ready(f32x16& s0, f32x16& s1) {
+  asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s0), "+v"(s1));
+}
+
+// One 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4), wave-uniform base
+// plus per-lane offset; active lane i's 16 bytes land at LDS byte lds + 16 i.  Inline
+// asm so that the compiler does not make later LDS reads of the current stage wait for
+// it; completion is awaited with s_waitcnt vmcnt(0) + a barrier before a stage is read.
+__device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(sbase)
+               : "memory");
+}
+
+// Copy `row` (0..17) of this wave's share of a page into stage `c_base`: rows 0..15 are
+// the latent rows of tokens 16w + row (1 KB each), rows 16, 17 the RoPE rows of tokens
+// 16w + 8 (row - 16) .. +7.  Rows at or past n_valid fetch token 0 (always valid).
+__device__ __forceinline__ void load_row(uint32_t c_base, const char* page, int n_valid,
+                                         int wave, int lane, int row) {
+  if (row < 16) {
+    const int t = wave * 16 + row;
+    const int src_t = t < n_valid ? t : 0;
+    dma16(page + src_t * kRowBytes, static_cast<uint32_t>((lane ^ static_cast<int>(swz_f(t))) << 4),
+          c_base + t * 1024);
+  } else {
+    const int t0 = wave * 16 + 8 * (row - 16);
+    const int t = t0 + (lane >> 3);
+    const int src_t = t < n_valid ? t : 0;
+    dma16(page, static_cast<uint32_t>(src_t * kRowBytes + kDc * 2 + (((lane & 7) ^ ((t >> 2) & 7)) << 4)),
+          c_base + kCBytes + t0 * 128);
+  }
+}
+
+__global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+decode_m32_kernel(DecodeArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int S = a.num_splits;
+  const int t = static_cast<int>(blockIdx.x) / S;
+  const int split = static_cast<int>(blockIdx.x) - t * S;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int n = lane & 31, h = lane >> 5;  // head within the wave, lane half
+  const int head = wave * 32 + n;
+  const QueryWork w = query_work(a.cu_q, a.seq_lens, a.batch, t, split, S, a.pages_per_split, kTok,
+                                 a.max_pages, a.causal);
+  const size_t row = (static_cast<size_t>(t) * kHeads + head) * S + split;
+  __bf16* o_out = static_cast<__bf16*>(a.o_part) + row * kDc;
+  if (w.k0 >= w.k1) {  // empty split: only the LSE is written
+    if (h == 0) a.lse_part[row] = -INFINITY;
+    return;
+  }
+  const char* kv = static_cast<const char*>(a.kv);
+  const int32_t* ptab = a.page_table + static_cast<size_t>(w.b) * a.max_pages;
+  const int page0 = w.k0 / kTok;
+  const int n_split_pages = (w.k1 - w.k0 + kTok - 1) / kTok;
+  int pid_v = 0;
+  auto fetch_ids = [&](int chunk) {
+    const int idx = chunk * 64 + lane;
+    pid_v = idx < n_split_pages ? ptab[page0 + idx] : 0;
+    asm volatile("" : "+v"(pid_v));
+  };
+  auto page_ptr = [&](int i) {
+    const int id = clamp_page(__builtin_amdgcn_readlane(pid_v, i & 63), a.num_pool_pages);
+    return kv + static_cast<size_t>(id) * kTok * kRowBytes;
+  };
+  fetch_ids(0);
+  const uint32_t smem_base = lds_addr(smem);
+  int j0 = w.k0;
+  {
+    const char* p0 = page_ptr(0);
+    const int nv = min(kTok, w.k1 - j0);
+#pragma unroll
+    for (int r = 0; r < 18; ++r) load_row(smem_base, p0, nv, wave, lane, r);
+  }
+
+  // Query: latent part in registers (B operand of the scores: head n, dims 16 ks + 8 h ..),
+  // RoPE part rotated in fp32 and parked in LDS as bf16.
+  bf16x8 q[kQSteps];
+  {
+    const uint16_t* qa = static_cast<const uint16_t*>(a.q_abs) +
+                         (static_cast<size_t>(t) * kHeads + head) * kDc + 8 * h;
+#pragma unroll
+    for (int k = 0; k < kQSteps; ++k) q[k] = *reinterpret_cast<const bf16x8*>(qa + 16 * k);
+  }
+  {
+    const uint16_t* qr = static_cast<const uint16_t*>(a.q_r) +
+                         (static_cast<size_t>(t) * kHeads + head) * kDr;
+    const int p = min(max(w.pos, 0), max(a.rope_max_pos - 1, 0));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {  // chunks h, h + 2, h + 4, h + 6 of this head
+      const int c = 2 * k + h;
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = bf16_to_f32(qr[8 * c + e]);
+      if (a.rope_cos != nullptr) {
+        const float* cs = a.rope_cos + static_cast<size_t>(p) * (kDr / 2) + 4 * c;
+        const float* sn = a.rope_sin + static_cast<size_t>(p) * (kDr / 2) + 4 * c;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x0 = x[2 * i], x1 = x[2 * i + 1];
+          x[2 * i] = fmaf(x0, cs[i], -x1 * sn[i]);
+          x[2 * i + 1] = fmaf(x0, sn[i], x1 * cs[i]);
+        }
+      }
+      *(lds_bf16x8_t*)(uintptr_t)(smem_base + kQrOff + head * 128 + ((c ^ ((head >> 2) & 7)) << 4)) =
+          to_bf16x8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+    }
+  }
+
+  const float scale_log2 = a.scale * kLog2e;
+  float m_ref = -INFINITY;  // softmax reference of this lane's head (log2 units)
+  float l_run = 0.f;        // this lane's share of the running sum against m_ref
+  f32x16 o[kColBlocks];     // O^T block nb: columns 32 nb + 8 (r/4) + 4 h + r%4, head n
+#pragma unroll
+  for (int nb = 0; nb < kColBlocks; ++nb) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[nb][r] = 0.f;
+    asm volatile("" : "+a"(o[nb]));  // accumulator registers from the start
+  }
+
+  // Per-lane parts of the LDS addresses (stage base added per page).
+  //   score read, block mb, latent step ks: st + (n * 1024 | ((f(n) ^ h) << 4)) ^ ((2 ks & 31) << 4)
+  //                                          + 512 (ks >= 16) + 32768 mb
+  //   RoPE read, step rs:  st + kCBytes + n * 128 + (((2 rs + h) ^ ((n >> 2) & 7)) << 4) + 4096 mb
+  //   output read (nb, mb, q, part p): lane i = lane % 16 of 16-lane group g = lane / 16 reads
+  //     token 32 mb + 16 q + 8 p + 4 (g >> 1) + i / 4, column 32 nb + 16 (g & 1) + 4 (i % 4):
+  //     st + (tok_l * 1024 + 8 (i & 1) | (key_l << 4)) ^ (K(nb, p, q) << 4) + 32768 mb + 16384 q + 8192 p
+  //     with tok_l = 4 (g >> 1) + i / 4, key_l = (2 (g & 1) + ((i & 3) >> 1)) ^ ((i >> 2) << 2 | (g >> 1)),
+  //     K = 4 nb ^ 2 p ^ 16 q.
+  const int li = lane & 15, lg = lane >> 4;
+  const uint32_t s_lane = static_cast<uint32_t>(n * 1024) | ((swz_f(n) ^ static_cast<uint32_t>(h)) << 4);
+  const int tok_l = 4 * (lg >> 1) + (li >> 2);
+  const uint32_t key_l = static_cast<uint32_t>((2 * (lg & 1) + ((li & 3) >> 1)) ^ (((li >> 2) << 2) | (lg >> 1)));
+  const uint32_t o_lane = static_cast<uint32_t>(tok_l * 1024 + 8 * (li & 1)) | (key_l << 4);
+
+  int stage = 0;
+  for (; j0 < w.k1; j0 += kTok) {
+    const int n_valid = min(kTok, w.k1 - j0);
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's page copies have landed
+    __syncthreads();                     // ... and every wave's; the other stage is free again
+    const int j_next = j0 + kTok;
+    const bool has_next = j_next < w.k1;
+    const char* next_page = kv;
+    const int next_valid = min(kTok, w.k1 - j_next);
+    if (has_next) {
+      const int i_next = (j_next - w.k0) / kTok;
+      if ((i_next & 63) == 0) fetch_ids(i_next >> 6);
+      next_page = page_ptr(i_next);
+    }
+    const uint32_t next_base = smem_base + (stage ^ 1) * kStageBytes;
+    const uint32_t st_base = smem_base + stage * kStageBytes;
+    const uint32_t sb = opaque(st_base + s_lane);
+
+    // ---- scores: RoPE steps, then the latent steps, the two token blocks alternating.
+    f32x16 s[2];
+    {
+      const uint32_t rb = opaque(st_base + kCBytes + n * 128);
+      const uint32_t qb = smem_base + kQrOff + head * 128;
+      const int swr = (n >> 2) & 7, swq = (head >> 2) & 7;
+#pragma unroll
+      for (int rs = 0; rs < kRSteps; ++rs) {
+        const int c = 2 * rs + h;
+        const bf16x8 qrf = lds_read8(qb + ((c ^ swq) << 4));
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          const bf16x8 cf = lds_read8(rb + ((c ^ swr) << 4) + 4096 * mb);
+          if (rs == 0)
+            mfma32_first(s[mb], cf, qrf);
+          else
+            mfma32_acc(s[mb], cf, qrf);
+        }
+      }
+    }
+    {
+      constexpr int kSteps = 2 * kQSteps;  // (ks, mb) steps
+      constexpr int kRing = 4;
+      auto frag = [&](int st) {
+        const int ks = st >> 1, mb = st & 1;
+        const uint32_t addr = (sb ^ static_cast<uint32_t>((2 * ks & 31) << 4)) +
+                              512 * (ks >> 4) + 32768 * mb;
+        return lds_read8(addr);
+      };
+      bf16x8 ring[kRing];
+#pragma unroll
+      for (int st = 0; st < kRing; ++st) ring[st] = frag(st);
+#pragma unroll
+      for (int st = 0; st < kSteps; ++st) {
+        const bf16x8 cf = ring[st % kRing];
+        if (st + kRing < kSteps) ring[st % kRing] = frag(st + kRing);
+        mfma32_acc(s[st & 1], cf, q[st >> 1]);
+        if ((st & 3) == 1 && has_next)  // 18 copies over the 64 steps
+          load_row(next_base, next_page, next_valid, wave, static_cast<int>(opaque(lane)), st >> 2);
+        if ((st == 34 || st == 50) && has_next)
+          load_row(next_base, next_page, next_valid, wave, static_cast<int>(opaque(lane)),
+                   st == 34 ? 16 : 17);
+      }
+    }
+
+    // ---- online softmax.  s[mb][r] is the raw score of token 32 mb + 8 (r/4) + 4 h + r%4.
+    mfma_results_ready(s[0], s[1]);
+    if (n_valid < kTok) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (32 * mb + 8 * (r >> 2) + 4 * h + (r & 3) >= n_valid) s[mb][r] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
+    mx = halves_max(mx) * scale_log2;
+    // Reference: a head's first page maximum.  Later terms are taken against it (up to
+    // 2^kJump: no overflow in fp32 or bf16, whose range is 2^127), so the output is never
+    // rescaled.  A page whose maximum exceeds the reference by more than kJump restarts
+    // the head at that maximum: everything accumulated before weighs at most
+    // 2^-kJump * (keys so far) < 2^-40 of the new maximum's term, below fp32 resolution,
+    // and is cleared instead of rescaled.
+    const bool restart = mx > m_ref + kJump;  // always true on a head's first page
+    if (restart) {
+      m_ref = mx;
+      l_run = 0.f;
+#pragma unroll
+      for (int nb = 0; nb < kColBlocks; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[nb][r] = 0.f;
+    }
+    float psum = 0.f;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[mb][r], scale_log2, -m_ref));
+        s[mb][r] = p;
+        psum += p;
+      }
+    l_run += psum;
+
+    // ---- P^T operands: K-step kq = 2 mb + q holds elements 8q .. 8q+7 of block mb
+    bf16x8 pb[4];
+#pragma unroll
+    for (int kq = 0; kq < 4; ++kq) {
+      const f32x16& v = s[kq >> 1];
+      const int b8 = 8 * (kq & 1);
+      pb[kq] = to_bf16x8(v[b8], v[b8 + 1], v[b8 + 2], v[b8 + 3], v[b8 + 4], v[b8 + 5], v[b8 + 6], v[b8 + 7]);
+    }
+
+    // ---- O^T[cols 32 nb .. +31] += C^T . P^T, (kq, nb) steps through a ring
+    const uint32_t ob = opaque(st_base + o_lane);
+    {
+      constexpr int kSteps = 4 * kColBlocks;
+      constexpr int kRing = 4;
+      auto frag = [&](int st) {
+        const int kq = st / kColBlocks, nb = st % kColBlocks;
+        const int mb = kq >> 1, qq = kq & 1;
+        const uint32_t k0 = static_cast<uint32_t>((4 * nb) ^ (16 * qq)) << 4;
+        const uint32_t k1 = static_cast<uint32_t>((4 * nb) ^ 2 ^ (16 * qq)) << 4;
+        const uint32_t a0 = (ob ^ k0) + 32768 * mb + 16384 * qq;
+        const uint32_t a1 = (ob ^ k1) + 32768 * mb + 16384 * qq + 8192;
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(uintptr_t)a0);
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(uintptr_t)a1);
+        return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+      };
+      bf16x8 ring[kRing];
+#pragma unroll
+      for (int st = 0; st < kRing; ++st) ring[st] = frag(st);
+#pragma unroll
+      for (int st = 0; st < kSteps; ++st) {
+        const bf16x8 cf = ring[st % kRing];
+        if (st + kRing < kSteps) ring[st % kRing] = frag(st + kRing);
+        const int kq = st / kColBlocks, nb = st % kColBlocks;
+        o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cf, pb[kq], o[nb], 0, 0, 0);
+      }
+    }
+    // Keep the output accumulators in the accumulator registers across the loop (the
+    // allocator otherwise moves some of them to VGPRs and spills).
+#pragma unroll
+    for (int nb = 0; nb < kColBlocks; ++nb) asm volatile("" : "+a"(o[nb]));
+    stage ^= 1;
+  }
+
+  // ---- finalize: normalise and write this split's partial output (bf16) and LSE
+  const float l_tot = halves_sum(l_run);
+  const float inv = 1.f / l_tot;
+#pragma unroll
+  for (int nb = 0; nb < kColBlocks; ++nb) {  // one 32-column block at a time
+    asm volatile("" : "+a"(o[nb]));
+    const f32x16 v = o[nb];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<bf16x4*>(o_out + 32 * nb + 8 * j + 4 * h) =
+          bf16x4{static_cast<__bf16>(v[4 * j] * inv), static_cast<__bf16>(v[4 * j + 1] * inv),
+                 static_cast<__bf16>(v[4 * j + 2] * inv), static_cast<__bf16>(v[4 * j + 3] * inv)};
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (h == 0) a.lse_part[row] = (m_ref + __log2f(l_tot)) * kLn2;
+}
+
+}  // namespace
+
+bool decode_m32_supported(const DecodeArgs& a, bool bf16) {
+  return bf16 && a.heads == kHeads && a.groups == 1 && a.d_c == kDc && a.d_R == kDr &&
+         a.page_size == kTok;
+}
+
+hipError_t launch_decode_m32(const DecodeArgs& a, hipStream_t s) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_m32_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const dim3 grid(a.total_q * a.num_splits);
+  decode_m32_kernel<<<grid, kThreads, kLdsBytes, s>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace mla

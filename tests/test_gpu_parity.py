@@ -84,6 +84,21 @@ def test_parity_small(case, rope):
     assert lse_err <= (1e-4 if fp32 else 2e-2)
 
 
+@pytest.mark.parametrize("case", ["dsv3_small", "long_small", "ragged_small"])
+@pytest.mark.parametrize("rope", [True, False])
+def test_parity_small_mfma32(case, rope, monkeypatch):
+    """The 32x32x16 kernel (four 32-head waves per (token, split)) on the one-group cases."""
+    monkeypatch.setenv("MLA_KV_DECODE_KERNEL", "mfma32")
+    cfg = SMALL_CASES[case]
+    print(f"case {case} rope={rope} kernel mfma32", flush=True)
+    w = wl.make_workload(cfg)
+    step = run_step(w, rope=rope)
+    ref = oracle_for(w, rope=rope)
+    assert_parity(_f64(step.out), ref["out"])
+    assert_parity(_f64(step.o_latent), ref["o_latent"], what="o_latent")
+    assert np.max(np.abs(_f64(step.lse) - ref["lse"])) <= 2e-2
+
+
 @pytest.mark.parametrize("splits", [1, 3, 8, 40])
 def test_split_count_invariance(splits):
     """Split count changes only rounding; empty splits (more splits than pages) are harmless."""
@@ -115,7 +130,8 @@ def test_bitwise_repeatable():
     ((1,), (1,)), ((64,), (1,)), ((65,), (1,)), ((2,), (2,)), ((128, 129, 63), (1, 2, 1)),
     ((31, 32, 33, 96, 97), (1, 1, 2, 1, 2)),
 ])
-@pytest.mark.parametrize("heads,kind", [(16, None), (128, "mfma128"), (128, "mfma64")])
+@pytest.mark.parametrize("heads,kind", [(16, None), (128, "mfma128"), (128, "mfma64"),
+                                        (128, "mfma32")])
 def test_edge_lengths(lens, q_lens, heads, kind, monkeypatch):
     """16 heads run the generic kernel; 128 heads the MFMA kernel with one workgroup of
     128 heads or two of 64 heads per (token, split).  Lengths of 1, 2, 31-33 and 65 keys
@@ -162,7 +178,8 @@ def _with_lengths(cfg, lens, q_lens):
                        latents=latents, w_uk=w.w_uk, w_uv=w.w_uv, page_table=pt, pool=pool)
 
 
-@pytest.mark.parametrize("heads,kind", [(16, None), (128, "mfma128"), (128, "mfma64")])
+@pytest.mark.parametrize("heads,kind", [(16, None), (128, "mfma128"), (128, "mfma64"),
+                                        (128, "mfma32")])
 def test_empty_sequence_gives_zero_and_minus_inf(heads, kind, monkeypatch):
     """A sequence with no keys: output 0 and LSE -inf on every head, from the generic
     kernel and from both head splits of the MFMA kernel (where both workgroups of an
@@ -232,7 +249,7 @@ def test_decode_kernels_agree(case, monkeypatch):
     cfg = SMALL_CASES[case]
     w = wl.make_workload(cfg)
     outs = {}
-    kinds = ("mfma128", "mfma64", "generic") if cfg.groups == 1 else ("mfma128", "generic")
+    kinds = ("mfma128", "mfma64", "mfma32", "generic") if cfg.groups == 1 else ("mfma128", "generic")
     for kind in kinds:
         monkeypatch.setenv("MLA_KV_DECODE_KERNEL", kind)
         print(f"  kernel {kind}", flush=True)
@@ -244,7 +261,7 @@ def test_decode_kernels_agree(case, monkeypatch):
         assert_parity(outs[kind], outs["generic"], what=f"{kind} vs generic")
 
 
-@pytest.mark.parametrize("kind", ["mfma128", "mfma64", "generic"])
+@pytest.mark.parametrize("kind", ["mfma128", "mfma64", "mfma32", "generic"])
 @pytest.mark.parametrize("case,mode", [("dsv3_small", "grow"), ("dsv3_small", "flood"),
                                        ("dsv3_small", "shrink"), ("gla2_small", "grow"),
                                        ("gla2_small", "flood")])
@@ -259,12 +276,14 @@ def test_softmax_reference_moves(kind, case, mode, monkeypatch):
             underflows to zero) and a softmax spread evenly over identical rows, so the
             output is that row exactly; the other heads keep the first pages.
     shrink: rows scaled by 1/64; the first pages keep the reference for the whole split.
+    The 32x32 kernel (mfma32) never rescales: grow takes later terms of up to about 2^17
+    against the first page's reference, and flood restarts the head at the new maximum.
     Scaled rows scale the rounding error of a score with them, so W_UK is a selection
     matrix (q_abs = q_c on the first d_hc latent columns, exact in bf16) and RoPE is
     off (a rotated q_R is rounded to bf16): the scores then differ from the oracle's
     by fp32 accumulation only, and the comparison tests the kernels' softmax."""
-    if kind == "mfma64" and SMALL_CASES[case].groups != 1:
-        pytest.skip("the 64-head split exists for one latent group only")
+    if kind in ("mfma64", "mfma32") and SMALL_CASES[case].groups != 1:
+        pytest.skip("the 64-head split and the 32x32 kernel exist for one latent group only")
     w = wl.make_workload(SMALL_CASES[case])
     H, d_hc, d_cg = w.w_uk.shape
     w.w_uk = np.zeros_like(w.w_uk)
