@@ -86,20 +86,23 @@ def source_hash(path):
 
 
 def measured_traffic(kernel, workload, splits):
-    """HBM bytes per decode launch from committed rocprofv3 counters, if they were taken
-    on this kernel, its current source, this workload and this split count."""
+    """HBM bytes per decode launch from committed rocprofv3 counters (one record per
+    kernel and workload), if they were taken on this kernel, its current source, this
+    workload and this split count."""
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)
-    except (OSError, ValueError):
+            recs = json.load(f).get("records", [])
+    except (OSError, ValueError, AttributeError):
         return None
-    if rec.get("kernel") != kernel:
-        return None
-    if rec.get("kernel_source_sha256_16") != source_hash(os.path.join(CSRC, KERNEL_SRC[kernel])):
-        return None
-    if rec.get("workload") != workload or rec.get("num_splits") != splits:
-        return None
-    return rec.get("bytes_per_launch")
+    for rec in recs:
+        if rec.get("kernel") != kernel or rec.get("workload") != workload:
+            continue
+        if rec.get("num_splits") != splits:
+            continue
+        if rec.get("kernel_source_sha256_16") != source_hash(os.path.join(CSRC, KERNEL_SRC[kernel])):
+            continue
+        return rec.get("bytes_per_launch")
+    return None
 
 
 def cpu_baseline(w, att_flops_full, min_s=10.0):

@@ -138,12 +138,14 @@ int mla_rope_table(float* cos_out, float* sin_out, int max_pos, int d_R, double 
  * j <= its position; otherwise all keys.  softmax_scale <= 0 selects
  * 1/sqrt(d_hc + d_R).  total_q * num_splits above 2^31 - 1 is MLA_ERR_UNSUPPORTED.
  * Work split (no effect on the results beyond rounding order): with bf16 storage, 128
- * heads, d_c 512 and d_R 64 the MFMA kernel runs one workgroup of 128 heads per
- * (token, split), or, with one latent group and 2 * total_q * num_splits at most the
- * device's compute-unit count, two workgroups of 64 heads each.  The environment
- * variable MLA_KV_DECODE_KERNEL overrides the choice: "generic" (the shape-generic
- * kernel), "mfma" (MFMA kernel, automatic head split), "mfma128" / "mfma64" (MFMA
- * kernel with the given heads per workgroup); an MFMA choice the shape does not
+ * heads, d_c 512 and d_R 64 an MFMA kernel runs one workgroup of 128 heads per
+ * (token, split) -- for one latent group the 32x32x16 kernel (four waves of 32 heads),
+ * for two groups the 16x16x32 kernel -- or, with one latent group and
+ * 2 * total_q * num_splits at most the device's compute-unit count, two 16x16x32
+ * workgroups of 64 heads each.  The environment variable MLA_KV_DECODE_KERNEL
+ * overrides the choice: "generic" (the shape-generic kernel), "mfma" (automatic MFMA
+ * choice), "mfma128" / "mfma64" (16x16x32 kernel with the given heads per workgroup),
+ * "mfma32" (32x32x16 kernel, one latent group); an MFMA choice the shape does not
  * support returns MLA_ERR_UNSUPPORTED.
  */
 int mla_decode_paged(const void* q_abs, const void* q_r, const void* kv_cache,
