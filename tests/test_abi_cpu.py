@@ -6,6 +6,7 @@ that validation rejects, so the fake (never dereferenced) device addresses are
 safe even on a machine with a GPU.
 """
 import ctypes
+import json
 import os
 import re
 
@@ -171,3 +172,35 @@ def _append(lib, **kw):
 ])
 def test_append_validation(lib, kw, code):
     assert _append(lib, **kw) == code
+
+
+# -------------------------------------------------------------- bench helpers (host only)
+
+def test_bench_traffic_records_match_kernel_workload_splits_and_source():
+    import bench
+    recs = json.load(open(bench.TRAFFIC_FILE))["records"]
+    assert recs, "the committed traffic file holds at least one record"
+    for rec in recs:
+        got = bench.measured_traffic(rec["kernel"], rec["workload"], rec["num_splits"])
+        # a record is reported only while its kernel source is unchanged
+        src = os.path.join(bench.CSRC, bench.KERNEL_SRC[rec["kernel"]])
+        if bench.source_hash(src) == rec["kernel_source_sha256_16"]:
+            assert got == rec["bytes_per_launch"]
+        assert bench.measured_traffic(rec["kernel"], rec["workload"], rec["num_splits"] + 1) is None
+        assert bench.measured_traffic(rec["kernel"], "no_such_workload", rec["num_splits"]) is None
+
+
+def test_bench_decode_kernel_name_follows_the_library_rule(monkeypatch):
+    import bench
+    from mla_latent_kv_09_amd import workloads as wl
+    monkeypatch.delenv("MLA_KV_DECODE_KERNEL", raising=False)
+    c = wl.CONFIGS
+    assert bench.decode_kernel_name(c["dsv3_b16_l4096"], 16, 8, mla) == "decode_mfma_kernel"
+    assert bench.decode_kernel_name(c["long_b16_l65536"], 16, 16, mla) == "decode_m32_kernel"
+    assert bench.decode_kernel_name(c["ragged_b64"], 96, 17, mla) == "decode_m32_kernel"
+    assert bench.decode_kernel_name(c["gla2_b32_l16384"], 32, 8, mla) == "decode_mfma_kernel"
+    assert bench.decode_kernel_name(c["tiny_fp32"], 1, 1, mla) == "decode_generic_kernel"
+    monkeypatch.setenv("MLA_KV_DECODE_KERNEL", "mfma128")
+    assert bench.decode_kernel_name(c["long_b16_l65536"], 16, 16, mla) == "decode_mfma_kernel"
+    monkeypatch.setenv("MLA_KV_DECODE_KERNEL", "mfma32")
+    assert bench.decode_kernel_name(c["dsv3_b16_l4096"], 16, 16, mla) == "decode_m32_kernel"
