@@ -27,10 +27,19 @@ def _f64(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("name", FULL)
-def test_fullsize_sampled_parity(name):
+# The default plan runs the 32x32x16 kernel on long and ragged and the 16x16x32 kernel
+# (64-head split, or two latent groups) on dsv3 and gla2; the extra cases run each
+# one-group kernel on the other's full-size shapes too.
+CASES = [(n, None) for n in FULL] + [("dsv3_b16_l4096", "mfma32"), ("long_b16_l65536", "mfma128"),
+                                     ("ragged_b64", "mfma128")]
+
+
+@pytest.mark.parametrize("name,kind", CASES)
+def test_fullsize_sampled_parity(name, kind, monkeypatch):
+    if kind is not None:
+        monkeypatch.setenv("MLA_KV_DECODE_KERNEL", kind)
     cfg = wl.CONFIGS[name]
-    print(f"full-size {name}: generating", flush=True)
+    print(f"full-size {name} kernel {kind or 'default'}: generating", flush=True)
     w = wl.make_workload(cfg)
     d = harness.to_device(w)
     step = harness.make_step(w, d)           # the bench's split plan
