@@ -148,8 +148,32 @@ __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1
 decode_m32_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int S = a.num_splits;
-  const int t = static_cast<int>(blockIdx.x) / S;
-  const int split = static_cast<int>(blockIdx.x) - t * S;
+  // Launch order.  The units of sequence b (its n query tokens x S splits) are the
+  // workgroups [cu_q[b] S, cu_q[b+1] S).  With one token they run in split order.  With
+  // n tokens, which read the same pages, each block of 8 splits takes 8 n consecutive
+  // workgroups, token-major: the n workgroups of one split are 8 apart, so the
+  // dispatcher (workgroup L to XCD L mod 8) places them on one XCD at about the same
+  // time, and that XCD's L2 serves the later reads of each page.
+  int t, split;
+  {
+    const int L = static_cast<int>(blockIdx.x);
+    const int b = find_seq(a.cu_q, a.batch, L / S);
+    const int q0 = a.cu_q[b], nq = a.cu_q[b + 1] - q0;
+    const int u = L - q0 * S;
+    if (nq <= 1) {
+      t = q0 + u / S;
+      split = u - (u / S) * S;
+    } else {
+      const int blk = u / (8 * nq), r = u - blk * 8 * nq;
+      const int k = min(8, S - 8 * blk);
+      t = q0 + r / k;
+      split = 8 * blk + (r - (r / k) * k);
+    }
+    if (t < 0 || t >= a.total_q || split < 0 || split >= S) {  // malformed cu_q: identity
+      t = L / S;
+      split = L - t * S;
+    }
+  }
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h = lane >> 5;  // head within the wave, lane half
