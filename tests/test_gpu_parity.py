@@ -178,6 +178,21 @@ def _with_lengths(cfg, lens, q_lens):
                        latents=latents, w_uk=w.w_uk, w_uv=w.w_uv, page_table=pt, pool=pool)
 
 
+@pytest.mark.parametrize("kind", ["mfma128", "mfma64", "mfma32", "generic"])
+def test_splits_longer_than_64_pages(kind, monkeypatch):
+    """One split per sequence of 70 and 140 pages (4470 and 8960 keys, the second with two
+    query tokens): the MFMA kernels hold a split's page ids 64 at a time and load the next
+    64 while streaming, a path no shorter split reaches."""
+    monkeypatch.setenv("MLA_KV_DECODE_KERNEL", kind)
+    cfg = _small("dsv3_b16_l4096", batch=2, seq_len=8960)
+    w = _with_lengths(cfg, (4470, 8960), (1, 2))
+    print(f"kernel {kind}: one split of 70 and of 140 pages", flush=True)
+    step = run_step(w, num_splits=1)
+    ref = oracle_for(w)
+    assert_parity(_f64(step.out), ref["out"])
+    assert np.max(np.abs(_f64(step.lse) - ref["lse"])) <= 2e-2
+
+
 @pytest.mark.parametrize("heads,kind", [(16, None), (128, "mfma128"), (128, "mfma64"),
                                         (128, "mfma32")])
 def test_empty_sequence_gives_zero_and_minus_inf(heads, kind, monkeypatch):
