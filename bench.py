@@ -442,7 +442,7 @@ def measure_append(args, w, torch, harness, mla, wl, steps, runner, timed, reps,
 
 def decode_kernel_name(cfg, total_q, num_splits, mla):
     """The decode kernel the library dispatches for this shape (same rule as the library:
-    MLA_KV_DECODE_KERNEL = generic / mfma / mfma128 / mfma64 / mfma32; by default, for one
+    MLA_KV_DECODE_KERNEL = generic / mfma / mfma128 / mfma64 / mfma32[-128|-64]; by default, for one
     latent group, the 32x32x16 kernel when one workgroup per (token, split) fills the
     device and the 16x16x32 kernel's 64-head split otherwise)."""
     mfma_shape = (cfg.dtype == "bf16" and cfg.heads == 128 and cfg.groups in (1, 2)
@@ -452,7 +452,7 @@ def decode_kernel_name(cfg, total_q, num_splits, mla):
         return "decode_generic_kernel"
     if cfg.groups != 1 or choice in ("mfma128", "mfma64"):
         return "decode_mfma_kernel"
-    if choice == "mfma32" or mla.head_split(total_q, num_splits, cfg.groups) == 1:
+    if choice.startswith("mfma32") or mla.head_split(total_q, num_splits, cfg.groups) == 1:
         return "decode_m32_kernel"
     return "decode_mfma_kernel"
 

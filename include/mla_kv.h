@@ -145,8 +145,9 @@ int mla_rope_table(float* cos_out, float* sin_out, int max_pos, int d_R, double 
  * workgroups of 64 heads each.  The environment variable MLA_KV_DECODE_KERNEL
  * overrides the choice: "generic" (the shape-generic kernel), "mfma" (automatic MFMA
  * choice), "mfma128" / "mfma64" (16x16x32 kernel with the given heads per workgroup),
- * "mfma32" (32x32x16 kernel, one latent group); an MFMA choice the shape does not
- * support returns MLA_ERR_UNSUPPORTED.
+ * "mfma32" (32x32x16 kernel, one latent group, heads per workgroup chosen like the
+ * automatic split), "mfma32-128" / "mfma32-64" (32x32x16 kernel with the given heads per
+ * workgroup); an MFMA choice the shape does not support returns MLA_ERR_UNSUPPORTED.
  */
 int mla_decode_paged(const void* q_abs, const void* q_r, const void* kv_cache,
                      const int32_t* page_table, const int32_t* seq_lens, const int32_t* cu_q,

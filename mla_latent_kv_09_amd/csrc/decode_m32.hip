@@ -39,6 +39,8 @@
 // RoPE row t (128 B) holds chunk c at c ^ ((t >> 2) & 7); q_R of head n the same with n.
 #include <math.h>
 
+#include <type_traits>
+
 #include "mla_device.h"
 #include "mla_internal.h"
 
@@ -144,6 +146,12 @@ __device__ __forceinline__ void load_row(uint32_t c_base, const char* page, int 
   }
 }
 
+// HS = 1: one workgroup per (token, split), wave w owns heads 32w .. 32w+31 over all
+// 64 tokens of a page.
+// HS = 2: two workgroups of 64 heads per (token, split).  Wave w owns heads
+// 32 (w % 2) .. +31 of its half over tokens 32 (w / 2) .. +31 of each page; waves w and
+// w ^ 2 (same heads, other token half) merge their outputs through LDS at the end.
+template <int HS>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 decode_m32_kernel(DecodeArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -154,8 +162,18 @@ decode_m32_kernel(DecodeArgs a) {
   // workgroups, token-major: the n workgroups of one split are 8 apart, so the
   // dispatcher (workgroup L to XCD L mod 8) places them on one XCD at about the same
   // time, and that XCD's L2 serves the later reads of each page.
-  int t, split;
-  {
+  int t, split, h2 = 0;
+  if constexpr (HS == 2) {
+    // Blocks of 8 (token, split) pairs take 16 consecutive workgroups: half h2 of pair
+    // 8k + i is workgroup 16k + 8 h2 + i (in a last block of r < 8 pairs, 16k + r h2 + i),
+    // so the two halves of a pair, which stream the same pages, share one XCD's L2.
+    const int L = static_cast<int>(blockIdx.x), kb = L >> 4, base = kb * 8;
+    const int r8 = min(8, a.total_q * S - base), off = L - 16 * kb;
+    const int pair = base + off % r8;
+    h2 = off / r8;
+    t = pair / S;
+    split = pair - t * S;
+  } else {
     const int L = static_cast<int>(blockIdx.x);
     const int b = find_seq(a.cu_q, a.batch, L / S);
     const int q0 = a.cu_q[b], nq = a.cu_q[b + 1] - q0;
@@ -177,13 +195,16 @@ decode_m32_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h = lane >> 5;  // head within the wave, lane half
-  const int head = wave * 32 + n;
+  const int hb = HS == 1 ? wave : (wave & 1);  // 32-head block within the workgroup
+  const int th = HS == 1 ? 0 : (wave >> 1);    // token half of each page (HS = 2)
+  const int hl = hb * 32 + n;                  // head within the workgroup
+  const int head = h2 * (kHeads / HS) + hl;
   const QueryWork w = query_work(a.cu_q, a.seq_lens, a.batch, t, split, S, a.pages_per_split, kTok,
                                  a.max_pages, a.causal);
   const size_t row = (static_cast<size_t>(t) * kHeads + head) * S + split;
   __bf16* o_out = static_cast<__bf16*>(a.o_part) + row * kDc;
   if (w.k0 >= w.k1) {  // empty split: only the LSE is written
-    if (h == 0) a.lse_part[row] = -INFINITY;
+    if (h == 0 && th == 0) a.lse_part[row] = -INFINITY;
     return;
   }
   const char* kv = static_cast<const char*>(a.kv);
@@ -219,7 +240,7 @@ decode_m32_kernel(DecodeArgs a) {
 #pragma unroll
     for (int k = 0; k < kQSteps; ++k) q[k] = *reinterpret_cast<const bf16x8*>(qa + 16 * k);
   }
-  {
+  if (th == 0) {
     const uint16_t* qr = static_cast<const uint16_t*>(a.q_r) +
                          (static_cast<size_t>(t) * kHeads + head) * kDr;
     const int p = min(max(w.pos, 0), max(a.rope_max_pos - 1, 0));
@@ -239,7 +260,7 @@ decode_m32_kernel(DecodeArgs a) {
           x[2 * i + 1] = fmaf(x0, sn[i], x1 * cs[i]);
         }
       }
-      *(lds_bf16x8_t*)(uintptr_t)(smem_base + kQrOff + head * 128 + ((c ^ ((head >> 2) & 7)) << 4)) =
+      *(lds_bf16x8_t*)(uintptr_t)(smem_base + kQrOff + hl * 128 + ((c ^ ((hl >> 2) & 7)) << 4)) =
           to_bf16x8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
     }
   }
@@ -288,31 +309,41 @@ decode_m32_kernel(DecodeArgs a) {
     const uint32_t st_base = smem_base + stage * kStageBytes;
     const uint32_t sb = opaque(st_base + s_lane);
 
-    // ---- scores: RoPE steps, then the latent steps, the two token blocks alternating.
+    // ---- scores.  HS = 1: RoPE steps, then the latent steps, the two 32-token blocks
+    // alternating.  HS = 2: this wave's one 32-token block, two chains over alternate
+    // K-steps (summed below).
     f32x16 s[2];
     {
       const uint32_t rb = opaque(st_base + kCBytes + n * 128);
-      const uint32_t qb = smem_base + kQrOff + head * 128;
-      const int swr = (n >> 2) & 7, swq = (head >> 2) & 7;
+      const uint32_t qb = smem_base + kQrOff + hl * 128;
+      const int swr = (n >> 2) & 7, swq = (hl >> 2) & 7;
 #pragma unroll
       for (int rs = 0; rs < kRSteps; ++rs) {
         const int c = 2 * rs + h;
         const bf16x8 qrf = lds_read8(qb + ((c ^ swq) << 4));
+        if constexpr (HS == 1) {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-          const bf16x8 cf = lds_read8(rb + ((c ^ swr) << 4) + 4096 * mb);
-          if (rs == 0)
-            mfma32_first(s[mb], cf, qrf);
+          for (int mb = 0; mb < 2; ++mb) {
+            const bf16x8 cf = lds_read8(rb + ((c ^ swr) << 4) + 4096 * mb);
+            if (rs == 0)
+              mfma32_first(s[mb], cf, qrf);
+            else
+              mfma32_acc(s[mb], cf, qrf);
+          }
+        } else {
+          const bf16x8 cf = lds_read8(rb + ((c ^ swr) << 4) + 4096 * th);
+          if (rs < 2)
+            mfma32_first(s[rs & 1], cf, qrf);
           else
-            mfma32_acc(s[mb], cf, qrf);
+            mfma32_acc(s[rs & 1], cf, qrf);
         }
       }
     }
     {
-      constexpr int kSteps = 2 * kQSteps;  // (ks, mb) steps
+      constexpr int kSteps = 2 * kQSteps / HS;  // (ks, mb) steps, or ks steps with HS = 2
       constexpr int kRing = 4;
       auto frag = [&](int st) {
-        const int ks = st >> 1, mb = st & 1;
+        const int ks = HS == 1 ? st >> 1 : st, mb = HS == 1 ? (st & 1) : th;
         const uint32_t addr = (sb ^ static_cast<uint32_t>((2 * ks & 31) << 4)) +
                               512 * (ks >> 4) + 32768 * mb;
         return lds_read8(addr);
@@ -324,27 +355,36 @@ decode_m32_kernel(DecodeArgs a) {
       for (int st = 0; st < kSteps; ++st) {
         const bf16x8 cf = ring[st % kRing];
         if (st + kRing < kSteps) ring[st % kRing] = frag(st + kRing);
-        mfma32_acc(s[st & 1], cf, q[st >> 1]);
-        if ((st & 3) == 1 && has_next)  // 18 copies over the 64 steps
-          load_row(next_base, next_page, next_valid, wave, static_cast<int>(opaque(lane)), st >> 2);
-        if ((st == 34 || st == 50) && has_next)
-          load_row(next_base, next_page, next_valid, wave, static_cast<int>(opaque(lane)),
-                   st == 34 ? 16 : 17);
+        mfma32_acc(s[st & 1], cf, q[HS == 1 ? st >> 1 : st]);
+        if constexpr (HS == 1) {
+          if ((st & 3) == 1 && has_next)  // 18 copies over the 64 steps
+            load_row(next_base, next_page, next_valid, wave, static_cast<int>(opaque(lane)), st >> 2);
+          if ((st == 34 || st == 50) && has_next)
+            load_row(next_base, next_page, next_valid, wave, static_cast<int>(opaque(lane)),
+                     st == 34 ? 16 : 17);
+        } else {
+          if ((st & 1) == 1 && has_next)  // latent rows 0..15 over the 32 steps
+            load_row(next_base, next_page, next_valid, wave, static_cast<int>(opaque(lane)), st >> 1);
+        }
       }
     }
 
-    // ---- online softmax.  s[mb][r] is the raw score of token 32 mb + 8 (r/4) + 4 h + r%4.
+    // ---- online softmax.  HS = 1: s[mb][r] is the raw score of token 32 mb + 8 (r/4) +
+    // 4 h + r%4.  HS = 2: s[0][r] (after the two chains are summed) is that of token
+    // 32 th + 8 (r/4) + 4 h + r%4.
     mfma_results_ready(s[0], s[1]);
+    if constexpr (HS == 2) s[0] += s[1];
+    constexpr int kBlocks = HS == 1 ? 2 : 1;
     if (n_valid < kTok) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+      for (int mb = 0; mb < kBlocks; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (32 * mb + 8 * (r >> 2) + 4 * h + (r & 3) >= n_valid) s[mb][r] = -INFINITY;
+          if (32 * (HS == 1 ? mb : th) + 8 * (r >> 2) + 4 * h + (r & 3) >= n_valid) s[mb][r] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < kBlocks; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
     mx = halves_max(mx) * scale_log2;
@@ -354,7 +394,7 @@ decode_m32_kernel(DecodeArgs a) {
     // the head at that maximum: everything accumulated before weighs at most
     // 2^-kJump * (keys so far) < 2^-40 of the new maximum's term, below fp32 resolution,
     // and is cleared instead of rescaled.
-    const bool restart = mx > m_ref + kJump;  // always true on a head's first page
+    const bool restart = mx > m_ref + kJump;  // true on a head's first page with a key
     if (restart) {
       m_ref = mx;
       l_run = 0.f;
@@ -363,21 +403,26 @@ decode_m32_kernel(DecodeArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[nb][r] = 0.f;
     }
+    // With HS = 2 a token half can hold no key yet (the second half of a split's only,
+    // partial page): its reference is still -inf and is subtracted as 0, so its
+    // exponentials are 0 rather than NaN.
+    const float m_sub = (HS == 2 && m_ref == -INFINITY) ? 0.f : m_ref;
     float psum = 0.f;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < kBlocks; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(s[mb][r], scale_log2, -m_ref));
+        const float p = __builtin_amdgcn_exp2f(fmaf(s[mb][r], scale_log2, -m_sub));
         s[mb][r] = p;
         psum += p;
       }
     l_run += psum;
 
     // ---- P^T operands: K-step kq = 2 mb + q holds elements 8q .. 8q+7 of block mb
-    bf16x8 pb[4];
+    constexpr int kKQ = 4 / HS;  // 16-token K-steps of the output
+    bf16x8 pb[kKQ];
 #pragma unroll
-    for (int kq = 0; kq < 4; ++kq) {
+    for (int kq = 0; kq < kKQ; ++kq) {
       const f32x16& v = s[kq >> 1];
       const int b8 = 8 * (kq & 1);
       pb[kq] = to_bf16x8(v[b8], v[b8 + 1], v[b8 + 2], v[b8 + 3], v[b8 + 4], v[b8 + 5], v[b8 + 6], v[b8 + 7]);
@@ -386,11 +431,11 @@ decode_m32_kernel(DecodeArgs a) {
     // ---- O^T[cols 32 nb .. +31] += C^T . P^T, (kq, nb) steps through a ring
     const uint32_t ob = opaque(st_base + o_lane);
     {
-      constexpr int kSteps = 4 * kColBlocks;
+      constexpr int kSteps = kKQ * kColBlocks;
       constexpr int kRing = 4;
       auto frag = [&](int st) {
         const int kq = st / kColBlocks, nb = st % kColBlocks;
-        const int mb = kq >> 1, qq = kq & 1;
+        const int mb = HS == 1 ? kq >> 1 : th, qq = HS == 1 ? (kq & 1) : kq;
         const uint32_t k0 = static_cast<uint32_t>((4 * nb) ^ (16 * qq)) << 4;
         const uint32_t k1 = static_cast<uint32_t>((4 * nb) ^ 2 ^ (16 * qq)) << 4;
         const uint32_t a0 = (ob ^ k0) + 32768 * mb + 16384 * qq;
@@ -408,6 +453,11 @@ decode_m32_kernel(DecodeArgs a) {
         if (st + kRing < kSteps) ring[st % kRing] = frag(st + kRing);
         const int kq = st / kColBlocks, nb = st % kColBlocks;
         o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cf, pb[kq], o[nb], 0, 0, 0);
+        if constexpr (HS == 2) {  // the RoPE rows of the next page
+          if ((st == 8 || st == 24) && has_next)
+            load_row(next_base, next_page, next_valid, wave, static_cast<int>(opaque(lane)),
+                     st == 8 ? 16 : 17);
+        }
       }
     }
     // Keep the output accumulators in the accumulator registers across the loop (the
@@ -419,19 +469,74 @@ decode_m32_kernel(DecodeArgs a) {
 
   // ---- finalize: normalise and write this split's partial output (bf16) and LSE
   const float l_tot = halves_sum(l_run);
-  const float inv = 1.f / l_tot;
+  if constexpr (HS == 1) {
+    const float inv = 1.f / l_tot;
 #pragma unroll
-  for (int nb = 0; nb < kColBlocks; ++nb) {  // one 32-column block at a time
-    asm volatile("" : "+a"(o[nb]));
-    const f32x16 v = o[nb];
+    for (int nb = 0; nb < kColBlocks; ++nb) {  // one 32-column block at a time
+      asm volatile("" : "+a"(o[nb]));
+      const f32x16 v = o[nb];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      *reinterpret_cast<bf16x4*>(o_out + 32 * nb + 8 * j + 4 * h) =
-          bf16x4{static_cast<__bf16>(v[4 * j] * inv), static_cast<__bf16>(v[4 * j + 1] * inv),
-                 static_cast<__bf16>(v[4 * j + 2] * inv), static_cast<__bf16>(v[4 * j + 3] * inv)};
-    __builtin_amdgcn_sched_barrier(0);
+      for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<bf16x4*>(o_out + 32 * nb + 8 * j + 4 * h) =
+            bf16x4{static_cast<__bf16>(v[4 * j] * inv), static_cast<__bf16>(v[4 * j + 1] * inv),
+                   static_cast<__bf16>(v[4 * j + 2] * inv), static_cast<__bf16>(v[4 * j + 3] * inv)};
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (h == 0) a.lse_part[row] = (m_ref + __log2f(l_tot)) * kLn2;
+  } else {
+    // Merge the two token halves of each head: wave w keeps column blocks 8 th .. +7 and
+    // hands the other 8, with its (m, l), to its partner w ^ 2 through LDS (the stages are
+    // free once every wave has finished the last page).  Lane-linear 64-byte slots.
+    typedef __attribute__((address_space(3))) f32x16 lds_f32x16_t;
+    typedef __attribute__((address_space(3))) float lds_f32_t;
+    const uint32_t xo_mine = smem_base + static_cast<uint32_t>(wave) * 32768 + lane * 64;
+    const uint32_t xo_part = smem_base + static_cast<uint32_t>(wave ^ 2) * 32768 + lane * 64;
+    const uint32_t ml_mine = smem_base + 4 * 32768 + (wave * 64 + lane) * 8;
+    const uint32_t ml_part = smem_base + 4 * 32768 + ((wave ^ 2) * 64 + lane) * 8;
+    __syncthreads();  // every wave is done with the stages
+    auto hand_over = [&](auto first) {  // blocks first .. first + 7 to the partner
+#pragma unroll
+      for (int i = 0; i < kColBlocks / 2; ++i) {
+        asm volatile("" : "+a"(o[decltype(first)::value + i]));
+        *(lds_f32x16_t*)(uintptr_t)(xo_mine + i * 4096) = o[decltype(first)::value + i];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    if (th == 0)
+      hand_over(std::integral_constant<int, 8>{});
+    else
+      hand_over(std::integral_constant<int, 0>{});
+    *(lds_f32_t*)(uintptr_t)(ml_mine) = m_ref;
+    *(lds_f32_t*)(uintptr_t)(ml_mine + 4) = l_tot;
+    __syncthreads();
+    const float m_p = *(lds_f32_t*)(uintptr_t)(ml_part);
+    const float l_p = *(lds_f32_t*)(uintptr_t)(ml_part + 4);
+    const float m = fmaxf(m_ref, m_p);  // finite: token 0 of every page is in half 0
+    const float a_me = __builtin_amdgcn_exp2f(m_ref - m), a_p = __builtin_amdgcn_exp2f(m_p - m);
+    const float l = l_tot * a_me + l_p * a_p;
+    const float inv = 1.f / l;
+    const float w_me = a_me * inv, w_p = a_p * inv;
+    auto finish = [&](auto first) {  // merge and store blocks first .. first + 7
+#pragma unroll
+      for (int i = 0; i < kColBlocks / 2; ++i) {
+        constexpr int kFirst = decltype(first)::value;
+        asm volatile("" : "+a"(o[kFirst + i]));
+        const f32x16 other = *(lds_f32x16_t*)(uintptr_t)(xo_part + i * 4096);
+        const f32x16 v = o[kFirst + i] * w_me + other * w_p;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          *reinterpret_cast<bf16x4*>(o_out + 32 * (kFirst + i) + 8 * j + 4 * h) =
+              bf16x4{static_cast<__bf16>(v[4 * j]), static_cast<__bf16>(v[4 * j + 1]),
+                     static_cast<__bf16>(v[4 * j + 2]), static_cast<__bf16>(v[4 * j + 3])};
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    if (th == 0)
+      finish(std::integral_constant<int, 0>{});
+    else
+      finish(std::integral_constant<int, 8>{});
+    if (th == 0 && h == 0) a.lse_part[row] = (m + __log2f(l)) * kLn2;
   }
-  if (h == 0) a.lse_part[row] = (m_ref + __log2f(l_tot)) * kLn2;
 }
 
 }  // namespace
@@ -441,17 +546,22 @@ bool decode_m32_supported(const DecodeArgs& a, bool bf16) {
          a.page_size == kTok;
 }
 
-hipError_t launch_decode_m32(const DecodeArgs& a, hipStream_t s) {
+template <int HS>
+hipError_t launch_decode_m32_k(const DecodeArgs& a, hipStream_t s) {
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_m32_kernel),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_m32_kernel<HS>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const dim3 grid(a.total_q * a.num_splits);
-  decode_m32_kernel<<<grid, kThreads, kLdsBytes, s>>>(a);
+  const dim3 grid(a.total_q * a.num_splits * HS);
+  decode_m32_kernel<HS><<<grid, kThreads, kLdsBytes, s>>>(a);
   return hipGetLastError();
+}
+
+hipError_t launch_decode_m32(const DecodeArgs& a, int head_split, hipStream_t s) {
+  return head_split == 2 ? launch_decode_m32_k<2>(a, s) : launch_decode_m32_k<1>(a, s);
 }
 
 }  // namespace mla

@@ -36,10 +36,11 @@ int launch_status(hipError_t e) { return e == hipSuccess ? MLA_OK : MLA_ERR_LAUN
 // MLA_ERR_UNSUPPORTED) with the head split chosen from the grid size, "mfma128" and
 // "mfma64" require the 16x16x32 kernel with one workgroup of 128 heads, resp. two of 64
 // heads (one latent group only), per (token, split), "mfma32" requires the 32x32x16
-// kernel (four 32-head waves per (token, split), one latent group); anything else picks
+// kernel (one latent group; head split chosen from the grid size), "mfma32-128" and
+// "mfma32-64" require it with the given heads per workgroup; anything else picks
 // an MFMA kernel whenever the shape has one: for one latent group the 32x32x16 kernel
 // when one workgroup per (token, split) fills the device, else the 64-head split.
-enum class DecodeKernel { kAuto, kGeneric, kMfma, kMfma128, kMfma64, kMfma32 };
+enum class DecodeKernel { kAuto, kGeneric, kMfma, kMfma128, kMfma64, kMfma32, kMfma32x128, kMfma32x64 };
 DecodeKernel decode_kernel_choice() {
   const char* v = getenv("MLA_KV_DECODE_KERNEL");
   if (v == nullptr) return DecodeKernel::kAuto;
@@ -48,6 +49,8 @@ DecodeKernel decode_kernel_choice() {
   if (strcmp(v, "mfma128") == 0) return DecodeKernel::kMfma128;
   if (strcmp(v, "mfma64") == 0) return DecodeKernel::kMfma64;
   if (strcmp(v, "mfma32") == 0) return DecodeKernel::kMfma32;
+  if (strcmp(v, "mfma32-128") == 0) return DecodeKernel::kMfma32x128;
+  if (strcmp(v, "mfma32-64") == 0) return DecodeKernel::kMfma32x64;
   return DecodeKernel::kAuto;
 }
 
@@ -174,9 +177,13 @@ int mla_decode_paged(const void* q_abs, const void* q_r, const void* kv_cache,
   const bool bf16 = dtype == MLA_DTYPE_BF16;
   const DecodeKernel choice = decode_kernel_choice();
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (choice == DecodeKernel::kMfma32) {
+  if (choice == DecodeKernel::kMfma32 || choice == DecodeKernel::kMfma32x128 ||
+      choice == DecodeKernel::kMfma32x64) {
     if (!mla::decode_m32_supported(a, bf16)) return MLA_ERR_UNSUPPORTED;
-    return launch_status(mla::launch_decode_m32(a, s));
+    a.head_split = choice == DecodeKernel::kMfma32x128 ? 1 : choice == DecodeKernel::kMfma32x64 ? 2 : 0;
+    const int hs = mla::decode_mfma_head_split(a, cu_count_of_current_device());
+    if (static_cast<long long>(total_q) * num_splits * hs > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+    return launch_status(mla::launch_decode_m32(a, hs, s));
   }
   const bool mfma_ok = mla::decode_mfma_supported(a, bf16);
   const bool mfma_required = choice == DecodeKernel::kMfma || choice == DecodeKernel::kMfma128 ||
@@ -190,7 +197,7 @@ int mla_decode_paged(const void* q_abs, const void* q_r, const void* kv_cache,
     // One workgroup of 128 heads per (token, split): the 32x32x16 kernel, unless the
     // 16x16x32 one was asked for by name.
     if (hs == 1 && choice != DecodeKernel::kMfma128 && mla::decode_m32_supported(a, bf16))
-      return launch_status(mla::launch_decode_m32(a, s));
+      return launch_status(mla::launch_decode_m32(a, 1, s));
     return launch_status(mla::launch_decode_mfma(a, hs, s));
   }
   return launch_status(mla::launch_decode_generic(a, bf16, s));

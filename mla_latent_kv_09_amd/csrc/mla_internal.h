@@ -65,9 +65,10 @@ namespace mla {
 // compute units idle).
 bool decode_mfma_supported(const DecodeArgs& a, bool bf16);
 // 32x32x16 MFMA split-KV decode: bf16, 128 heads, one latent group, d_c 512, d_R 64;
-// one workgroup of four 32-head waves per (token, split).
+// one workgroup of four 32-head waves per (token, split) (head split 1), or two
+// workgroups of 64 heads, each wave covering half of every page's tokens (head split 2).
 bool decode_m32_supported(const DecodeArgs& a, bool bf16);
-hipError_t launch_decode_m32(const DecodeArgs& a, hipStream_t s);
+hipError_t launch_decode_m32(const DecodeArgs& a, int head_split, hipStream_t s);
 int decode_mfma_head_split(const DecodeArgs& a, int cu_count);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int head_split, hipStream_t s);
 }  // namespace mla

@@ -84,13 +84,15 @@ def test_parity_small(case, rope):
     assert lse_err <= (1e-4 if fp32 else 2e-2)
 
 
+@pytest.mark.parametrize("kind", ["mfma32-128", "mfma32-64"])
 @pytest.mark.parametrize("case", ["dsv3_small", "long_small", "ragged_small"])
 @pytest.mark.parametrize("rope", [True, False])
-def test_parity_small_mfma32(case, rope, monkeypatch):
-    """The 32x32x16 kernel (four 32-head waves per (token, split)) on the one-group cases."""
-    monkeypatch.setenv("MLA_KV_DECODE_KERNEL", "mfma32")
+def test_parity_small_mfma32(case, rope, kind, monkeypatch):
+    """The 32x32x16 kernel on the one-group cases: four 32-head waves per (token, split)
+    (mfma32-128), or two 64-head workgroups whose waves split each page's tokens (mfma32-64)."""
+    monkeypatch.setenv("MLA_KV_DECODE_KERNEL", kind)
     cfg = SMALL_CASES[case]
-    print(f"case {case} rope={rope} kernel mfma32", flush=True)
+    print(f"case {case} rope={rope} kernel {kind}", flush=True)
     w = wl.make_workload(cfg)
     step = run_step(w, rope=rope)
     ref = oracle_for(w, rope=rope)
@@ -131,7 +133,7 @@ def test_bitwise_repeatable():
     ((31, 32, 33, 96, 97), (1, 1, 2, 1, 2)),
 ])
 @pytest.mark.parametrize("heads,kind", [(16, None), (128, "mfma128"), (128, "mfma64"),
-                                        (128, "mfma32")])
+                                        (128, "mfma32-128"), (128, "mfma32-64")])
 def test_edge_lengths(lens, q_lens, heads, kind, monkeypatch):
     """16 heads run the generic kernel; 128 heads the MFMA kernel with one workgroup of
     128 heads or two of 64 heads per (token, split).  Lengths of 1, 2, 31-33 and 65 keys
@@ -178,7 +180,7 @@ def _with_lengths(cfg, lens, q_lens):
                        latents=latents, w_uk=w.w_uk, w_uv=w.w_uv, page_table=pt, pool=pool)
 
 
-@pytest.mark.parametrize("kind", ["mfma128", "mfma64", "mfma32", "generic"])
+@pytest.mark.parametrize("kind", ["mfma128", "mfma64", "mfma32-128", "mfma32-64", "generic"])
 def test_splits_longer_than_64_pages(kind, monkeypatch):
     """One split per sequence of 70 and 140 pages (4470 and 8960 keys, the second with two
     query tokens): the MFMA kernels hold a split's page ids 64 at a time and load the next
@@ -194,7 +196,7 @@ def test_splits_longer_than_64_pages(kind, monkeypatch):
 
 
 @pytest.mark.parametrize("heads,kind", [(16, None), (128, "mfma128"), (128, "mfma64"),
-                                        (128, "mfma32")])
+                                        (128, "mfma32-128"), (128, "mfma32-64")])
 def test_empty_sequence_gives_zero_and_minus_inf(heads, kind, monkeypatch):
     """A sequence with no keys: output 0 and LSE -inf on every head, from the generic
     kernel and from both head splits of the MFMA kernel (where both workgroups of an
@@ -264,7 +266,8 @@ def test_decode_kernels_agree(case, monkeypatch):
     cfg = SMALL_CASES[case]
     w = wl.make_workload(cfg)
     outs = {}
-    kinds = ("mfma128", "mfma64", "mfma32", "generic") if cfg.groups == 1 else ("mfma128", "generic")
+    kinds = (("mfma128", "mfma64", "mfma32-128", "mfma32-64", "generic") if cfg.groups == 1
+             else ("mfma128", "generic"))
     for kind in kinds:
         monkeypatch.setenv("MLA_KV_DECODE_KERNEL", kind)
         print(f"  kernel {kind}", flush=True)
@@ -276,7 +279,7 @@ def test_decode_kernels_agree(case, monkeypatch):
         assert_parity(outs[kind], outs["generic"], what=f"{kind} vs generic")
 
 
-@pytest.mark.parametrize("kind", ["mfma128", "mfma64", "mfma32", "generic"])
+@pytest.mark.parametrize("kind", ["mfma128", "mfma64", "mfma32-128", "mfma32-64", "generic"])
 @pytest.mark.parametrize("case,mode", [("dsv3_small", "grow"), ("dsv3_small", "flood"),
                                        ("dsv3_small", "shrink"), ("gla2_small", "grow"),
                                        ("gla2_small", "flood")])
@@ -297,7 +300,7 @@ def test_softmax_reference_moves(kind, case, mode, monkeypatch):
     matrix (q_abs = q_c on the first d_hc latent columns, exact in bf16) and RoPE is
     off (a rotated q_R is rounded to bf16): the scores then differ from the oracle's
     by fp32 accumulation only, and the comparison tests the kernels' softmax."""
-    if kind in ("mfma64", "mfma32") and SMALL_CASES[case].groups != 1:
+    if kind in ("mfma64", "mfma32-128", "mfma32-64") and SMALL_CASES[case].groups != 1:
         pytest.skip("the 64-head split and the 32x32 kernel exist for one latent group only")
     w = wl.make_workload(SMALL_CASES[case])
     H, d_hc, d_cg = w.w_uk.shape
