@@ -104,3 +104,40 @@ def test_ragged_plan_no_worse_than_any_candidate_length():
     for other in (4, 8, 16, 24, 28, 32, 48, 64, 128):
         if math.ceil(max(pages) / other) <= 256:
             assert best <= mla.plan_makespan(pages, q, other) + 1e-9
+
+
+def _launch_unit(L, S, cu_q):
+    """The 32x32x16 decode kernel's launch order (one workgroup per (token, split)),
+    written out: the units of sequence b are workgroups [cu_q[b] S, cu_q[b+1] S); one
+    token runs in split order, n tokens in blocks of 8 splits x n tokens, token-major."""
+    t0 = L // S
+    b = max(i for i in range(len(cu_q) - 1) if cu_q[i] <= t0)
+    q0, n = cu_q[b], cu_q[b + 1] - cu_q[b]
+    u = L - q0 * S
+    if n <= 1:
+        return q0 + u // S, u % S
+    blk, r = divmod(u, 8 * n)
+    k = min(8, S - 8 * blk)
+    return q0 + r // k, 8 * blk + r % k
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_launch_order_is_a_bijection_that_groups_tokens_of_a_split(seed):
+    rng = np.random.default_rng(seed)
+    B, S = int(rng.integers(1, 10)), int(rng.integers(1, 40))
+    q_lens = rng.choice([1, 1, 2, 3], size=B)
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).tolist()
+    T = cu[-1]
+    where = {}
+    for L in range(T * S):
+        t, s = _launch_unit(L, S, cu)
+        assert 0 <= t < T and 0 <= s < S and (t, s) not in where
+        where[(t, s)] = L
+    assert len(where) == T * S
+    for b in range(B):
+        q0, n = cu[b], cu[b + 1] - cu[b]
+        for s in range(S):
+            if n == 1:
+                assert where[(q0, s)] == q0 * S + s          # split order, as before
+            elif s < 8 * (S // 8):                           # full blocks: 8 apart, one XCD
+                assert all(where[(q0 + i, s)] - where[(q0, s)] == 8 * i for i in range(n))
