@@ -162,6 +162,8 @@ decode_m32_kernel(DecodeArgs a) {
   // workgroups, token-major: the n workgroups of one split are 8 apart, so the
   // dispatcher (workgroup L to XCD L mod 8) places them on one XCD at about the same
   // time, and that XCD's L2 serves the later reads of each page.
+  SeqIndex ix;
+  ix.load(a.cu_q, a.seq_lens, a.batch);
   int t, split, h2 = 0;
   if constexpr (HS == 2) {
     // Blocks of 8 (token, split) pairs take 16 consecutive workgroups: half h2 of pair
@@ -175,8 +177,8 @@ decode_m32_kernel(DecodeArgs a) {
     split = pair - t * S;
   } else {
     const int L = static_cast<int>(blockIdx.x);
-    const int b = find_seq(a.cu_q, a.batch, L / S);
-    const int q0 = a.cu_q[b], nq = a.cu_q[b + 1] - q0;
+    const int b = ix.find(L / S);
+    const int q0 = ix.start(b), nq = ix.stop(b) - q0;
     const int u = L - q0 * S;
     if (nq <= 1) {
       t = q0 + u / S;
@@ -199,8 +201,7 @@ decode_m32_kernel(DecodeArgs a) {
   const int th = HS == 1 ? 0 : (wave >> 1);    // token half of each page (HS = 2)
   const int hl = hb * 32 + n;                  // head within the workgroup
   const int head = h2 * (kHeads / HS) + hl;
-  const QueryWork w = query_work(a.cu_q, a.seq_lens, a.batch, t, split, S, a.pages_per_split, kTok,
-                                 a.max_pages, a.causal);
+  const QueryWork w = query_work(ix, t, split, S, a.pages_per_split, kTok, a.max_pages, a.causal);
   const size_t row = (static_cast<size_t>(t) * kHeads + head) * S + split;
   __bf16* o_out = static_cast<__bf16*>(a.o_part) + row * kDc;
   if (w.k0 >= w.k1) {  // empty split: only the LSE is written

@@ -215,14 +215,24 @@ decode_mfma_kernel(DecodeArgs a) {
   const int S = a.num_splits;
   // 1-D grid in split-fastest order over pairs P = t * S + split.  The dispatcher deals
   // workgroups to the 8 XCDs in turn (L mod 8), so the splits of one token spread over
-  // the XCDs, and a batch whose sequences differ in length loads every XCD alike.  With
-  // HS = 2, blocks of 8 pairs take 16 consecutive workgroups: half h2 of pair 8k + i is
-  // workgroup 16k + 8 h2 + i (in a last block of r < 8 pairs, 16k + r h2 + i), so the
-  // two halves of a pair land on the same XCD.
+  // the XCDs, and a batch whose sequences differ in length loads every XCD alike.
+  // HS = 2 (short batches, where the first page and the query load are much of the
+  // kernel): when T is a multiple of 8, the 2 S workgroups of token t all go to XCD
+  // t mod 8, consecutive in its order, the two halves of a pair adjacent.  The token's
+  // query rows then reach one L2 instead of all eight, and both halves of a pair read
+  // their pages from the same L2.  Otherwise blocks of 8 pairs take 16 consecutive
+  // workgroups: half h2 of pair 8k + i is workgroup 16k + 8 h2 + i (in a last block of
+  // r < 8 pairs, 16k + r h2 + i), so the halves of a pair in a full block share an XCD.
   int t, split, h2 = 0;
   if constexpr (HS == 1) {
     t = static_cast<int>(blockIdx.x) / S;
     split = static_cast<int>(blockIdx.x) - t * S;
+  } else if (a.total_q % 8 == 0) {
+    const int L = static_cast<int>(blockIdx.x), x = L & 7, r = L >> 3;
+    const int k = r / (2 * S), rem = r - k * 2 * S;
+    t = x + 8 * k;
+    split = rem >> 1;
+    h2 = rem & 1;
   } else {
     const int L = static_cast<int>(blockIdx.x), kb = L >> 4, base = kb * 8;
     const int r = min(8, a.total_q * S - base), off = L - 16 * kb;
@@ -240,8 +250,9 @@ decode_mfma_kernel(DecodeArgs a) {
   const int head = h2 * kHeadsWG + hl;
   const int grp = wave / Sh::kWavesPerGroup;             // latent group of this wave
   const uint32_t grp_off = static_cast<uint32_t>(grp) * kDcg * 2;  // its columns in a token row
-  const QueryWork w = query_work(a.cu_q, a.seq_lens, a.batch, t, split, S,
-                                 a.pages_per_split, kTok, a.max_pages, a.causal);
+  SeqIndex ix;
+  ix.load(a.cu_q, a.seq_lens, a.batch);
+  const QueryWork w = query_work(ix, t, split, S, a.pages_per_split, kTok, a.max_pages, a.causal);
   const size_t row = (static_cast<size_t>(t) * kHeads + head) * S + split;
   __bf16* o_out = static_cast<__bf16*>(a.o_part) + row * kDcg;  // bf16 partials
   if (w.k0 >= w.k1) {  // empty split: only the LSE is written

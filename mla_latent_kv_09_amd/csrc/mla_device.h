@@ -46,18 +46,15 @@ struct QueryWork {
   int k0, k1;  // key range [k0, k1) of this split, already clipped to the visible keys
 };
 
-__device__ __forceinline__ QueryWork query_work(const int32_t* __restrict__ cu_q,
-                                                const int32_t* __restrict__ seq_lens, int batch,
-                                                int t, int split, int num_splits,
-                                                int pages_per_split, int page_size,
-                                                int max_pages, int causal) {
+// The key range of split `split` for query row t of sequence b, which starts at query
+// row q0, has q_len query rows and L_raw keys.
+__device__ __forceinline__ QueryWork split_work(int b, int q0, int q_len, int L_raw, int t, int split,
+                                               int num_splits, int pages_per_split, int page_size,
+                                               int max_pages, int causal) {
   QueryWork w;
-  w.b = find_seq(cu_q, batch, t);
-  const int q0 = cu_q[w.b];
-  const int q_len = cu_q[w.b + 1] - q0;
-  int L = seq_lens[w.b];
+  w.b = b;
   const int cap = max_pages * page_size;
-  L = L < 0 ? 0 : (L > cap ? cap : L);
+  const int L = L_raw < 0 ? 0 : (L_raw > cap ? cap : L_raw);
   w.L = L;
   w.pos = L - q_len + (t - q0);
   int n_vis = causal ? min(L, w.pos + 1) : L;
@@ -68,6 +65,68 @@ __device__ __forceinline__ QueryWork query_work(const int32_t* __restrict__ cu_q
   w.k0 = split * per_split * page_size;
   w.k1 = split == num_splits - 1 ? n_vis : min((split + 1) * per_split * page_size, n_vis);
   return w;
+}
+
+__device__ __forceinline__ QueryWork query_work(const int32_t* __restrict__ cu_q,
+                                                const int32_t* __restrict__ seq_lens, int batch,
+                                                int t, int split, int num_splits,
+                                                int pages_per_split, int page_size,
+                                                int max_pages, int causal) {
+  const int b = find_seq(cu_q, batch, t);
+  const int q0 = cu_q[b];
+  return split_work(b, q0, cu_q[b + 1] - q0, seq_lens[b], t, split, num_splits, pages_per_split,
+                    page_size, max_pages, causal);
+}
+
+// The batch's sequence table spread over one wave: for batch <= 64, lane l holds the end
+// offset cu_q[l + 1] and the length seq_lens[l] of sequence l, fetched in one round trip
+// at the start of a kernel, and a lookup is a ballot and a lane read instead of the
+// binary search's chain of dependent loads.  Larger batches fall back to those loads.
+// Every lane of the wave must be active when it is loaded and queried.
+struct SeqIndex {
+  const int32_t* cu_q;
+  const int32_t* seq_lens;
+  int batch;
+  int end, len, first;
+
+  __device__ __forceinline__ bool wide() const { return batch <= 64; }
+  __device__ __forceinline__ void load(const int32_t* __restrict__ cu, const int32_t* __restrict__ lens,
+                                       int n) {
+    cu_q = cu;
+    seq_lens = lens;
+    batch = n;
+    const int lane = static_cast<int>(threadIdx.x) & 63;
+    const bool in = wide() && lane < n;
+    end = in ? cu[lane + 1] : 0;
+    len = in ? lens[lane] : 0;
+    first = cu[0];
+  }
+  // The largest b with cu_q[b] <= t (cu_q non-decreasing): the number of sequences
+  // 1 .. batch-1 that start at or before row t.
+  __device__ __forceinline__ int find(int t) const {
+    if (!wide()) return find_seq(cu_q, batch, t);
+    const int lane = static_cast<int>(threadIdx.x) & 63;
+    return __builtin_popcountll(__builtin_amdgcn_ballot_w64(lane < batch - 1 && end <= t));
+  }
+  __device__ __forceinline__ int start(int b) const {
+    if (!wide()) return cu_q[b];
+    return b > 0 ? __builtin_amdgcn_readlane(end, b - 1) : first;
+  }
+  __device__ __forceinline__ int stop(int b) const {
+    return wide() ? __builtin_amdgcn_readlane(end, b) : cu_q[b + 1];
+  }
+  __device__ __forceinline__ int length(int b) const {
+    return wide() ? __builtin_amdgcn_readlane(len, b) : seq_lens[b];
+  }
+};
+
+__device__ __forceinline__ QueryWork query_work(const SeqIndex& ix, int t, int split, int num_splits,
+                                                int pages_per_split, int page_size, int max_pages,
+                                                int causal) {
+  const int b = ix.find(t);
+  const int q0 = ix.start(b);
+  return split_work(b, q0, ix.stop(b) - q0, ix.length(b), t, split, num_splits, pages_per_split,
+                    page_size, max_pages, causal);
 }
 
 __device__ __forceinline__ int clamp_page(int32_t p, int num_pool_pages) {

@@ -141,3 +141,66 @@ def test_launch_order_is_a_bijection_that_groups_tokens_of_a_split(seed):
                 assert where[(q0, s)] == q0 * S + s          # split order, as before
             elif s < 8 * (S // 8):                           # full blocks: 8 apart, one XCD
                 assert all(where[(q0 + i, s)] - where[(q0, s)] == 8 * i for i in range(n))
+
+
+def _find_seq_binary(cu_q, batch, t):
+    lo, hi = 0, batch - 1
+    while lo < hi:
+        mid = (lo + hi + 1) >> 1
+        if cu_q[mid] <= t:
+            lo = mid
+        else:
+            hi = mid - 1
+    return lo
+
+
+def _find_seq_wave(cu_q, batch, t):
+    """The decode kernels' wave-wide lookup for batch <= 64: lane l holds cu_q[l + 1];
+    the sequence is the number of lanes l < batch - 1 with cu_q[l + 1] <= t."""
+    return sum(1 for lane in range(64) if lane < batch - 1 and cu_q[lane + 1] <= t)
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_wave_sequence_lookup_matches_binary_search(seed):
+    rng = np.random.default_rng(seed)
+    batch = int(rng.choice([1, 2, 3, 16, 63, 64]))
+    q_lens = rng.choice([0, 1, 1, 2, 3], size=batch)
+    q_lens[int(rng.integers(batch))] = max(1, q_lens[0])
+    cu = np.concatenate([[0], np.cumsum(q_lens)]).tolist()
+    for t in range(cu[-1]):
+        b = _find_seq_wave(cu, batch, t)
+        assert b == _find_seq_binary(cu, batch, t)
+        assert cu[b] <= t < cu[b + 1]  # the row belongs to a non-empty sequence
+
+
+def _k2_half_unit(L, S, T):
+    """The 16x16x32 decode kernel's launch order with two workgroups per (token, split),
+    written out: (token, split, half) of workgroup L."""
+    if T % 8 == 0:
+        x, r = L & 7, L >> 3
+        k, rem = divmod(r, 2 * S)
+        return x + 8 * k, rem >> 1, rem & 1
+    kb = L >> 4
+    base = kb * 8
+    r = min(8, T * S - base)
+    off = L - 16 * kb
+    pair = base + off % r
+    return pair // S, pair % S, off // r
+
+
+@pytest.mark.parametrize("T", [1, 3, 8, 16, 24, 40])
+@pytest.mark.parametrize("S", [1, 2, 5, 8])
+def test_head_split_launch_order_is_a_bijection_with_halves_on_one_xcd(T, S):
+    where = {}
+    for L in range(2 * T * S):
+        t, s, h = _k2_half_unit(L, S, T)
+        assert 0 <= t < T and 0 <= s < S and h in (0, 1) and (t, s, h) not in where
+        where[(t, s, h)] = L
+    assert len(where) == 2 * T * S
+    for t in range(T):
+        for s in range(S):
+            full_block = (t * S + s) < 8 * (T * S // 8)
+            if T % 8 == 0 or full_block:                       # halves share an L2
+                assert where[(t, s, 0)] % 8 == where[(t, s, 1)] % 8
+            if T % 8 == 0:                                     # a token's units share one
+                assert where[(t, s, 0)] % 8 == t % 8
