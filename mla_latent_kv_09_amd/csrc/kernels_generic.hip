@@ -391,10 +391,109 @@ hipError_t launch_decode_generic(const DecodeArgs& a, bool bf16, hipStream_t s) 
   return hipGetLastError();
 }
 
+// Many-row form of the same merge, for launches whose partial bytes dominate (thousands
+// of rows).  Each wave walks `rpw` consecutive rows.  A row's LSEs are requested while
+// the previous row's partials are in flight, and only the partials of splits that hold
+// keys (LSE > -inf) are read.  Splits past a short sequence's end are never written, so
+// a batch of unequal lengths reads just the written partials, still at one memory round
+// trip per row.  Needs S <= kChunk (all splits of a row in one request).
+template <typename T, int kDcg, int kChunk>
+__global__ void __launch_bounds__(kThreads)
+combine_rows_kernel(const T* __restrict__ o_part, const float* __restrict__ lse_part,
+                    T* __restrict__ o_lat, float* __restrict__ lse_out, int rows, int S, int rpw) {
+  constexpr int kE = kDcg / 64;
+  constexpr int kW = kE * static_cast<int>(sizeof(T)) / 4;
+  static_assert(kChunk * kW <= 128 && kChunk <= 64, "one request of at most 128 words per lane");
+  const int lane = threadIdx.x & 63;
+  const size_t wv = static_cast<size_t>(blockIdx.x) * (kThreads / 64) + (threadIdx.x >> 6);
+  size_t r = wv * static_cast<size_t>(rpw);
+  if (r >= static_cast<size_t>(rows)) return;
+  const size_t r_end = r + rpw < static_cast<size_t>(rows) ? r + rpw : static_cast<size_t>(rows);
+  float l_next = lane < S ? lse_part[r * S + lane] : -INFINITY;
+  for (; r < r_end; ++r) {
+    const float l_lane = l_next;
+    // Splits with keys, as a wave-uniform bit mask (lanes >= S hold -inf).
+    const uint64_t live = __builtin_amdgcn_ballot_w64(l_lane != -INFINITY);
+    const T* base = o_part + r * S * kDcg + kE * lane;
+    uint32_t x[kChunk][kW];
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u)
+      if ((live >> u) & 1) load_words<T, kW>(base + static_cast<size_t>(u) * kDcg, x[u]);
+    if (r + 1 < r_end) l_next = lane < S ? lse_part[(r + 1) * S + lane] : -INFINITY;
+    float mx = l_lane;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    float acc[kE];
+#pragma unroll
+    for (int e = 0; e < kE; ++e) acc[e] = 0.f;
+    float sum = 0.f;
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      if ((live >> u) & 1) {
+        const float l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_lane), u));
+        const float wt = expf(l - mx);
+        sum += wt;
+#pragma unroll
+        for (int e = 0; e < kE; ++e) acc[e] += wt * word_elem<T>(x[u], e);
+      }
+    }
+    const float inv = live == 0 ? 0.f : 1.f / sum;
+    uint32_t y[kW];
+    if constexpr (sizeof(T) == 2) {
+#pragma unroll
+      for (int w = 0; w < kW; ++w)
+        y[w] = static_cast<uint32_t>(f32_to_bf16(acc[2 * w] * inv)) |
+               (static_cast<uint32_t>(f32_to_bf16(acc[2 * w + 1] * inv)) << 16);
+    } else {
+#pragma unroll
+      for (int w = 0; w < kW; ++w) y[w] = __float_as_uint(acc[w] * inv);
+    }
+    T* dst = o_lat + r * kDcg + kE * lane;
+    if constexpr (kW == 2) {
+      *reinterpret_cast<uint2*>(dst) = uint2{y[0], y[1]};
+    } else {
+#pragma unroll
+      for (int i = 0; i < kW / 4; ++i)
+        reinterpret_cast<uint4*>(dst)[i] = uint4{y[4 * i], y[4 * i + 1], y[4 * i + 2], y[4 * i + 3]};
+    }
+    if (lane == 0 && lse_out != nullptr) lse_out[r] = live == 0 ? -INFINITY : mx + logf(sum);
+  }
+}
+
+// Waves per SIMD that a many-row combine keeps resident, from its partial registers per
+// lane (64 words: about 105 VGPRs; 96: about 140; 128: about 170).
+constexpr int combine_rows_occupancy(int words) { return words <= 64 ? 4 : (words <= 96 ? 3 : 2); }
+
+// The many-row form, when the rows outnumber the waves the chip keeps resident (its
+// 1024 SIMDs times the occupancy above): then each wave takes rpw >= 2 rows.  Returns
+// false (nothing launched) when one round of waves covers the rows.
+template <typename T, int kDcg, int kChunk>
+bool launch_combine_rows(const T* o_part, const float* lse_part, T* o_lat, float* lse_out, int rows,
+                         int S, hipStream_t s) {
+  constexpr int kWords = kChunk * (kDcg / 64) * static_cast<int>(sizeof(T)) / 4;
+  constexpr int kResident = 1024 * combine_rows_occupancy(kWords);
+  if (rows <= kResident) return false;
+  const int rpw = (rows + kResident - 1) / kResident;
+  const int waves = (rows + rpw - 1) / rpw;
+  const dim3 grid((waves + 3) / 4);
+  combine_rows_kernel<T, kDcg, kChunk><<<grid, kThreads, 0, s>>>(o_part, lse_part, o_lat, lse_out, rows, S, rpw);
+  return true;
+}
+
 template <typename T, int kDcg>
 hipError_t launch_combine_vec(const T* o_part, const float* lse_part, T* o_lat, float* lse_out,
                               int rows, int S, hipStream_t s) {
   constexpr int kMax = combine_max_chunk<T, kDcg>();
+  bool done = false;
+  if (S <= 8)
+    done = launch_combine_rows<T, kDcg, 8>(o_part, lse_part, o_lat, lse_out, rows, S, s);
+  else if (S <= 16 && kMax >= 16)
+    done = launch_combine_rows<T, kDcg, 16>(o_part, lse_part, o_lat, lse_out, rows, S, s);
+  else if (S <= 24 && kMax >= 24)
+    done = launch_combine_rows<T, kDcg, (kMax >= 24 ? 24 : 8)>(o_part, lse_part, o_lat, lse_out, rows, S, s);
+  else if (S <= 32 && kMax >= 32)
+    done = launch_combine_rows<T, kDcg, (kMax >= 32 ? 32 : 8)>(o_part, lse_part, o_lat, lse_out, rows, S, s);
+  if (done) return hipGetLastError();
   const dim3 grid((rows + 3) / 4);
   if (S <= 8)
     combine_vec_kernel<T, kDcg, 8><<<grid, kThreads, 0, s>>>(o_part, lse_part, o_lat, lse_out, rows, S);

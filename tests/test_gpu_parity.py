@@ -333,11 +333,17 @@ def test_softmax_reference_moves(kind, case, mode, monkeypatch):
 
 
 @pytest.mark.parametrize("T,d_cg,S,dt", [(37, 512, 16, "bf16"), (9, 256, 70, "bf16"),
-                                         (5, 512, 3, "fp32")])
+                                         (5, 512, 3, "fp32"),
+                                         # more rows than resident waves: the many-row
+                                         # form (several rows per wave, empty splits not read)
+                                         (40, 512, 5, "bf16"), (25, 512, 17, "bf16"),
+                                         (33, 512, 30, "bf16"), (40, 256, 12, "bf16"),
+                                         (300, 512, 16, "fp32")])
 def test_combine_against_oracle_merge(T, d_cg, S, dt):
     """mla_combine alone on synthetic partials: a third of the splits empty (LSE = -inf,
-    partials NaN), one token with no keys at all, and split counts past one wave's 64
-    lanes; o_latent and the LSE against the oracle's fp64 merge."""
+    partials NaN), one token with no keys at all, split counts past one wave's 64 lanes,
+    and row counts (T x H) past the waves the chip keeps resident; o_latent and the LSE
+    against the oracle's fp64 merge."""
     H = 128 if dt == "bf16" else 16
     rng = np.random.default_rng(T * 1000 + S)
     tdt = torch.bfloat16 if dt == "bf16" else torch.float32
