@@ -101,6 +101,24 @@ def test_parity_small_mfma32(case, rope, kind, monkeypatch):
     assert np.max(np.abs(_f64(step.lse) - ref["lse"])) <= 2e-2
 
 
+@pytest.mark.parametrize("batch,mix", [(1, False), (16, False), (64, True), (65, True), (70, False)])
+@pytest.mark.parametrize("kind", ["mfma64", "mfma128", "mfma32-128", "mfma32-64"])
+def test_batch_sizes_around_the_wave_sequence_lookup(batch, mix, kind, monkeypatch):
+    """Batches of 1, 16, 64 (the largest whose sequence table one wave holds), 65 and 70
+    (the binary search over cu_q), with and without two-token sequences, on every MFMA
+    decode form; 16 one-token sequences with 64-head workgroups take the launch order
+    that puts a token's workgroups on one XCD."""
+    monkeypatch.setenv("MLA_KV_DECODE_KERNEL", kind)
+    cfg = _small("ragged_b64", batch=batch, seq_len_range=(1, 160), q_len_mix=mix)
+    print(f"batch {batch} q_len_mix={mix} kernel {kind}", flush=True)
+    w = wl.make_workload(cfg)
+    step = run_step(w, rope=True)
+    ref = oracle_for(w, rope=True)
+    assert_parity(_f64(step.out), ref["out"])
+    assert_parity(_f64(step.o_latent), ref["o_latent"], what="o_latent")
+    assert np.max(np.abs(_f64(step.lse) - ref["lse"])) <= 2e-2
+
+
 @pytest.mark.parametrize("splits", [1, 3, 8, 40])
 def test_split_count_invariance(splits):
     """Split count changes only rounding; empty splits (more splits than pages) are harmless."""
