@@ -87,6 +87,80 @@ up_v_mfma_kernel(const uint16_t* __restrict__ o_lat, const uint16_t* __restrict_
   }
 }
 
+// up_v with shared activation rows: one workgroup of 4 waves per (head h, 64 output
+// dims); wave w owns dims d0 = 64 x + 16 w .. +15, its W_UV slice in registers as above.
+// Each 16-row block of o_latent[t][h][:] is read from memory once per workgroup, into
+// LDS (rows padded by 16 bytes so the 16 rows of a fragment read start in different
+// banks; two buffers, the next block requested while the current one is multiplied), and
+// every wave takes its A fragments from there.  The rows of a head are then fetched
+// d_hc / 64 times rather than d_hc / 16 times, which is what bounds up_v at large T.
+constexpr int kUpCols = 64;
+
+template <int kSteps>  // d_cg / 32
+__global__ void __launch_bounds__(256)
+up_v_lds_kernel(const uint16_t* __restrict__ o_lat, const uint16_t* __restrict__ w_uv,
+                uint16_t* __restrict__ out, int T, int H, int d_hc) {
+  constexpr int d_cg = kSteps * 32;
+  constexpr int kRowBytes = d_cg * 2 + 16;
+  constexpr int kBlockBytes = 16 * kRowBytes;
+  constexpr int kChunks = d_cg / 8;                 // 16-byte pieces of one row
+  constexpr int kPerThread = 16 * kChunks / 256;    // pieces of a block per thread
+  static_assert(kPerThread * 256 == 16 * kChunks, "a block splits evenly over 256 threads");
+  __shared__ __attribute__((aligned(16))) char buf[2 * kBlockBytes];
+  const HeadTile ht = head_tile(d_hc / kUpCols, H);
+  const int h = ht.head;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, j = lane & 15;
+  const int d0 = ht.x * kUpCols + 16 * wave;
+  const size_t astride = static_cast<size_t>(H) * d_cg;
+  const uint16_t* abase = o_lat + static_cast<size_t>(h) * d_cg;
+  // Piece i of this thread: block row (tid + 256 i) / kChunks, chunk (tid + 256 i) % kChunks.
+  bf16x8 stage[kPerThread];
+  auto fetch = [&](int t0) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int pc = tid + 256 * i, row = pc / kChunks, ch = pc - row * kChunks;
+      const int t = t0 + row;
+      const bf16x8 v = *reinterpret_cast<const bf16x8*>(abase + static_cast<size_t>(t < T ? t : 0) * astride + ch * 8);
+      stage[i] = t < T ? v : bf16x8{};
+    }
+  };
+  auto put = [&](int bi) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int pc = tid + 256 * i, row = pc / kChunks, ch = pc - row * kChunks;
+      *reinterpret_cast<bf16x8*>(buf + bi * kBlockBytes + row * kRowBytes + ch * 16) = stage[i];
+    }
+  };
+  fetch(0);
+  const uint16_t* wrow = w_uv + (static_cast<size_t>(h) * d_hc + d0 + j) * d_cg + 8 * g;
+  bf16x8 b[kSteps];
+#pragma unroll
+  for (int k = 0; k < kSteps; ++k) b[k] = *reinterpret_cast<const bf16x8*>(wrow + 32 * k);
+  put(0);
+  __syncthreads();
+  int cur = 0;
+  for (int t0 = 0; t0 < T; t0 += 16) {
+    const bool more = t0 + 16 < T;
+    if (more) fetch(t0 + 16);
+    // A fragment, K-step k: row j, columns 32 k + 8 g .. +7.
+    const char* arow = buf + cur * kBlockBytes + j * kRowBytes + 16 * g;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < kSteps; ++k)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(arow + 64 * k), b[k],
+                                                    acc, 0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + 4 * g + i;
+      if (t < T) out[(static_cast<size_t>(t) * H + h) * d_hc + d0 + j] = f32_to_bf16(acc[i]);
+    }
+    if (more) put(cur ^ 1);  // the other buffer: every wave left it at the last barrier
+    __syncthreads();
+    cur ^= 1;
+  }
+}
+
 // ---------------------------------------------------------------- absorb
 // One workgroup (4 waves) per (head h, 64 latent columns c0..c0+63).  The
 // [d_hc x 64] slice of W_UK[h] is staged in LDS (rows padded to 144 B) and read
@@ -162,10 +236,18 @@ bool absorb_mfma_supported(int d_hc, int d_cg, bool bf16) {
 
 hipError_t launch_up_v_mfma(const void* o_lat, const void* w_uv, void* out, int T, int H, int d_hc,
                             int d_cg, hipStream_t s) {
-  const dim3 grid((d_hc / 16) * H);
   const auto* o = static_cast<const uint16_t*>(o_lat);
   const auto* wt = static_cast<const uint16_t*>(w_uv);
   auto* dst = static_cast<uint16_t*>(out);
+  if (d_hc % kUpCols == 0) {
+    const dim3 grid_l((d_hc / kUpCols) * H);
+    if (d_cg == 512)
+      up_v_lds_kernel<16><<<grid_l, 256, 0, s>>>(o, wt, dst, T, H, d_hc);
+    else
+      up_v_lds_kernel<8><<<grid_l, 256, 0, s>>>(o, wt, dst, T, H, d_hc);
+    return hipGetLastError();
+  }
+  const dim3 grid((d_hc / 16) * H);
   if (d_cg == 512)
     up_v_mfma_kernel<16><<<grid, 64, 0, s>>>(o, wt, dst, T, H, d_hc);
   else
