@@ -175,18 +175,34 @@ __global__ void __launch_bounds__(256)
 absorb_mfma_kernel(const uint16_t* __restrict__ q_c, const uint16_t* __restrict__ w_uk,
                    uint16_t* __restrict__ q_abs, int T, int H, int d_cg) {
   constexpr int d_hc = kSteps * 32;
+  // Query rows: each 16-row block of q_c[t][h][:] is read once per workgroup into LDS
+  // (rows padded by 16 bytes, two buffers) and shared by the 4 waves, instead of once
+  // per wave; one 16-byte piece per thread.
+  constexpr int kARowBytes = d_hc * 2 + 16;
+  constexpr int kABlockBytes = 16 * kARowBytes;
+  constexpr int kAChunks = d_hc / 8;
+  static_assert(16 * kAChunks == 256, "one piece of a query block per thread");
   __shared__ __attribute__((aligned(16))) char tile[d_hc * kAbsRowBytes];
+  __shared__ __attribute__((aligned(16))) char abuf[2 * kABlockBytes];
   const HeadTile ht = head_tile(d_cg / kAbsCols, H);
   const int h = ht.head;
   const int c0 = ht.x * kAbsCols;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, j = lane & 15;
+  const uint16_t* abase = q_c + static_cast<size_t>(h) * d_hc;
+  const size_t astride = static_cast<size_t>(H) * d_hc;
+  const int a_row = tid / kAChunks, a_ch = tid - a_row * kAChunks;
+  auto fetch = [&](int t0) {
+    const int t = t0 + a_row;
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(abase + static_cast<size_t>(t < T ? t : 0) * astride + a_ch * 8);
+    return t < T ? v : bf16x8{};
+  };
+  auto put = [&](int bi, const bf16x8& v) {
+    *reinterpret_cast<bf16x8*>(abuf + bi * kABlockBytes + a_row * kARowBytes + a_ch * 16) = v;
+  };
   // The first block's query rows are requested before the weight tile, so both
   // round trips overlap.
-  const uint16_t* abase = q_c + static_cast<size_t>(h) * d_hc + 8 * g;
-  const size_t astride = static_cast<size_t>(H) * d_hc;
-  bf16x8 a[kSteps];
-  load_rows<kSteps>(abase, astride, j, T, a);
+  bf16x8 staged = fetch(0);
   // Stage the tile: thread -> (row d = tid/8 + 32r, chunk tid%8 of 8 columns).
   const uint16_t* wsrc = w_uk + static_cast<size_t>(h) * d_hc * d_cg + c0;
 #pragma unroll
@@ -195,6 +211,7 @@ absorb_mfma_kernel(const uint16_t* __restrict__ q_c, const uint16_t* __restrict_
     *reinterpret_cast<bf16x8*>(tile + d * kAbsRowBytes + ch * 16) =
         *reinterpret_cast<const bf16x8*>(wsrc + static_cast<size_t>(d) * d_cg + ch * 8);
   }
+  put(0, staged);
   __syncthreads();
   // B fragments: K-step k covers d = 32k + 8g + {0..3} (first read) and {4..7} (second).
   const uint32_t tile_base = static_cast<uint32_t>(
@@ -211,16 +228,25 @@ absorb_mfma_kernel(const uint16_t* __restrict__ q_c, const uint16_t* __restrict_
     b[k] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   }
   const int cout = c0 + 16 * wave + j;
+  int cur = 0;
   for (int t0 = 0; t0 < T; t0 += 16) {
+    const bool more = t0 + 16 < T;
+    if (more) staged = fetch(t0 + 16);
+    // A fragment, K-step k: row j, dims 32 k + 8 g .. +7.
+    const char* arow = abuf + cur * kABlockBytes + j * kARowBytes + 16 * g;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int k = 0; k < kSteps; ++k) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[k], b[k], acc, 0, 0, 0);
-    if (t0 + 16 < T) load_rows<kSteps>(abase, astride, t0 + 16 + j, T, a);
+    for (int k = 0; k < kSteps; ++k)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(arow + 64 * k), b[k],
+                                                    acc, 0, 0, 0);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = t0 + 4 * g + i;
       if (t < T) q_abs[(static_cast<size_t>(t) * H + h) * d_cg + cout] = f32_to_bf16(acc[i]);
     }
+    if (more) put(cur ^ 1, staged);  // the other buffer: every wave left it at the last barrier
+    __syncthreads();
+    cur ^= 1;
   }
 }
 
