@@ -260,10 +260,13 @@ def test_zero_queries_is_a_no_op():
 
 @pytest.mark.parametrize("T", [1, 16, 37, 96])
 @pytest.mark.parametrize("d_cg", [512, 256])
-def test_projections_against_reference(T, d_cg):
-    """mla_absorb_q and mla_up_v alone, on the MFMA shapes and a ragged row count."""
-    rng = np.random.default_rng(T + d_cg)
-    H, d_hc = 128, 128
+@pytest.mark.parametrize("d_hc", [128, 80])
+def test_projections_against_reference(T, d_cg, d_hc):
+    """mla_absorb_q and mla_up_v alone, on the MFMA shapes and a ragged row count.  With
+    d_hc = 128 both take their LDS-staged MFMA kernels; with d_hc = 80 (not a multiple of
+    64) up_v takes the one-wave-per-16-dims MFMA kernel and absorb the generic one."""
+    rng = np.random.default_rng(T + d_cg + d_hc)
+    H = 128
     q_c = wl.round_bf16(rng.standard_normal((T, H, d_hc)).astype(np.float32))
     w = wl.round_bf16((rng.standard_normal((H, d_hc, d_cg)) / np.sqrt(d_cg)).astype(np.float32))
     o = wl.round_bf16(rng.standard_normal((T, H, d_cg)).astype(np.float32))
