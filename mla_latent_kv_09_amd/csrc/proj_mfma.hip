@@ -36,6 +36,9 @@ __device__ __forceinline__ HeadTile head_tile(int nx, int n_heads) {
 }
 
 // ---------------------------------------------------------------- up_v
+// Two forms.  up_v_lds_kernel (below) shares each block of activation rows across a
+// workgroup through LDS and is used whenever d_hc is a multiple of 64; this one, for the
+// other shapes, loads its rows itself.
 // One wave per (head h, 16 output dims d0..d0+15).  B operand = W_UV[h][d][c]:
 // lane (n = d0 + l%16, k = 8*(l/16) + e) reads 16 contiguous bytes of row d, so
 // the wave's 16 x d_cg weight slice goes straight from HBM into registers (once).
