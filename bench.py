@@ -46,7 +46,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "MLA decode attention TFLOP/s + latent-KV GB/s (% MI355X roofline), seqs/s"
-HEADLINE = "dsv3_b16_l4096"
+HEADLINE = "ragged_b64"
 HBM_PEAK_GBPS = 8000.0
 MALL_BYTES = 256 << 20  # Infinity Cache of one MI355X
 BF16_PEAK_TFLOPS = 2500.0
@@ -359,7 +359,8 @@ def main():
     peak_f = BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else FP32_PEAK_TFLOPS
     t_hbm = kv_bytes / (HBM_PEAK_GBPS * 1e9)
     t_mfma = att / (peak_f * 1e12)
-    kernel = decode_kernel_name(cfg, int(w.total_q), S, mla)
+    kernel = decode_kernel_name(cfg, int(w.total_q), S,
+                                torch.cuda.get_device_properties(0).multi_processor_count)
     traffic = measured_traffic(kernel, cfg.name, S)
     if t_hbm >= t_mfma:
         achieved = kv_bytes / (dec * 1e-3) / 1e9
@@ -440,7 +441,7 @@ def measure_append(args, w, torch, harness, mla, wl, steps, runner, timed, reps,
     return res
 
 
-def decode_kernel_name(cfg, total_q, num_splits, mla):
+def decode_kernel_name(cfg, total_q, num_splits, cu_count=256):
     """The decode kernel the library dispatches for this shape (same rule as the library:
     MLA_KV_DECODE_KERNEL = generic / mfma / mfma128 / mfma64 / mfma32[-128|-64]; by default, for one
     latent group, the 32x32x16 kernel when one workgroup per (token, split) fills the
@@ -452,7 +453,10 @@ def decode_kernel_name(cfg, total_q, num_splits, mla):
         return "decode_generic_kernel"
     if cfg.groups != 1 or choice in ("mfma128", "mfma64"):
         return "decode_mfma_kernel"
-    if choice.startswith("mfma32") or mla.head_split(total_q, num_splits, cfg.groups) == 1:
+    # The library's rule for one latent group: two 64-head workgroups per (token, split)
+    # when 2 * total_q * num_splits fits the compute units.
+    head_split = 2 if 2 * total_q * num_splits <= cu_count else 1
+    if choice.startswith("mfma32") or head_split == 1:
         return "decode_m32_kernel"
     return "decode_mfma_kernel"
 

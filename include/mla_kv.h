@@ -13,7 +13,8 @@
  *
  * plus mla_rope_table (the fp32 cos/sin table the decode call reads),
  * mla_append_kv (writes the new tokens' latent rows, with their rotated RoPE keys,
- * into the paged cache before the decode reads them) and mla_status_string.
+ * into the paged cache before the decode reads them), mla_decode_plan (host-only
+ * split plan) and mla_status_string.
  *
  * Sources, cited by page address and section:
  *   P3 = www.nxmr.cn/news/151634  (MLA operators: absorption, paged latent cache)
@@ -26,7 +27,11 @@
  *   the caller.  The library never allocates, frees or keeps a pointer after a
  *   call returns, and never synchronizes.  Work is enqueued on `stream`
  *   (a hipStream_t; NULL = the default stream) and runs asynchronously.
- *   Calls keep no global state and may be issued from several host threads.
+ *   Calls may be issued from several host threads.  The only state kept between
+ *   calls is filled once per device and is safe under concurrent first calls: the
+ *   device's compute-unit count and each decode kernel's dynamic-LDS limit.  The
+ *   decode-kernel override MLA_KV_DECODE_KERNEL is read from the environment on
+ *   every mla_decode_paged call.
  * - Every pointer must be 16-byte aligned (the pages' "misaligned address"
  *   failure of a vectorized gather, P3 §5).
  * - dtype selects the storage type of the non-float32 tensors: MLA_DTYPE_BF16
@@ -193,7 +198,11 @@ int mla_append_kv(const void* c_kv_new, const void* k_r_new, void* kv_cache,
                   int d_c, int d_R, int page_size, int dtype, void* stream);
 
 /*
- * mla_combine -- merge the split partials by their log-sum-exp:
+ * mla_combine -- merge the split partials by their log-sum-exp.  No page describes
+ * splitting the keys or merging partial results; this step is the library's own
+ * reading, derived from the softmax definition alone (the softmax over the union of
+ * disjoint key sets, written through each set's normaliser; P2 §2.5 names softmax
+ * attention):
  *   M = max_s lse[s],  w_s = exp(lse[s] - M),
  *   o_latent = sum_s w_s o_part[s] / sum_s w_s,  lse = M + log(sum_s w_s).
  * A row whose splits are all empty gets o_latent = 0 and lse = -INFINITY.
@@ -223,6 +232,34 @@ int mla_up_v(const void* o_latent, const void* w_uv, void* out,
  * (0 on bad sizes or dtype): T*H*num_splits*(d_cg*elem + 4), elem = 2 for bf16. */
 size_t mla_decode_workspace_bytes(int total_q, int heads, int groups, int d_c, int num_splits,
                                   int dtype);
+
+/*
+ * mla_decode_plan -- host-only choice of the split plan (num_splits, pages_per_split) for
+ * mla_decode_paged.  The pages give no split plan; this is the library's own dispatch
+ * model.  It touches no GPU, allocates nothing and keeps no state.
+ *
+ *   seq_lens  [batch] int32, HOST memory: keys of each sequence (incl. its new tokens)
+ *   q_lens    [batch] int32, HOST memory: query rows of each sequence
+ *   groups    latent groups of the decode (1 = MLA)
+ *   cu_count  compute units of the device the decode will run on (256 on an MI355X),
+ *             at most 4096
+ *   num_splits, pages_per_split  outputs
+ *
+ * Model: a sequence of L keys has max(1, ceil(L / 64)) pages; a split of c pages costs
+ * 2.5 + c page units (0.2 when it holds no page); the grid is launched split-fastest and
+ * workgroup L goes to XCD L mod 8, whose CUs (cu_count / 8 of them) each take the next
+ * workgroup when free.  Candidates are the shortest split length for each split count
+ * of the longest sequence (at most 256 splits) and the lengths that give k workgroups
+ * per CU (k = 1 .. 16), thinned to the 64 longest plus every (n/32)-th when there are
+ * more than 96.  The plan is the candidate that finishes first, ties going to the fewer
+ * workgroups and then the shorter split.  With groups == 1 a plan of at most 6 pages per
+ * split is doubled in length when 2 * (sum of q_lens) * (the halved split count) <=
+ * cu_count, so the decode runs two 64-head workgroups per (token, split).
+ * Returns MLA_ERR_NULL for a NULL pointer, MLA_ERR_DIM for batch, groups or cu_count
+ * <= 0 or a negative length, MLA_ERR_UNSUPPORTED for cu_count > 4096.
+ */
+int mla_decode_plan(const int32_t* seq_lens, const int32_t* q_lens, int batch, int groups,
+                    int cu_count, int* num_splits, int* pages_per_split);
 
 /* Static text for a status code (never NULL). */
 const char* mla_status_string(int status);

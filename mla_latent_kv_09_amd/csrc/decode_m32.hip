@@ -124,7 +124,7 @@ __device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
                : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(sbase)
-               : "memory");
+               : "memory", "m0");
 }
 
 // Copy `row` (0..17) of this wave's share of a page into stage `c_base`: rows 0..15 are
@@ -164,36 +164,16 @@ decode_m32_kernel(DecodeArgs a) {
   // time, and that XCD's L2 serves the later reads of each page.
   SeqIndex ix;
   ix.load(a.cu_q, a.seq_lens, a.batch);
-  int t, split, h2 = 0;
+  Unit u;
   if constexpr (HS == 2) {
-    // Blocks of 8 (token, split) pairs take 16 consecutive workgroups: half h2 of pair
-    // 8k + i is workgroup 16k + 8 h2 + i (in a last block of r < 8 pairs, 16k + r h2 + i),
-    // so the two halves of a pair, which stream the same pages, share one XCD's L2.
-    const int L = static_cast<int>(blockIdx.x), kb = L >> 4, base = kb * 8;
-    const int r8 = min(8, a.total_q * S - base), off = L - 16 * kb;
-    const int pair = base + off % r8;
-    h2 = off / r8;
-    t = pair / S;
-    split = pair - t * S;
+    u = unit_pair_blocks(static_cast<int>(blockIdx.x), S, a.total_q);
   } else {
     const int L = static_cast<int>(blockIdx.x);
     const int b = ix.find(L / S);
-    const int q0 = ix.start(b), nq = ix.stop(b) - q0;
-    const int u = L - q0 * S;
-    if (nq <= 1) {
-      t = q0 + u / S;
-      split = u - (u / S) * S;
-    } else {
-      const int blk = u / (8 * nq), r = u - blk * 8 * nq;
-      const int k = min(8, S - 8 * blk);
-      t = q0 + r / k;
-      split = 8 * blk + (r - (r / k) * k);
-    }
-    if (t < 0 || t >= a.total_q || split < 0 || split >= S) {  // malformed cu_q: identity
-      t = L / S;
-      split = L - t * S;
-    }
+    const int q0 = ix.start(b);
+    u = unit_m32(L, S, q0, ix.stop(b) - q0, a.total_q);
   }
+  const int t = u.t, split = u.split, h2 = u.half;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int n = lane & 31, h = lane >> 5;  // head within the wave, lane half
@@ -549,13 +529,10 @@ bool decode_m32_supported(const DecodeArgs& a, bool bf16) {
 
 template <int HS>
 hipError_t launch_decode_m32_k(const DecodeArgs& a, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_m32_kernel<HS>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_limit_set{0};
+  const hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(decode_m32_kernel<HS>), kLdsBytes,
+                                        lds_limit_set);
+  if (e != hipSuccess) return e;
   const dim3 grid(a.total_q * a.num_splits * HS);
   decode_m32_kernel<HS><<<grid, kThreads, kLdsBytes, s>>>(a);
   return hipGetLastError();

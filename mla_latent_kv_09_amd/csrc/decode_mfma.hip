@@ -134,7 +134,7 @@ __device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                :
                : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(sbase)
-               : "memory");
+               : "memory", "m0");
 }
 
 // This wave's share of one page in LDS stage `c_base`: latent rows 8w .. 8w+7 (one
@@ -223,24 +223,9 @@ decode_mfma_kernel(DecodeArgs a) {
   // their pages from the same L2.  Otherwise blocks of 8 pairs take 16 consecutive
   // workgroups: half h2 of pair 8k + i is workgroup 16k + 8 h2 + i (in a last block of
   // r < 8 pairs, 16k + r h2 + i), so the halves of a pair in a full block share an XCD.
-  int t, split, h2 = 0;
-  if constexpr (HS == 1) {
-    t = static_cast<int>(blockIdx.x) / S;
-    split = static_cast<int>(blockIdx.x) - t * S;
-  } else if (a.total_q % 8 == 0) {
-    const int L = static_cast<int>(blockIdx.x), x = L & 7, r = L >> 3;
-    const int k = r / (2 * S), rem = r - k * 2 * S;
-    t = x + 8 * k;
-    split = rem >> 1;
-    h2 = rem & 1;
-  } else {
-    const int L = static_cast<int>(blockIdx.x), kb = L >> 4, base = kb * 8;
-    const int r = min(8, a.total_q * S - base), off = L - 16 * kb;
-    const int pair = base + off % r;
-    h2 = off / r;
-    t = pair / S;
-    split = pair - t * S;
-  }
+  const Unit u = HS == 1 ? unit_split_fastest(static_cast<int>(blockIdx.x), S)
+                         : unit_mfma_half(static_cast<int>(blockIdx.x), S, a.total_q);
+  const int t = u.t, split = u.split, h2 = u.half;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, kept in an SGPR
   const int g = lane >> 4, j = lane & 15;   // 16-lane group, position in group
@@ -556,13 +541,10 @@ bool decode_mfma_supported(const DecodeArgs& a, bool bf16) {
 
 template <int G, int HS>
 hipError_t launch_decode_mfma_k(const DecodeArgs& a, hipStream_t s) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(decode_mfma_kernel<G, HS>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
+  static std::atomic<uint64_t> lds_limit_set{0};
+  const hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(decode_mfma_kernel<G, HS>), kLdsBytes,
+                                        lds_limit_set);
+  if (e != hipSuccess) return e;
   const dim3 grid(a.total_q * a.num_splits * HS);
   decode_mfma_kernel<G, HS><<<grid, kThreads, kLdsBytes, s>>>(a);
   return hipGetLastError();

@@ -6,6 +6,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "mla_internal.h"
 #include "mla_kv.h"
 
@@ -54,18 +56,22 @@ DecodeKernel decode_kernel_choice() {
   return DecodeKernel::kAuto;
 }
 
-// Compute units of the current device, looked up once per device (0 if unknown).
+// Compute units of the current device, looked up once per device (0 if unknown).  The
+// cache is atomic: concurrent first calls may both query the device and store the same
+// value.
 int cu_count_of_current_device() {
   constexpr int kMaxDevices = 64;
-  static int cached[kMaxDevices] = {};
+  static std::atomic<int> cached[kMaxDevices] = {};
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
-  if (cached[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    cached[dev] = n;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < kMaxDevices) {
+    const int c = cached[dev].load(std::memory_order_relaxed);
+    if (c != 0) return c;
   }
-  return cached[dev];
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (dev < kMaxDevices) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
 }
 
 }  // namespace
@@ -138,6 +144,7 @@ int mla_decode_paged(const void* q_abs, const void* q_r, const void* kv_cache,
   if ((st = check_heads(heads, groups, d_c)) != MLA_OK) return st;
   if (page_size != MLA_PAGE_SIZE || num_splits > kMaxSplits) return MLA_ERR_UNSUPPORTED;
   if (static_cast<long long>(total_q) * num_splits > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+  if (static_cast<long long>(max_pages_per_seq) * page_size > INT32_MAX) return MLA_ERR_UNSUPPORTED;
   if (d_c / groups > kMaxGenericCols || d_R > kMaxGenericRope) return MLA_ERR_UNSUPPORTED;
   if ((rope_cos == nullptr) != (rope_sin == nullptr)) return MLA_ERR_NULL;
   if (rope_cos != nullptr && rope_max_pos <= 0) return MLA_ERR_DIM;
@@ -171,7 +178,9 @@ int mla_decode_paged(const void* q_abs, const void* q_r, const void* kv_cache,
   a.d_R = d_R;
   a.page_size = page_size;
   a.num_splits = num_splits;
-  a.pages_per_split = pages_per_split;
+  // A split longer than the page table covers every page of a sequence: any larger
+  // value gives the same plan.
+  a.pages_per_split = pages_per_split < max_pages_per_seq ? pages_per_split : max_pages_per_seq;
   a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(d_hc + d_R));
   a.causal = causal != 0;
   const bool bf16 = dtype == MLA_DTYPE_BF16;

@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "mla_index.h"
+
 namespace mla {
 
 constexpr float kLog2e = 1.4426950408889634f;
@@ -27,45 +29,6 @@ __device__ __forceinline__ float load_elem(const uint16_t* p, size_t i) { return
 __device__ __forceinline__ float load_elem(const float* p, size_t i) { return p[i]; }
 __device__ __forceinline__ void store_elem(uint16_t* p, size_t i, float v) { p[i] = f32_to_bf16(v); }
 __device__ __forceinline__ void store_elem(float* p, size_t i, float v) { p[i] = v; }
-
-// Sequence owning packed query row t: the largest b with cu_q[b] <= t.
-__device__ __forceinline__ int find_seq(const int32_t* __restrict__ cu_q, int batch, int t) {
-  int lo = 0, hi = batch - 1;
-  while (lo < hi) {
-    int mid = (lo + hi + 1) >> 1;
-    if (cu_q[mid] <= t) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
-// Where query row t sits and which keys split s of its sequence covers.
-struct QueryWork {
-  int b;       // sequence
-  int L;       // keys of the sequence (clamped to the page-table capacity)
-  int pos;     // absolute position of the query
-  int k0, k1;  // key range [k0, k1) of this split, already clipped to the visible keys
-};
-
-// The key range of split `split` for query row t of sequence b, which starts at query
-// row q0, has q_len query rows and L_raw keys.
-__device__ __forceinline__ QueryWork split_work(int b, int q0, int q_len, int L_raw, int t, int split,
-                                               int num_splits, int pages_per_split, int page_size,
-                                               int max_pages, int causal) {
-  QueryWork w;
-  w.b = b;
-  const int cap = max_pages * page_size;
-  const int L = L_raw < 0 ? 0 : (L_raw > cap ? cap : L_raw);
-  w.L = L;
-  w.pos = L - q_len + (t - q0);
-  int n_vis = causal ? min(L, w.pos + 1) : L;
-  if (n_vis < 0) n_vis = 0;
-  const int n_pages = (L + page_size - 1) / page_size;
-  const int per_split = pages_per_split > 0 ? pages_per_split
-                                            : (n_pages + num_splits - 1) / num_splits;
-  w.k0 = split * per_split * page_size;
-  w.k1 = split == num_splits - 1 ? n_vis : min((split + 1) * per_split * page_size, n_vis);
-  return w;
-}
 
 __device__ __forceinline__ QueryWork query_work(const int32_t* __restrict__ cu_q,
                                                 const int32_t* __restrict__ seq_lens, int batch,

@@ -5,7 +5,23 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace mla {
+
+// Raise kernel `fn`'s dynamic-LDS limit to `bytes` on the current device, once per
+// device.  `done` holds one bit per device id below 64; concurrent first calls may both
+// set the attribute, which is idempotent.  Devices 64 and up set it on every call.
+inline hipError_t ensure_lds_limit(const void* fn, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t{1} << dev) : 0;
+  if (bit != 0 && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 struct DecodeArgs {
   const void* q_abs;

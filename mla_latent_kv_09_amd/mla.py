@@ -10,8 +10,6 @@ has not been built.
 from __future__ import annotations
 
 import ctypes
-import heapq
-import math
 import os
 from typing import Optional
 
@@ -24,7 +22,7 @@ DTYPE_FP32 = 1
 PAGE_SIZE = 64
 
 EXPORTED = ("mla_absorb_q", "mla_rope_table", "mla_decode_paged", "mla_combine", "mla_up_v",
-            "mla_append_kv", "mla_decode_workspace_bytes", "mla_status_string")
+            "mla_append_kv", "mla_decode_workspace_bytes", "mla_decode_plan", "mla_status_string")
 
 _lib = None
 
@@ -54,10 +52,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_append_kv.argtypes = [P] * 8 + [I] * 9 + [P]
     lib.mla_decode_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.mla_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.mla_decode_plan.argtypes = [P, P, I, I, I, P, P]
     lib.mla_status_string.argtypes = [I]
     lib.mla_status_string.restype = ctypes.c_char_p
     for name in ("mla_absorb_q", "mla_rope_table", "mla_decode_paged", "mla_combine", "mla_up_v",
-                 "mla_append_kv"):
+                 "mla_append_kv", "mla_decode_plan"):
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -99,6 +98,33 @@ def _dev(*ts: Optional[torch.Tensor]) -> None:
             raise ValueError("tensors must be contiguous")
 
 
+def _expect(name: str, t: Optional[torch.Tensor], shape, dtype) -> None:
+    """A caller-supplied buffer must have exactly this shape and dtype."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _rope_pair(rope: Optional[tuple], d_R: int, device) -> tuple:
+    """(cos, sin, max_pos) of a RoPE table pair: float32 [max_pos, d_R/2] each, on the
+    device of the other tensors, or (None, None, 0) for no rotation."""
+    if rope is None:
+        return None, None, 0
+    cos, sin = rope
+    if cos is None or sin is None:
+        raise ValueError("rope must be a (cos, sin) pair of tables")
+    if cos.dim() != 2 or cos.shape[1] != d_R // 2 or cos.shape[0] < 1:
+        raise ValueError(f"rope tables must be [max_pos, {d_R // 2}], got {tuple(cos.shape)}")
+    _expect("rope sin table", sin, cos.shape, torch.float32)
+    _expect("rope cos table", cos, cos.shape, torch.float32)
+    if cos.device != device or sin.device != device:
+        raise ValueError("rope tables must live on the device of the other tensors")
+    return cos, sin, int(cos.shape[0])
+
+
 def absorb_q(q_c: torch.Tensor, w_uk: torch.Tensor, q_abs: Optional[torch.Tensor] = None, *,
              groups: int = 1, stream=None) -> torch.Tensor:
     """q_abs[t,h,:] = q_c[t,h,:] @ w_uk[h]; q_c [T,H,d_hc], w_uk [H,d_hc,d_c/G]."""
@@ -108,6 +134,7 @@ def absorb_q(q_c: torch.Tensor, w_uk: torch.Tensor, q_abs: Optional[torch.Tensor
         raise ValueError("w_uk must be [H, d_hc, d_c/G] with q_c's dtype")
     if q_abs is None:
         q_abs = torch.empty((T, H, d_cg), dtype=q_c.dtype, device=q_c.device)
+    _expect("q_abs", q_abs, (T, H, d_cg), q_c.dtype)
     _dev(q_c, w_uk, q_abs)
     _check("mla_absorb_q", load().mla_absorb_q(
         _ptr(q_c), _ptr(w_uk), _ptr(q_abs), T, H, groups, d_hc, d_cg * groups, _dtype_code(q_c),
@@ -154,8 +181,7 @@ def decode_paged(q_abs, q_r, kv_cache, page_table, seq_lens, cu_q, o_part, lse_p
         raise ValueError("seq_lens must be [B] and cu_q [B+1]")
     if q_r.dtype != q_abs.dtype or kv_cache.dtype != q_abs.dtype:
         raise TypeError("q_abs, q_r and kv_cache must share the storage dtype")
-    cos, sin = rope if rope is not None else (None, None)
-    rope_max_pos = 0 if cos is None else cos.shape[0]
+    cos, sin, rope_max_pos = _rope_pair(rope, d_R, q_abs.device)
     _dev(q_abs, q_r, kv_cache, page_table, seq_lens, cu_q, o_part, lse_part, cos, sin)
     _check("mla_decode_paged", load().mla_decode_paged(
         _ptr(q_abs), _ptr(q_r), _ptr(kv_cache), _ptr(page_table), _ptr(seq_lens), _ptr(cu_q),
@@ -182,8 +208,7 @@ def append_kv(c_kv_new, k_r_new, kv_cache, page_table, seq_lens, cu_q, *,
             raise TypeError(f"expected int32, got {t.dtype}")
     if seq_lens.shape != (B,) or cu_q.shape != (B + 1,):
         raise ValueError("seq_lens must be [B] and cu_q [B+1]")
-    cos, sin = rope if rope is not None else (None, None)
-    rope_max_pos = 0 if cos is None else cos.shape[0]
+    cos, sin, rope_max_pos = _rope_pair(rope, d_R, kv_cache.device)
     _dev(c_kv_new, k_r_new, kv_cache, page_table, seq_lens, cu_q, cos, sin)
     _check("mla_append_kv", load().mla_append_kv(
         _ptr(c_kv_new), _ptr(k_r_new), _ptr(kv_cache), _ptr(page_table), _ptr(seq_lens),
@@ -198,6 +223,9 @@ def combine(o_part, lse_part, o_latent=None, lse_out=None, *, dtype=torch.bfloat
         o_latent = torch.empty((T, H, d_cg), dtype=dtype, device=o_part.device)
     if o_part.dtype != o_latent.dtype or lse_part.dtype != torch.float32:
         raise TypeError("o_part must share o_latent's dtype and lse_part must be float32")
+    _expect("lse_part", lse_part, (T, H, S), torch.float32)
+    _expect("o_latent", o_latent, (T, H, d_cg), o_part.dtype)
+    _expect("lse_out", lse_out, (T, H), torch.float32)
     _dev(o_part, lse_part, o_latent, lse_out)
     _check("mla_combine", load().mla_combine(
         _ptr(o_part), _ptr(lse_part), _ptr(o_latent), _ptr(lse_out), T, H, 1, d_cg, S,
@@ -213,6 +241,7 @@ def up_v(o_latent, w_uv, out=None, *, groups: int = 1, stream=None):
         raise ValueError("w_uv must be [H, d_hc, d_c/G] with o_latent's dtype")
     if out is None:
         out = torch.empty((T, H, d_hc), dtype=o_latent.dtype, device=o_latent.device)
+    _expect("out", out, (T, H, d_hc), o_latent.dtype)
     _dev(o_latent, w_uv, out)
     _check("mla_up_v", load().mla_up_v(
         _ptr(o_latent), _ptr(w_uv), _ptr(out), T, H, groups, d_hc, d_cg * groups,
@@ -220,83 +249,18 @@ def up_v(o_latent, w_uv, out=None, *, groups: int = 1, stream=None):
     return out
 
 
-# Cost of one split in units of one page (streaming 72 KB and computing 128 heads
-# over it): a fixed part for the prologue (queries fetched, first page in flight) and
-# the epilogue (bf16 partial written, 128 KB), measured at about 2.5 pages on MI355X,
-# plus one unit per page.  A split with no keys exits at once.
-SPLIT_OVERHEAD_PAGES = 2.5
-EMPTY_SPLIT_PAGES = 0.2
-XCDS = 8
-
-
-def plan_makespan(pages, q_lens, pages_per_split: int, cu_count: int = 256) -> float:
-    """Finish time, in page units, of the decode grid under the cost model above.  The
-    grid is launched in split-fastest order (workgroup L = token * S + split); the
-    dispatcher deals workgroup L to XCD L mod 8, and each XCD hands its workgroups to
-    the first of its CUs to come free, one workgroup per CU at a time."""
-    n_splits = max(math.ceil(p / pages_per_split) for p in pages)
-    per_xcd = max(1, cu_count // XCDS)
-    free = [[0.0] * per_xcd for _ in range(XCDS)]
-    wg = 0
-    for p, n in zip(pages, q_lens):
-        for _ in range(n):
-            for y in range(n_splits):
-                work = min(pages_per_split, p - y * pages_per_split)
-                cost = SPLIT_OVERHEAD_PAGES + work if work > 0 else EMPTY_SPLIT_PAGES
-                f = free[wg % XCDS]
-                heapq.heapreplace(f, f[0] + cost)
-                wg += 1
-    return max(max(f) for f in free)
-
-
-# Longest split (pages) for which two 64-head workgroups per (token, split) pay off: the
-# half-head workgroups run a page at about 0.66 of a full page's time, so twice the
-# pages cost about 1.3x; in exchange the split count halves, which halves the partial
-# output the decode writes and the merge reads.  Measured on 4096-key sequences at
-# batch 16 (4 pages per full-head split): 58.1 against 61.4 us per step; at 1024
-# pages per sequence (64 per split) the head split loses (383 against 348 us).
-HEAD_SPLIT_MAX_PAGES = 6
-
-
-def head_split(total_q: int, num_splits: int, groups: int, cu_count: int = 256) -> int:
-    """Workgroups per (token, split) pair of the MFMA decode kernel: 2 (64 heads each)
-    for one latent group when 2 * total_q * num_splits <= cu_count, else 1 (128 heads).
-    The library applies the same rule to the device's compute-unit count."""
-    return 2 if groups == 1 and 2 * total_q * num_splits <= cu_count else 1
-
-
 def split_plan(seq_lens_host, q_lens_host, cu_count: int = 256, groups: int = 1):
-    """(num_splits, pages_per_split) for a batch: the split length whose grid finishes
-    first under plan_makespan's model, among at most 256 splits per sequence.  The
-    candidates are the shortest split lengths for each split count of the longest
-    sequence and the lengths that give k workgroups per CU for small k; a tie goes
-    to the fewer workgroups (less partial output to merge).  With one latent group, a
-    plan of at most HEAD_SPLIT_MAX_PAGES pages per split is then doubled in length
-    when the halved split count lets the kernel run two 64-head workgroups per
-    (token, split) (head_split)."""
-    pages = [max(1, math.ceil(int(L) / PAGE_SIZE)) for L in seq_lens_host]
-    q = [int(x) for x in q_lens_host]
-    max_p = max(pages)
-    total = sum(p * n for p, n in zip(pages, q))
-    cands = {math.ceil(max_p / s) for s in range(1, min(256, max_p) + 1)}
-    cands |= {max(1, math.ceil(total / (cu_count * k))) for k in range(1, 17)}
-    cands = sorted(c for c in cands if math.ceil(max_p / c) <= 256)
-    if len(cands) > 96:  # keep the evaluation cheap: the longest splits plus a spread
-        cands = sorted(set(cands[-64:]) | set(cands[:: max(1, len(cands) // 32)]))
-    best = None
-    for pps in cands:
-        n_wg = sum(n * math.ceil(p / pps) for p, n in zip(pages, q))
-        key = (plan_makespan(pages, q, pps, cu_count), n_wg)
-        if best is None or key < best[0]:
-            best = (key, pps)
-    pps = best[1]
-    S = max(1, math.ceil(max_p / pps))
-    if groups == 1 and S >= 2 and pps <= HEAD_SPLIT_MAX_PAGES:
-        pps2 = 2 * pps
-        S2 = max(1, math.ceil(max_p / pps2))
-        if head_split(sum(q), S2, groups, cu_count) == 2:
-            return S2, pps2
-    return S, pps
+    """(num_splits, pages_per_split) for a batch, from the library's host-only planner
+    ``mla_decode_plan`` (host lists or arrays of int; no GPU is touched)."""
+    B = len(seq_lens_host)
+    if B == 0 or len(q_lens_host) != B:
+        raise ValueError("seq_lens and q_lens must be non-empty and of equal length")
+    lens = (ctypes.c_int32 * B)(*[int(x) for x in seq_lens_host])
+    qs = (ctypes.c_int32 * B)(*[int(x) for x in q_lens_host])
+    S, pps = ctypes.c_int(0), ctypes.c_int(0)
+    _check("mla_decode_plan", load().mla_decode_plan(lens, qs, B, int(groups), int(cu_count),
+                                                     ctypes.byref(S), ctypes.byref(pps)))
+    return S.value, pps.value
 
 
 class DecodeStep:
@@ -312,8 +276,9 @@ class DecodeStep:
         if num_splits is None:
             lens = seq_lens_host if seq_lens_host is not None else seq_lens.cpu().tolist()
             cu = cu_q.cpu().tolist()
+            cus = torch.cuda.get_device_properties(q_c.device).multi_processor_count
             num_splits, self.pages_per_split = split_plan(lens, [b - a for a, b in zip(cu, cu[1:])],
-                                                          groups=groups)
+                                                          cu_count=cus, groups=groups)
         else:
             self.pages_per_split = int(pages_per_split)
         self.num_splits = num_splits

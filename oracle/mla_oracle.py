@@ -230,8 +230,11 @@ def mla_decode(q_c, q_r, latents, w_uk, w_uv, cu_q, *, groups=1, d_c=None,
 
 
 def merge_splits(o_parts, lses):
-    """Log-sum-exp merge of split-KV partial results (P3 §5: the split partials are
-    combined by a separate step).  o_parts [..., S, d] holds each split's softmax-
+    """Log-sum-exp merge of split-KV partial results.  None of the pages mentions a
+    split of the keys or a merge of partial results: the split-KV decode with a separate
+    log-sum-exp combine is this library's own reading of the decode task, and the merge
+    below is derived from the softmax definition alone (softmax over the union of
+    disjoint key sets, written through each set's normaliser).  o_parts [..., S, d] holds each split's softmax-
     normalised output over its own keys and lses [..., S] the natural-log log-sum-exp of
     its scaled scores; a split with lse = -inf holds no keys and its partial never
     enters (it may be unwritten).  With M = max_s lse_s and w_s = exp(lse_s - M):

@@ -133,6 +133,7 @@ def _decode(lib, **kw):
     (dict(d_R=63, kv=None), DIM), (dict(H=100, G=3, kv=None), DIM), (dict(S=0, kv=None), DIM),
     (dict(B=0, kv=None), DIM), (dict(maxp=0, kv=None), DIM), (dict(cos=A, sin=A, rmp=0), DIM),
     (dict(pps=-1, kv=None), DIM),
+    (dict(maxp=(1 << 31) // 64 + 1, kv=None), UNSUP),   # max_pages * 64 past int32
     (dict(ps=16, kv=None), UNSUP), (dict(S=257, kv=None), UNSUP), (dict(d_c=4096, kv=None), UNSUP),
     (dict(dt=2), DTYPE),
     (dict(T=0, kv=None), OK),
@@ -195,12 +196,91 @@ def test_bench_decode_kernel_name_follows_the_library_rule(monkeypatch):
     from mla_latent_kv_09_amd import workloads as wl
     monkeypatch.delenv("MLA_KV_DECODE_KERNEL", raising=False)
     c = wl.CONFIGS
-    assert bench.decode_kernel_name(c["dsv3_b16_l4096"], 16, 8, mla) == "decode_mfma_kernel"
-    assert bench.decode_kernel_name(c["long_b16_l65536"], 16, 16, mla) == "decode_m32_kernel"
-    assert bench.decode_kernel_name(c["ragged_b64"], 96, 17, mla) == "decode_m32_kernel"
-    assert bench.decode_kernel_name(c["gla2_b32_l16384"], 32, 8, mla) == "decode_mfma_kernel"
-    assert bench.decode_kernel_name(c["tiny_fp32"], 1, 1, mla) == "decode_generic_kernel"
+    assert bench.decode_kernel_name(c["dsv3_b16_l4096"], 16, 8) == "decode_mfma_kernel"
+    assert bench.decode_kernel_name(c["long_b16_l65536"], 16, 16) == "decode_m32_kernel"
+    assert bench.decode_kernel_name(c["ragged_b64"], 96, 17) == "decode_m32_kernel"
+    assert bench.decode_kernel_name(c["gla2_b32_l16384"], 32, 8) == "decode_mfma_kernel"
+    assert bench.decode_kernel_name(c["tiny_fp32"], 1, 1) == "decode_generic_kernel"
     monkeypatch.setenv("MLA_KV_DECODE_KERNEL", "mfma128")
-    assert bench.decode_kernel_name(c["long_b16_l65536"], 16, 16, mla) == "decode_mfma_kernel"
+    assert bench.decode_kernel_name(c["long_b16_l65536"], 16, 16) == "decode_mfma_kernel"
     monkeypatch.setenv("MLA_KV_DECODE_KERNEL", "mfma32")
-    assert bench.decode_kernel_name(c["dsv3_b16_l4096"], 16, 16, mla) == "decode_m32_kernel"
+    assert bench.decode_kernel_name(c["dsv3_b16_l4096"], 16, 16) == "decode_m32_kernel"
+
+
+# -------------------------------------------------------------- split planner (host only)
+
+def _plan(lib, lens, qs, groups=1, cus=256):
+    B = len(lens)
+    L = (ctypes.c_int32 * max(B, 1))(*lens)
+    Q = (ctypes.c_int32 * max(B, 1))(*qs)
+    S, P = ctypes.c_int(-7), ctypes.c_int(-7)
+    st = lib.mla_decode_plan(L, Q, B, groups, cus, ctypes.byref(S), ctypes.byref(P))
+    return st, S.value, P.value
+
+
+def test_plan_validation(lib):
+    S = ctypes.c_int(0)
+    L = (ctypes.c_int32 * 2)(100, 200)
+    assert lib.mla_decode_plan(None, L, 2, 1, 256, ctypes.byref(S), ctypes.byref(S)) == NULL
+    assert lib.mla_decode_plan(L, L, 2, 1, 256, None, ctypes.byref(S)) == NULL
+    assert _plan(lib, [100, 200], [1, 1], cus=0)[0] == DIM
+    assert _plan(lib, [100, 200], [1, 1], groups=0)[0] == DIM
+    assert _plan(lib, [], [])[0] == DIM
+    assert _plan(lib, [100, -1], [1, 1])[0] == DIM
+    assert _plan(lib, [100, 200], [1, -1])[0] == DIM
+    assert _plan(lib, [100, 200], [1, 1], cus=5000)[0] == UNSUP
+    st, S, P = _plan(lib, [0], [1])
+    assert st == OK and (S, P) == (1, 1)               # an empty sequence still has one page
+
+
+# -------------------------------------------------------------- binding checks (host only)
+
+def _t(*shape, dtype=None):
+    import torch
+    return torch.zeros(shape, dtype=dtype or torch.bfloat16)
+
+
+def test_binding_rejects_wrong_output_buffers():
+    """Caller-supplied outputs are checked for shape and dtype before anything reaches the
+    library (CPU tensors: every case here fails on its shape or dtype first)."""
+    import torch
+    q_c, w = _t(4, 8, 16), _t(8, 16, 32)
+    with pytest.raises(ValueError, match="q_abs must have shape"):
+        mla.absorb_q(q_c, w, _t(4, 8, 16))
+    with pytest.raises(TypeError, match="q_abs must be"):
+        mla.absorb_q(q_c, w, _t(4, 8, 32, dtype=torch.float32))
+    o_lat = _t(4, 8, 32)
+    with pytest.raises(ValueError, match="out must have shape"):
+        mla.up_v(o_lat, w, _t(4, 8, 32))
+    with pytest.raises(TypeError, match="out must be"):
+        mla.up_v(o_lat, w, _t(4, 8, 16, dtype=torch.float32))
+    o_part, lse_part = _t(4, 8, 3, 32), _t(4, 8, 3, dtype=torch.float32)
+    with pytest.raises(ValueError, match="o_latent must have shape"):
+        mla.combine(o_part, lse_part, _t(4, 8, 16))
+    with pytest.raises(ValueError, match="lse_out must have shape"):
+        mla.combine(o_part, lse_part, _t(4, 8, 32), lse_out=_t(4, 9, dtype=torch.float32))
+    with pytest.raises(TypeError, match="lse_out must be"):
+        mla.combine(o_part, lse_part, _t(4, 8, 32), lse_out=_t(4, 8))
+    with pytest.raises(ValueError, match="lse_part must have shape"):
+        mla.combine(o_part, _t(4, 8, 2, dtype=torch.float32), _t(4, 8, 32))
+
+
+def test_binding_rejects_wrong_rope_tables():
+    import torch
+    T, H, d_cg, d_R = 2, 8, 32, 16
+    args = (_t(T, H, d_cg), _t(T, H, d_R), _t(3, 64, d_cg + d_R),
+            torch.zeros((1, 3), dtype=torch.int32), torch.zeros(1, dtype=torch.int32),
+            torch.zeros(2, dtype=torch.int32), _t(T, H, 2, d_cg), _t(T, H, 2, dtype=torch.float32))
+    good = torch.zeros((100, d_R // 2), dtype=torch.float32)
+    with pytest.raises(ValueError, match="rope tables must be"):
+        mla.decode_paged(*args, d_hc=16, rope=(torch.zeros((100, d_R)), good))
+    with pytest.raises(TypeError, match="rope sin table must be"):
+        mla.decode_paged(*args, d_hc=16, rope=(good, good.double()))
+    with pytest.raises(TypeError, match="rope cos table must be"):
+        mla.decode_paged(*args, d_hc=16, rope=(good.double(), good))
+    with pytest.raises(ValueError, match="rope must be a"):
+        mla.decode_paged(*args, d_hc=16, rope=(good, None))
+    new_c, new_k = _t(T, d_cg), _t(T, d_R)
+    with pytest.raises(ValueError, match="rope tables must be"):
+        mla.append_kv(new_c, new_k, args[2], args[3], args[4], args[5],
+                      rope=(torch.zeros((100, 3)), torch.zeros((100, 3))))

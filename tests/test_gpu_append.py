@@ -17,6 +17,7 @@ import pytest
 import torch
 
 import oracle.mla_oracle as om
+import parity_log
 from mla_latent_kv_09_amd import harness, mla
 from mla_latent_kv_09_amd import workloads as wl
 
@@ -136,6 +137,7 @@ def test_append_then_decode_matches_oracle():
     err = np.max(np.abs(out - ref)) / np.max(np.abs(ref))
     cos = float(out.ravel() @ ref.ravel() / (np.linalg.norm(out) * np.linalg.norm(ref)))
     print(f"append+decode: normwise err {err:.3e}, 1-cos {1 - cos:.3e}", flush=True)
+    parity_log.record("append+dec", err, cos, tol=1e-2, cos_tol=0.99999)
     assert np.isfinite(out).all() and err <= 1e-2 and cos >= 0.99999
 
 

@@ -14,6 +14,7 @@ import pytest
 import torch
 
 import oracle.mla_oracle as om
+import parity_log
 from mla_latent_kv_09_amd import harness
 from mla_latent_kv_09_amd import workloads as wl
 
@@ -53,16 +54,31 @@ def test_fullsize_sampled_parity(name, kind, monkeypatch):
     seqs = sorted({0, B // 2, B - 1})
     if cfg.q_len_mix:  # make sure a two-query (causal) sequence is in the sample
         seqs = sorted(set(seqs) | {int(np.argmax(w.q_lens == 2)), int(np.argmax(w.q_lens == 1))})
-    print(f"  oracle on sequences {seqs}, heads {SAMPLE_HEADS}", flush=True)
+    # One sequence with every head (a two-query one where the batch has them), the others
+    # on a sample of heads that covers every wave position and both latent groups.
+    full = int(np.argmax(w.q_lens == 2)) if cfg.q_len_mix else B // 2
+    print(f"  oracle on sequence {full} (all heads) and {seqs} (heads {SAMPLE_HEADS})", flush=True)
+    ref_full = om.mla_decode(w.q_c, w.q_r, w.latents, w.w_uk, w.w_uv, w.cu_q, groups=cfg.groups,
+                             rope_base=cfg.rope_base, causal=cfg.causal, seq_subset=[full])
     ref = om.mla_decode(w.q_c, w.q_r, w.latents, w.w_uk, w.w_uv, w.cu_q, groups=cfg.groups,
                         rope_base=cfg.rope_base, causal=cfg.causal, heads_subset=SAMPLE_HEADS,
                         seq_subset=seqs)
+    label = f"{name}[{kind or 'default'}]"
+    rows = np.arange(w.cu_q[full], w.cu_q[full + 1])
+    _check(out[rows], ref_full["out"][rows], lse[rows], ref_full["lse"][rows],
+           f"{label} seq {full} all heads")
     rows = np.concatenate([np.arange(w.cu_q[b], w.cu_q[b + 1]) for b in seqs])
-    got = out[rows][:, SAMPLE_HEADS]
-    exp = ref["out"][rows][:, SAMPLE_HEADS]
+    _check(out[rows][:, SAMPLE_HEADS], ref["out"][rows][:, SAMPLE_HEADS],
+           lse[rows][:, SAMPLE_HEADS], ref["lse"][rows][:, SAMPLE_HEADS],
+           f"{label} seqs {seqs} sampled heads")
+
+
+def _check(got, exp, got_lse, exp_lse, what):
     err = np.max(np.abs(got - exp)) / np.max(np.abs(exp))
     cos = float(got.ravel() @ exp.ravel() / (np.linalg.norm(got) * np.linalg.norm(exp)))
-    lse_err = np.max(np.abs(lse[rows][:, SAMPLE_HEADS] - ref["lse"][rows][:, SAMPLE_HEADS]))
-    print(f"  normwise err {err:.3e}  1-cos {1 - cos:.3e}  lse err {lse_err:.3e}", flush=True)
+    lse_err = float(np.max(np.abs(got_lse - exp_lse)))
+    print(f"  {what}: normwise err {err:.3e}  1-cos {1 - cos:.3e}  lse err {lse_err:.3e}", flush=True)
+    parity_log.record("all heads" if what.endswith("all heads") else "sampled", err, cos, lse_err,
+                      tol=1e-2, cos_tol=0.99999, show=True)
     assert err <= 1e-2 and cos >= 0.99999
     assert lse_err <= 5e-2

@@ -1,12 +1,25 @@
-"""Host-side split planning (CPU only): coverage, the split-count limit, one workgroup
-per CU on uniform batches, and the dispatch model it optimises."""
+"""Host-side split planning and index arithmetic (CPU only).
+
+The library's planner (``mla_decode_plan``, called through ``mla.split_plan``) is checked
+against its Python transcription in ``plan_reference`` on the five workloads and on
+random ragged batches, and the plan's properties (coverage, the split-count limit, one
+workgroup per CU on uniform batches, optimality under the dispatch model) are checked
+on the C result.  The kernels' own index code (``csrc/mla_index.h``: sequence lookup,
+split key ranges, launch orders) is checked by a host program compiled from that header
+under the address and undefined-behaviour sanitizers.
+"""
 import math
+import os
+import subprocess
 
 import numpy as np
 import pytest
 
-from mla_latent_kv_09_amd import mla
+import plan_reference as pr
+from mla_latent_kv_09_amd import build_lib, mla
 from mla_latent_kv_09_amd import workloads as wl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def _lens(cfg):
@@ -27,7 +40,7 @@ def _lens(cfg):
 def test_plan_covers_every_page_within_the_split_limit(name):
     L, q = _lens(wl.CONFIGS[name])
     S, pps = mla.split_plan(L, q)
-    pages = [math.ceil(x / mla.PAGE_SIZE) for x in L]
+    pages = [math.ceil(x / pr.PAGE_SIZE) for x in L]
     assert 1 <= S <= 256 and pps >= 1
     assert S * pps >= max(pages)               # the last split never has to take extra pages
     assert (S - 1) * pps < max(pages)          # and no split is empty for the longest sequence
@@ -44,18 +57,18 @@ def test_uniform_batches_get_one_workgroup_per_cu(name, expect, hs):
     S, pps = mla.split_plan(L, q, groups=cfg.groups)
     assert (S, pps) == expect
     T = sum(q)
-    assert mla.head_split(T, S, cfg.groups) == hs
+    assert pr.head_split(T, S, cfg.groups) == hs
     assert T * S * hs == 256
 
 
 def test_head_split_rule():
     # one latent group: two workgroups per pair while the doubled grid fits the CUs
-    assert mla.head_split(16, 8, 1) == 2
-    assert mla.head_split(16, 9, 1) == 1
-    assert mla.head_split(1, 128, 1) == 2 and mla.head_split(1, 129, 1) == 1
-    assert mla.head_split(16, 8, 1, cu_count=128) == 1
+    assert pr.head_split(16, 8, 1) == 2
+    assert pr.head_split(16, 9, 1) == 1
+    assert pr.head_split(1, 128, 1) == 2 and pr.head_split(1, 129, 1) == 1
+    assert pr.head_split(16, 8, 1, cu_count=128) == 1
     # two latent groups: never
-    assert mla.head_split(1, 1, 2) == 1
+    assert pr.head_split(1, 1, 2) == 1
 
 
 @pytest.mark.parametrize("B,L,groups", [(16, 2048, 1), (16, 4096, 1), (32, 4096, 1), (16, 4096, 2),
@@ -67,140 +80,90 @@ def test_head_split_only_doubles_short_splits(B, L, groups):
     lens, q = [L] * B, [1] * B
     S, pps = mla.split_plan(lens, q, groups=groups)
     S1, pps1 = mla.split_plan(lens, q, groups=2)      # the plan without a head split
-    pages = math.ceil(L / mla.PAGE_SIZE)
+    pages = math.ceil(L / pr.PAGE_SIZE)
     assert S * pps >= pages and (S - 1) * pps < pages
     if groups == 2:
-        assert mla.head_split(B, S, groups) == 1
+        assert pr.head_split(B, S, groups) == 1
     elif (S, pps) != (S1, pps1):
-        assert pps == 2 * pps1 and pps1 <= mla.HEAD_SPLIT_MAX_PAGES
-        assert mla.head_split(B, S, groups) == 2
+        assert pps == 2 * pps1 and pps1 <= pr.HEAD_SPLIT_MAX_PAGES
+        assert pr.head_split(B, S, groups) == 2
     else:
-        assert pps1 > mla.HEAD_SPLIT_MAX_PAGES or S1 == 1 or mla.head_split(
-            B, math.ceil(pages / (2 * pps1)), groups) == 1 or mla.head_split(B, S, groups) == 2
+        assert pps1 > pr.HEAD_SPLIT_MAX_PAGES or S1 == 1 or pr.head_split(
+            B, math.ceil(pages / (2 * pps1)), groups) == 1 or pr.head_split(B, S, groups) == 2
 
 
 def test_makespan_model_by_hand():
-    one = mla.SPLIT_OVERHEAD_PAGES + 4
+    one = pr.SPLIT_OVERHEAD_PAGES + 4
     # 8 CUs = one per XCD.  Two sequences of 8 pages, splits of 4 pages: workgroups
     # 0..3 go to XCDs 0..3 and run side by side.
-    assert mla.plan_makespan([8, 8], [1, 1], 4, cu_count=8) == pytest.approx(one)
+    assert pr.plan_makespan([8, 8], [1, 1], 4, cu_count=8) == pytest.approx(one)
     # nine splits of one sequence: workgroup 8 is dealt to XCD 0 again and queues there
     # although the other seven XCDs are idle.
-    assert mla.plan_makespan([36], [1], 4, cu_count=8) == pytest.approx(2 * one)
+    assert pr.plan_makespan([36], [1], 4, cu_count=8) == pytest.approx(2 * one)
     # with two CUs per XCD it runs next to workgroup 0 instead
-    assert mla.plan_makespan([36], [1], 4, cu_count=16) == pytest.approx(one)
+    assert pr.plan_makespan([36], [1], 4, cu_count=16) == pytest.approx(one)
     # an empty split (short sequence past its pages) costs only the early exit
-    assert mla.plan_makespan([8, 1], [1, 1], 4, cu_count=8) == pytest.approx(one)
+    assert pr.plan_makespan([8, 1], [1, 1], 4, cu_count=8) == pytest.approx(one)
     # a query length of 2 runs the sequence's splits once per query token
-    assert mla.plan_makespan([8], [2], 4, cu_count=8) == pytest.approx(one)
-    assert mla.plan_makespan([4] * 9, [1] * 9, 4, cu_count=8) == pytest.approx(2 * one)
+    assert pr.plan_makespan([8], [2], 4, cu_count=8) == pytest.approx(one)
+    assert pr.plan_makespan([4] * 9, [1] * 9, 4, cu_count=8) == pytest.approx(2 * one)
 
 
 def test_ragged_plan_no_worse_than_any_candidate_length():
     L, q = _lens(wl.CONFIGS["ragged_b64"])
-    pages = [math.ceil(x / mla.PAGE_SIZE) for x in L]
+    pages = [math.ceil(x / pr.PAGE_SIZE) for x in L]
     S, pps = mla.split_plan(L, q)
-    best = mla.plan_makespan(pages, q, pps)
+    best = pr.plan_makespan(pages, q, pps)
     for other in (4, 8, 16, 24, 28, 32, 48, 64, 128):
         if math.ceil(max(pages) / other) <= 256:
-            assert best <= mla.plan_makespan(pages, q, other) + 1e-9
+            assert best <= pr.plan_makespan(pages, q, other) + 1e-9
 
 
-def _launch_unit(L, S, cu_q):
-    """The 32x32x16 decode kernel's launch order (one workgroup per (token, split)),
-    written out: the units of sequence b are workgroups [cu_q[b] S, cu_q[b+1] S); one
-    token runs in split order, n tokens in blocks of 8 splits x n tokens, token-major."""
-    t0 = L // S
-    b = max(i for i in range(len(cu_q) - 1) if cu_q[i] <= t0)
-    q0, n = cu_q[b], cu_q[b + 1] - cu_q[b]
-    u = L - q0 * S
-    if n <= 1:
-        return q0 + u // S, u % S
-    blk, r = divmod(u, 8 * n)
-    k = min(8, S - 8 * blk)
-    return q0 + r // k, 8 * blk + r % k
 
 
-@pytest.mark.parametrize("seed", range(20))
-def test_launch_order_is_a_bijection_that_groups_tokens_of_a_split(seed):
-    rng = np.random.default_rng(seed)
-    B, S = int(rng.integers(1, 10)), int(rng.integers(1, 40))
-    q_lens = rng.choice([1, 1, 2, 3], size=B)
-    cu = np.concatenate([[0], np.cumsum(q_lens)]).tolist()
-    T = cu[-1]
-    where = {}
-    for L in range(T * S):
-        t, s = _launch_unit(L, S, cu)
-        assert 0 <= t < T and 0 <= s < S and (t, s) not in where
-        where[(t, s)] = L
-    assert len(where) == T * S
-    for b in range(B):
-        q0, n = cu[b], cu[b + 1] - cu[b]
-        for s in range(S):
-            if n == 1:
-                assert where[(q0, s)] == q0 * S + s          # split order, as before
-            elif s < 8 * (S // 8):                           # full blocks: 8 apart, one XCD
-                assert all(where[(q0 + i, s)] - where[(q0, s)] == 8 * i for i in range(n))
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(mla.LIB_PATH):
+        build_lib.build()
+    return mla.load()
 
 
-def _find_seq_binary(cu_q, batch, t):
-    lo, hi = 0, batch - 1
-    while lo < hi:
-        mid = (lo + hi + 1) >> 1
-        if cu_q[mid] <= t:
-            lo = mid
-        else:
-            hi = mid - 1
-    return lo
-
-
-def _find_seq_wave(cu_q, batch, t):
-    """The decode kernels' wave-wide lookup for batch <= 64: lane l holds cu_q[l + 1];
-    the sequence is the number of lanes l < batch - 1 with cu_q[l + 1] <= t."""
-    return sum(1 for lane in range(64) if lane < batch - 1 and cu_q[lane + 1] <= t)
+@pytest.mark.parametrize("name", wl.CONFIG_ORDER)
+def test_c_planner_equals_reference_on_the_workloads(lib, name):
+    cfg = wl.CONFIGS[name]
+    L, q = _lens(cfg)
+    assert mla.split_plan(L, q, groups=cfg.groups) == pr.split_plan(L, q, groups=cfg.groups)
 
 
 @pytest.mark.parametrize("seed", range(40))
-def test_wave_sequence_lookup_matches_binary_search(seed):
+def test_c_planner_equals_reference_on_random_batches(lib, seed):
     rng = np.random.default_rng(seed)
-    batch = int(rng.choice([1, 2, 3, 16, 63, 64]))
-    q_lens = rng.choice([0, 1, 1, 2, 3], size=batch)
-    q_lens[int(rng.integers(batch))] = max(1, q_lens[0])
-    cu = np.concatenate([[0], np.cumsum(q_lens)]).tolist()
-    for t in range(cu[-1]):
-        b = _find_seq_wave(cu, batch, t)
-        assert b == _find_seq_binary(cu, batch, t)
-        assert cu[b] <= t < cu[b + 1]  # the row belongs to a non-empty sequence
+    B = int(rng.integers(1, 80))
+    hi = int(rng.choice([64, 700, 5000, 40000, 140000]))
+    L = rng.integers(0, hi + 1, size=B).tolist()
+    q = rng.choice([1, 1, 2, 3], size=B).tolist()
+    groups = int(rng.choice([1, 2]))
+    cus = int(rng.choice([256, 256, 128, 304, 8]))
+    assert mla.split_plan(L, q, cu_count=cus, groups=groups) == pr.split_plan(
+        L, q, cu_count=cus, groups=groups), (L, q, cus, groups)
 
 
-def _k2_half_unit(L, S, T):
-    """The 16x16x32 decode kernel's launch order with two workgroups per (token, split),
-    written out: (token, split, half) of workgroup L."""
-    if T % 8 == 0:
-        x, r = L & 7, L >> 3
-        k, rem = divmod(r, 2 * S)
-        return x + 8 * k, rem >> 1, rem & 1
-    kb = L >> 4
-    base = kb * 8
-    r = min(8, T * S - base)
-    off = L - 16 * kb
-    pair = base + off % r
-    return pair // S, pair % S, off // r
-
-
-@pytest.mark.parametrize("T", [1, 3, 8, 16, 24, 40])
-@pytest.mark.parametrize("S", [1, 2, 5, 8])
-def test_head_split_launch_order_is_a_bijection_with_halves_on_one_xcd(T, S):
-    where = {}
-    for L in range(2 * T * S):
-        t, s, h = _k2_half_unit(L, S, T)
-        assert 0 <= t < T and 0 <= s < S and h in (0, 1) and (t, s, h) not in where
-        where[(t, s, h)] = L
-    assert len(where) == 2 * T * S
-    for t in range(T):
-        for s in range(S):
-            full_block = (t * S + s) < 8 * (T * S // 8)
-            if T % 8 == 0 or full_block:                       # halves share an L2
-                assert where[(t, s, 0)] % 8 == where[(t, s, 1)] % 8
-            if T % 8 == 0:                                     # a token's units share one
-                assert where[(t, s, 0)] % 8 == t % 8
+def test_native_index_code_under_sanitizers():
+    """Build tests/native/index_check.hip (host code around csrc/mla_index.h) with
+    AddressSanitizer and UBSan (host side only) and run it: launch-order bijections and
+    locality, the wave-wide sequence lookup, and split key ranges that tile the visible
+    keys for any split count and split length, with no signed overflow."""
+    out = os.path.join(ROOT, "_build", "index_check")
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    src = os.path.join(ROOT, "tests", "native", "index_check.hip")
+    cmd = [build_lib.hipcc(), "-x", "hip", f"--offload-arch={build_lib.ARCH}", "-O1", "-g",
+           "-std=c++17", f"-I{build_lib.CSRC}",
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=all", src, "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    r = subprocess.run([out], capture_output=True, text=True, timeout=120,
+                       env={**os.environ, "ASAN_OPTIONS": "detect_leaks=1"})
+    print(r.stdout)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "all index checks passed" in r.stdout
