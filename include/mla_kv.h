@@ -261,6 +261,42 @@ size_t mla_decode_workspace_bytes(int total_q, int heads, int groups, int d_c, i
 int mla_decode_plan(const int32_t* seq_lens, const int32_t* q_lens, int batch, int groups,
                     int cu_count, int* num_splits, int* pages_per_split);
 
+/*
+ * mla_attend_noalloc -- for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the split-KV
+ * decode followed by the log-sum-exp merge, i.e. mla_decode_paged then mla_combine with
+ * the same arguments, the split partials kept in library-owned static device memory
+ * instead of a caller workspace.  Same kernels, so the result is bitwise that of the
+ * two calls.
+ *
+ *   arguments as mla_decode_paged, except that o_part / lse_part are replaced by the
+ *   merge's outputs
+ *   o_latent  [T, H, d_cg] dtype, output (required)
+ *   lse_out   [T, H] float32, output, or NULL
+ *
+ * Scratch: one array of MLA_NOALLOC_SCRATCH_BYTES (64 MiB) per device, held from the
+ * library's first call on that device until the process ends; its address is looked up
+ * once per device.  The partials of a call, T*H*num_splits*(d_cg*elem + 4) bytes (the
+ * LSEs 256-byte aligned after the outputs), must fit: larger calls return
+ * MLA_ERR_UNSUPPORTED before anything is enqueued (batch 16 at 16 splits of 128 heads
+ * and d_c 512 takes 32.1 MiB).  Nothing in the array needs to start at zero: the decode
+ * writes every split's LSE and the merge reads only the partials of splits with keys.
+ * Every call on a device shares that device's array, so calls that overlap on one
+ * device (different streams, or different host threads) race; calls on one stream are
+ * ordered.  The call allocates and frees nothing.  Errors as mla_decode_paged, plus
+ * MLA_ERR_NULL for o_latent == NULL and MLA_ERR_ALIGN for a misaligned o_latent or
+ * lse_out, all detected before anything is enqueued.
+ */
+#define MLA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int mla_attend_noalloc(const void* q_abs, const void* q_r, const void* kv_cache,
+                       const int32_t* page_table, const int32_t* seq_lens, const int32_t* cu_q,
+                       const float* rope_cos, const float* rope_sin, int rope_max_pos,
+                       void* o_latent, float* lse_out,
+                       int batch, int total_q, int max_pages_per_seq, int num_pool_pages,
+                       int heads, int groups, int d_hc, int d_c, int d_R, int page_size,
+                       int num_splits, int pages_per_split, float softmax_scale, int causal,
+                       int dtype, void* stream);
+
 /* Static text for a status code (never NULL). */
 const char* mla_status_string(int status);
 

@@ -76,6 +76,97 @@ int cu_count_of_current_device() {
 
 }  // namespace
 
+namespace mla {
+
+int decode_validate(const void* q_abs, const void* q_r, const void* kv_cache,
+                    const int32_t* page_table, const int32_t* seq_lens, const int32_t* cu_q,
+                    const float* rope_cos, const float* rope_sin, int rope_max_pos, void* o_part,
+                    float* lse_part, int batch, int total_q, int max_pages_per_seq,
+                    int num_pool_pages, int heads, int groups, int d_hc, int d_c, int d_R,
+                    int page_size, int num_splits, int pages_per_split, float softmax_scale,
+                    int causal, int dtype, bool check_parts, DecodeArgs* out, bool* bf16) {
+  int st = check_dtype(dtype);
+  if (st != MLA_OK) return st;
+  if (total_q < 0 || batch <= 0 || d_hc <= 0 || d_R <= 0 || (d_R & 1) || num_splits <= 0 ||
+      pages_per_split < 0 || max_pages_per_seq <= 0 || num_pool_pages <= 0 || page_size <= 0)
+    return MLA_ERR_DIM;
+  if ((st = check_heads(heads, groups, d_c)) != MLA_OK) return st;
+  if (page_size != MLA_PAGE_SIZE || num_splits > kMaxSplits) return MLA_ERR_UNSUPPORTED;
+  if (static_cast<long long>(total_q) * num_splits > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+  if (static_cast<long long>(max_pages_per_seq) * page_size > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+  if (d_c / groups > kMaxGenericCols || d_R > kMaxGenericRope) return MLA_ERR_UNSUPPORTED;
+  if ((rope_cos == nullptr) != (rope_sin == nullptr)) return MLA_ERR_NULL;
+  if (rope_cos != nullptr && rope_max_pos <= 0) return MLA_ERR_DIM;
+  if (total_q == 0) return MLA_OK;
+  if (!q_abs || !q_r || !kv_cache || !page_table || !seq_lens || !cu_q) return MLA_ERR_NULL;
+  if (check_parts && (!o_part || !lse_part)) return MLA_ERR_NULL;
+  const void* ptrs[] = {q_abs, q_r, kv_cache, page_table, seq_lens, cu_q};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MLA_ERR_ALIGN;
+  if (check_parts && (!aligned16(o_part) || !aligned16(lse_part))) return MLA_ERR_ALIGN;
+  if (rope_cos && (!aligned16(rope_cos) || !aligned16(rope_sin))) return MLA_ERR_ALIGN;
+
+  out->q_abs = q_abs;
+  out->q_r = q_r;
+  out->kv = kv_cache;
+  out->page_table = page_table;
+  out->seq_lens = seq_lens;
+  out->cu_q = cu_q;
+  out->rope_cos = rope_cos;
+  out->rope_sin = rope_sin;
+  out->rope_max_pos = rope_max_pos;
+  out->o_part = o_part;
+  out->lse_part = lse_part;
+  out->batch = batch;
+  out->total_q = total_q;
+  out->max_pages = max_pages_per_seq;
+  out->num_pool_pages = num_pool_pages;
+  out->heads = heads;
+  out->groups = groups;
+  out->d_c = d_c;
+  out->d_R = d_R;
+  out->page_size = page_size;
+  out->num_splits = num_splits;
+  // A split longer than the page table covers every page of a sequence: any larger
+  // value gives the same plan.
+  out->pages_per_split = pages_per_split < max_pages_per_seq ? pages_per_split : max_pages_per_seq;
+  out->scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(d_hc + d_R));
+  out->causal = causal != 0;
+  *bf16 = dtype == MLA_DTYPE_BF16;
+  return MLA_OK;
+}
+
+int decode_launch(DecodeArgs& a, bool bf16, hipStream_t s) {
+  const DecodeKernel choice = decode_kernel_choice();
+  if (choice == DecodeKernel::kMfma32 || choice == DecodeKernel::kMfma32x128 ||
+      choice == DecodeKernel::kMfma32x64) {
+    if (!mla::decode_m32_supported(a, bf16)) return MLA_ERR_UNSUPPORTED;
+    a.head_split = choice == DecodeKernel::kMfma32x128 ? 1 : choice == DecodeKernel::kMfma32x64 ? 2 : 0;
+    const int hs = mla::decode_mfma_head_split(a, cu_count_of_current_device());
+    if (static_cast<long long>(a.total_q) * a.num_splits * hs > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+    return launch_status(mla::launch_decode_m32(a, hs, s));
+  }
+  const bool mfma_ok = mla::decode_mfma_supported(a, bf16);
+  const bool mfma_required = choice == DecodeKernel::kMfma || choice == DecodeKernel::kMfma128 ||
+                             choice == DecodeKernel::kMfma64;
+  if (mfma_required && !mfma_ok) return MLA_ERR_UNSUPPORTED;
+  if (choice == DecodeKernel::kMfma64 && a.groups != 1) return MLA_ERR_UNSUPPORTED;
+  if (mfma_ok && choice != DecodeKernel::kGeneric) {
+    a.head_split = choice == DecodeKernel::kMfma128 ? 1 : choice == DecodeKernel::kMfma64 ? 2 : 0;
+    const int hs = mla::decode_mfma_head_split(a, cu_count_of_current_device());
+    if (static_cast<long long>(a.total_q) * a.num_splits * hs > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+    // One workgroup of 128 heads per (token, split): the 32x32x16 kernel, unless the
+    // 16x16x32 one was asked for by name.
+    if (hs == 1 && choice != DecodeKernel::kMfma128 && mla::decode_m32_supported(a, bf16))
+      return launch_status(mla::launch_decode_m32(a, 1, s));
+    return launch_status(mla::launch_decode_mfma(a, hs, s));
+  }
+  return launch_status(mla::launch_decode_generic(a, bf16, s));
+}
+
+
+}  // namespace mla
+
 extern "C" {
 
 const char* mla_status_string(int status) {
@@ -136,80 +227,15 @@ int mla_decode_paged(const void* q_abs, const void* q_r, const void* kv_cache,
                      int num_pool_pages, int heads, int groups, int d_hc, int d_c, int d_R,
                      int page_size, int num_splits, int pages_per_split, float softmax_scale,
                      int causal, int dtype, void* stream) {
-  int st = check_dtype(dtype);
-  if (st != MLA_OK) return st;
-  if (total_q < 0 || batch <= 0 || d_hc <= 0 || d_R <= 0 || (d_R & 1) || num_splits <= 0 ||
-      pages_per_split < 0 || max_pages_per_seq <= 0 || num_pool_pages <= 0 || page_size <= 0)
-    return MLA_ERR_DIM;
-  if ((st = check_heads(heads, groups, d_c)) != MLA_OK) return st;
-  if (page_size != MLA_PAGE_SIZE || num_splits > kMaxSplits) return MLA_ERR_UNSUPPORTED;
-  if (static_cast<long long>(total_q) * num_splits > INT32_MAX) return MLA_ERR_UNSUPPORTED;
-  if (static_cast<long long>(max_pages_per_seq) * page_size > INT32_MAX) return MLA_ERR_UNSUPPORTED;
-  if (d_c / groups > kMaxGenericCols || d_R > kMaxGenericRope) return MLA_ERR_UNSUPPORTED;
-  if ((rope_cos == nullptr) != (rope_sin == nullptr)) return MLA_ERR_NULL;
-  if (rope_cos != nullptr && rope_max_pos <= 0) return MLA_ERR_DIM;
-  if (total_q == 0) return MLA_OK;
-  if (!q_abs || !q_r || !kv_cache || !page_table || !seq_lens || !cu_q || !o_part || !lse_part)
-    return MLA_ERR_NULL;
-  const void* ptrs[] = {q_abs, q_r, kv_cache, page_table, seq_lens, cu_q, o_part, lse_part};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return MLA_ERR_ALIGN;
-  if (rope_cos && (!aligned16(rope_cos) || !aligned16(rope_sin))) return MLA_ERR_ALIGN;
-
   mla::DecodeArgs a{};
-  a.q_abs = q_abs;
-  a.q_r = q_r;
-  a.kv = kv_cache;
-  a.page_table = page_table;
-  a.seq_lens = seq_lens;
-  a.cu_q = cu_q;
-  a.rope_cos = rope_cos;
-  a.rope_sin = rope_sin;
-  a.rope_max_pos = rope_max_pos;
-  a.o_part = o_part;
-  a.lse_part = lse_part;
-  a.batch = batch;
-  a.total_q = total_q;
-  a.max_pages = max_pages_per_seq;
-  a.num_pool_pages = num_pool_pages;
-  a.heads = heads;
-  a.groups = groups;
-  a.d_c = d_c;
-  a.d_R = d_R;
-  a.page_size = page_size;
-  a.num_splits = num_splits;
-  // A split longer than the page table covers every page of a sequence: any larger
-  // value gives the same plan.
-  a.pages_per_split = pages_per_split < max_pages_per_seq ? pages_per_split : max_pages_per_seq;
-  a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(d_hc + d_R));
-  a.causal = causal != 0;
-  const bool bf16 = dtype == MLA_DTYPE_BF16;
-  const DecodeKernel choice = decode_kernel_choice();
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  if (choice == DecodeKernel::kMfma32 || choice == DecodeKernel::kMfma32x128 ||
-      choice == DecodeKernel::kMfma32x64) {
-    if (!mla::decode_m32_supported(a, bf16)) return MLA_ERR_UNSUPPORTED;
-    a.head_split = choice == DecodeKernel::kMfma32x128 ? 1 : choice == DecodeKernel::kMfma32x64 ? 2 : 0;
-    const int hs = mla::decode_mfma_head_split(a, cu_count_of_current_device());
-    if (static_cast<long long>(total_q) * num_splits * hs > INT32_MAX) return MLA_ERR_UNSUPPORTED;
-    return launch_status(mla::launch_decode_m32(a, hs, s));
-  }
-  const bool mfma_ok = mla::decode_mfma_supported(a, bf16);
-  const bool mfma_required = choice == DecodeKernel::kMfma || choice == DecodeKernel::kMfma128 ||
-                             choice == DecodeKernel::kMfma64;
-  if (mfma_required && !mfma_ok) return MLA_ERR_UNSUPPORTED;
-  if (choice == DecodeKernel::kMfma64 && groups != 1) return MLA_ERR_UNSUPPORTED;
-  if (mfma_ok && choice != DecodeKernel::kGeneric) {
-    a.head_split = choice == DecodeKernel::kMfma128 ? 1 : choice == DecodeKernel::kMfma64 ? 2 : 0;
-    const int hs = mla::decode_mfma_head_split(a, cu_count_of_current_device());
-    if (static_cast<long long>(total_q) * num_splits * hs > INT32_MAX) return MLA_ERR_UNSUPPORTED;
-    // One workgroup of 128 heads per (token, split): the 32x32x16 kernel, unless the
-    // 16x16x32 one was asked for by name.
-    if (hs == 1 && choice != DecodeKernel::kMfma128 && mla::decode_m32_supported(a, bf16))
-      return launch_status(mla::launch_decode_m32(a, 1, s));
-    return launch_status(mla::launch_decode_mfma(a, hs, s));
-  }
-  return launch_status(mla::launch_decode_generic(a, bf16, s));
+  bool bf16 = false;
+  const int st = mla::decode_validate(q_abs, q_r, kv_cache, page_table, seq_lens, cu_q, rope_cos,
+                                      rope_sin, rope_max_pos, o_part, lse_part, batch, total_q,
+                                      max_pages_per_seq, num_pool_pages, heads, groups, d_hc, d_c,
+                                      d_R, page_size, num_splits, pages_per_split, softmax_scale,
+                                      causal, dtype, true, &a, &bf16);
+  if (st != MLA_OK || total_q == 0) return st;
+  return mla::decode_launch(a, bf16, static_cast<hipStream_t>(stream));
 }
 
 int mla_append_kv(const void* c_kv_new, const void* k_r_new, void* kv_cache,

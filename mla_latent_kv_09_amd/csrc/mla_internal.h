@@ -42,6 +42,19 @@ struct DecodeArgs {
   int head_split;    // MFMA decode, one latent group: 0 = chosen from the grid size, 1 or 2
 };
 
+// mla_decode_paged in two steps.  decode_validate checks every argument on the host
+// (o_part / lse_part only when check_parts) and fills *out; it returns MLA_OK without
+// filling anything for total_q == 0.  decode_launch picks the kernel for the device and
+// enqueues it (returns an MLA_* status).
+int decode_validate(const void* q_abs, const void* q_r, const void* kv_cache,
+                    const int32_t* page_table, const int32_t* seq_lens, const int32_t* cu_q,
+                    const float* rope_cos, const float* rope_sin, int rope_max_pos, void* o_part,
+                    float* lse_part, int batch, int total_q, int max_pages_per_seq,
+                    int num_pool_pages, int heads, int groups, int d_hc, int d_c, int d_R,
+                    int page_size, int num_splits, int pages_per_split, float softmax_scale,
+                    int causal, int dtype, bool check_parts, DecodeArgs* out, bool* bf16);
+int decode_launch(DecodeArgs& a, bool bf16, hipStream_t s);
+
 // Latent-cache append of the new tokens' rows (c_KV | RoPE(k_R, pos)).
 struct AppendArgs {
   const void* c_new;   // [T, d_c] storage type

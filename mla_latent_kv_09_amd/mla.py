@@ -22,7 +22,8 @@ DTYPE_FP32 = 1
 PAGE_SIZE = 64
 
 EXPORTED = ("mla_absorb_q", "mla_rope_table", "mla_decode_paged", "mla_combine", "mla_up_v",
-            "mla_append_kv", "mla_decode_workspace_bytes", "mla_decode_plan", "mla_status_string")
+            "mla_append_kv", "mla_decode_workspace_bytes", "mla_decode_plan", "mla_attend_noalloc",
+            "mla_status_string")
 
 _lib = None
 
@@ -53,10 +54,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_decode_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.mla_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.mla_decode_plan.argtypes = [P, P, I, I, I, P, P]
+    lib.mla_attend_noalloc.argtypes = ([P] * 8 + [I] + [P] * 2 + [I] * 12 + [F, I, I, P])
     lib.mla_status_string.argtypes = [I]
     lib.mla_status_string.restype = ctypes.c_char_p
     for name in ("mla_absorb_q", "mla_rope_table", "mla_decode_paged", "mla_combine", "mla_up_v",
-                 "mla_append_kv", "mla_decode_plan"):
+                 "mla_append_kv", "mla_decode_plan", "mla_attend_noalloc"):
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -189,6 +191,41 @@ def decode_paged(q_abs, q_r, kv_cache, page_table, seq_lens, cu_q, o_part, lse_p
         B, T, max_pages, P, H, groups, d_hc, d_cg * groups, d_R, ps, S, int(pages_per_split),
         float(softmax_scale),
         int(bool(causal)), _dtype_code(q_abs), _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def attend_noalloc(q_abs, q_r, kv_cache, page_table, seq_lens, cu_q, o_latent, lse_out=None, *,
+                   d_hc: int, num_splits: int, groups: int = 1, rope: Optional[tuple] = None,
+                   softmax_scale: float = 0.0, causal: bool = True, pages_per_split: int = 0,
+                   stream=None) -> None:
+    """mla_decode_paged followed by mla_combine, with the split partials in the library's
+    static device scratch (no allocation by the library): writes o_latent [T,H,d_c/G] and,
+    if given, lse_out [T,H]."""
+    T, H, d_cg = q_abs.shape
+    d_R = q_r.shape[2]
+    P, ps, width = kv_cache.shape
+    B, max_pages = page_table.shape
+    if q_r.shape[:2] != (T, H) or width != d_cg * groups + d_R:
+        raise ValueError("inconsistent q_r / kv_cache shapes")
+    for t in (page_table, seq_lens, cu_q):
+        if t.dtype != torch.int32:
+            raise TypeError(f"expected int32, got {t.dtype}")
+    if seq_lens.shape != (B,) or cu_q.shape != (B + 1,):
+        raise ValueError("seq_lens must be [B] and cu_q [B+1]")
+    if q_r.dtype != q_abs.dtype or kv_cache.dtype != q_abs.dtype:
+        raise TypeError("q_abs, q_r and kv_cache must share the storage dtype")
+    _expect("o_latent", o_latent, (T, H, d_cg), q_abs.dtype)
+    _expect("lse_out", lse_out, (T, H), torch.float32)
+    cos, sin, rope_max_pos = _rope_pair(rope, d_R, q_abs.device)
+    _dev(q_abs, q_r, kv_cache, page_table, seq_lens, cu_q, o_latent, lse_out, cos, sin)
+    _check("mla_attend_noalloc", load().mla_attend_noalloc(
+        _ptr(q_abs), _ptr(q_r), _ptr(kv_cache), _ptr(page_table), _ptr(seq_lens), _ptr(cu_q),
+        _ptr(cos), _ptr(sin), rope_max_pos, _ptr(o_latent), _ptr(lse_out),
+        B, T, max_pages, P, H, groups, d_hc, d_cg * groups, d_R, ps, int(num_splits),
+        int(pages_per_split), float(softmax_scale), int(bool(causal)), _dtype_code(q_abs),
+        _stream(stream)))
 
 
 def append_kv(c_kv_new, k_r_new, kv_cache, page_table, seq_lens, cu_q, *,

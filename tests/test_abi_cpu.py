@@ -284,3 +284,31 @@ def test_binding_rejects_wrong_rope_tables():
     with pytest.raises(ValueError, match="rope tables must be"):
         mla.append_kv(new_c, new_k, args[2], args[3], args[4], args[5],
                       rope=(torch.zeros((100, 3)), torch.zeros((100, 3))))
+
+
+# -------------------------------------------------------------- no-allocation entry point
+
+def _noalloc(lib, **kw):
+    a = dict(q=A, qr=A, kv=A, pt=A, sl=A, cu=A, cos=None, sin=None, rmp=0, ol=A, lo=None,
+             B=16, T=16, maxp=64, pool=1024, H=128, G=1, d_hc=128, d_c=512, d_R=64, ps=64, S=16,
+             pps=0, scale=0.0, causal=1, dt=0)
+    a.update(kw)
+    return lib.mla_attend_noalloc(a["q"], a["qr"], a["kv"], a["pt"], a["sl"], a["cu"], a["cos"],
+                                  a["sin"], a["rmp"], a["ol"], a["lo"], a["B"], a["T"], a["maxp"],
+                                  a["pool"], a["H"], a["G"], a["d_hc"], a["d_c"], a["d_R"], a["ps"],
+                                  a["S"], a["pps"], a["scale"], a["causal"], a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ol=None), NULL), (dict(ol=MIS), ALIGN), (dict(lo=MIS), ALIGN),
+    # partials past the 64 MiB scratch: 96 tokens x 128 heads x 17 splits x 1028 B
+    (dict(T=96, B=64, S=17), UNSUP),
+    (dict(T=16, S=40), UNSUP),                   # 84 MB
+    (dict(T=96, B=64, S=17, ol=None), NULL),     # pointers are checked before the capacity
+    (dict(kv=None), NULL), (dict(d_R=63, kv=None), DIM), (dict(S=0, kv=None), DIM),
+    (dict(dt=4), DTYPE), (dict(T=0, kv=None, ol=None), OK),
+])
+def test_noalloc_validation(lib, kw, code):
+    """Every rejection happens on the host before any device call: the decode's own
+    validation first, then the merge's output pointers, then the capacity."""
+    assert _noalloc(lib, **kw) == code
