@@ -1,7 +1,8 @@
 """CPU float64 oracle for absorbed paged MLA decode -- test infrastructure only.
 
 Only the tests, the smoke entry and the bench's CPU-baseline leg use it; the
-product library never does.
+product library never does.  ``mla_oracle`` holds the decode and the cache append,
+``fp8_cache`` the E4M3 format and the per-token quantization of the FP8 latent cache.
 """
 from .mla_oracle import (  # noqa: F401
     absorb_reference,
