@@ -228,6 +228,53 @@ int mla_up_v(const void* o_latent, const void* w_uv, void* out,
              int total_q, int heads, int groups, int d_hc, int d_c,
              int dtype, void* stream);
 
+/*
+ * FP8 latent cache (P3 intro and §5: a quantized gather of the latent cache whose 16-byte
+ * vector loads need 16-byte-aligned pages and offsets).  The page gives no format; the
+ * one here is the library's reading on gfx950's native 8-bit float (E4M3: 1 sign bit,
+ * 4 exponent bits with bias 7, 3 mantissa bits, largest finite value 448, 0x7F/0xFF NaN,
+ * no infinities):
+ *   one page = { codes [64][d_c] uint8 E4M3 | k_R [64][d_R] bf16 | scale [64] float32 },
+ *   mla_fp8_page_bytes(d_c, d_R) = 64 * (d_c + 2 d_R + 4) bytes (41216 for 512 / 64), pages
+ *   back to back, a multiple of 16 bytes each.  Token j's latent is code_i * scale_j; its
+ *   k_R stays bf16 (P3 §4: reduced RoPE precision is what breaks the absorbed scores).
+ */
+size_t mla_fp8_page_bytes(int d_c, int d_R);
+
+/*
+ * mla_append_kv_fp8 -- mla_append_kv into an FP8 cache: the new token's latent row x gets
+ * scale = amax / 448 (amax = max |x_i|; 1 for an all-zero row) and code_i = the E4M3 value
+ * nearest to x_i / scale (ties to the even code, saturating at 448), both divisions
+ * correctly rounded float32; k_R is rotated at the token's position and rounded to bf16
+ * exactly as mla_append_kv does.  c_kv_new [T, d_c] and k_r_new [T, d_R] are bf16.
+ * d_c and d_R must be multiples of 8 and at most 512 (MLA_ERR_UNSUPPORTED otherwise);
+ * other arguments and errors as mla_append_kv.
+ */
+int mla_append_kv_fp8(const void* c_kv_new, const void* k_r_new, void* kv_cache,
+                      const int32_t* page_table, const int32_t* seq_lens, const int32_t* cu_q,
+                      const float* rope_cos, const float* rope_sin, int rope_max_pos,
+                      int batch, int total_q, int max_pages_per_seq, int num_pool_pages,
+                      int d_c, int d_R, int page_size, void* stream);
+
+/*
+ * mla_decode_paged_fp8 -- mla_decode_paged over an FP8 cache: same arguments, results
+ * and split plan, with kv_cache the FP8 pages above, q_abs, q_r and o_part bf16 (the
+ * storage type is bf16; there is no dtype argument).  The scores are
+ * scale_j (q_abs . code_j) + RoPE(q_R) . k_R_j times softmax_scale, the output weights
+ * are p_j scale_j: the result of mla_decode_paged on the dequantized rows.  The codes are
+ * converted to bf16 exactly for the MFMAs.  Implemented for 128 heads, one latent group,
+ * d_c 512 and d_R 64 (MLA_ERR_UNSUPPORTED otherwise); MLA_KV_DECODE_KERNEL "mfma32-128" /
+ * "mfma32-64" force one or two workgroups per (token, split).
+ */
+int mla_decode_paged_fp8(const void* q_abs, const void* q_r, const void* kv_cache,
+                         const int32_t* page_table, const int32_t* seq_lens, const int32_t* cu_q,
+                         const float* rope_cos, const float* rope_sin, int rope_max_pos,
+                         void* o_part, float* lse_part,
+                         int batch, int total_q, int max_pages_per_seq, int num_pool_pages,
+                         int heads, int groups, int d_hc, int d_c, int d_R, int page_size,
+                         int num_splits, int pages_per_split, float softmax_scale, int causal,
+                         void* stream);
+
 /* Bytes of the o_part + lse_part workspace mla_decode_paged needs for this dtype
  * (0 on bad sizes or dtype): T*H*num_splits*(d_cg*elem + 4), elem = 2 for bf16. */
 size_t mla_decode_workspace_bytes(int total_q, int heads, int groups, int d_c, int num_splits,

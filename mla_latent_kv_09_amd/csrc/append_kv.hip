@@ -116,7 +116,125 @@ __global__ void __launch_bounds__(kBlock) append_kv_kernel(
   }
 }
 
+// Nearest E4M3 code to x, ties to the even code, magnitudes at or past 448 saturating to
+// 448, NaN to 0x7F, the sign bit taken from x (E4M3: 1 sign, 4 exponent bits with bias
+// 7, 3 mantissa bits; exponent field 0 holds the subnormals m/8 * 2^-6).
+__device__ __forceinline__ uint32_t e4m3_from_f32(float x) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return 0x7fu;          // NaN
+  if (a >= 0x43e00000u) return sign | 0x7eu;  // |x| >= 448, infinities included
+  if (a < 0x3c800000u) {                      // |x| < 2^-6: steps of 2^-9, 8 steps = 2^-6 = 0x08
+    return sign | static_cast<uint32_t>(rintf(__uint_as_float(a) * 512.f));
+  }
+  uint32_t e = (a >> 23) - 120u;              // biased E4M3 exponent: (E - 127) + 7
+  uint32_t m = (a >> 20) & 7u;                // top 3 of the 23 mantissa bits
+  const uint32_t rest = a & 0xfffffu;
+  if (rest > 0x80000u || (rest == 0x80000u && (m & 1u))) ++m;
+  if (m == 8u) {
+    m = 0;
+    ++e;
+  }
+  const uint32_t code = (e << 3) | m;
+  return sign | (code > 0x7eu ? 0x7eu : code);
+}
+
+// FP8 cache append: one wave per new token row.  The page holds the latent codes
+// [64][d_c] (E4M3), then k_R [64][d_R] (bf16), then one float32 scale per token; the
+// row's latent gets scale = amax / 448 (1 for an all-zero row) and code_i =
+// e4m3(x_i / scale), both divisions correctly rounded fp32; k_R is rotated at the
+// token's position as in the bf16 append.  Lane l takes latent elements 8l .. 8l+7 and
+// k_R elements 8l .. 8l+7 (the launcher requires d_c <= 512, d_R <= 512, both multiples
+// of 8).
+__global__ void __launch_bounds__(kBlock) append_kv_fp8_kernel(
+    const uint16_t* __restrict__ c_new, const uint16_t* __restrict__ k_new, uint8_t* __restrict__ kv,
+    const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ cu_q, const float* __restrict__ rope_cos,
+    const float* __restrict__ rope_sin, int rope_max_pos, int batch, int total_q, int max_pages,
+    int num_pool_pages, int d_c, int d_R, int page_size) {
+  const int lane = threadIdx.x & 63;
+  const int t = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * (kBlock / 64) +
+                                               static_cast<int>(threadIdx.x >> 6));
+  if (t >= total_q) return;
+  const bool has_c = lane < d_c / 8, has_k = lane < d_R / 8;
+  uint4 cv{}, kvv{};
+  if (has_c) cv = *reinterpret_cast<const uint4*>(c_new + static_cast<size_t>(t) * d_c + 8 * lane);
+  if (has_k) kvv = *reinterpret_cast<const uint4*>(k_new + static_cast<size_t>(t) * d_R + 8 * lane);
+
+  const int b = find_seq(cu_q, batch, t);
+  const int q0 = cu_q[b];
+  const int q_len = cu_q[b + 1] - q0;
+  const int cap = max_pages * page_size;
+  int L = seq_lens[b];
+  L = L < 0 ? 0 : (L > cap ? cap : L);
+  const int pos = L - q_len + (t - q0);
+  if (pos < 0 || pos >= cap) return;
+  const int page = clamp_page(page_table[static_cast<size_t>(b) * max_pages + pos / page_size],
+                              num_pool_pages);
+  const int slot = pos % page_size;
+  uint8_t* pg = kv + static_cast<size_t>(page) * page_size * (d_c + 2 * d_R + 4);
+
+  // Latent: row maximum over the wave, then the codes.
+  float x[8];
+  const uint16_t* xs = reinterpret_cast<const uint16_t*>(&cv);
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    x[e] = bf16_to_f32(xs[e]);
+    amax = fmaxf(amax, fabsf(x[e]));
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  const float scale = amax > 0.f ? __fdiv_rn(amax, 448.f) : 1.f;
+  if (has_c) {
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      w0 |= e4m3_from_f32(__fdiv_rn(x[e], scale)) << (8 * e);
+      w1 |= e4m3_from_f32(__fdiv_rn(x[4 + e], scale)) << (8 * e);
+    }
+    *reinterpret_cast<uint2*>(pg + static_cast<size_t>(slot) * d_c + 8 * lane) = uint2{w0, w1};
+  }
+  if (has_k) {
+    float k[8];
+    const uint16_t* ks = reinterpret_cast<const uint16_t*>(&kvv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) k[e] = bf16_to_f32(ks[e]);
+    if (rope_cos != nullptr) {
+      const int p = min(pos, rope_max_pos - 1);
+      const size_t off = static_cast<size_t>(p) * (d_R / 2) + 4 * lane;
+      float cs[4], sn[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        cs[i] = rope_cos[off + i];
+        sn[i] = rope_sin[off + i];
+      }
+      rotate_pairs(k, 8, cs, sn);
+    }
+    uint4 o;
+    uint16_t* os = reinterpret_cast<uint16_t*>(&o);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) os[e] = f32_to_bf16(k[e]);
+    *reinterpret_cast<uint4*>(pg + static_cast<size_t>(page_size) * d_c +
+                              (static_cast<size_t>(slot) * d_R + 8 * lane) * 2) = o;
+  }
+  if (lane == 0)
+    *reinterpret_cast<float*>(pg + static_cast<size_t>(page_size) * (d_c + 2 * d_R) + 4 * slot) = scale;
+}
+
 }  // namespace
+
+hipError_t launch_append_kv_fp8(const AppendArgs& a, hipStream_t s) {
+  const long long rows_per_block = kBlock / 64;
+  const dim3 grid(static_cast<unsigned>((a.total_q + rows_per_block - 1) / rows_per_block));
+  append_kv_fp8_kernel<<<grid, kBlock, 0, s>>>(
+      static_cast<const uint16_t*>(a.c_new), static_cast<const uint16_t*>(a.k_new),
+      static_cast<uint8_t*>(a.kv), a.page_table, a.seq_lens, a.cu_q, a.rope_cos, a.rope_sin,
+      a.rope_max_pos, a.batch, a.total_q, a.max_pages, a.num_pool_pages, a.d_c, a.d_R,
+      a.page_size);
+  return hipGetLastError();
+}
 
 hipError_t launch_append_kv(const AppendArgs& a, bool bf16, hipStream_t s) {
   const long long rows_per_block = kBlock / 64;

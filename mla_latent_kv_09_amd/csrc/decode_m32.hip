@@ -37,6 +37,19 @@
 // A score read (32 consecutive tokens, one chunk) then hits 32 distinct 16-byte slots of
 // a 512-byte bank row, and so does a transposing read (4 tokens x 4 chunks x 2 halves).
 // RoPE row t (128 B) holds chunk c at c ^ ((t >> 2) & 7); q_R of head n the same with n.
+//
+// FP8 cache (F8 = true; the quantized latent gather of nxmr.cn/news/151634, intro and §5,
+// on gfx950's E4M3 format): a page holds the latent codes [64][512] (E4M3, 32 KB), k_R
+// [64][64] (bf16, 8 KB) and one float32 scale per token (256 B), 41 KB in all, so three
+// stages fit next to q_R and the copies run two pages ahead.  A latent row (512 B) holds
+// 16-byte chunk c at position c ^ 2 (t mod 16).  Scores: one 16-byte read per lane and
+// token feeds two K-steps (K-step pair j, lane half h: dims 32 j + 16 h .. +15, the query
+// registers loaded in the same order); codes are converted to bf16 exactly
+// (v_cvt_scalef32_pk_bf16_fp8 with scale 1), the latent part of each score is multiplied
+// by its token's scale, and the RoPE K-steps then accumulate on top.  Output: P^T is
+// multiplied by the token scales before the bf16 rounding, and each C^T fragment is one
+// transposing 8-bit read (ds_read_b64_tr_b8: lanes 2e, 2e + 1 of a 16-lane group supply
+// row e, 8 columns each; lane j receives column j of the 8 rows) and four conversions.
 #include <math.h>
 
 #include <type_traits>
@@ -50,6 +63,8 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4_t;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8_t;
 
@@ -70,6 +85,27 @@ constexpr int kRSteps = kDr / 16;        // 4 RoPE K-steps
 constexpr int kColBlocks = kDc / 32;     // 16 output blocks of 32 columns
 constexpr float kJump = 64.f;            // reference restart threshold, log2 units
 static_assert(kLdsBytes <= 160 * 1024, "stages + q_R must fit the 160 KB LDS of a gfx950 CU");
+
+// FP8 cache page (= one LDS stage): codes, then k_R, then the token scales.
+constexpr int kC8Bytes = kTok * kDc;              // 32 KB of E4M3 codes
+constexpr int kR8Off = kC8Bytes;                  // k_R [64][64] bf16
+constexpr int kS8Off = kC8Bytes + kRBytes;        // scales [64] float32
+constexpr int kStage8Bytes = kS8Off + kTok * 4;   // 41216 B, also the page stride in HBM
+constexpr int kQrOff8 = 3 * kStage8Bytes;
+constexpr int kLds8Bytes = kQrOff8 + kHeads * kDr * 2;
+constexpr int kCopies8 = 11;                      // global->LDS copies per wave and page
+static_assert(kLds8Bytes <= 160 * 1024, "three FP8 stages + q_R must fit the 160 KB LDS");
+static_assert(kStage8Bytes % 16 == 0, "FP8 pages are whole 16-byte units");
+
+template <bool F8>
+struct Form {
+  static constexpr int kStages = F8 ? 3 : 2;
+  static constexpr int kStage = F8 ? kStage8Bytes : kStageBytes;
+  static constexpr int kPage = F8 ? kStage8Bytes : kTok * kRowBytes;  // page stride in HBM
+  static constexpr int kRopeOff = F8 ? kR8Off : kCBytes;              // k_R block in a stage
+  static constexpr int kQr = F8 ? kQrOff8 : kQrOff;
+  static constexpr int kLds = F8 ? kLds8Bytes : kLdsBytes;
+};
 
 __device__ __forceinline__ uint32_t swz_f(int t) {
   return static_cast<uint32_t>(((t & 3) << 2) | ((t >> 2) & 3) | (t & 16));
@@ -127,6 +163,53 @@ __device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t
                : "memory", "m0");
 }
 
+// Exact E4M3 -> bf16 of the two codes in the low (kHi = false) or high 16 bits of v.
+// Inline asm: the builtin's bf16x2 result is split wrongly by the compiler.  The pad
+// keeps two wait states between this VALU write and an MFMA that reads the result.
+template <bool kHi>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t v) {
+  uint32_t r;
+  if constexpr (kHi)
+    asm volatile("v_cvt_scalef32_pk_bf16_fp8 %0, %1, 1.0 op_sel:[1,0,0]\n\ts_nop 1" : "=v"(r) : "v"(v));
+  else
+    asm volatile("v_cvt_scalef32_pk_bf16_fp8 %0, %1, 1.0\n\ts_nop 1" : "=v"(r) : "v"(v));
+  return r;
+}
+// 8 codes (two dwords) -> one bf16x8 MFMA operand.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 r{fp8x2_to_bf16x2<false>(lo), fp8x2_to_bf16x2<true>(lo), fp8x2_to_bf16x2<false>(hi),
+                fp8x2_to_bf16x2<true>(hi)};
+  return __builtin_bit_cast(bf16x8, r);
+}
+// FP8 latent row swizzle: chunk c of token t at 16-byte position c ^ swz8(t).
+__device__ __forceinline__ uint32_t swz8(int t) { return static_cast<uint32_t>(2 * (t & 15)); }
+
+// FP8 form: copy `row` (0..10) of this wave's share of a page into stage `c_base`: rows
+// 0..7 are the latent rows of tokens 16w + 2 row and 16w + 2 row + 1 (512 B each, one per
+// lane half), rows 8, 9 the RoPE rows of tokens 16w + 8 (row - 8) .. +7, row 10 the scales
+// of tokens 16w .. 16w+15 (lanes 0..3).  Rows at or past n_valid fetch token 0.
+__device__ __forceinline__ void load_row8(uint32_t c_base, const char* page, int n_valid,
+                                          int wave, int lane, int row) {
+  if (row < 8) {
+    const int t0 = wave * 16 + 2 * row;
+    const int t = t0 + (lane >> 5);
+    const int src_t = t < n_valid ? t : 0;
+    dma16(page, static_cast<uint32_t>(src_t * kDc + (((lane & 31) ^ static_cast<int>(swz8(t))) << 4)),
+          c_base + t0 * kDc);
+  } else if (row < 10) {
+    const int t0 = wave * 16 + 8 * (row - 8);
+    const int t = t0 + (lane >> 3);
+    const int src_t = t < n_valid ? t : 0;
+    dma16(page, static_cast<uint32_t>(kR8Off + src_t * 128 + (((lane & 7) ^ ((t >> 2) & 7)) << 4)),
+          c_base + kR8Off + t0 * 128);
+  } else if (lane < 4) {
+    // Scales of tokens past n_valid may be anything: the softmax masks those tokens and
+    // their P entries are set to 0, not multiplied by the scale.
+    dma16(page, static_cast<uint32_t>(kS8Off + wave * 64 + 16 * lane), c_base + kS8Off + wave * 64);
+  }
+}
+
 // Copy `row` (0..17) of this wave's share of a page into stage `c_base`: rows 0..15 are
 // the latent rows of tokens 16w + row (1 KB each), rows 16, 17 the RoPE rows of tokens
 // 16w + 8 (row - 16) .. +7.  Rows at or past n_valid fetch token 0 (always valid).
@@ -151,9 +234,10 @@ __device__ __forceinline__ void load_row(uint32_t c_base, const char* page, int 
 // HS = 2: two workgroups of 64 heads per (token, split).  Wave w owns heads
 // 32 (w % 2) .. +31 of its half over tokens 32 (w / 2) .. +31 of each page; waves w and
 // w ^ 2 (same heads, other token half) merge their outputs through LDS at the end.
-template <int HS>
+template <int HS, bool F8>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 decode_m32_kernel(DecodeArgs a) {
+  using Fm = Form<F8>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int S = a.num_splits;
   // Launch order.  The units of sequence b (its n query tokens x S splits) are the
@@ -200,12 +284,23 @@ decode_m32_kernel(DecodeArgs a) {
   };
   auto page_ptr = [&](int i) {
     const int id = clamp_page(__builtin_amdgcn_readlane(pid_v, i & 63), a.num_pool_pages);
-    return kv + static_cast<size_t>(id) * kTok * kRowBytes;
+    return kv + static_cast<size_t>(id) * Fm::kPage;
   };
   fetch_ids(0);
   const uint32_t smem_base = lds_addr(smem);
   int j0 = w.k0;
-  {
+  if constexpr (F8) {  // pages 0 and 1 into stages 0 and 1
+    const char* p0 = page_ptr(0);
+    const int nv = min(kTok, w.k1 - j0);
+#pragma unroll
+    for (int r = 0; r < kCopies8; ++r) load_row8(smem_base, p0, nv, wave, lane, r);
+    if (n_split_pages > 1) {
+      const char* p1 = page_ptr(1);
+      const int nv1 = min(kTok, w.k1 - j0 - kTok);
+#pragma unroll
+      for (int r = 0; r < kCopies8; ++r) load_row8(smem_base + kStage8Bytes, p1, nv1, wave, lane, r);
+    }
+  } else {
     const char* p0 = page_ptr(0);
     const int nv = min(kTok, w.k1 - j0);
 #pragma unroll
@@ -218,8 +313,12 @@ decode_m32_kernel(DecodeArgs a) {
   {
     const uint16_t* qa = static_cast<const uint16_t*>(a.q_abs) +
                          (static_cast<size_t>(t) * kHeads + head) * kDc + 8 * h;
+    // FP8: K-step 2j + s takes dims 32 j + 16 h + 8 s .. +7 (one 16-byte LDS read of the
+    // codes then feeds K-steps 2j and 2j + 1); bf16: K-step k takes dims 16 k + 8 h .. +7.
 #pragma unroll
-    for (int k = 0; k < kQSteps; ++k) q[k] = *reinterpret_cast<const bf16x8*>(qa + 16 * k);
+    for (int k = 0; k < kQSteps; ++k)
+      q[k] = *reinterpret_cast<const bf16x8*>(
+          F8 ? qa + 32 * (k >> 1) + 8 * h + 8 * (k & 1) : qa + 16 * k);
   }
   if (th == 0) {
     const uint16_t* qr = static_cast<const uint16_t*>(a.q_r) +
@@ -241,7 +340,7 @@ decode_m32_kernel(DecodeArgs a) {
           x[2 * i + 1] = fmaf(x0, sn[i], x1 * cs[i]);
         }
       }
-      *(lds_bf16x8_t*)(uintptr_t)(smem_base + kQrOff + hl * 128 + ((c ^ ((hl >> 2) & 7)) << 4)) =
+      *(lds_bf16x8_t*)(uintptr_t)(smem_base + Fm::kQr + hl * 128 + ((c ^ ((hl >> 2) & 7)) << 4)) =
           to_bf16x8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
     }
   }
@@ -272,12 +371,35 @@ decode_m32_kernel(DecodeArgs a) {
   const uint32_t key_l = static_cast<uint32_t>((2 * (lg & 1) + ((li & 3) >> 1)) ^ (((li >> 2) << 2) | (lg >> 1)));
   const uint32_t o_lane = static_cast<uint32_t>(tok_l * 1024 + 8 * (li & 1)) | (key_l << 4);
 
+  // FP8 lane parts: score read of K-step pair j, block mb:
+  //   st + 16384 mb + n * 512 + 16 h + ((32 j) ^ (32 (n mod 16)));
+  // transposing output read of (nb, mb, q): lane jj = lane % 16 of group g = lane / 16 supplies
+  //   row e = jj / 2 (token T = 32 mb + 16 q + tl, tl = 8 (e / 4) + 4 (g / 2) + e % 4), bytes
+  //   8 (jj % 2) .. +7 of chunk 2 nb + g % 2:
+  //   st + (32 mb + 16 q) * 512 + tl * 512 + 16 (g % 2) + 8 (jj % 2) + ((32 nb) ^ (32 tl)).
+  const uint32_t s8_lane = static_cast<uint32_t>(n * 512 + 16 * h);
+  const uint32_t s8_x = static_cast<uint32_t>(32 * (n & 15));
+  const int tl8 = 8 * ((li >> 1) >> 2) + 4 * (lg >> 1) + ((li >> 1) & 3);
+  const uint32_t o8_lane = static_cast<uint32_t>(tl8 * 512 + 16 * (lg & 1) + 8 * (li & 1));
+  const uint32_t o8_x = static_cast<uint32_t>(32 * tl8);
+
   int stage = 0;
   for (; j0 < w.k1; j0 += kTok) {
     const int n_valid = min(kTok, w.k1 - j0);
-    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's page copies have landed
-    __syncthreads();                     // ... and every wave's; the other stage is free again
-    const int j_next = j0 + kTok;
+    if constexpr (F8) {
+      // This wave's copies of this page have landed once at most the next page's are
+      // still in flight (vector-memory operations complete in issue order).
+      if (j0 + kTok < w.k1)
+        __builtin_amdgcn_s_waitcnt(0x0f70 | kCopies8);  // vmcnt(11)
+      else
+        __builtin_amdgcn_s_waitcnt(0x0f70);             // vmcnt(0)
+    } else {
+      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's page copies have landed
+    }
+    __syncthreads();  // ... and every wave's; the stage of the previous page is free again
+    // The page whose copies this iteration issues: the next one (bf16, two stages) or the
+    // one after (FP8, three stages).
+    const int j_next = j0 + (F8 ? 2 : 1) * kTok;
     const bool has_next = j_next < w.k1;
     const char* next_page = kv;
     const int next_valid = min(kTok, w.k1 - j_next);
@@ -286,15 +408,91 @@ decode_m32_kernel(DecodeArgs a) {
       if ((i_next & 63) == 0) fetch_ids(i_next >> 6);
       next_page = page_ptr(i_next);
     }
-    const uint32_t next_base = smem_base + (stage ^ 1) * kStageBytes;
-    const uint32_t st_base = smem_base + stage * kStageBytes;
+    const int next_stage = F8 ? (stage == 0 ? 2 : stage - 1) : (stage ^ 1);
+    const uint32_t next_base = smem_base + next_stage * Fm::kStage;
+    const uint32_t st_base = smem_base + stage * Fm::kStage;
     const uint32_t sb = opaque(st_base + s_lane);
 
     // ---- scores.  HS = 1: RoPE steps, then the latent steps, the two 32-token blocks
     // alternating.  HS = 2: this wave's one 32-token block, two chains over alternate
     // K-steps (summed below).
     f32x16 s[2];
-    {
+    if constexpr (F8) {
+      // Latent K-step pairs first.  HS = 1: per pair, one read for each 32-token block and
+      // four MFMAs, the two blocks' chains alternating.  HS = 2: this wave's block, the two
+      // chains taking the pair's first and second K-step (summed below).
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
+      constexpr int kPairs = kDc / 32;
+      constexpr int kMBs = HS == 1 ? 2 : 1;
+      const uint32_t sb8 = opaque(st_base + s8_lane);
+      auto rd = [&](int j, int mb) {
+        return *(const lds_u32x4_t*)(uintptr_t)(sb8 + 16384 * (HS == 1 ? mb : th) +
+                                                 ((32u * static_cast<uint32_t>(j)) ^ s8_x));
+      };
+      u32x4 raw[3][kMBs];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int mb = 0; mb < kMBs; ++mb) raw[j][mb] = rd(j, mb);
+#pragma unroll
+      for (int j = 0; j < kPairs; ++j) {
+        u32x4 cur[kMBs];
+#pragma unroll
+        for (int mb = 0; mb < kMBs; ++mb) cur[mb] = raw[j % 3][mb];
+        if (j + 2 < kPairs) {
+#pragma unroll
+          for (int mb = 0; mb < kMBs; ++mb) raw[(j + 2) % 3][mb] = rd(j + 2, mb);
+        }
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+          for (int mb = 0; mb < kMBs; ++mb) {
+            const bf16x8 af = fp8x8_to_bf16x8(cur[mb][2 * sub], cur[mb][2 * sub + 1]);
+            f32x16& acc = s[HS == 1 ? mb : sub];
+            if (j == 0 && (HS == 1 ? sub == 0 : true))
+              mfma32_first(acc, af, q[2 * j + sub]);
+            else
+              mfma32_acc(acc, af, q[2 * j + sub]);
+          }
+        }
+        if (j < kCopies8 && has_next)
+          load_row8(next_base, next_page, next_valid, wave, static_cast<int>(opaque(lane)), j);
+      }
+      // Latent part times the token's scale, then the RoPE K-steps on top.
+      mfma_results_ready(s[0], s[1]);
+      if constexpr (HS == 2) s[0] += s[1];
+#pragma unroll
+      for (int mb = 0; mb < kMBs; ++mb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x4 sc = *(const lds_f32x4_t*)(uintptr_t)(
+              st_base + kS8Off + 4 * (32 * (HS == 1 ? mb : th) + 8 * g + 4 * h));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) s[mb][4 * g + i] *= sc[i];
+        }
+      // wait states between these vector-ALU writes and the MFMAs that read them as srcC
+      asm volatile("s_nop 7" : "+v"(s[0]), "+v"(s[1]));
+      const uint32_t rb = opaque(st_base + kR8Off + n * 128);
+      const uint32_t qb = smem_base + kQrOff8 + hl * 128;
+      const int swr = (n >> 2) & 7, swq = (hl >> 2) & 7;
+#pragma unroll
+      for (int rs = 0; rs < kRSteps; ++rs) {
+        const int c = 2 * rs + h;
+        const bf16x8 qrf = lds_read8(qb + ((c ^ swq) << 4));
+        if constexpr (HS == 1) {
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+            mfma32_acc(s[mb], lds_read8(rb + ((c ^ swr) << 4) + 4096 * mb), qrf);
+        } else {
+          const bf16x8 cf = lds_read8(rb + ((c ^ swr) << 4) + 4096 * th);
+          if (rs == 1)
+            mfma32_first(s[1], cf, qrf);
+          else
+            mfma32_acc(s[rs & 1], cf, qrf);
+        }
+      }
+    } else {
       const uint32_t rb = opaque(st_base + kCBytes + n * 128);
       const uint32_t qb = smem_base + kQrOff + hl * 128;
       const int swr = (n >> 2) & 7, swq = (hl >> 2) & 7;
@@ -319,8 +517,6 @@ decode_m32_kernel(DecodeArgs a) {
             mfma32_acc(s[rs & 1], cf, qrf);
         }
       }
-    }
-    {
       constexpr int kSteps = 2 * kQSteps / HS;  // (ks, mb) steps, or ks steps with HS = 2
       constexpr int kRing = 4;
       auto frag = [&](int st) {
@@ -398,6 +594,20 @@ decode_m32_kernel(DecodeArgs a) {
         psum += p;
       }
     l_run += psum;
+    if constexpr (F8) {
+      // P^T times each token's scale (the latent rows are code * scale); tokens past the
+      // page's keys get 0 whatever their scale slot holds.
+#pragma unroll
+      for (int mb = 0; mb < kBlocks; ++mb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int tok = 32 * (HS == 1 ? mb : th) + 8 * g + 4 * h;
+          const f32x4 sc = *(const lds_f32x4_t*)(uintptr_t)(st_base + kS8Off + 4 * tok);
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            s[mb][4 * g + i] = tok + i < n_valid ? s[mb][4 * g + i] * sc[i] : 0.f;
+        }
+    }
 
     // ---- P^T operands: K-step kq = 2 mb + q holds elements 8q .. 8q+7 of block mb
     constexpr int kKQ = 4 / HS;  // 16-token K-steps of the output
@@ -411,7 +621,31 @@ decode_m32_kernel(DecodeArgs a) {
 
     // ---- O^T[cols 32 nb .. +31] += C^T . P^T, (kq, nb) steps through a ring
     const uint32_t ob = opaque(st_base + o_lane);
-    {
+    if constexpr (F8) {
+      typedef int i32x2 __attribute__((ext_vector_type(2)));
+      typedef __attribute__((address_space(3))) i32x2 lds_i32x2_t;
+      constexpr int kSteps = kKQ * kColBlocks;
+      constexpr int kRing = 4;
+      const uint32_t ob8 = opaque(st_base + o8_lane);
+      auto frag = [&](int st) {
+        const int kq = st / kColBlocks, nb = st % kColBlocks;
+        const int mb = HS == 1 ? kq >> 1 : th, qq = HS == 1 ? (kq & 1) : kq;
+        const uint32_t addr = ob8 + static_cast<uint32_t>((32 * mb + 16 * qq) * 512) +
+                              ((32u * static_cast<uint32_t>(nb)) ^ o8_x);
+        return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(uintptr_t)addr);
+      };
+      i32x2 ring[kRing];
+#pragma unroll
+      for (int st = 0; st < kRing; ++st) ring[st] = frag(st);
+#pragma unroll
+      for (int st = 0; st < kSteps; ++st) {
+        const i32x2 raw8 = ring[st % kRing];
+        if (st + kRing < kSteps) ring[st % kRing] = frag(st + kRing);
+        const bf16x8 cf = fp8x8_to_bf16x8(static_cast<uint32_t>(raw8[0]), static_cast<uint32_t>(raw8[1]));
+        const int kq = st / kColBlocks, nb = st % kColBlocks;
+        o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cf, pb[kq], o[nb], 0, 0, 0);
+      }
+    } else {
       constexpr int kSteps = kKQ * kColBlocks;
       constexpr int kRing = 4;
       auto frag = [&](int st) {
@@ -445,7 +679,7 @@ decode_m32_kernel(DecodeArgs a) {
     // allocator otherwise moves some of them to VGPRs and spills).
 #pragma unroll
     for (int nb = 0; nb < kColBlocks; ++nb) asm volatile("" : "+a"(o[nb]));
-    stage ^= 1;
+    stage = F8 ? (stage == 2 ? 0 : stage + 1) : (stage ^ 1);
   }
 
   // ---- finalize: normalise and write this split's partial output (bf16) and LSE
@@ -527,19 +761,27 @@ bool decode_m32_supported(const DecodeArgs& a, bool bf16) {
          a.page_size == kTok;
 }
 
-template <int HS>
+template <int HS, bool F8>
 hipError_t launch_decode_m32_k(const DecodeArgs& a, hipStream_t s) {
   static std::atomic<uint64_t> lds_limit_set{0};
-  const hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(decode_m32_kernel<HS>), kLdsBytes,
-                                        lds_limit_set);
+  const hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(decode_m32_kernel<HS, F8>),
+                                        Form<F8>::kLds, lds_limit_set);
   if (e != hipSuccess) return e;
   const dim3 grid(a.total_q * a.num_splits * HS);
-  decode_m32_kernel<HS><<<grid, kThreads, kLdsBytes, s>>>(a);
+  decode_m32_kernel<HS, F8><<<grid, kThreads, Form<F8>::kLds, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_m32(const DecodeArgs& a, int head_split, hipStream_t s) {
-  return head_split == 2 ? launch_decode_m32_k<2>(a, s) : launch_decode_m32_k<1>(a, s);
+  return head_split == 2 ? launch_decode_m32_k<2, false>(a, s) : launch_decode_m32_k<1, false>(a, s);
+}
+
+bool decode_fp8_supported(const DecodeArgs& a) {
+  return a.heads == kHeads && a.groups == 1 && a.d_c == kDc && a.d_R == kDr && a.page_size == kTok;
+}
+
+hipError_t launch_decode_fp8(const DecodeArgs& a, int head_split, hipStream_t s) {
+  return head_split == 2 ? launch_decode_m32_k<2, true>(a, s) : launch_decode_m32_k<1, true>(a, s);
 }
 
 }  // namespace mla

@@ -70,6 +70,8 @@ struct AppendArgs {
   int d_c, d_R, page_size;
 };
 hipError_t launch_append_kv(const AppendArgs& a, bool bf16, hipStream_t s);
+// FP8 cache: bf16 inputs, pages of [64][d_c] E4M3 codes, [64][d_R] bf16 k_R, [64] f32 scales.
+hipError_t launch_append_kv_fp8(const AppendArgs& a, hipStream_t s);
 
 // Generic kernels: any (d_cg <= 1024, d_R <= 256), bf16 or fp32 storage.
 hipError_t launch_absorb_generic(const void* q_c, const void* w_uk, void* q_abs, int T, int H,
@@ -98,6 +100,10 @@ bool decode_mfma_supported(const DecodeArgs& a, bool bf16);
 // workgroups of 64 heads, each wave covering half of every page's tokens (head split 2).
 bool decode_m32_supported(const DecodeArgs& a, bool bf16);
 hipError_t launch_decode_m32(const DecodeArgs& a, int head_split, hipStream_t s);
+// The same kernel over an FP8 cache (pages of [64][512] E4M3 codes, [64][64] bf16 k_R and
+// [64] float32 scales): 128 heads, one latent group, d_c 512, d_R 64.
+bool decode_fp8_supported(const DecodeArgs& a);
+hipError_t launch_decode_fp8(const DecodeArgs& a, int head_split, hipStream_t s);
 int decode_mfma_head_split(const DecodeArgs& a, int cu_count);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int head_split, hipStream_t s);
 }  // namespace mla

@@ -36,8 +36,10 @@ def _storage_tensor(w: Workload, x: np.ndarray, device) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
 
 
-def to_device(w: Workload, device="cuda", *, rope: bool = True) -> DeviceWorkload:
-    """Copy ``w`` to ``device``; with ``rope`` the fp32 table is built there by the library."""
+def to_device(w: Workload, device="cuda", *, rope: bool = True,
+              kv: Optional[np.ndarray] = None) -> DeviceWorkload:
+    """Copy ``w`` to ``device``; with ``rope`` the fp32 table is built there by the library.
+    ``kv`` replaces the workload's bf16 pool (an FP8 pool: uint8 [P, page bytes])."""
     dev = torch.device(device)
     table = None
     if rope and w.cfg.rope_base is not None:
@@ -48,7 +50,7 @@ def to_device(w: Workload, device="cuda", *, rope: bool = True) -> DeviceWorkloa
         q_r=_storage_tensor(w, w.q_r, dev),
         w_uk=_storage_tensor(w, w.w_uk, dev),
         w_uv=_storage_tensor(w, w.w_uv, dev),
-        kv=_storage_tensor(w, w.pool, dev),
+        kv=_storage_tensor(w, w.pool, dev) if kv is None else torch.from_numpy(kv).to(dev),
         page_table=torch.from_numpy(w.page_table).to(dev),
         seq_lens=torch.from_numpy(w.seq_lens).to(dev),
         cu_q=torch.from_numpy(w.cu_q).to(dev),
@@ -71,3 +73,25 @@ def new_tokens_to_device(w: Workload, new: NewTokens, device="cuda"):
     """(c_kv_new, k_r_new) device tensors of the storage dtype for ``mla.append_kv``."""
     dev = torch.device(device)
     return _storage_tensor(w, new.c_kv, dev), _storage_tensor(w, new.k_r, dev)
+
+
+def fp8_pool_by_append(w: Workload, d: DeviceWorkload) -> torch.Tensor:
+    """An FP8 cache holding ``w``'s sequences, written by the library's FP8 append
+    (mla_append_kv_fp8) from the bf16 rows already on the device: every sequence appended
+    whole from position 0, k_R copied unrotated (it is stored rotated already).  Unused
+    slots hold 0xFF bytes (NaN codes, NaN k_R, NaN scales)."""
+    cfg = w.cfg
+    ps = cfg.page_size
+    lens = [int(L) for L in w.seq_lens]
+    idx = np.concatenate([
+        w.page_table[b, np.arange(L) // ps].astype(np.int64) * ps + np.arange(L) % ps
+        for b, L in enumerate(lens) if L > 0] or [np.zeros(0, np.int64)])
+    rows = d.kv.view(-1, cfg.row)[torch.from_numpy(idx).to(d.kv.device)]
+    c = rows[:, :cfg.d_c].contiguous()
+    k = rows[:, cfg.d_c:].contiguous()
+    P = w.num_pool_pages
+    kv8 = torch.full((P, mla.fp8_page_bytes(cfg.d_c, cfg.d_R)), 0xFF, dtype=torch.uint8,
+                     device=d.kv.device)
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).to(d.kv.device)
+    mla.append_kv_fp8(c, k, kv8, d.page_table, d.seq_lens, cu)
+    return kv8

@@ -23,7 +23,7 @@ PAGE_SIZE = 64
 
 EXPORTED = ("mla_absorb_q", "mla_rope_table", "mla_decode_paged", "mla_combine", "mla_up_v",
             "mla_append_kv", "mla_decode_workspace_bytes", "mla_decode_plan", "mla_attend_noalloc",
-            "mla_status_string")
+            "mla_decode_paged_fp8", "mla_append_kv_fp8", "mla_fp8_page_bytes", "mla_status_string")
 
 _lib = None
 
@@ -55,10 +55,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.mla_decode_plan.argtypes = [P, P, I, I, I, P, P]
     lib.mla_attend_noalloc.argtypes = ([P] * 8 + [I] + [P] * 2 + [I] * 12 + [F, I, I, P])
+    lib.mla_decode_paged_fp8.argtypes = ([P] * 8 + [I] + [P] * 2 + [I] * 12 + [F, I, P])
+    lib.mla_append_kv_fp8.argtypes = [P] * 8 + [I] * 8 + [P]
+    lib.mla_fp8_page_bytes.argtypes = [I, I]
+    lib.mla_fp8_page_bytes.restype = ctypes.c_size_t
     lib.mla_status_string.argtypes = [I]
     lib.mla_status_string.restype = ctypes.c_char_p
     for name in ("mla_absorb_q", "mla_rope_table", "mla_decode_paged", "mla_combine", "mla_up_v",
-                 "mla_append_kv", "mla_decode_plan", "mla_attend_noalloc"):
+                 "mla_append_kv", "mla_decode_plan", "mla_attend_noalloc", "mla_decode_paged_fp8",
+                 "mla_append_kv_fp8"):
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -191,6 +196,68 @@ def decode_paged(q_abs, q_r, kv_cache, page_table, seq_lens, cu_q, o_part, lse_p
         B, T, max_pages, P, H, groups, d_hc, d_cg * groups, d_R, ps, S, int(pages_per_split),
         float(softmax_scale),
         int(bool(causal)), _dtype_code(q_abs), _stream(stream)))
+
+
+def fp8_page_bytes(d_c: int, d_R: int) -> int:
+    """Bytes of one FP8 cache page: 64 x (d_c E4M3 codes + d_R bf16 + one float32 scale)."""
+    return int(load().mla_fp8_page_bytes(int(d_c), int(d_R)))
+
+
+def decode_paged_fp8(q_abs, q_r, kv_fp8, page_table, seq_lens, cu_q, o_part, lse_part, *,
+                     d_hc: int, d_R: int, groups: int = 1, rope: Optional[tuple] = None,
+                     softmax_scale: float = 0.0, causal: bool = True, pages_per_split: int = 0,
+                     stream=None) -> None:
+    """mla_decode_paged over an FP8 cache kv_fp8 (uint8 [P, fp8_page_bytes(d_c, d_R)]):
+    bf16 queries and partials, as mla_decode_paged."""
+    T, H, d_cg = q_abs.shape
+    P, page_bytes = kv_fp8.shape
+    B, max_pages = page_table.shape
+    S = o_part.shape[2]
+    d_c = d_cg * groups
+    if kv_fp8.dtype != torch.uint8 or page_bytes != fp8_page_bytes(d_c, d_R):
+        raise ValueError("kv_fp8 must be uint8 [P, fp8_page_bytes(d_c, d_R)]")
+    if q_abs.dtype != torch.bfloat16 or q_r.dtype != torch.bfloat16:
+        raise TypeError("the FP8 cache decode takes bf16 queries")
+    if q_r.shape != (T, H, d_R):
+        raise ValueError("q_r must be [T, H, d_R]")
+    _expect("o_part", o_part, (T, H, S, d_cg), torch.bfloat16)
+    _expect("lse_part", lse_part, (T, H, S), torch.float32)
+    for t in (page_table, seq_lens, cu_q):
+        if t.dtype != torch.int32:
+            raise TypeError(f"expected int32, got {t.dtype}")
+    if seq_lens.shape != (B,) or cu_q.shape != (B + 1,):
+        raise ValueError("seq_lens must be [B] and cu_q [B+1]")
+    cos, sin, rope_max_pos = _rope_pair(rope, d_R, q_abs.device)
+    _dev(q_abs, q_r, kv_fp8, page_table, seq_lens, cu_q, o_part, lse_part, cos, sin)
+    _check("mla_decode_paged_fp8", load().mla_decode_paged_fp8(
+        _ptr(q_abs), _ptr(q_r), _ptr(kv_fp8), _ptr(page_table), _ptr(seq_lens), _ptr(cu_q),
+        _ptr(cos), _ptr(sin), rope_max_pos, _ptr(o_part), _ptr(lse_part),
+        B, T, max_pages, P, H, groups, d_hc, d_c, d_R, 64, S, int(pages_per_split),
+        float(softmax_scale), int(bool(causal)), _stream(stream)))
+
+
+def append_kv_fp8(c_kv_new, k_r_new, kv_fp8, page_table, seq_lens, cu_q, *,
+                  rope: Optional[tuple] = None, stream=None) -> None:
+    """Quantize the new tokens' latents into the FP8 cache kv_fp8 (uint8 [P, page bytes]):
+    codes and scale per token, k_R rotated at its position and kept bf16."""
+    T, d_c = c_kv_new.shape
+    d_R = k_r_new.shape[1]
+    P, page_bytes = kv_fp8.shape
+    B, max_pages = page_table.shape
+    if k_r_new.shape[0] != T or c_kv_new.dtype != torch.bfloat16 or k_r_new.dtype != torch.bfloat16:
+        raise ValueError("c_kv_new [T, d_c] and k_r_new [T, d_R] must be bf16")
+    if kv_fp8.dtype != torch.uint8 or page_bytes != fp8_page_bytes(d_c, d_R):
+        raise ValueError("kv_fp8 must be uint8 [P, fp8_page_bytes(d_c, d_R)]")
+    for t in (page_table, seq_lens, cu_q):
+        if t.dtype != torch.int32:
+            raise TypeError(f"expected int32, got {t.dtype}")
+    if seq_lens.shape != (B,) or cu_q.shape != (B + 1,):
+        raise ValueError("seq_lens must be [B] and cu_q [B+1]")
+    cos, sin, rope_max_pos = _rope_pair(rope, d_R, kv_fp8.device)
+    _dev(c_kv_new, k_r_new, kv_fp8, page_table, seq_lens, cu_q, cos, sin)
+    _check("mla_append_kv_fp8", load().mla_append_kv_fp8(
+        _ptr(c_kv_new), _ptr(k_r_new), _ptr(kv_fp8), _ptr(page_table), _ptr(seq_lens), _ptr(cu_q),
+        _ptr(cos), _ptr(sin), rope_max_pos, B, T, max_pages, P, d_c, d_R, 64, _stream(stream)))
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -331,6 +398,12 @@ class DecodeStep:
         absorb_q(self.q_c, self.w_uk, self.q_abs, groups=self.groups, stream=stream)
 
     def attend(self, stream=None):
+        if self.kv.dtype == torch.uint8:  # FP8 cache pages
+            decode_paged_fp8(self.q_abs, self.q_r, self.kv, self.page_table, self.seq_lens, self.cu_q,
+                             self.o_part, self.lse_part, d_hc=self.d_hc, d_R=self.q_r.shape[2],
+                             groups=self.groups, rope=self.rope, causal=self.causal,
+                             pages_per_split=self.pages_per_split, stream=stream)
+            return
         decode_paged(self.q_abs, self.q_r, self.kv, self.page_table, self.seq_lens, self.cu_q,
                      self.o_part, self.lse_part, d_hc=self.d_hc, groups=self.groups, rope=self.rope,
                      causal=self.causal, pages_per_split=self.pages_per_split, stream=stream)

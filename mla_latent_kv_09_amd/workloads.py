@@ -286,3 +286,33 @@ def gather_sequence(w: Workload, b: int) -> np.ndarray:
     n = (L + ps - 1) // ps
     pages = w.pool[w.page_table[b, :n]].reshape(n * ps, w.cfg.row)[:L]
     return bf16_bits_to_f32(pages) if w.cfg.dtype == "bf16" else pages.astype(np.float32)
+
+
+def fp8_pool(w: Workload, codes: Sequence, scales: Sequence, *, nan_fill: bool = True) -> np.ndarray:
+    """Place per-sequence FP8 latent codes (uint8 [L_b, d_c]) and token scales (float32
+    [L_b]) into FP8 cache pages laid out as {codes [64][d_c] | k_R [64][d_R] bf16 |
+    scales [64] float32}, the k_R rows taken from ``w``'s bf16 pool.  Pure data placement:
+    the codes and scales are given.  Slots past a sequence's end hold NaN codes (0x7F),
+    NaN k_R and NaN scales when ``nan_fill``.  Returns uint8 [P, 64 (d_c + 2 d_R + 4)]."""
+    cfg = w.cfg
+    if cfg.dtype != "bf16":
+        raise ValueError("FP8 pages take a bf16 workload's k_R rows")
+    ps, d_c, d_R = cfg.page_size, cfg.d_c, cfg.d_R
+    P = w.num_pool_pages
+    pool = np.zeros((P, ps * (d_c + 2 * d_R + 4)), np.uint8)
+    code_part = pool[:, : ps * d_c].reshape(P, ps, d_c)
+    rope_part = pool[:, ps * d_c: ps * (d_c + 2 * d_R)].view(np.uint16).reshape(P, ps, d_R)
+    scale_part = pool[:, ps * (d_c + 2 * d_R):].view(np.float32).reshape(P, ps)
+    if nan_fill:
+        code_part[...] = 0x7F
+        rope_part[...] = BF16_NAN_BITS
+        scale_part[...] = np.nan
+    for b in range(len(w.seq_lens)):
+        L = int(w.seq_lens[b])
+        for k in range((L + ps - 1) // ps):
+            pg = int(w.page_table[b, k])
+            n = min(ps, L - k * ps)
+            code_part[pg, :n] = codes[b][k * ps: k * ps + n]
+            scale_part[pg, :n] = scales[b][k * ps: k * ps + n]
+            rope_part[pg, :n] = w.pool[pg, :n, d_c:]
+    return pool

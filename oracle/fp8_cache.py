@@ -74,8 +74,12 @@ def quantize_rows(latent) -> tuple[np.ndarray, np.ndarray]:
     x = np.asarray(latent, dtype=np.float32)
     amax = np.max(np.abs(x), axis=-1)
     scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
-    q = (x / scale[..., None]).astype(np.float32)
-    return e4m3_round(q), scale
+    codes = np.empty(x.shape, np.uint8)
+    step = 4096  # rows at a time (the same arithmetic, in cache-sized pieces)
+    for r in range(0, x.shape[0], step):
+        q = (x[r:r + step] / scale[r:r + step, None]).astype(np.float32)
+        codes[r:r + step] = e4m3_round(q)
+    return codes, scale
 
 
 def dequantize_rows(codes, scales) -> np.ndarray:
