@@ -54,18 +54,27 @@ FP32_PEAK_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode.json")
 CSRC = os.path.join(ROOT, "mla_latent_kv_09_amd", "csrc")
 KERNEL_SRC = {"decode_mfma_kernel": "decode_mfma.hip", "decode_m32_kernel": "decode_m32.hip",
-              "decode_generic_kernel": "kernels_generic.hip"}
+              "decode_m32_kernel_fp8": "decode_m32.hip", "decode_generic_kernel": "kernels_generic.hip"}
 
 
-def algorithmic_work(cfg, seq_lens, q_lens):
+def cache_row_bytes(cfg, kv_dtype="bf16"):
+    """Bytes one token occupies in the latent cache: d_c + d_R elements of the storage
+    type, or for the FP8 cache d_c E4M3 codes, d_R bf16 and one float32 scale."""
+    if kv_dtype == "fp8":
+        return cfg.d_c + 2 * cfg.d_R + 4
+    return (cfg.d_c + cfg.d_R) * (2 if cfg.dtype == "bf16" else 4)
+
+
+def algorithmic_work(cfg, seq_lens, q_lens, kv_dtype="bf16"):
     """(attention flops, projection flops, latent-KV bytes, weight bytes) of one step.
 
     Per (query row, visible key): 2*(d_c/G + d_R) flops for the score and 2*d_c/G for
-    P.c_KV.  Latent rows are counted once per sequence (d_c + d_R elements).  The two
+    P.c_KV.  Latent rows are counted once per sequence (cache_row_bytes each).  The two
     projections are 2*T*H*d_hc*d_c/G flops each.
     """
     d_cg = cfg.d_c // cfg.groups
     elem = 2 if cfg.dtype == "bf16" else 4
+    row_bytes = cache_row_bytes(cfg, kv_dtype)
     per_key = cfg.heads * (2 * (d_cg + cfg.d_R) + 2 * d_cg)
     att = 0
     kv_bytes = 0
@@ -73,7 +82,7 @@ def algorithmic_work(cfg, seq_lens, q_lens):
         L, q = int(L), int(q)
         for i in range(q):
             att += per_key * (L - q + i + 1 if cfg.causal else L)
-        kv_bytes += L * (cfg.d_c + cfg.d_R) * elem
+        kv_bytes += L * row_bytes
     T = int(sum(q_lens))
     proj = 2 * (2 * T * cfg.heads * cfg.d_hc * d_cg)
     w_bytes = 2 * cfg.heads * cfg.d_hc * d_cg * elem
@@ -250,6 +259,9 @@ def main():
                     help="one input copy and a 1 GiB read-only cache flush before every step, "
                          "each step timed alone (the earlier method) instead of rotating copies")
     ap.add_argument("--no-graph", action="store_true", help="launch the calls eagerly")
+    ap.add_argument("--kv-dtype", choices=["bf16", "fp8"], default="bf16",
+                    help="latent cache format: bf16 rows (default) or FP8 E4M3 pages written by "
+                         "mla_append_kv_fp8 (a separate line, never the headline)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the decode path is built "
@@ -268,7 +280,10 @@ def main():
 
     cfg = wl.CONFIGS[args.config]
     w = wl.make_workload(cfg)
-    att, proj, kv_bytes, w_bytes = algorithmic_work(cfg, w.seq_lens, w.q_lens)
+    if args.kv_dtype == "fp8" and args.flush:
+        print("--kv-dtype fp8 takes the default (rotated copies) timing", file=sys.stderr)
+        sys.exit(2)
+    att, proj, kv_bytes, w_bytes = algorithmic_work(cfg, w.seq_lens, w.q_lens, args.kv_dtype)
     stream = torch.cuda.current_stream()
     names = ["absorb_q", "decode_paged", "combine", "up_v"]
 
@@ -279,7 +294,8 @@ def main():
         # evicted from L2 and MALL: each step starts from HBM.  Steps and calls are
         # timed back to back inside HIP graphs, as a serving loop runs them.
         n_copies = max(2, min(8, math.ceil(2 * MALL_BYTES / (kv_bytes + w_bytes))))
-        steps = [harness.make_step(w, harness.to_device(w), args.splits, args.pages_per_split)
+        steps = [harness.make_step(w, device_copy(w, harness, args.kv_dtype), args.splits,
+                                   args.pages_per_split)
                  for _ in range(n_copies)]
         step = steps[0]
         S = step.num_splits
@@ -359,7 +375,7 @@ def main():
     peak_f = BF16_PEAK_TFLOPS if cfg.dtype == "bf16" else FP32_PEAK_TFLOPS
     t_hbm = kv_bytes / (HBM_PEAK_GBPS * 1e9)
     t_mfma = att / (peak_f * 1e12)
-    kernel = decode_kernel_name(cfg, int(w.total_q), S,
+    kernel = decode_kernel_name(cfg, int(w.total_q), S, args.kv_dtype,
                                 torch.cuda.get_device_properties(0).multi_processor_count)
     traffic = measured_traffic(kernel, cfg.name, S)
     if t_hbm >= t_mfma:
@@ -377,7 +393,8 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": cfg.dtype, "data": "synthetic",
-        "config": {"workload": cfg.name, "batch": cfg.batch, "heads": cfg.heads, "d_hc": cfg.d_hc,
+        "config": {"workload": cfg.name, "kv_cache": "fp8_e4m3" if args.kv_dtype == "fp8" else cfg.dtype,
+                   "batch": cfg.batch, "heads": cfg.heads, "d_hc": cfg.d_hc,
                    "d_c": cfg.d_c, "d_R": cfg.d_R, "groups": cfg.groups, "page_size": cfg.page_size,
                    "seq_len": cfg.seq_len, "seq_len_range": cfg.seq_len_range,
                    "total_q": int(w.total_q), "num_splits": S,
@@ -401,17 +418,20 @@ def measure_append(args, w, torch, harness, mla, wl, steps, runner, timed, reps,
     step): (1) this workload's T new rows per call, back to back over the rotated copies;
     (2) a prefill-shaped bulk append that writes every slot of the first sequences (at
     most 65536 rows; q_len = seq_len, so each sequence's rows 0 .. L-1), rotated over the
-    copies like the step, whose bytes (each row read once and written once: 2 (d_c + d_R)
-    elements) give the kernel's HBM roofline."""
+    copies like the step, whose bytes (each row read once and written once in the cache's
+    format) give the kernel's HBM roofline.  With --kv-dtype fp8 the call is
+    mla_append_kv_fp8, which also quantizes the latent."""
     cfg = w.cfg
     elem = 2 if cfg.dtype == "bf16" else 4
+    kv_dtype = args.kv_dtype
+    append = mla.append_kv_fp8 if kv_dtype == "fp8" else mla.append_kv
     n = len(steps)
     new = wl.make_new_tokens(w)
     tensors = [harness.new_tokens_to_device(w, new, st.kv.device) for st in steps]
 
     def call(i):
         st, (c, k) = steps[i % n], tensors[i % n]
-        return lambda: mla.append_kv(c, k, st.kv, st.page_table, st.seq_lens, st.cu_q, rope=st.rope)
+        return lambda: append(c, k, st.kv, st.page_table, st.seq_lens, st.cu_q, rope=st.rope)
 
     run = runner([call(i) for i in range(per_graph)])
     ms_t = statistics.median(timed(run, reps) / (reps * per_graph) for _ in range(5))
@@ -428,20 +448,30 @@ def measure_append(args, w, torch, harness, mla, wl, steps, runner, timed, reps,
 
     def bulk_call(i):
         st, (c, k) = steps[i % n], bulk_t[i % n]
-        return lambda: mla.append_kv(c, k, st.kv, st.page_table, st.seq_lens, cu, rope=st.rope)
+        return lambda: append(c, k, st.kv, st.page_table, st.seq_lens, cu, rope=st.rope)
 
     run = runner([bulk_call(i) for i in range(n)])
     bulk_reps = max(2, min(10, reps))
     ms_b = statistics.median(timed(run, bulk_reps) / (bulk_reps * n) for _ in range(5))
     del run, bulk_t
-    nbytes = 2 * nb * L * (cfg.d_c + cfg.d_R) * elem
+    # each row read once (bf16 or fp32 inputs) and written once in the cache's format
+    nbytes = nb * L * ((cfg.d_c + cfg.d_R) * elem + cache_row_bytes(cfg, kv_dtype))
     gbps = nbytes / (ms_b * 1e-3) / 1e9
     res["bulk"] = {"rows": nb * L, "ms": ms_b, "algorithmic_bytes": nbytes, "gbps": gbps,
                    "frac_hbm_peak": gbps / HBM_PEAK_GBPS}
     return res
 
 
-def decode_kernel_name(cfg, total_q, num_splits, cu_count=256):
+def device_copy(w, harness, kv_dtype):
+    """One device copy of the workload; with kv_dtype fp8 its cache replaced by FP8 pages
+    that the library's FP8 append writes from the bf16 rows (the bf16 pool is freed)."""
+    d = harness.to_device(w)
+    if kv_dtype == "fp8":
+        d.kv = harness.fp8_pool_by_append(w, d)
+    return d
+
+
+def decode_kernel_name(cfg, total_q, num_splits, kv_dtype="bf16", cu_count=256):
     """The decode kernel the library dispatches for this shape (same rule as the library:
     MLA_KV_DECODE_KERNEL = generic / mfma / mfma128 / mfma64 / mfma32[-128|-64]; by default, for one
     latent group, the 32x32x16 kernel when one workgroup per (token, split) fills the
@@ -449,6 +479,8 @@ def decode_kernel_name(cfg, total_q, num_splits, cu_count=256):
     mfma_shape = (cfg.dtype == "bf16" and cfg.heads == 128 and cfg.groups in (1, 2)
                   and cfg.d_c == 512 and cfg.d_R == 64 and cfg.page_size == 64)
     choice = os.environ.get("MLA_KV_DECODE_KERNEL", "")
+    if kv_dtype == "fp8":  # one kernel form over FP8 pages
+        return "decode_m32_kernel_fp8"
     if choice == "generic" or not mfma_shape:
         return "decode_generic_kernel"
     if cfg.groups != 1 or choice in ("mfma128", "mfma64"):

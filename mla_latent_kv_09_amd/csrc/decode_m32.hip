@@ -164,22 +164,24 @@ __device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t
 }
 
 // Exact E4M3 -> bf16 of the two codes in the low (kHi = false) or high 16 bits of v.
-// Inline asm: the builtin's bf16x2 result is split wrongly by the compiler.  The pad
-// keeps two wait states between this VALU write and an MFMA that reads the result.
+// Inline asm: the builtin's bf16x2 result is split wrongly by the compiler.
 template <bool kHi>
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t v) {
   uint32_t r;
   if constexpr (kHi)
-    asm volatile("v_cvt_scalef32_pk_bf16_fp8 %0, %1, 1.0 op_sel:[1,0,0]\n\ts_nop 1" : "=v"(r) : "v"(v));
+    asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, 1.0 op_sel:[1,0,0]" : "=v"(r) : "v"(v));
   else
-    asm volatile("v_cvt_scalef32_pk_bf16_fp8 %0, %1, 1.0\n\ts_nop 1" : "=v"(r) : "v"(v));
+    asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, 1.0" : "=v"(r) : "v"(v));
   return r;
 }
-// 8 codes (two dwords) -> one bf16x8 MFMA operand.
+// 8 codes (two dwords) -> one bf16x8 MFMA operand.  The pad, tied to the result, keeps
+// two wait states between the last conversion (a vector-ALU write the compiler does not
+// see as one) and the MFMA that reads the operand.
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 r{fp8x2_to_bf16x2<false>(lo), fp8x2_to_bf16x2<true>(lo), fp8x2_to_bf16x2<false>(hi),
-                fp8x2_to_bf16x2<true>(hi)};
+  u32x4 r{fp8x2_to_bf16x2<false>(lo), fp8x2_to_bf16x2<true>(lo), fp8x2_to_bf16x2<false>(hi),
+          fp8x2_to_bf16x2<true>(hi)};
+  asm("s_nop 1" : "+v"(r));
   return __builtin_bit_cast(bf16x8, r);
 }
 // FP8 latent row swizzle: chunk c of token t at 16-byte position c ^ swz8(t).

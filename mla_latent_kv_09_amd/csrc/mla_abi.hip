@@ -341,7 +341,13 @@ int mla_decode_paged_fp8(const void* q_abs, const void* q_r, const void* kv_cach
                                 page_size, num_splits, pages_per_split, softmax_scale, causal,
                                 MLA_DTYPE_BF16, true, &a, &bf16);
   if (st != MLA_OK) return st;
-  if (!mla::decode_fp8_supported(a)) return MLA_ERR_UNSUPPORTED;
+  mla::DecodeArgs shape{};
+  shape.heads = heads;
+  shape.groups = groups;
+  shape.d_c = d_c;
+  shape.d_R = d_R;
+  shape.page_size = page_size;
+  if (!mla::decode_fp8_supported(shape)) return MLA_ERR_UNSUPPORTED;
   if (total_q == 0) return MLA_OK;
   const DecodeKernel choice = decode_kernel_choice();
   a.head_split = choice == DecodeKernel::kMfma32x128 ? 1 : choice == DecodeKernel::kMfma32x64 ? 2 : 0;

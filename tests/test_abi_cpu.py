@@ -312,3 +312,64 @@ def test_noalloc_validation(lib, kw, code):
     """Every rejection happens on the host before any device call: the decode's own
     validation first, then the merge's output pointers, then the capacity."""
     assert _noalloc(lib, **kw) == code
+
+
+# -------------------------------------------------------------- FP8 cache entry points
+
+def test_fp8_page_bytes(lib):
+    assert lib.mla_fp8_page_bytes(512, 64) == 64 * (512 + 128 + 4) == 41216
+    assert lib.mla_fp8_page_bytes(64, 16) == 64 * (64 + 32 + 4)
+    assert lib.mla_fp8_page_bytes(0, 64) == 0 and lib.mla_fp8_page_bytes(512, 63) == 0
+
+
+def _decode8(lib, **kw):
+    a = dict(q=A, qr=A, kv=A, pt=A, sl=A, cu=A, cos=None, sin=None, rmp=0, op=A, lp=A,
+             B=16, T=16, maxp=64, pool=1024, H=128, G=1, d_hc=128, d_c=512, d_R=64, ps=64, S=16,
+             pps=0, scale=0.0, causal=1)
+    a.update(kw)
+    return lib.mla_decode_paged_fp8(a["q"], a["qr"], a["kv"], a["pt"], a["sl"], a["cu"], a["cos"],
+                                    a["sin"], a["rmp"], a["op"], a["lp"], a["B"], a["T"], a["maxp"],
+                                    a["pool"], a["H"], a["G"], a["d_hc"], a["d_c"], a["d_R"],
+                                    a["ps"], a["S"], a["pps"], a["scale"], a["causal"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(kv=None), NULL), (dict(op=None), NULL), (dict(kv=MIS), ALIGN),
+    (dict(d_R=63, kv=None), DIM), (dict(S=0, kv=None), DIM),
+    (dict(ps=16, kv=None), UNSUP),
+    # valid arguments but a shape the FP8 kernel does not implement
+    (dict(H=64), UNSUP), (dict(G=2), UNSUP), (dict(d_c=256), UNSUP), (dict(d_R=32), UNSUP),
+    (dict(T=0, kv=None), OK),
+])
+def test_fp8_decode_validation(lib, kw, code):
+    assert _decode8(lib, **kw) == code
+
+
+def _append8(lib, **kw):
+    a = dict(c=A, k=A, kv=A, pt=A, sl=A, cu=A, cos=None, sin=None, rmp=0, B=16, T=16, maxp=64,
+             pool=1024, d_c=512, d_R=64, ps=64)
+    a.update(kw)
+    return lib.mla_append_kv_fp8(a["c"], a["k"], a["kv"], a["pt"], a["sl"], a["cu"], a["cos"],
+                                 a["sin"], a["rmp"], a["B"], a["T"], a["maxp"], a["pool"], a["d_c"],
+                                 a["d_R"], a["ps"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(c=None), NULL), (dict(kv=None), NULL), (dict(sin=A), NULL), (dict(kv=MIS), ALIGN),
+    (dict(d_R=63, kv=None), DIM), (dict(B=0, kv=None), DIM),
+    (dict(ps=16, kv=None), UNSUP), (dict(d_c=1024, kv=None), UNSUP), (dict(d_c=500, kv=None), UNSUP),
+    (dict(d_R=12, kv=None), UNSUP), (dict(T=0, kv=None), OK),
+])
+def test_fp8_append_validation(lib, kw, code):
+    assert _append8(lib, **kw) == code
+
+
+def test_bench_names_the_fp8_kernel_and_counts_fp8_bytes():
+    import bench
+    from mla_latent_kv_09_amd import workloads as wl
+    c = wl.CONFIGS["long_b16_l65536"]
+    assert bench.decode_kernel_name(c, 16, 16, "fp8") == "decode_m32_kernel_fp8"
+    assert bench.cache_row_bytes(c, "fp8") == 644 and bench.cache_row_bytes(c) == 1152
+    att8, _, kv8, _ = bench.algorithmic_work(c, [65536] * 16, [1] * 16, "fp8")
+    att, _, kv, _ = bench.algorithmic_work(c, [65536] * 16, [1] * 16)
+    assert att8 == att and kv8 == 16 * 65536 * 644 and kv == 16 * 65536 * 1152
