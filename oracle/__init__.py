@@ -18,6 +18,7 @@ from .mla_oracle import (  # noqa: F401
     naive_scores,
     new_token_positions,
     page_bytes,
+    reconstruct_kv,
     rope_angles,
     rope_rotate,
     softmax_rows,

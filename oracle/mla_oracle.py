@@ -252,6 +252,17 @@ def merge_splits(o_parts, lses):
     return out, np.where(has, m + np.log(np.where(has, z, 1.0)), -np.inf)
 
 
+def reconstruct_kv(latent, w_uk, w_uv):
+    """The decompressed (non-absorbed) branch's first step (P3 §4 path A; P2 §2.4: K and V
+    are mapped back up from the latent): per-head keys and values of latent rows
+    c [n, d_c'], K[j,h,:] = W_UK[h] c_j and V[j,h,:] = W_UV[h] c_j, float64 [n, H, d_hc]
+    each."""
+    c = np.asarray(latent, np.float64)
+    w_uk = np.asarray(w_uk, np.float64)
+    w_uv = np.asarray(w_uv, np.float64)
+    return np.einsum("hdc,jc->jhd", w_uk, c), np.einsum("hdc,jc->jhd", w_uv, c)
+
+
 def absorb_reference(q_c, w_uk):
     """q_abs[t,h,:] = q_c[t,h,:] @ W_UK[h]  (P3 §4 path B, first product), float64."""
     q_c = np.asarray(q_c, np.float64)

@@ -373,3 +373,38 @@ def test_merge_of_key_chunks_equals_attention_over_all_keys():
     # no keys anywhere: zero output, -inf lse
     o0, l0 = om.merge_splits(np.full((2, 3, 5), np.nan), np.full((2, 3), -np.inf))
     assert np.all(o0 == 0) and np.all(np.isneginf(l0))
+
+
+def test_reconstruct_kv_matches_scalar_sums():
+    rng = np.random.default_rng(41)
+    c = rng.standard_normal((5, 7))
+    w_uk = rng.standard_normal((3, 4, 7))
+    w_uv = rng.standard_normal((3, 4, 7))
+    k, v = om.reconstruct_kv(c, w_uk, w_uv)
+    assert k.shape == v.shape == (5, 3, 4)
+    for j in range(5):
+        for h in range(3):
+            for d in range(4):
+                assert k[j, h, d] == pytest.approx(sum(w_uk[h, d, x] * c[j, x] for x in range(7)), rel=1e-13)
+                assert v[j, h, d] == pytest.approx(sum(w_uv[h, d, x] * c[j, x] for x in range(7)), rel=1e-13)
+
+
+def test_prefill_shaped_batch_is_causal_attention():
+    """A prompt whose every token is a query (q_len = L, the decompressed branch's shape):
+    the oracle equals SDPA with the causal triangle over [c W_UK^T | k_R] keys and
+    c W_UV^T values, and query i sees exactly keys 0 .. i."""
+    p = _rand_problem(43, B=1, H=2, d_hc=8, d_c=12, d_R=4, lens=(70,), q_lens=(70,))
+    base = 10000.0
+    r = _run(p, rope_base=base)
+    rows = p["latents"][0]
+    k, v = om.reconstruct_kv(rows[:, :12], p["w_uk"], p["w_uv"])
+    for h in range(2):
+        kk = np.concatenate([k[:, h], rows[:, 12:]], axis=1)
+        qs = np.stack([np.concatenate([p["q_c"][i, h], _rotate_complex(p["q_r"][i, h], i, base)])
+                       for i in range(70)])
+        o = torch.nn.functional.scaled_dot_product_attention(
+            torch.tensor(qs)[None], torch.tensor(kk)[None], torch.tensor(v[:, h])[None],
+            is_causal=True).numpy()[0]
+        assert np.max(np.abs(r["out"][:, h] - o)) <= 1e-12 * np.max(np.abs(o))
+    # the first query sees only key 0: its output is that key's value exactly
+    assert np.allclose(r["out"][0], v[0], rtol=1e-13, atol=0)
