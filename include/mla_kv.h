@@ -275,6 +275,57 @@ int mla_decode_paged_fp8(const void* q_abs, const void* q_r, const void* kv_cach
                          int num_splits, int pages_per_split, float softmax_scale, int causal,
                          void* stream);
 
+/*
+ * Prefill/decode dispatch (P3 §3: kPrefillThresh = 256, the "absorption / decompression
+ * switch-over threshold"; §6: prefill takes the decompressed branch and decode the
+ * absorbed one, measured there at about 12 % end-to-end over absorbing everything on one
+ * configuration, and to be re-measured per machine).
+ *
+ * mla_branch -- host-only: MLA_BRANCH_DECOMPRESSED when the batch's largest query count
+ * (q_lens, host memory) is at least threshold, else MLA_BRANCH_ABSORBED.  A batch is
+ * dispatched whole; a batch that mixes prompts and decode tokens takes the branch of its
+ * largest member (split it to route each part).  MLA_ERR_NULL / MLA_ERR_DIM on a NULL
+ * q_lens, batch or threshold <= 0, or a negative count.
+ */
+#define MLA_PREFILL_THRESHOLD 256
+enum mla_branch_kind { MLA_BRANCH_ABSORBED = 0, MLA_BRANCH_DECOMPRESSED = 1 };
+int mla_branch(const int32_t* q_lens, int batch, int threshold);
+
+/*
+ * mla_prefill_paged -- the decompressed branch (P3 §4 path A: K and V are expanded from
+ * the latent, P2 §2.4): for every cache row j of every sequence b and every head h,
+ *   K[j,h,:] = W_UK[h] c_j,  V[j,h,:] = W_UV[h] c_j     (fp32 accumulation, rounded to bf16)
+ * into `workspace`, then per query row t (position p = seq_lens[b] - q_len_b + i) and head
+ * h the softmax over the visible keys (j <= p with causal, else all) of
+ *   (q_c[t,h] . K[j,h] + RoPE(q_R[t,h], p) . k_R[j]) * scale
+ * applied to V[j,h], written to out[t,h,:] (the step's output: no mla_up_v after it).
+ * The same result as the four absorbed calls, up to rounding.
+ *
+ *   q_c [T, H, d_hc], q_r [T, H, d_R], kv_cache, page_table, seq_lens, cu_q, rope tables:
+ *               as mla_decode_paged (bf16)
+ *   w_uk, w_uv  [H, d_hc, d_c] bf16
+ *   workspace   caller-owned, mla_prefill_workspace_bytes(num_pool_pages, H, d_hc, dtype)
+ *               bytes: K then V, each [num_pool_pages * 64, H, d_hc] bf16 (row = physical
+ *               cache row page * 64 + slot; only the batch's pages are written)
+ *   out         [T, H, d_hc] bf16 output;  lse_out [T, H] float32 (natural log) or NULL
+ *   max_q_len   at least the largest query count of the batch (rows past it are not
+ *               computed)
+ * Implemented for bf16, one latent group, d_hc 128, d_c 512, d_R 64, page_size 64, any head
+ * count (MLA_ERR_UNSUPPORTED otherwise).  Errors as mla_decode_paged.
+ */
+int mla_prefill_paged(const void* q_c, const void* q_r, const void* kv_cache,
+                      const int32_t* page_table, const int32_t* seq_lens, const int32_t* cu_q,
+                      const float* rope_cos, const float* rope_sin, int rope_max_pos,
+                      const void* w_uk, const void* w_uv, void* workspace, void* out,
+                      float* lse_out, int batch, int total_q, int max_pages_per_seq,
+                      int num_pool_pages, int max_q_len, int heads, int groups, int d_hc,
+                      int d_c, int d_R, int page_size, float softmax_scale, int causal,
+                      int dtype, void* stream);
+
+/* Bytes of mla_prefill_paged's workspace (0 on bad sizes or a dtype other than bf16):
+ * 2 * num_pool_pages * 64 * heads * d_hc * 2. */
+size_t mla_prefill_workspace_bytes(int num_pool_pages, int heads, int d_hc, int dtype);
+
 /* Bytes of the o_part + lse_part workspace mla_decode_paged needs for this dtype
  * (0 on bad sizes or dtype): T*H*num_splits*(d_cg*elem + 4), elem = 2 for bf16. */
 size_t mla_decode_workspace_bytes(int total_q, int heads, int groups, int d_c, int num_splits,

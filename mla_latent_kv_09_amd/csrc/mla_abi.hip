@@ -282,6 +282,85 @@ int mla_append_kv(const void* c_kv_new, const void* k_r_new, void* kv_cache,
                                              static_cast<hipStream_t>(stream)));
 }
 
+size_t mla_prefill_workspace_bytes(int num_pool_pages, int heads, int d_hc, int dtype) {
+  if (num_pool_pages <= 0 || heads <= 0 || d_hc <= 0 || dtype != MLA_DTYPE_BF16) return 0;
+  return 2 * static_cast<size_t>(num_pool_pages) * MLA_PAGE_SIZE * heads * d_hc * 2;
+}
+
+int mla_branch(const int32_t* q_lens, int batch, int threshold) {
+  if (!q_lens) return MLA_ERR_NULL;
+  if (batch <= 0 || threshold <= 0) return MLA_ERR_DIM;
+  int max_q = 0;
+  for (int b = 0; b < batch; ++b) {
+    if (q_lens[b] < 0) return MLA_ERR_DIM;
+    max_q = q_lens[b] > max_q ? q_lens[b] : max_q;
+  }
+  return max_q >= threshold ? MLA_BRANCH_DECOMPRESSED : MLA_BRANCH_ABSORBED;
+}
+
+int mla_prefill_paged(const void* q_c, const void* q_r, const void* kv_cache,
+                      const int32_t* page_table, const int32_t* seq_lens, const int32_t* cu_q,
+                      const float* rope_cos, const float* rope_sin, int rope_max_pos,
+                      const void* w_uk, const void* w_uv, void* workspace, void* out,
+                      float* lse_out, int batch, int total_q, int max_pages_per_seq,
+                      int num_pool_pages, int max_q_len, int heads, int groups, int d_hc,
+                      int d_c, int d_R, int page_size, float softmax_scale, int causal, int dtype,
+                      void* stream) {
+  int st = check_dtype(dtype);
+  if (st != MLA_OK) return st;
+  if (total_q < 0 || batch <= 0 || max_q_len <= 0 || d_hc <= 0 || d_R <= 0 || (d_R & 1) ||
+      max_pages_per_seq <= 0 || num_pool_pages <= 0 || page_size <= 0)
+    return MLA_ERR_DIM;
+  if ((st = check_heads(heads, groups, d_c)) != MLA_OK) return st;
+  mla::PrefillArgs a{};
+  a.groups = groups;
+  a.d_hc = d_hc;
+  a.d_c = d_c;
+  a.d_R = d_R;
+  a.page_size = page_size;
+  if (dtype != MLA_DTYPE_BF16 || !mla::prefill_supported(a)) return MLA_ERR_UNSUPPORTED;
+  if (static_cast<long long>(max_pages_per_seq) * page_size > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+  const long long q_blocks = (static_cast<long long>(max_q_len) + 127) / 128;
+  const long long dec_runs = (static_cast<long long>(max_pages_per_seq) + 7) / 8;
+  if (q_blocks * batch * heads > INT32_MAX || dec_runs * batch * heads > INT32_MAX ||
+      static_cast<long long>(num_pool_pages) * page_size * heads > INT32_MAX)
+    return MLA_ERR_UNSUPPORTED;
+  if ((rope_cos == nullptr) != (rope_sin == nullptr)) return MLA_ERR_NULL;
+  if (rope_cos != nullptr && rope_max_pos <= 0) return MLA_ERR_DIM;
+  if (total_q == 0) return MLA_OK;
+  if (!q_c || !q_r || !kv_cache || !page_table || !seq_lens || !cu_q || !w_uk || !w_uv ||
+      !workspace || !out)
+    return MLA_ERR_NULL;
+  const void* ptrs[] = {q_c, q_r, kv_cache, page_table, seq_lens, cu_q, w_uk, w_uv, workspace, out};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MLA_ERR_ALIGN;
+  if (lse_out && !aligned16(lse_out)) return MLA_ERR_ALIGN;
+  if (rope_cos && (!aligned16(rope_cos) || !aligned16(rope_sin))) return MLA_ERR_ALIGN;
+  a.q_c = q_c;
+  a.q_r = q_r;
+  a.kv = kv_cache;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.cu_q = cu_q;
+  a.rope_cos = rope_cos;
+  a.rope_sin = rope_sin;
+  a.rope_max_pos = rope_max_pos;
+  a.w_uk = w_uk;
+  a.w_uv = w_uv;
+  a.workspace = workspace;
+  a.out = out;
+  a.lse_out = lse_out;
+  a.batch = batch;
+  a.total_q = total_q;
+  a.max_pages = max_pages_per_seq;
+  a.num_pool_pages = num_pool_pages;
+  a.max_q_len = max_q_len;
+  a.heads = heads;
+  a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(d_hc + d_R));
+  a.causal = causal != 0;
+  return launch_status(mla::launch_prefill(a, static_cast<hipStream_t>(stream)));
+}
+
 size_t mla_fp8_page_bytes(int d_c, int d_R) {
   if (d_c <= 0 || d_R <= 0 || (d_R & 1)) return 0;
   return static_cast<size_t>(MLA_PAGE_SIZE) * (static_cast<size_t>(d_c) + 2 * d_R + 4);

@@ -55,6 +55,31 @@ int decode_validate(const void* q_abs, const void* q_r, const void* kv_cache,
                     int causal, int dtype, bool check_parts, DecodeArgs* out, bool* bf16);
 int decode_launch(DecodeArgs& a, bool bf16, hipStream_t s);
 
+// Decompressed (non-absorbed) branch: K / V up-projection of every cache row of the batch
+// into a workspace indexed by physical row, then attention over them.
+struct PrefillArgs {
+  const void* q_c;         // [T, H, d_hc] bf16
+  const void* q_r;         // [T, H, d_R] bf16, before rotation
+  const void* kv;          // [num_pool_pages, 64, d_c + d_R] bf16
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  const int32_t* cu_q;
+  const float* rope_cos;
+  const float* rope_sin;
+  int rope_max_pos;
+  const void* w_uk;        // [H, d_hc, d_c] bf16
+  const void* w_uv;
+  void* workspace;         // K then V: [num_pool_pages * 64, H, d_hc] bf16 each
+  void* out;               // [T, H, d_hc] bf16
+  float* lse_out;          // [T, H] or NULL
+  int batch, total_q, max_pages, num_pool_pages, max_q_len;
+  int heads, groups, d_hc, d_c, d_R, page_size;
+  float scale;
+  int causal;
+};
+bool prefill_supported(const PrefillArgs& a);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+
 // Latent-cache append of the new tokens' rows (c_KV | RoPE(k_R, pos)).
 struct AppendArgs {
   const void* c_new;   // [T, d_c] storage type

@@ -23,7 +23,8 @@ PAGE_SIZE = 64
 
 EXPORTED = ("mla_absorb_q", "mla_rope_table", "mla_decode_paged", "mla_combine", "mla_up_v",
             "mla_append_kv", "mla_decode_workspace_bytes", "mla_decode_plan", "mla_attend_noalloc",
-            "mla_decode_paged_fp8", "mla_append_kv_fp8", "mla_fp8_page_bytes", "mla_status_string")
+            "mla_decode_paged_fp8", "mla_append_kv_fp8", "mla_fp8_page_bytes", "mla_branch",
+            "mla_prefill_paged", "mla_prefill_workspace_bytes", "mla_status_string")
 
 _lib = None
 
@@ -57,13 +58,17 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_attend_noalloc.argtypes = ([P] * 8 + [I] + [P] * 2 + [I] * 12 + [F, I, I, P])
     lib.mla_decode_paged_fp8.argtypes = ([P] * 8 + [I] + [P] * 2 + [I] * 12 + [F, I, P])
     lib.mla_append_kv_fp8.argtypes = [P] * 8 + [I] * 8 + [P]
+    lib.mla_branch.argtypes = [P, I, I]
+    lib.mla_prefill_paged.argtypes = [P] * 8 + [I] + [P] * 5 + [I] * 11 + [F, I, I, P]
+    lib.mla_prefill_workspace_bytes.argtypes = [I, I, I, I]
+    lib.mla_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.mla_fp8_page_bytes.argtypes = [I, I]
     lib.mla_fp8_page_bytes.restype = ctypes.c_size_t
     lib.mla_status_string.argtypes = [I]
     lib.mla_status_string.restype = ctypes.c_char_p
     for name in ("mla_absorb_q", "mla_rope_table", "mla_decode_paged", "mla_combine", "mla_up_v",
                  "mla_append_kv", "mla_decode_plan", "mla_attend_noalloc", "mla_decode_paged_fp8",
-                 "mla_append_kv_fp8"):
+                 "mla_append_kv_fp8", "mla_branch", "mla_prefill_paged"):
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -196,6 +201,72 @@ def decode_paged(q_abs, q_r, kv_cache, page_table, seq_lens, cu_q, o_part, lse_p
         B, T, max_pages, P, H, groups, d_hc, d_cg * groups, d_R, ps, S, int(pages_per_split),
         float(softmax_scale),
         int(bool(causal)), _dtype_code(q_abs), _stream(stream)))
+
+
+BRANCH_ABSORBED = 0
+BRANCH_DECOMPRESSED = 1
+PREFILL_THRESHOLD = 256
+
+
+def branch(q_lens_host, threshold: int = PREFILL_THRESHOLD) -> int:
+    """The library's host-only dispatch (mla_branch): BRANCH_DECOMPRESSED when the batch's
+    largest query count reaches ``threshold``, else BRANCH_ABSORBED."""
+    B = len(q_lens_host)
+    if B == 0:
+        raise ValueError("q_lens must be non-empty")
+    qs = (ctypes.c_int32 * B)(*[int(x) for x in q_lens_host])
+    r = load().mla_branch(qs, B, int(threshold))
+    if r < 0:
+        raise MLAError("mla_branch", r)
+    return r
+
+
+def prefill_workspace(num_pool_pages: int, heads: int, d_hc: int, device="cuda") -> torch.Tensor:
+    """The decompressed branch's K/V workspace (mla_prefill_workspace_bytes bytes)."""
+    n = int(load().mla_prefill_workspace_bytes(int(num_pool_pages), int(heads), int(d_hc), DTYPE_BF16))
+    if n == 0:
+        raise ValueError("bad sizes for the prefill workspace")
+    return torch.empty(n // 2, dtype=torch.bfloat16, device=device)
+
+
+def prefill_paged(q_c, q_r, kv_cache, page_table, seq_lens, cu_q, w_uk, w_uv, workspace,
+                  out=None, lse_out=None, *, max_q_len: int, groups: int = 1,
+                  rope: Optional[tuple] = None, softmax_scale: float = 0.0, causal: bool = True,
+                  stream=None) -> torch.Tensor:
+    """The decompressed branch (mla_prefill_paged): out[t,h,:] [T,H,d_hc] straight from
+    q_c / q_R and the paged latent cache, K and V expanded into ``workspace``."""
+    T, H, d_hc = q_c.shape
+    d_R = q_r.shape[2]
+    P, ps, width = kv_cache.shape
+    B, max_pages = page_table.shape
+    d_c = w_uk.shape[2] * groups
+    if q_r.shape[:2] != (T, H) or width != d_c + d_R:
+        raise ValueError("inconsistent q_r / kv_cache shapes")
+    if w_uk.shape != (H, d_hc, d_c // groups) or w_uv.shape != w_uk.shape:
+        raise ValueError("w_uk and w_uv must be [H, d_hc, d_c/G]")
+    for t in (q_c, q_r, kv_cache, w_uk, w_uv):
+        if t.dtype != torch.bfloat16:
+            raise TypeError("the decompressed branch takes bf16 tensors")
+    for t in (page_table, seq_lens, cu_q):
+        if t.dtype != torch.int32:
+            raise TypeError(f"expected int32, got {t.dtype}")
+    if seq_lens.shape != (B,) or cu_q.shape != (B + 1,):
+        raise ValueError("seq_lens must be [B] and cu_q [B+1]")
+    need = int(load().mla_prefill_workspace_bytes(P, H, d_hc, DTYPE_BF16))
+    if workspace.numel() * workspace.element_size() < need:
+        raise ValueError(f"workspace must hold {need} bytes")
+    if out is None:
+        out = torch.empty((T, H, d_hc), dtype=torch.bfloat16, device=q_c.device)
+    _expect("out", out, (T, H, d_hc), torch.bfloat16)
+    _expect("lse_out", lse_out, (T, H), torch.float32)
+    cos, sin, rope_max_pos = _rope_pair(rope, d_R, q_c.device)
+    _dev(q_c, q_r, kv_cache, page_table, seq_lens, cu_q, w_uk, w_uv, workspace, out, lse_out, cos, sin)
+    _check("mla_prefill_paged", load().mla_prefill_paged(
+        _ptr(q_c), _ptr(q_r), _ptr(kv_cache), _ptr(page_table), _ptr(seq_lens), _ptr(cu_q),
+        _ptr(cos), _ptr(sin), rope_max_pos, _ptr(w_uk), _ptr(w_uv), _ptr(workspace), _ptr(out),
+        _ptr(lse_out), B, T, max_pages, P, int(max_q_len), H, groups, d_hc, d_c, d_R, ps,
+        float(softmax_scale), int(bool(causal)), DTYPE_BF16, _stream(stream)))
+    return out
 
 
 def fp8_page_bytes(d_c: int, d_R: int) -> int:
@@ -371,25 +442,35 @@ class DecodeStep:
     """The four calls of one decode step over preallocated buffers (no allocation per call)."""
 
     def __init__(self, *, q_c, q_r, w_uk, w_uv, kv_cache, page_table, seq_lens, cu_q, groups=1,
-                 num_splits=None, rope=None, causal=True, seq_lens_host=None, pages_per_split=0):
+                 num_splits=None, rope=None, causal=True, seq_lens_host=None, pages_per_split=0,
+                 threshold=None):
         self.q_c, self.q_r, self.w_uk, self.w_uv = q_c, q_r, w_uk, w_uv
         self.kv, self.page_table, self.seq_lens, self.cu_q = kv_cache, page_table, seq_lens, cu_q
         self.groups, self.rope, self.causal = groups, rope, causal
         T, H, d_hc = q_c.shape
         d_cg = w_uk.shape[2]
-        if num_splits is None:
-            lens = seq_lens_host if seq_lens_host is not None else seq_lens.cpu().tolist()
-            cu = cu_q.cpu().tolist()
-            cus = torch.cuda.get_device_properties(q_c.device).multi_processor_count
-            num_splits, self.pages_per_split = split_plan(lens, [b - a for a, b in zip(cu, cu[1:])],
-                                                          cu_count=cus, groups=groups)
-        else:
-            self.pages_per_split = int(pages_per_split)
-        self.num_splits = num_splits
+        cu = cu_q.cpu().tolist()
+        q_lens = [b - a for a, b in zip(cu, cu[1:])]
+        self.max_q_len = max(q_lens) if q_lens else 0
+        # threshold None: always the absorbed calls; else the library's dispatch decides.
+        self.branch = (BRANCH_ABSORBED if threshold is None or T == 0
+                       else branch(q_lens, threshold))
+        if self.branch == BRANCH_DECOMPRESSED:
+            self.workspace = prefill_workspace(kv_cache.shape[0], H, d_hc, q_c.device)
         dev = q_c.device
-        self.q_abs = torch.empty((T, H, d_cg), dtype=q_c.dtype, device=dev)
-        self.o_part, self.lse_part = workspace(T, H, d_cg, num_splits, dev, q_c.dtype)
-        self.o_latent = torch.empty((T, H, d_cg), dtype=q_c.dtype, device=dev)
+        if self.branch == BRANCH_DECOMPRESSED:  # the absorbed calls' buffers are not needed
+            self.num_splits, self.pages_per_split = 0, 0
+        else:
+            if num_splits is None:
+                lens = seq_lens_host if seq_lens_host is not None else seq_lens.cpu().tolist()
+                cus = torch.cuda.get_device_properties(q_c.device).multi_processor_count
+                num_splits, self.pages_per_split = split_plan(lens, q_lens, cu_count=cus, groups=groups)
+            else:
+                self.pages_per_split = int(pages_per_split)
+            self.num_splits = num_splits
+            self.q_abs = torch.empty((T, H, d_cg), dtype=q_c.dtype, device=dev)
+            self.o_part, self.lse_part = workspace(T, H, d_cg, num_splits, dev, q_c.dtype)
+            self.o_latent = torch.empty((T, H, d_cg), dtype=q_c.dtype, device=dev)
         self.lse = torch.empty((T, H), dtype=torch.float32, device=dev)
         self.out = torch.empty((T, H, d_hc), dtype=q_c.dtype, device=dev)
         self.d_hc = d_hc
@@ -414,7 +495,16 @@ class DecodeStep:
     def project(self, stream=None):
         up_v(self.o_latent, self.w_uv, self.out, groups=self.groups, stream=stream)
 
+    def prefill(self, stream=None):
+        prefill_paged(self.q_c, self.q_r, self.kv, self.page_table, self.seq_lens, self.cu_q,
+                      self.w_uk, self.w_uv, self.workspace, self.out, self.lse,
+                      max_q_len=self.max_q_len, groups=self.groups, rope=self.rope,
+                      causal=self.causal, stream=stream)
+
     def __call__(self, stream=None):
+        if self.branch == BRANCH_DECOMPRESSED:
+            self.prefill(stream)
+            return self.out
         self.absorb(stream)
         self.attend(stream)
         self.merge(stream)

@@ -137,6 +137,12 @@ CONFIGS = {
         seq_len=16384, w_std=1.0 / 16.0,
         note="grouped latent (2 groups of 64 heads, 256-d slice each + shared 64-d k_R), "
              "batch 32, 16384 tokens, bf16"),
+    # The prefill/decode dispatch measurement of the MLA-operators page (§6): batch 8,
+    # 4096-token prompts, every prompt token a query (causal), at the 256-row threshold.
+    "prefill_b8_l4096": MLAConfig(
+        name="prefill_b8_l4096", batch=8, heads=128, d_hc=128, d_c=512, d_R=64,
+        seq_len=4096, q_len=4096,
+        note="prefill: batch 8, 4096-token prompts, q_len = 4096 (causal), 128 heads, bf16"),
 }
 
 CONFIG_ORDER = ["tiny_fp32", "dsv3_b16_l4096", "long_b16_l65536", "ragged_b64", "gla2_b32_l16384"]

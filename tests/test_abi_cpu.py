@@ -373,3 +373,48 @@ def test_bench_names_the_fp8_kernel_and_counts_fp8_bytes():
     att8, _, kv8, _ = bench.algorithmic_work(c, [65536] * 16, [1] * 16, "fp8")
     att, _, kv, _ = bench.algorithmic_work(c, [65536] * 16, [1] * 16)
     assert att8 == att and kv8 == 16 * 65536 * 644 and kv == 16 * 65536 * 1152
+
+
+# -------------------------------------------------------------- prefill dispatch (host only)
+
+def test_branch_threshold(lib):
+    assert mla.branch([1, 2, 1]) == mla.BRANCH_ABSORBED
+    assert mla.branch([1, 255]) == mla.BRANCH_ABSORBED
+    assert mla.branch([1, 256]) == mla.BRANCH_DECOMPRESSED
+    assert mla.branch([4096] * 8) == mla.BRANCH_DECOMPRESSED
+    assert mla.branch([300], threshold=512) == mla.BRANCH_ABSORBED
+    L = (ctypes.c_int32 * 2)(1, 2)
+    assert lib.mla_branch(None, 2, 256) == NULL
+    assert lib.mla_branch(L, 0, 256) == DIM and lib.mla_branch(L, 2, 0) == DIM
+    assert lib.mla_branch((ctypes.c_int32 * 1)(-1), 1, 256) == DIM
+
+
+def test_prefill_workspace_bytes(lib):
+    assert lib.mla_prefill_workspace_bytes(512, 128, 128, 0) == 2 * 512 * 64 * 128 * 128 * 2
+    assert lib.mla_prefill_workspace_bytes(0, 128, 128, 0) == 0
+    assert lib.mla_prefill_workspace_bytes(10, 128, 128, 1) == 0     # bf16 only
+
+
+def _prefill(lib, **kw):
+    a = dict(qc=A, qr=A, kv=A, pt=A, sl=A, cu=A, cos=None, sin=None, rmp=0, wk=A, wv=A, ws=A,
+             out=A, lse=None, B=8, T=32768, maxp=64, pool=512, maxq=4096, H=128, G=1, d_hc=128,
+             d_c=512, d_R=64, ps=64, scale=0.0, causal=1, dt=0)
+    a.update(kw)
+    return lib.mla_prefill_paged(a["qc"], a["qr"], a["kv"], a["pt"], a["sl"], a["cu"], a["cos"],
+                                 a["sin"], a["rmp"], a["wk"], a["wv"], a["ws"], a["out"], a["lse"],
+                                 a["B"], a["T"], a["maxp"], a["pool"], a["maxq"], a["H"], a["G"],
+                                 a["d_hc"], a["d_c"], a["d_R"], a["ps"], a["scale"], a["causal"],
+                                 a["dt"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ws=None), NULL), (dict(wk=None), NULL), (dict(out=None), NULL), (dict(cos=A), NULL),
+    (dict(ws=MIS), ALIGN), (dict(lse=MIS), ALIGN),
+    (dict(maxq=0, ws=None), DIM), (dict(d_R=63, ws=None), DIM), (dict(B=0, ws=None), DIM),
+    (dict(H=128, G=3, ws=None), DIM),
+    (dict(G=2, ws=None), UNSUP), (dict(d_hc=64, ws=None), UNSUP), (dict(ps=16, ws=None), UNSUP),
+    (dict(dt=1, ws=None), UNSUP), (dict(dt=9), DTYPE),
+    (dict(T=0, ws=None), OK),
+])
+def test_prefill_validation(lib, kw, code):
+    assert _prefill(lib, **kw) == code

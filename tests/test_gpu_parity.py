@@ -298,8 +298,11 @@ def test_decode_kernels_agree(case, monkeypatch):
     ref = oracle_for(w)["out"]
     for kind in kinds:
         assert_parity(outs[kind], ref, what=kind)
+    # Kernel against kernel: each within the bar of the oracle, with independent
+    # roundings, so their difference is bounded by twice the bar.
     for kind in kinds[:-1]:
-        assert_parity(outs[kind], outs["generic"], what=f"{kind} vs generic")
+        assert_parity(outs[kind], outs["generic"], tol=2 * NORM_TOL, cos_tol=1 - 2 * (1 - COS_TOL),
+                      what=f"{kind} vs generic")
 
 
 @pytest.mark.parametrize("kind", ["mfma128", "mfma64", "mfma32-128", "mfma32-64", "generic"])
