@@ -259,6 +259,10 @@ def main():
                     help="one input copy and a 1 GiB read-only cache flush before every step, "
                          "each step timed alone (the earlier method) instead of rotating copies")
     ap.add_argument("--no-graph", action="store_true", help="launch the calls eagerly")
+    ap.add_argument("--threshold", type=int, default=256,
+                    help="query rows at which the library's dispatch takes the decompressed "
+                         "branch (batches whose largest q_len reaches it, e.g. --config "
+                         "prefill_b8_l4096)")
     ap.add_argument("--kv-dtype", choices=["bf16", "fp8"], default="bf16",
                     help="latent cache format: bf16 rows (default) or FP8 E4M3 pages written by "
                          "mla_append_kv_fp8 (a separate line, never the headline)")
@@ -286,6 +290,12 @@ def main():
     att, proj, kv_bytes, w_bytes = algorithmic_work(cfg, w.seq_lens, w.q_lens, args.kv_dtype)
     stream = torch.cuda.current_stream()
     names = ["absorb_q", "decode_paged", "combine", "up_v"]
+    if mla.branch(w.q_lens.tolist(), args.threshold) == mla.BRANCH_DECOMPRESSED:
+        if args.kv_dtype != "bf16" or args.flush:
+            print("the decompressed branch takes the bf16 cache and the default timing", file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps(prefill_bench(args, w, torch, harness, mla, stream)))
+        return
 
     if not args.flush:
         # Rotation: n_copies independent device copies of the step's inputs, outputs and
@@ -460,6 +470,97 @@ def measure_append(args, w, torch, harness, mla, wl, steps, runner, timed, reps,
     res["bulk"] = {"rows": nb * L, "ms": ms_b, "algorithmic_bytes": nbytes, "gbps": gbps,
                    "frac_hbm_peak": gbps / HBM_PEAK_GBPS}
     return res
+
+
+def prefill_work(cfg, seq_lens, q_lens):
+    """(attention flops, decompression flops, latent-KV bytes, workspace bytes) of the
+    decompressed branch: per (query row, visible key, head) 2 (d_hc + d_R) + 2 d_hc flops;
+    per cache row and head 2 * 2 d_c d_hc flops for K and V; the workspace (K and V of
+    every row, bf16) written once and read back once."""
+    per_key = cfg.heads * (2 * (cfg.d_hc + cfg.d_R) + 2 * cfg.d_hc)
+    att = dec = kv = 0
+    for L, q in zip(seq_lens, q_lens):
+        L, q = int(L), int(q)
+        for i in range(q):
+            att += per_key * (L - q + i + 1 if cfg.causal else L)
+        dec += L * cfg.heads * 2 * 2 * cfg.d_c * cfg.d_hc
+        kv += L * (cfg.d_c + cfg.d_R) * 2
+    ws = sum(int(L) for L in seq_lens) * cfg.heads * cfg.d_hc * 2 * 2
+    return att, dec, kv, ws
+
+
+def prefill_bench(args, w, torch, harness, mla, stream):
+    """The decompressed branch (mla_decompress_kv + mla_prefill_attention), timed like the
+    decode step (two device copies, used in turn, back to back in HIP graphs), plus the
+    four absorbed calls on the same inputs for the dispatch comparison (fewer steps: the
+    absorbed form of a prompt is several times slower)."""
+    cfg = w.cfg
+    att, dec, kv_bytes, ws_bytes = prefill_work(cfg, w.seq_lens, w.q_lens)
+    steps = [harness.make_step(w, harness.to_device(w), threshold=args.threshold) for _ in range(2)]
+
+    def timed(calls, reps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for c in calls:
+                c()
+        g.replay()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            g.replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / (reps * len(calls))
+
+    for _ in range(max(1, args.warmup)):
+        for st in steps:
+            st()
+    torch.cuda.synchronize()
+    reps = max(1, math.ceil(args.steps / 2))
+    parts = {
+        "decompress_kv": statistics.median(timed([steps[0].decompress, steps[1].decompress], reps)
+                                           for _ in range(3)),
+        "prefill_attention": statistics.median(timed([steps[0].prefill_attend, steps[1].prefill_attend],
+                                                     reps) for _ in range(3)),
+    }
+    wall0 = time.perf_counter()
+    full, rest = divmod(args.steps, 2)
+    ms = (timed([steps[0], steps[1]], full) * 2 * full + (timed([steps[0]], rest) * rest if rest else 0.0)) / args.steps
+    wall = time.perf_counter() - wall0
+    # The absorbed calls on the first copy (a step without a threshold never dispatches).
+    d0 = harness.DeviceWorkload(q_c=steps[0].q_c, q_r=steps[0].q_r, w_uk=steps[0].w_uk,
+                                w_uv=steps[0].w_uv, kv=steps[0].kv, page_table=steps[0].page_table,
+                                seq_lens=steps[0].seq_lens, cu_q=steps[0].cu_q, rope=steps[0].rope)
+    absorbed = harness.make_step(w, d0)
+    absorbed()
+    torch.cuda.synchronize()
+    abs_reps = max(2, min(10, args.steps // 20))
+    abs_ms = statistics.median(timed([absorbed], abs_reps) for _ in range(3))
+    abs_att, abs_proj, _, _ = algorithmic_work(cfg, w.seq_lens, w.q_lens)
+    del absorbed
+    t_att = parts["prefill_attention"]
+    achieved = att / (t_att * 1e-3) / 1e12
+    return {
+        "metric": METRIC, "value": (att + dec) / (ms * 1e-3) / 1e12, "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": cfg.name, "branch": "decompressed", "threshold": args.threshold,
+                   "batch": cfg.batch, "heads": cfg.heads, "d_hc": cfg.d_hc, "d_c": cfg.d_c,
+                   "d_R": cfg.d_R, "q_len": cfg.q_len, "seq_len": cfg.seq_len,
+                   "total_q": int(w.total_q), "timing": {"method": "rotate", "copies": 2}},
+        "kernel_ms": parts, "wall_s_timed_region": wall,
+        "seqs_per_s": cfg.batch / (ms * 1e-3),
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+                     "kernel": "prefill_attn_kernel", "kernel_ms": t_att, "algorithmic_flops": att},
+        "decompress": {"ms": parts["decompress_kv"], "algorithmic_flops": dec,
+                       "tflops": dec / (parts["decompress_kv"] * 1e-3) / 1e12,
+                       "workspace_bytes": ws_bytes, "latent_kv_bytes": kv_bytes},
+        "absorbed_branch": {"ms_per_step": abs_ms, "algorithmic_flops": abs_att + abs_proj,
+                            "speedup_of_dispatch": abs_ms / ms},
+    }
 
 
 def device_copy(w, harness, kv_dtype):

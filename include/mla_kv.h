@@ -322,6 +322,25 @@ int mla_prefill_paged(const void* q_c, const void* q_r, const void* kv_cache,
                       int d_c, int d_R, int page_size, float softmax_scale, int causal,
                       int dtype, void* stream);
 
+/*
+ * The two halves of mla_prefill_paged, for callers that time or schedule them apart:
+ * mla_decompress_kv writes the workspace (K and V of every cache row of the batch's
+ * sequences, all heads), mla_prefill_attention reads it with the queries and the cache's
+ * k_R rows and writes out / lse_out.  Arguments, limits and errors as mla_prefill_paged
+ * (mla_decompress_kv takes no query arguments and always enqueues its kernel).
+ */
+int mla_decompress_kv(const void* kv_cache, const int32_t* page_table, const int32_t* seq_lens,
+                      const void* w_uk, const void* w_uv, void* workspace, int batch,
+                      int max_pages_per_seq, int num_pool_pages, int heads, int groups, int d_hc,
+                      int d_c, int d_R, int page_size, int dtype, void* stream);
+int mla_prefill_attention(const void* q_c, const void* q_r, const void* kv_cache,
+                          const int32_t* page_table, const int32_t* seq_lens, const int32_t* cu_q,
+                          const float* rope_cos, const float* rope_sin, int rope_max_pos,
+                          const void* workspace, void* out, float* lse_out, int batch,
+                          int total_q, int max_pages_per_seq, int num_pool_pages, int max_q_len,
+                          int heads, int groups, int d_hc, int d_c, int d_R, int page_size,
+                          float softmax_scale, int causal, int dtype, void* stream);
+
 /* Bytes of mla_prefill_paged's workspace (0 on bad sizes or a dtype other than bf16):
  * 2 * num_pool_pages * 64 * heads * d_hc * 2. */
 size_t mla_prefill_workspace_bytes(int num_pool_pages, int heads, int d_hc, int dtype);

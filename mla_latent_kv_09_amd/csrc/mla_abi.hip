@@ -298,6 +298,78 @@ int mla_branch(const int32_t* q_lens, int batch, int threshold) {
   return max_q >= threshold ? MLA_BRANCH_DECOMPRESSED : MLA_BRANCH_ABSORBED;
 }
 
+// Checks of the decompressed branch's calls.  Stage 1 = mla_decompress_kv (cache, page
+// table, lengths, weights, workspace), 2 = mla_prefill_attention (queries, cache, page
+// table, lengths, query offsets, workspace, output), 3 = both.  Fills *a on success.
+int prefill_validate(int stage, const void* q_c, const void* q_r, const void* kv_cache,
+                     const int32_t* page_table, const int32_t* seq_lens, const int32_t* cu_q,
+                     const float* rope_cos, const float* rope_sin, int rope_max_pos,
+                     const void* w_uk, const void* w_uv, void* workspace, void* out,
+                     float* lse_out, int batch, int total_q, int max_pages_per_seq,
+                     int num_pool_pages, int max_q_len, int heads, int groups, int d_hc, int d_c,
+                     int d_R, int page_size, float softmax_scale, int causal, int dtype,
+                     mla::PrefillArgs* a) {
+  int st = check_dtype(dtype);
+  if (st != MLA_OK) return st;
+  const bool attn = stage & 2, dec = stage & 1;
+  if (total_q < 0 || batch <= 0 || (attn && max_q_len <= 0) || d_hc <= 0 || d_R <= 0 || (d_R & 1) ||
+      max_pages_per_seq <= 0 || num_pool_pages <= 0 || page_size <= 0)
+    return MLA_ERR_DIM;
+  if ((st = check_heads(heads, groups, d_c)) != MLA_OK) return st;
+  a->groups = groups;
+  a->d_hc = d_hc;
+  a->d_c = d_c;
+  a->d_R = d_R;
+  a->page_size = page_size;
+  if (dtype != MLA_DTYPE_BF16 || !mla::prefill_supported(*a)) return MLA_ERR_UNSUPPORTED;
+  if (static_cast<long long>(max_pages_per_seq) * page_size > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+  const long long q_blocks = attn ? (static_cast<long long>(max_q_len) + 127) / 128 : 0;
+  const long long dec_runs = (static_cast<long long>(max_pages_per_seq) + 7) / 8;
+  if (q_blocks * batch * heads > INT32_MAX || dec_runs * batch * heads > INT32_MAX ||
+      static_cast<long long>(num_pool_pages) * page_size * heads > INT32_MAX)
+    return MLA_ERR_UNSUPPORTED;
+  if (attn && (rope_cos == nullptr) != (rope_sin == nullptr)) return MLA_ERR_NULL;
+  if (attn && rope_cos != nullptr && rope_max_pos <= 0) return MLA_ERR_DIM;
+  if (total_q == 0) return MLA_OK;
+  if (!kv_cache || !page_table || !seq_lens || !workspace) return MLA_ERR_NULL;
+  if (dec && (!w_uk || !w_uv)) return MLA_ERR_NULL;
+  if (attn && (!q_c || !q_r || !cu_q || !out)) return MLA_ERR_NULL;
+  const void* ptrs[] = {kv_cache, page_table, seq_lens, workspace};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MLA_ERR_ALIGN;
+  if (dec && (!aligned16(w_uk) || !aligned16(w_uv))) return MLA_ERR_ALIGN;
+  if (attn) {
+    const void* aptrs[] = {q_c, q_r, cu_q, out};
+    for (const void* p : aptrs)
+      if (!aligned16(p)) return MLA_ERR_ALIGN;
+    if (lse_out && !aligned16(lse_out)) return MLA_ERR_ALIGN;
+    if (rope_cos && (!aligned16(rope_cos) || !aligned16(rope_sin))) return MLA_ERR_ALIGN;
+  }
+  a->q_c = q_c;
+  a->q_r = q_r;
+  a->kv = kv_cache;
+  a->page_table = page_table;
+  a->seq_lens = seq_lens;
+  a->cu_q = cu_q;
+  a->rope_cos = rope_cos;
+  a->rope_sin = rope_sin;
+  a->rope_max_pos = rope_max_pos;
+  a->w_uk = w_uk;
+  a->w_uv = w_uv;
+  a->workspace = workspace;
+  a->out = out;
+  a->lse_out = lse_out;
+  a->batch = batch;
+  a->total_q = total_q;
+  a->max_pages = max_pages_per_seq;
+  a->num_pool_pages = num_pool_pages;
+  a->max_q_len = max_q_len;
+  a->heads = heads;
+  a->scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(d_hc + d_R));
+  a->causal = causal != 0;
+  return MLA_OK;
+}
+
 int mla_prefill_paged(const void* q_c, const void* q_r, const void* kv_cache,
                       const int32_t* page_table, const int32_t* seq_lens, const int32_t* cu_q,
                       const float* rope_cos, const float* rope_sin, int rope_max_pos,
@@ -306,59 +378,47 @@ int mla_prefill_paged(const void* q_c, const void* q_r, const void* kv_cache,
                       int num_pool_pages, int max_q_len, int heads, int groups, int d_hc,
                       int d_c, int d_R, int page_size, float softmax_scale, int causal, int dtype,
                       void* stream) {
-  int st = check_dtype(dtype);
-  if (st != MLA_OK) return st;
-  if (total_q < 0 || batch <= 0 || max_q_len <= 0 || d_hc <= 0 || d_R <= 0 || (d_R & 1) ||
-      max_pages_per_seq <= 0 || num_pool_pages <= 0 || page_size <= 0)
-    return MLA_ERR_DIM;
-  if ((st = check_heads(heads, groups, d_c)) != MLA_OK) return st;
   mla::PrefillArgs a{};
-  a.groups = groups;
-  a.d_hc = d_hc;
-  a.d_c = d_c;
-  a.d_R = d_R;
-  a.page_size = page_size;
-  if (dtype != MLA_DTYPE_BF16 || !mla::prefill_supported(a)) return MLA_ERR_UNSUPPORTED;
-  if (static_cast<long long>(max_pages_per_seq) * page_size > INT32_MAX) return MLA_ERR_UNSUPPORTED;
-  const long long q_blocks = (static_cast<long long>(max_q_len) + 127) / 128;
-  const long long dec_runs = (static_cast<long long>(max_pages_per_seq) + 7) / 8;
-  if (q_blocks * batch * heads > INT32_MAX || dec_runs * batch * heads > INT32_MAX ||
-      static_cast<long long>(num_pool_pages) * page_size * heads > INT32_MAX)
-    return MLA_ERR_UNSUPPORTED;
-  if ((rope_cos == nullptr) != (rope_sin == nullptr)) return MLA_ERR_NULL;
-  if (rope_cos != nullptr && rope_max_pos <= 0) return MLA_ERR_DIM;
-  if (total_q == 0) return MLA_OK;
-  if (!q_c || !q_r || !kv_cache || !page_table || !seq_lens || !cu_q || !w_uk || !w_uv ||
-      !workspace || !out)
-    return MLA_ERR_NULL;
-  const void* ptrs[] = {q_c, q_r, kv_cache, page_table, seq_lens, cu_q, w_uk, w_uv, workspace, out};
-  for (const void* p : ptrs)
-    if (!aligned16(p)) return MLA_ERR_ALIGN;
-  if (lse_out && !aligned16(lse_out)) return MLA_ERR_ALIGN;
-  if (rope_cos && (!aligned16(rope_cos) || !aligned16(rope_sin))) return MLA_ERR_ALIGN;
-  a.q_c = q_c;
-  a.q_r = q_r;
-  a.kv = kv_cache;
-  a.page_table = page_table;
-  a.seq_lens = seq_lens;
-  a.cu_q = cu_q;
-  a.rope_cos = rope_cos;
-  a.rope_sin = rope_sin;
-  a.rope_max_pos = rope_max_pos;
-  a.w_uk = w_uk;
-  a.w_uv = w_uv;
-  a.workspace = workspace;
-  a.out = out;
-  a.lse_out = lse_out;
-  a.batch = batch;
-  a.total_q = total_q;
-  a.max_pages = max_pages_per_seq;
-  a.num_pool_pages = num_pool_pages;
-  a.max_q_len = max_q_len;
-  a.heads = heads;
-  a.scale = softmax_scale > 0.f ? softmax_scale : 1.0f / sqrtf(static_cast<float>(d_hc + d_R));
-  a.causal = causal != 0;
-  return launch_status(mla::launch_prefill(a, static_cast<hipStream_t>(stream)));
+  const int st = prefill_validate(3, q_c, q_r, kv_cache, page_table, seq_lens, cu_q, rope_cos,
+                                  rope_sin, rope_max_pos, w_uk, w_uv, workspace, out, lse_out,
+                                  batch, total_q, max_pages_per_seq, num_pool_pages, max_q_len,
+                                  heads, groups, d_hc, d_c, d_R, page_size, softmax_scale, causal,
+                                  dtype, &a);
+  if (st != MLA_OK || total_q == 0) return st;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int sd = launch_status(mla::launch_decompress(a, s));
+  if (sd != MLA_OK) return sd;
+  return launch_status(mla::launch_prefill_attn(a, s));
+}
+
+int mla_decompress_kv(const void* kv_cache, const int32_t* page_table, const int32_t* seq_lens,
+                      const void* w_uk, const void* w_uv, void* workspace, int batch,
+                      int max_pages_per_seq, int num_pool_pages, int heads, int groups, int d_hc,
+                      int d_c, int d_R, int page_size, int dtype, void* stream) {
+  mla::PrefillArgs a{};
+  const int st = prefill_validate(1, nullptr, nullptr, kv_cache, page_table, seq_lens, nullptr,
+                                  nullptr, nullptr, 0, w_uk, w_uv, workspace, nullptr, nullptr,
+                                  batch, 1, max_pages_per_seq, num_pool_pages, 0, heads, groups,
+                                  d_hc, d_c, d_R, page_size, 0.f, 1, dtype, &a);
+  if (st != MLA_OK) return st;
+  return launch_status(mla::launch_decompress(a, static_cast<hipStream_t>(stream)));
+}
+
+int mla_prefill_attention(const void* q_c, const void* q_r, const void* kv_cache,
+                          const int32_t* page_table, const int32_t* seq_lens, const int32_t* cu_q,
+                          const float* rope_cos, const float* rope_sin, int rope_max_pos,
+                          const void* workspace, void* out, float* lse_out, int batch,
+                          int total_q, int max_pages_per_seq, int num_pool_pages, int max_q_len,
+                          int heads, int groups, int d_hc, int d_c, int d_R, int page_size,
+                          float softmax_scale, int causal, int dtype, void* stream) {
+  mla::PrefillArgs a{};
+  const int st = prefill_validate(2, q_c, q_r, kv_cache, page_table, seq_lens, cu_q, rope_cos,
+                                  rope_sin, rope_max_pos, nullptr, nullptr,
+                                  const_cast<void*>(workspace), out, lse_out, batch, total_q,
+                                  max_pages_per_seq, num_pool_pages, max_q_len, heads, groups,
+                                  d_hc, d_c, d_R, page_size, softmax_scale, causal, dtype, &a);
+  if (st != MLA_OK || total_q == 0) return st;
+  return launch_status(mla::launch_prefill_attn(a, static_cast<hipStream_t>(stream)));
 }
 
 size_t mla_fp8_page_bytes(int d_c, int d_R) {

@@ -78,7 +78,8 @@ struct PrefillArgs {
   int causal;
 };
 bool prefill_supported(const PrefillArgs& a);
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+hipError_t launch_decompress(const PrefillArgs& a, hipStream_t s);    // K / V into the workspace
+hipError_t launch_prefill_attn(const PrefillArgs& a, hipStream_t s);  // attention over them
 
 // Latent-cache append of the new tokens' rows (c_KV | RoPE(k_R, pos)).
 struct AppendArgs {

@@ -417,15 +417,18 @@ bool prefill_supported(const PrefillArgs& a) {
   return a.groups == 1 && a.d_hc == kDhc && a.d_c == kDc && a.d_R == kDr && a.page_size == kTok;
 }
 
-hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
-  static std::atomic<uint64_t> dec_set{0}, att_set{0};
-  hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(decompress_kernel), kDecLds, dec_set);
-  if (e != hipSuccess) return e;
-  e = ensure_lds_limit(reinterpret_cast<const void*>(prefill_attn_kernel), kAttLds, att_set);
+hipError_t launch_decompress(const PrefillArgs& a, hipStream_t s) {
+  static std::atomic<uint64_t> dec_set{0};
+  const hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(decompress_kernel), kDecLds, dec_set);
   if (e != hipSuccess) return e;
   const long long runs = (a.max_pages + kDecPages - 1) / kDecPages;
   decompress_kernel<<<dim3(static_cast<unsigned>(runs * a.batch * a.heads)), kDecThreads, kDecLds, s>>>(a);
-  e = hipGetLastError();
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_attn(const PrefillArgs& a, hipStream_t s) {
+  static std::atomic<uint64_t> att_set{0};
+  const hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(prefill_attn_kernel), kAttLds, att_set);
   if (e != hipSuccess) return e;
   const long long n_qb = (a.max_q_len + kQBlock - 1) / kQBlock;
   prefill_attn_kernel<<<dim3(static_cast<unsigned>(n_qb * a.batch * a.heads)), kAttThreads, kAttLds, s>>>(a);

@@ -24,7 +24,8 @@ PAGE_SIZE = 64
 EXPORTED = ("mla_absorb_q", "mla_rope_table", "mla_decode_paged", "mla_combine", "mla_up_v",
             "mla_append_kv", "mla_decode_workspace_bytes", "mla_decode_plan", "mla_attend_noalloc",
             "mla_decode_paged_fp8", "mla_append_kv_fp8", "mla_fp8_page_bytes", "mla_branch",
-            "mla_prefill_paged", "mla_prefill_workspace_bytes", "mla_status_string")
+            "mla_prefill_paged", "mla_prefill_workspace_bytes", "mla_decompress_kv",
+            "mla_prefill_attention", "mla_status_string")
 
 _lib = None
 
@@ -60,6 +61,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_append_kv_fp8.argtypes = [P] * 8 + [I] * 8 + [P]
     lib.mla_branch.argtypes = [P, I, I]
     lib.mla_prefill_paged.argtypes = [P] * 8 + [I] + [P] * 5 + [I] * 11 + [F, I, I, P]
+    lib.mla_decompress_kv.argtypes = [P] * 6 + [I] * 10 + [P]
+    lib.mla_prefill_attention.argtypes = [P] * 8 + [I] + [P] * 3 + [I] * 11 + [F, I, I, P]
     lib.mla_prefill_workspace_bytes.argtypes = [I, I, I, I]
     lib.mla_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.mla_fp8_page_bytes.argtypes = [I, I]
@@ -68,7 +71,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_status_string.restype = ctypes.c_char_p
     for name in ("mla_absorb_q", "mla_rope_table", "mla_decode_paged", "mla_combine", "mla_up_v",
                  "mla_append_kv", "mla_decode_plan", "mla_attend_noalloc", "mla_decode_paged_fp8",
-                 "mla_append_kv_fp8", "mla_branch", "mla_prefill_paged"):
+                 "mla_append_kv_fp8", "mla_branch", "mla_prefill_paged", "mla_decompress_kv",
+                 "mla_prefill_attention"):
         getattr(lib, name).restype = I
     _lib = lib
     return lib
@@ -267,6 +271,39 @@ def prefill_paged(q_c, q_r, kv_cache, page_table, seq_lens, cu_q, w_uk, w_uv, wo
         _ptr(lse_out), B, T, max_pages, P, int(max_q_len), H, groups, d_hc, d_c, d_R, ps,
         float(softmax_scale), int(bool(causal)), DTYPE_BF16, _stream(stream)))
     return out
+
+
+def decompress_kv(kv_cache, page_table, seq_lens, w_uk, w_uv, workspace, *, groups: int = 1,
+                  stream=None) -> None:
+    """First half of the decompressed branch (mla_decompress_kv): K and V of every cache
+    row of the batch into ``workspace``."""
+    P, ps, width = kv_cache.shape
+    B, max_pages = page_table.shape
+    H, d_hc, d_cg = w_uk.shape
+    d_c = d_cg * groups
+    _dev(kv_cache, page_table, seq_lens, w_uk, w_uv, workspace)
+    _check("mla_decompress_kv", load().mla_decompress_kv(
+        _ptr(kv_cache), _ptr(page_table), _ptr(seq_lens), _ptr(w_uk), _ptr(w_uv), _ptr(workspace),
+        B, max_pages, P, H, groups, d_hc, d_c, width - d_c, ps, DTYPE_BF16, _stream(stream)))
+
+
+def prefill_attention(q_c, q_r, kv_cache, page_table, seq_lens, cu_q, workspace, out, lse_out=None,
+                      *, max_q_len: int, d_c: int, groups: int = 1, rope: Optional[tuple] = None,
+                      softmax_scale: float = 0.0, causal: bool = True, stream=None) -> None:
+    """Second half of the decompressed branch (mla_prefill_attention)."""
+    T, H, d_hc = q_c.shape
+    d_R = q_r.shape[2]
+    P, ps, width = kv_cache.shape
+    B, max_pages = page_table.shape
+    _expect("out", out, (T, H, d_hc), torch.bfloat16)
+    _expect("lse_out", lse_out, (T, H), torch.float32)
+    cos, sin, rope_max_pos = _rope_pair(rope, d_R, q_c.device)
+    _dev(q_c, q_r, kv_cache, page_table, seq_lens, cu_q, workspace, out, lse_out, cos, sin)
+    _check("mla_prefill_attention", load().mla_prefill_attention(
+        _ptr(q_c), _ptr(q_r), _ptr(kv_cache), _ptr(page_table), _ptr(seq_lens), _ptr(cu_q),
+        _ptr(cos), _ptr(sin), rope_max_pos, _ptr(workspace), _ptr(out), _ptr(lse_out),
+        B, T, max_pages, P, int(max_q_len), H, groups, d_hc, d_c, d_R, ps,
+        float(softmax_scale), int(bool(causal)), DTYPE_BF16, _stream(stream)))
 
 
 def fp8_page_bytes(d_c: int, d_R: int) -> int:
@@ -500,6 +537,16 @@ class DecodeStep:
                       self.w_uk, self.w_uv, self.workspace, self.out, self.lse,
                       max_q_len=self.max_q_len, groups=self.groups, rope=self.rope,
                       causal=self.causal, stream=stream)
+
+    def decompress(self, stream=None):
+        decompress_kv(self.kv, self.page_table, self.seq_lens, self.w_uk, self.w_uv, self.workspace,
+                      groups=self.groups, stream=stream)
+
+    def prefill_attend(self, stream=None):
+        prefill_attention(self.q_c, self.q_r, self.kv, self.page_table, self.seq_lens, self.cu_q,
+                          self.workspace, self.out, self.lse, max_q_len=self.max_q_len,
+                          d_c=self.w_uk.shape[2] * self.groups, groups=self.groups, rope=self.rope,
+                          causal=self.causal, stream=stream)
 
     def __call__(self, stream=None):
         if self.branch == BRANCH_DECOMPRESSED:
