@@ -16,11 +16,14 @@ from __future__ import annotations
 import argparse
 import collections
 import glob
+import hashlib
 import json
 import os
 import re
 import sqlite3
 import statistics
+
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 
 
 def _db(path: str) -> str:
@@ -93,6 +96,30 @@ def cmd_traffic(args):
     print(json.dumps({"fetch_scale": f_scale, "write_scale": w_scale,
                       "copy_fetch_kib": fetch_copy, "copy_write_kib": write_copy,
                       "kernels": rows}, indent=1))
+    if args.record:
+        # One record per (kernel, workload): the named kernel's bytes per launch, tagged with
+        # its source's hash so that a later source change invalidates it.
+        match = [n for n in rows if re.search(args.record_regex, n)]
+        if len(match) != 1:
+            raise SystemExit(f"--record-regex matches {len(match)} kernels: {match}")
+        r = rows[match[0]]
+        with open(os.path.join(CSRC, args.kernel_source), "rb") as f:
+            sha = hashlib.sha256(f.read()).hexdigest()[:16]
+        rec = {"workload": args.workload, "num_splits": args.num_splits, "kernel": args.kernel_name,
+               "kernel_source_sha256_16": sha, "bytes_per_launch": r["bytes_per_launch"],
+               "fetch_bytes": r["fetch_bytes"], "write_bytes": r["write_bytes"],
+               "fetch_scale": f_scale, "write_scale": w_scale, "source": args.summary}
+        try:
+            with open(args.record) as f:
+                data = json.load(f)
+        except OSError:
+            data = {"records": []}
+        data["records"] = [x for x in data.get("records", [])
+                           if not (x.get("kernel") == rec["kernel"] and x.get("workload") == rec["workload"])]
+        data["records"].append(rec)
+        with open(args.record, "w") as f:
+            json.dump(data, f, indent=1)
+            f.write("\n")
 
 
 def main():
@@ -112,6 +139,13 @@ def main():
     f.add_argument("--calib-mib", type=float, required=True)
     f.add_argument("--calib-regex", default="copyBuffer")
     f.add_argument("--regex", default=".")
+    f.add_argument("--record", help="records file to update (e.g. profiles/traffic_decode.json)")
+    f.add_argument("--record-regex", default="decode", help="the one kernel the record is for")
+    f.add_argument("--kernel-name", default="decode_m32_kernel")
+    f.add_argument("--kernel-source", default="decode_m32.hip", help="file under csrc/")
+    f.add_argument("--workload", default="")
+    f.add_argument("--num-splits", type=int, default=0)
+    f.add_argument("--summary", default="", help="the profiles/ summary the record comes from")
     args = ap.parse_args()
     {"trace": cmd_trace, "counters": cmd_counters, "traffic": cmd_traffic}[args.cmd](args)
 
