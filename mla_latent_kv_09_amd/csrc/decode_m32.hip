@@ -20,7 +20,7 @@
 //
 // Per page and wave:
 //   scores  S^T[64 tok x 32 heads] = C[64 x 576] . Q^T as two 32-token blocks of 36
-//           K-steps (4 RoPE + 32 latent); A = C from LDS (ds_read_b128), B = Q.
+//           K-steps (32 latent + 4 RoPE); A = C from LDS (ds_read_b128), B = Q.
 //           Lane l then holds head l % 32 and 16 tokens per block:
 //           token 8 (r / 4) + 4 (l / 32) + r % 4 of accumulator element r.
 //   softmax fp32, per head, the two lane halves combined with v_permlane32_swap.
@@ -385,6 +385,10 @@ decode_m32_kernel(DecodeArgs a) {
   const uint32_t o8_lane = static_cast<uint32_t>(tl8 * 512 + 16 * (lg & 1) + 8 * (li & 1));
   const uint32_t o8_x = static_cast<uint32_t>(32 * tl8);
 
+  // Latent-row copies, 128-head form: wave w copies tokens 16 w + r, whose chunk c sits at
+  // c ^ swz_f(16 w + r) = c ^ swz_f(r) ^ 16 (w & 1); the lane part of the source offset.
+  const uint32_t cp_lane = static_cast<uint32_t>(lane ^ (16 * (wave & 1))) << 4;
+  const char* cur_page = page_ptr(0);  // this iteration's page
   int stage = 0;
   for (; j0 < w.k1; j0 += kTok) {
     const int n_valid = min(kTok, w.k1 - j0);
@@ -415,9 +419,9 @@ decode_m32_kernel(DecodeArgs a) {
     const uint32_t st_base = smem_base + stage * Fm::kStage;
     const uint32_t sb = opaque(st_base + s_lane);
 
-    // ---- scores.  HS = 1: RoPE steps, then the latent steps, the two 32-token blocks
-    // alternating.  HS = 2: this wave's one 32-token block, two chains over alternate
-    // K-steps (summed below).
+    // ---- scores.  HS = 1: the latent steps, then the RoPE steps, the two 32-token blocks
+    // alternating.  HS = 2: this wave's one 32-token block, RoPE steps first, two chains
+    // over alternate K-steps (summed below).
     f32x16 s[2];
     if constexpr (F8) {
       // Latent K-step pairs first.  HS = 1: per pair, one read for each 32-token block and
@@ -498,52 +502,100 @@ decode_m32_kernel(DecodeArgs a) {
       const uint32_t rb = opaque(st_base + kCBytes + n * 128);
       const uint32_t qb = smem_base + kQrOff + hl * 128;
       const int swr = (n >> 2) & 7, swq = (hl >> 2) & 7;
+      auto qr_frag = [&](int rs) { return lds_read8(qb + (((2 * rs + h) ^ swq) << 4)); };
+      auto rope_frag = [&](int rs, int mb) { return lds_read8(rb + (((2 * rs + h) ^ swr) << 4) + 4096 * mb); };
+      auto lat_frag = [&](int ks, int mb) {
+        return lds_read8((sb ^ static_cast<uint32_t>((2 * ks & 31) << 4)) + 512 * (ks >> 4) + 32768 * mb);
+      };
+      constexpr int kRing = 4;
+      bf16x8 ring[kRing];
+      if constexpr (HS == 2) {
+        // RoPE steps first, then the 32 latent steps of this wave's block through a ring of
+        // reads, the two chains over alternate K-steps; the copies go with the odd steps.
 #pragma unroll
-      for (int rs = 0; rs < kRSteps; ++rs) {
-        const int c = 2 * rs + h;
-        const bf16x8 qrf = lds_read8(qb + ((c ^ swq) << 4));
-        if constexpr (HS == 1) {
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb) {
-            const bf16x8 cf = lds_read8(rb + ((c ^ swr) << 4) + 4096 * mb);
-            if (rs == 0)
-              mfma32_first(s[mb], cf, qrf);
-            else
-              mfma32_acc(s[mb], cf, qrf);
-          }
-        } else {
-          const bf16x8 cf = lds_read8(rb + ((c ^ swr) << 4) + 4096 * th);
+        for (int rs = 0; rs < kRSteps; ++rs) {
+          const bf16x8 qrf = qr_frag(rs);
+          const bf16x8 cf = rope_frag(rs, th);
           if (rs < 2)
             mfma32_first(s[rs & 1], cf, qrf);
           else
             mfma32_acc(s[rs & 1], cf, qrf);
         }
-      }
-      constexpr int kSteps = 2 * kQSteps / HS;  // (ks, mb) steps, or ks steps with HS = 2
-      constexpr int kRing = 4;
-      auto frag = [&](int st) {
-        const int ks = HS == 1 ? st >> 1 : st, mb = HS == 1 ? (st & 1) : th;
-        const uint32_t addr = (sb ^ static_cast<uint32_t>((2 * ks & 31) << 4)) +
-                              512 * (ks >> 4) + 32768 * mb;
-        return lds_read8(addr);
-      };
-      bf16x8 ring[kRing];
 #pragma unroll
-      for (int st = 0; st < kRing; ++st) ring[st] = frag(st);
+        for (int st = 0; st < kRing; ++st) ring[st] = lat_frag(st, th);
 #pragma unroll
-      for (int st = 0; st < kSteps; ++st) {
-        const bf16x8 cf = ring[st % kRing];
-        if (st + kRing < kSteps) ring[st % kRing] = frag(st + kRing);
-        mfma32_acc(s[st & 1], cf, q[HS == 1 ? st >> 1 : st]);
-        if constexpr (HS == 1) {
-          if ((st & 3) == 1 && has_next)  // 18 copies over the 64 steps
-            load_row(next_base, next_page, next_valid, wave, static_cast<int>(opaque(lane)), st >> 2);
-          if ((st == 34 || st == 50) && has_next)
-            load_row(next_base, next_page, next_valid, wave, static_cast<int>(opaque(lane)),
-                     st == 34 ? 16 : 17);
-        } else {
+        for (int st = 0; st < kQSteps; ++st) {
+          const bf16x8 cf = ring[st % kRing];
+          if (st + kRing < kQSteps) ring[st % kRing] = lat_frag(st + kRing, th);
+          mfma32_acc(s[st & 1], cf, q[st]);
           if ((st & 1) == 1 && has_next)  // latent rows 0..15 over the 32 steps
             load_row(next_base, next_page, next_valid, wave, static_cast<int>(opaque(lane)), st >> 1);
+        }
+      } else {
+        // The 64 latent (ks, mb) steps, then the 8 RoPE (rs, mb) steps, all through one
+        // ring of fragment reads issued kRing steps ahead (the q_R operands of the RoPE
+        // steps in a ring of their own), so no step waits for a read issued just before it.
+        constexpr int kLat = 2 * kQSteps, kSteps = kLat + 2 * kRSteps;
+        auto frag = [&](int st) {
+          return st < kLat ? lat_frag(st >> 1, st & 1) : rope_frag((st - kLat) >> 1, st & 1);
+        };
+        bf16x8 qr_ring[3];  // q_R of RoPE step rs in slot rs % 3, read with rs's first fragment
+        auto refill = [&](int st) {  // request the fragment(s) of step st + kRing
+          if (st + kRing < kSteps) {
+            ring[st % kRing] = frag(st + kRing);
+            const int rn = st + kRing - kLat;  // RoPE step of the fragment just requested
+            if (rn >= 0 && (rn & 1) == 0) qr_ring[(rn >> 1) % 3] = qr_frag(rn >> 1);
+          }
+        };
+        // Copies of the next page's rows into the other stage: copy k (latent rows k < 16,
+        // RoPE rows k = 16, 17) is prepared at step 4k and issued at step 4k + 2, so each
+        // gap between two MFMAs takes only a few of its instructions.  The last page copies
+        // itself into the unused stage instead, so the copies need no branch.
+        const char* cp_page = has_next ? next_page : cur_page;
+        const int cp_valid = has_next ? next_valid : kTok;
+        const int cp_lim = cp_valid - 16 * wave;  // latent row r of this wave is a key iff r < cp_lim
+        const uint32_t cp_m0 = next_base + 16384u * static_cast<uint32_t>(wave);
+        uint32_t cp_voff = 0, cp_lds = 0;
+        auto cp_prepare = [&](int k) {
+          if (k < 16) {  // token 16 w + k; rows past the keys fetch token 0
+            const int roff = k < cp_lim ? (16 * wave + k) * kRowBytes : 0;
+            cp_voff = (cp_lane ^ (swz_f(k) << 4)) + static_cast<uint32_t>(roff);
+            cp_lds = cp_m0 + 1024u * static_cast<uint32_t>(k);
+          } else {  // RoPE rows of tokens t0 .. t0 + 7
+            const int t0 = wave * 16 + 8 * (k - 16);
+            const int t = t0 + (static_cast<int>(opaque(lane)) >> 3);
+            const int src_t = t < cp_valid ? t : 0;
+            cp_voff = static_cast<uint32_t>(src_t * kRowBytes + kDc * 2 +
+                                            (((lane & 7) ^ ((t >> 2) & 7)) << 4));
+            cp_lds = next_base + kCBytes + static_cast<uint32_t>(t0 * 128);
+          }
+        };
+        // Issue order = source order within each step: the read for step st + kRing, the
+        // MFMA of step st, the copy's part.  (Left to itself the scheduler may move each read
+        // next to its MFMA, which then waits for it.)
+        auto copy_part = [&](int st) {
+          if ((st & 3) == 0) cp_prepare(st >> 2);
+          if ((st & 3) == 2) dma16(cp_page, cp_voff, cp_lds);
+          __builtin_amdgcn_sched_barrier(0);
+        };
+#pragma unroll
+        for (int st = 0; st < kRing; ++st) ring[st] = frag(st);
+#pragma unroll
+        for (int st = 0; st < kLat; ++st) {
+          const bf16x8 cf = ring[st % kRing];
+          refill(st);
+          if (st < 2)
+            mfma32_first(s[st & 1], cf, q[0]);
+          else
+            mfma32_acc(s[st & 1], cf, q[st >> 1]);
+          copy_part(st);
+        }
+#pragma unroll
+        for (int st = kLat; st < kSteps; ++st) {
+          const bf16x8 cf = ring[st % kRing];
+          refill(st);
+          mfma32_acc(s[st & 1], cf, qr_ring[((st - kLat) >> 1) % 3]);
+          copy_part(st);
         }
       }
     }
@@ -682,7 +734,11 @@ decode_m32_kernel(DecodeArgs a) {
 #pragma unroll
     for (int nb = 0; nb < kColBlocks; ++nb) asm volatile("" : "+a"(o[nb]));
     stage = F8 ? (stage == 2 ? 0 : stage + 1) : (stage ^ 1);
+    if (has_next) cur_page = next_page;
   }
+  // The 128-head bf16 form copies on every page, the last one included: its copies must land
+  // before the workgroup's LDS is released.
+  if constexpr (HS == 1 && !F8) __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 
   // ---- finalize: normalise and write this split's partial output (bf16) and LSE
   const float l_tot = halves_sum(l_run);
