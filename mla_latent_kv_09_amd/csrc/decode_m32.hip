@@ -83,7 +83,7 @@ constexpr int kLdsBytes = kQrOff + kHeads * kDr * 2;
 constexpr int kQSteps = kDc / 16;        // 32 latent K-steps
 constexpr int kRSteps = kDr / 16;        // 4 RoPE K-steps
 constexpr int kColBlocks = kDc / 32;     // 16 output blocks of 32 columns
-constexpr float kJump = 64.f;            // reference restart threshold, log2 units
+constexpr float kJump = 64.f;            // reference move threshold, log2 units
 static_assert(kLdsBytes <= 160 * 1024, "stages + q_R must fit the 160 KB LDS of a gfx950 CU");
 
 // FP8 cache page (= one LDS stage): codes, then k_R, then the token scales.
@@ -150,6 +150,21 @@ __device__ __forceinline__ void mfma32_acc(f32x16& acc, const bf16x8& a, const b
 // 32x32 MFMA's result latency requires.  The operands tie the pad after those MFMAs.
 __device__ __forceinline__ void mfma_results_ready(f32x16& s0, f32x16& s1) {
   asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" : "+v"(s0), "+v"(s1));
+}
+
+// o[nb] *= alpha for all 16 accumulator blocks, one block at a time through VGPRs (the
+// blocks live in the accumulator registers, which a vector multiply cannot write).
+__device__ __forceinline__ void scale_acc(f32x16 (&o)[16], float alpha) {
+#pragma unroll
+  for (int nb = 0; nb < 16; ++nb) {
+    asm volatile("" : "+a"(o[nb]));
+    f32x16 t = o[nb];
+    asm volatile("" : "+v"(t));
+    t *= alpha;
+    o[nb] = t;
+    asm volatile("" : "+a"(o[nb]));
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 // One 16-byte-per-lane global -> LDS copy (global_load_lds_dwordx4), wave-uniform base
@@ -619,21 +634,18 @@ decode_m32_kernel(DecodeArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
     mx = halves_max(mx) * scale_log2;
-    // Reference: a head's first page maximum.  Later terms are taken against it (up to
-    // 2^kJump: no overflow in fp32 or bf16, whose range is 2^127), so the output is never
-    // rescaled.  A page whose maximum exceeds the reference by more than kJump restarts
-    // the head at that maximum: everything accumulated before weighs at most
-    // 2^-kJump * (keys so far) < 2^-40 of the new maximum's term, below fp32 resolution,
-    // and is cleared instead of rescaled.
-    const bool restart = mx > m_ref + kJump;  // true on a head's first page with a key
-    if (restart) {
-      m_ref = mx;
-      l_run = 0.f;
-#pragma unroll
-      for (int nb = 0; nb < kColBlocks; ++nb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[nb][r] = 0.f;
-    }
+    // Reference: a head's first page maximum.  Later terms are taken against it, up to
+    // 2^kJump (no overflow in fp32 or bf16, whose range is 2^127), so the output is
+    // rescaled only when a page's maximum exceeds the reference by more than kJump: the
+    // reference moves to that maximum and what was accumulated is multiplied by
+    // 2^(old - new).  Output and log-sum-exp are normalised against the final reference,
+    // so the result is the same softmax.
+    const float m_old = m_ref;
+    const bool grow = mx > m_old + kJump;  // true on a head's first page with a key
+    if (grow) m_ref = mx;
+    const float alpha = grow ? __builtin_amdgcn_exp2f(m_old - mx) : 1.f;  // 0 from -inf
+    l_run *= alpha;
+    if (__builtin_amdgcn_ballot_w64(grow && m_old != -INFINITY) != 0) scale_acc(o, alpha);  // rare
     // With HS = 2 a token half can hold no key yet (the second half of a split's only,
     // partial page): its reference is still -inf and is subtracted as 0, so its
     // exponentials are 0 rather than NaN.

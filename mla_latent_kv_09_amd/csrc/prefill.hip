@@ -34,7 +34,7 @@ constexpr int kDc = 512;
 constexpr int kDr = 64;
 constexpr int kDhc = 128;
 constexpr int kRowBytes = (kDc + kDr) * 2;  // one bf16 cache row
-constexpr float kJump = 64.f;               // softmax reference restart threshold (log2 units)
+constexpr float kJump = 64.f;               // softmax reference move threshold (log2 units)
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
@@ -174,7 +174,8 @@ decompress_kernel(PrefillArgs a) {
 //   scores  S^T[64 keys x 32 queries] = [K | k_R] . [q_c | RoPE(q_R)]^T, 12 K-steps per
 //           32-key block (8 over K, 4 over k_R); A from LDS, B = the queries in registers.
 //   softmax fp32 per query, the fixed-reference form of the decode kernel (a query's first
-//           page maximum; terms up to 2^kJump against it; a jump past that restarts it).
+//           page maximum; terms up to 2^kJump against it; a jump past that moves it and
+//           rescales what was accumulated).
 //   output  O[32 queries x 128] += P . V over 4 K-steps of 16 keys: A = P from the score
 //           registers (no LDS round trip), B = V^T through transposing reads.
 // K/V row t (256 B) holds chunk c at position c ^ g(t), g(t) = ((t >> 1) & 3) << 2 |
@@ -332,21 +333,21 @@ prefill_attn_kernel(PrefillArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[mb][r]);
     mx = halves_max(mx) * scale_log2;
-    const bool restart = mx > m_ref + kJump;
-    if (restart) {
-      m_ref = mx;
-      l_run = 0.f;
-    }
-    // O rows are queries: clear the rows of the restarted queries (a ballot over lanes).
-    const uint64_t rmask = __builtin_amdgcn_ballot_w64(restart && hh == 0);
-    if (rmask != 0) {
+    // A page whose maximum exceeds the reference by more than kJump moves it there, and
+    // what was accumulated is multiplied by 2^(old - new) (rare).
+    const float m_old = m_ref;
+    const bool grow = mx > m_old + kJump;  // true on a query's first page with a key
+    if (grow) m_ref = mx;
+    const float alpha = grow ? __builtin_amdgcn_exp2f(m_old - mx) : 1.f;  // 0 from -inf
+    l_run *= alpha;
+    // O rows are queries: element r of this lane is query 8 (r / 4) + 4 hh + r % 4, whose
+    // factor is held by that query's lane.
+    if (__builtin_amdgcn_ballot_w64(grow && m_old != -INFINITY) != 0) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int qr = 8 * (r >> 2) + 4 * hh + (r & 3);
-        if ((rmask >> qr) & 1) {
+        const float ar = __shfl(alpha, 8 * (r >> 2) + 4 * hh + (r & 3));
 #pragma unroll
-          for (int nb = 0; nb < 4; ++nb) o[nb][r] = 0.f;
-        }
+        for (int nb = 0; nb < 4; ++nb) o[nb][r] *= ar;
       }
     }
     const float m_sub = m_ref == -INFINITY ? 0.f : m_ref;

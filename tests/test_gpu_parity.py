@@ -12,6 +12,7 @@ import torch
 
 import oracle.mla_oracle as om
 import parity_log
+import spike_cases
 from mla_latent_kv_09_amd import harness, mla
 from mla_latent_kv_09_amd import workloads as wl
 
@@ -320,8 +321,8 @@ def test_softmax_reference_moves(kind, case, mode, monkeypatch):
             underflows to zero) and a softmax spread evenly over identical rows, so the
             output is that row exactly; the other heads keep the first pages.
     shrink: rows scaled by 1/64; the first pages keep the reference for the whole split.
-    The 32x32 kernel (mfma32) never rescales: grow takes later terms of up to about 2^17
-    against the first page's reference, and flood restarts the head at the new maximum.
+    The 32x32 kernel (mfma32) moves its reference only past 2^64: grow takes later terms
+    of up to about 2^17 against the first page's reference, and flood moves it.
     Scaled rows scale the rounding error of a score with them, so W_UK is a selection
     matrix (q_abs = q_c on the first d_hc latent columns, exact in bf16) and RoPE is
     off (a rotated q_R is rounded to bf16): the scores then differ from the oracle's
@@ -354,6 +355,28 @@ def test_softmax_reference_moves(kind, case, mode, monkeypatch):
     print(f"case {case} mode {mode} kernel {kind}", flush=True)
     step = run_step(w, num_splits=1, rope=False)
     ref = oracle_for(w, rope=False)
+    assert_parity(_f64(step.o_latent), ref["o_latent"], what="o_latent")
+    assert_parity(_f64(step.out), ref["out"])
+
+
+@pytest.mark.parametrize("kind", ["mfma128", "mfma64", "mfma32-128", "mfma32-64", "generic"])
+@pytest.mark.parametrize("slots", [(5, 9), (37, 40)])
+def test_softmax_reference_moves_keep_earlier_pages(kind, slots, monkeypatch):
+    """A later page moving the softmax reference must rescale what earlier pages added,
+    not drop it: pages 1 and 2 carry spikes 63 and 65 log2 units above page 0's maximum
+    (so only page 2 moves a reference that allows terms up to 2^64), and page 1's spike
+    keeps about a fifth of the output.  Dropping it misses the bar by about 20x.  The
+    spikes sit in the first or the second 32-token half of their pages."""
+    cfg = wl.CONFIGS["dsv3_b16_l4096"].replace(batch=1, seq_len=4 * 64 - 7, q_len=1)
+    w, gaps = spike_cases.climbing_spikes_workload(cfg, slots=slots)
+    assert 62.5 < gaps[0] < 63.5 and 64.5 < gaps[1] < 65.5, gaps
+    monkeypatch.setenv("MLA_KV_DECODE_KERNEL", kind)
+    print(f"kernel {kind}: spikes in rows {slots} at +{gaps[0]:.2f} and +{gaps[1]:.2f} log2 units",
+          flush=True)
+    step = run_step(w, num_splits=1, rope=False)
+    ref = oracle_for(w, rope=False)
+    lat = ref["o_latent"][0, 0]
+    assert 0.1 < lat[200] / lat[300] < 0.4       # the design: page 1's spike keeps weight
     assert_parity(_f64(step.o_latent), ref["o_latent"], what="o_latent")
     assert_parity(_f64(step.out), ref["out"])
 

@@ -16,6 +16,7 @@ import torch
 
 import oracle.mla_oracle as om
 import parity_log
+import spike_cases
 from mla_latent_kv_09_amd import harness, mla
 from mla_latent_kv_09_amd import workloads as wl
 
@@ -74,6 +75,20 @@ def test_prefill_matches_oracle(batch, q_len, seq_len, heads, rope):
     _check(_f64(step.out), ref["out"], f"q{q_len} L{seq_len}", show=rope and heads == 128,
            lse_err=lse_err)
     assert lse_err <= 2e-2
+
+
+@pytest.mark.parametrize("slots", [(5, 9), (37, 40)])
+def test_prefill_reference_moves_keep_earlier_pages(slots):
+    """The decompressed branch's softmax on a score maximum that climbs twice within the
+    keys every query sees (pages 1 and 2 hold spikes 63 and 65 log2 units above page 0's
+    maximum, one shared query): the move at page 2 must rescale page 1's spike, which
+    keeps about a fifth of the weight (dropping it misses the bar about 6x)."""
+    w, gaps = spike_cases.climbing_spikes_workload(_prefill_cfg(1, 256, 448), slots=slots)
+    assert 62.5 < gaps[0] < 63.5 and 64.5 < gaps[1] < 65.5, gaps
+    print(f"prefill spikes in rows {slots} at +{gaps[0]:.2f} and +{gaps[1]:.2f} log2 units", flush=True)
+    step, _ = _run(w, rope=False)
+    assert step.branch == mla.BRANCH_DECOMPRESSED
+    _check(_f64(step.out), _oracle(w, rope=False)["out"], f"climbing spikes {slots}")
 
 
 def test_prefill_workspace_holds_the_reconstructed_keys_and_values():
