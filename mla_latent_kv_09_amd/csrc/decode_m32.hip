@@ -257,11 +257,11 @@ decode_m32_kernel(DecodeArgs a) {
   using Fm = Form<F8>;
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int S = a.num_splits;
-  // Launch order.  The units of sequence b (its n query tokens x S splits) are the
-  // workgroups [cu_q[b] S, cu_q[b+1] S).  With one token they run in split order.  With
-  // n tokens, which read the same pages, each block of 8 splits takes 8 n consecutive
-  // workgroups, token-major: the n workgroups of one split are 8 apart, so the
-  // dispatcher (workgroup L to XCD L mod 8) places them on one XCD at about the same
+  // Launch order (HS = 1): every sequence's non-empty (token, split) units first, then
+  // the empty ones (unit_active_first).  Within a sequence of one token the splits run in
+  // order; with n tokens, which read the same pages, each block of 8 splits takes 8 n
+  // consecutive workgroups, token-major, so the n workgroups of one split are 8 apart:
+  // the dispatcher (workgroup L to XCD L mod 8) places them on one XCD at about the same
   // time, and that XCD's L2 serves the later reads of each page.
   SeqIndex ix;
   ix.load(a.cu_q, a.seq_lens, a.batch);
@@ -269,10 +269,10 @@ decode_m32_kernel(DecodeArgs a) {
   if constexpr (HS == 2) {
     u = unit_pair_blocks(static_cast<int>(blockIdx.x), S, a.total_q);
   } else {
-    const int L = static_cast<int>(blockIdx.x);
-    const int b = ix.find(L / S);
-    const int q0 = ix.start(b);
-    u = unit_m32(L, S, q0, ix.stop(b) - q0, a.total_q);
+    u = unit_active_first_wave(static_cast<int>(blockIdx.x), S, a.pages_per_split, kTok, a.max_pages,
+                               a.cu_q, a.seq_lens, a.batch);
+    if (u.t < 0 || u.t >= a.total_q || u.split < 0 || u.split >= S)
+      u = unit_split_fastest(static_cast<int>(blockIdx.x), S);  // malformed cu_q
   }
   const int t = u.t, split = u.split, h2 = u.half;
   const int tid = threadIdx.x, lane = tid & 63;

@@ -83,6 +83,51 @@ struct SeqIndex {
   }
 };
 
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_inclusive_sum(int x) {
+  const int lane = static_cast<int>(threadIdx.x) & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// unit_active_first (mla_index.h) for workgroup L, the sequences taken 64 at a time
+// (lane l holds sequence c + l of chunk c): per pass, a prefix sum of the units each
+// sequence contributes locates L's sequence, and unit_in_sequence places it there.
+__device__ __forceinline__ Unit unit_active_first_wave(int L, int S, int pages_per_split, int page_size,
+                                                       int max_pages, const int32_t* __restrict__ cu_q,
+                                                       const int32_t* __restrict__ seq_lens, int batch) {
+  const int lane = static_cast<int>(threadIdx.x) & 63;
+  int base = 0;
+  for (int pass = 0; pass < 2; ++pass)
+    for (int c = 0; c < batch; c += 64) {
+      const int b = c + lane;
+      int q0 = 0, nq = 0, a = 0;
+      if (b < batch) {
+        q0 = cu_q[b];
+        nq = cu_q[b + 1] - q0;
+        a = active_splits(seq_lens[b], S, pages_per_split, page_size, max_pages);
+      }
+      const int lo = pass == 0 ? 0 : a, cnt = pass == 0 ? a : S - a;
+      const int units = nq * cnt;
+      const int incl = wave_inclusive_sum(units);
+      const int total = __builtin_amdgcn_readlane(incl, 63);
+      if (L < base + total) {
+        const uint64_t m = __builtin_amdgcn_ballot_w64(b < batch && L < base + incl);
+        const int lb = static_cast<int>(__builtin_ctzll(m));
+        const int before = __builtin_amdgcn_readlane(incl - units, lb);
+        return unit_in_sequence(L - base - before, __builtin_amdgcn_readlane(q0, lb),
+                                __builtin_amdgcn_readlane(nq, lb), __builtin_amdgcn_readlane(lo, lb),
+                                __builtin_amdgcn_readlane(cnt, lb));
+      }
+      base += total;
+    }
+  return unit_split_fastest(L, S);
+}
+
 __device__ __forceinline__ QueryWork query_work(const SeqIndex& ix, int t, int split, int num_splits,
                                                 int pages_per_split, int page_size, int max_pages,
                                                 int causal) {

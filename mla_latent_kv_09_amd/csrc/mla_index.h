@@ -113,6 +113,63 @@ __host__ __device__ inline Unit unit_mfma_half(int L, int S, int T) {
   return u;
 }
 
+// Non-empty splits of a sequence for its last query row, which sees every key: the
+// splits s < num_splits with s * c * page_size < L (c and the clamp of L as in
+// split_work).  Earlier rows of a causal multi-token sequence may find the last of them
+// empty.
+__host__ __device__ inline int active_splits(int L_raw, int num_splits, int pages_per_split,
+                                             int page_size, int max_pages) {
+  const long long cap = static_cast<long long>(max_pages) * page_size;
+  const long long L = L_raw < 0 ? 0 : (L_raw > cap ? cap : L_raw);
+  if (L == 0 || num_splits <= 0) return 0;
+  const long long n_pages = (L + page_size - 1) / page_size;
+  const long long per = pages_per_split > 0 ? pages_per_split : (n_pages + num_splits - 1) / num_splits;
+  const long long step = per * page_size;
+  const long long s = (L + step - 1) / step;
+  return s < num_splits ? static_cast<int>(s) : num_splits;
+}
+
+// Unit v of the nq x cnt units (q0 + i, s_lo + j), i < nq, j < cnt: with one token in
+// split order; with nq tokens, which read the same pages, blocks of 8 splits taking 8 nq
+// consecutive units token-major, so the nq units of one split are 8 apart (one XCD,
+// about the same time, when the block starts at a multiple of 8).
+__host__ __device__ inline Unit unit_in_sequence(int v, int q0, int nq, int s_lo, int cnt) {
+  Unit u;
+  u.half = 0;
+  if (nq <= 1) {
+    u.t = q0;
+    u.split = s_lo + v;
+    return u;
+  }
+  const int blk = v / (8 * nq), r = v - blk * 8 * nq;
+  const int k = (cnt - 8 * blk) < 8 ? (cnt - 8 * blk) : 8;
+  u.t = q0 + r / k;
+  u.split = s_lo + 8 * blk + (r - (r / k) * k);
+  return u;
+}
+
+// Active-first launch order of the 32x32x16 kernel: first every sequence's non-empty
+// splits (sequence order, unit_in_sequence within one), then every empty one.  The
+// dispatcher deals the workgroups of an XCD round-robin to its shader engines and waits
+// while the next one's engine is full, so short empty workgroups scattered through the
+// order leave compute units idle until a long workgroup of that engine ends; at the end
+// they cost nothing.  Reference form over the arrays (the kernel computes the same map
+// with a wave-wide prefix sum).
+__host__ __device__ inline Unit unit_active_first(int L, int S, int pages_per_split, int page_size,
+                                                  int max_pages, const int32_t* cu_q,
+                                                  const int32_t* seq_lens, int batch) {
+  int base = 0;
+  for (int pass = 0; pass < 2; ++pass)
+    for (int b = 0; b < batch; ++b) {
+      const int q0 = cu_q[b], nq = cu_q[b + 1] - cu_q[b];
+      const int a = active_splits(seq_lens[b], S, pages_per_split, page_size, max_pages);
+      const int lo = pass == 0 ? 0 : a, cnt = pass == 0 ? a : S - a;
+      if (L < base + nq * cnt) return unit_in_sequence(L - base, q0, nq, lo, cnt);
+      base += nq * cnt;
+    }
+  return unit_split_fastest(L, S);
+}
+
 // One workgroup per (token, split) of the 32x32x16 kernel.  The units of sequence b (its
 // nq query tokens x S splits, first token q0) are the workgroups [q0 S, (q0 + nq) S).
 // With one token they run in split order.  With nq tokens, which read the same pages,

@@ -4,12 +4,16 @@
     python -m mla_latent_kv_09_amd.profile_summary counters DB [DB ...] [--regex R]
     python -m mla_latent_kv_09_amd.profile_summary traffic --fetch DB --write DB
             --calib-fetch DB --calib-write DB --calib-mib N --regex R
+    python -m mla_latent_kv_09_amd.profile_summary clock DB [--regex R] [--flops-per-dispatch F]
 
 `trace` lists per-kernel dispatch count and duration statistics from a
 `--kernel-trace` run; `counters` lists per-kernel mean counter values per
 dispatch from `--pmc` runs; `traffic` turns FETCH_SIZE / WRITE_SIZE (KiB per
 dispatch) into HBM bytes per dispatch, each scaled by what the same counter
-reads for a plain copy of known size.
+reads for a plain copy of known size; `clock` divides GRBM_GUI_ACTIVE (GPU
+cycles of a dispatch) by the dispatch's duration, giving the clock the chip ran
+at, and with SQ_VALU_MFMA_BUSY_CYCLES (summed over the 32 SIMDs of a shader
+engine) the matrix pipes' busy fraction at that clock.
 """
 from __future__ import annotations
 
@@ -78,6 +82,36 @@ def cmd_counters(args):
         print(f"| `{_short(name)}` | " + " | ".join(f"{v.get(c, float('nan')):.1f}" for c in counters) + " |")
 
 
+def dispatch_counters(path: str, regex: str = "."):
+    """{kernel: [(duration ns, {counter: mean over instances})]} per dispatch."""
+    con = sqlite3.connect(_db(path))
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    dur, names = {}, {}
+    for name, did, d, counter, value in con.execute(
+            "select name, dispatch_id, duration, counter_name, counter_value from pmc_events"):
+        if re.search(regex, name):
+            per[did][counter].append(value)
+            dur[did], names[did] = d, name
+    out = collections.defaultdict(list)
+    for did, cs in per.items():
+        out[names[did]].append((dur[did], {c: statistics.fmean(v) for c, v in cs.items()}))
+    return out
+
+
+def cmd_clock(args):
+    d = dispatch_counters(args.db, args.regex)
+    print("| kernel | dispatches | mean us | GRBM_GUI_ACTIVE | clock GHz | MFMA busy | TFLOP/s |")
+    print("|---|---|---|---|---|---|---|")
+    for name, rows in sorted(d.items(), key=lambda kv: -sum(r[0] for r in kv[1])):
+        us = statistics.fmean(r[0] for r in rows) / 1000.0
+        gui = statistics.fmean(r[1].get("GRBM_GUI_ACTIVE", float("nan")) for r in rows)
+        ghz = statistics.fmean(r[1].get("GRBM_GUI_ACTIVE", float("nan")) / r[0] for r in rows)
+        busy = statistics.fmean(r[1].get("SQ_VALU_MFMA_BUSY_CYCLES", float("nan")) / 32.0
+                                / r[1].get("GRBM_GUI_ACTIVE", float("nan")) for r in rows)
+        tf = args.flops_per_dispatch / (us * 1e-6) / 1e12 if args.flops_per_dispatch else float("nan")
+        print(f"| `{_short(name)}` | {len(rows)} | {us:.2f} | {gui:.0f} | {ghz:.3f} | {busy:.3f} | {tf:.0f} |")
+
+
 def cmd_traffic(args):
     mib_kib = args.calib_mib * 1024.0
     cf = counter_means([args.calib_fetch], args.calib_regex)
@@ -131,6 +165,10 @@ def main():
     c = sub.add_parser("counters")
     c.add_argument("db", nargs="+")
     c.add_argument("--regex", default=".")
+    k = sub.add_parser("clock")
+    k.add_argument("db")
+    k.add_argument("--regex", default=".")
+    k.add_argument("--flops-per-dispatch", type=float, default=0.0)
     f = sub.add_parser("traffic")
     f.add_argument("--fetch", required=True)
     f.add_argument("--write", required=True)
@@ -147,7 +185,7 @@ def main():
     f.add_argument("--num-splits", type=int, default=0)
     f.add_argument("--summary", default="", help="the profiles/ summary the record comes from")
     args = ap.parse_args()
-    {"trace": cmd_trace, "counters": cmd_counters, "traffic": cmd_traffic}[args.cmd](args)
+    {"trace": cmd_trace, "counters": cmd_counters, "traffic": cmd_traffic, "clock": cmd_clock}[args.cmd](args)
 
 
 if __name__ == "__main__":

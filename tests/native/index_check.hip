@@ -5,7 +5,8 @@
 //  - each launch-order map is a bijection from workgroup ids onto
 //    (query token, split[, head half]) and keeps its locality promise (the tokens of a
 //    split 8 workgroups apart, the halves of a pair on one XCD, a token's workgroups on
-//    XCD t mod 8);
+//    XCD t mod 8); the active-first order puts every non-empty split before every empty
+//    one, and its count of non-empty splits agrees with split_work;
 //  - split_work's key ranges tile the visible keys of every query exactly, for any
 //    split count and split length up to INT32_MAX, without signed overflow.
 // Prints one line per section and exits non-zero on the first failure.
@@ -89,6 +90,53 @@ static void check_m32(std::mt19937& g) {
   printf("m32 launch order: %d workgroups ok\n", n);
 }
 
+static void check_active_first(std::mt19937& g) {
+  long long n = 0;
+  for (int it = 0; it < 500; ++it) {
+    const int B = 1 + static_cast<int>(g() % 150);
+    const int S = 1 + static_cast<int>(g() % 40);
+    const int page = 64;
+    const std::vector<int32_t> cu = make_cu(g, B, true, 3);
+    const int T = cu[B];
+    std::vector<int32_t> lens(B);
+    for (int b = 0; b < B; ++b) lens[b] = static_cast<int32_t>(g() % 6000) - (g() % 20 == 0 ? 10 : 0);
+    const int max_pages = 1 + static_cast<int>(g() % 100);
+    const int pps = g() % 3 == 0 ? 0 : 1 + static_cast<int>(g() % 40);
+    std::vector<int> where(static_cast<size_t>(T) * S, -1);
+    int last_active = -1, first_empty = T * S;
+    for (int L = 0; L < T * S; ++L, ++n) {
+      const Unit u = mla::unit_active_first(L, S, pps, page, max_pages, cu.data(), lens.data(), B);
+      const bool ok = u.t >= 0 && u.t < T && u.split >= 0 && u.split < S;
+      CHECK(ok, "active-first range L=%d", L);
+      if (!ok) continue;
+      int& w = where[static_cast<size_t>(u.t) * S + u.split];
+      CHECK(w < 0, "active-first (t=%d, s=%d) hit twice", u.t, u.split);
+      w = L;
+      const int b = mla::find_seq(cu.data(), B, u.t);
+      const int a = mla::active_splits(lens[b], S, pps, page, max_pages);
+      if (u.split < a) last_active = L; else if (L < first_empty) first_empty = L;
+      // active_splits agrees with split_work for the sequence's last row
+      const int nq = cu[b + 1] - cu[b];
+      const mla::QueryWork wk = mla::split_work(b, cu[b], nq, lens[b], cu[b + 1] - 1, u.split, S, pps, page,
+                                                max_pages, 1);
+      CHECK((wk.k0 < wk.k1) == (u.split < a), "active_splits vs split_work (L=%d s=%d a=%d)", lens[b], u.split, a);
+    }
+    CHECK(last_active < first_empty, "an empty unit before an active one");
+    for (int b = 0; b < B; ++b) {
+      const int q0 = cu[b], nq = cu[b + 1] - cu[b];
+      const int a = mla::active_splits(lens[b], S, pps, page, max_pages);
+      for (int s = 1; s < a && nq == 1; ++s)
+        CHECK(where[static_cast<size_t>(q0) * S + s] == where[static_cast<size_t>(q0) * S + s - 1] + 1,
+              "active splits of a one-token sequence in order");
+      for (int s = 0; s < 8 * (a / 8) && nq > 1; ++s)
+        for (int i = 1; i < nq; ++i)
+          CHECK(where[static_cast<size_t>(q0 + i) * S + s] - where[static_cast<size_t>(q0) * S + s] == 8 * i,
+                "tokens of an active split 8 apart");
+    }
+  }
+  printf("active-first launch order: %lld workgroups ok\n", n);
+}
+
 static void check_halves(std::mt19937& g, bool mfma_form) {
   int n = 0;
   for (int it = 0; it < 400; ++it) {
@@ -161,6 +209,7 @@ int main() {
   std::mt19937 g(20261203);
   check_lookup(g);
   check_m32(g);
+  check_active_first(g);
   check_halves(g, false);
   check_halves(g, true);
   check_splits(g);

@@ -51,3 +51,22 @@ def climbing_spikes_workload(cfg, t_gaps=(63.0, 65.0), slots=(5, 9), beta=16.0):
         w.pool[pt[k], slot] = bits
         gaps.append(score_log2(wl.bf16_bits_to_f32(bits).astype(np.float64)) - t0)
     return w, gaps
+
+
+def realized_gaps(w, rows, slots=(5, 9)):
+    """Score gaps (log2 units) of the two spikes above the page-0 anchor, taken on the
+    logical rows ``rows`` of sequence 0 (for instance a quantized cache's dequantized
+    rows) with the workload's shared query, RoPE off."""
+    cfg = w.cfg
+    d_hc, d_c = w.w_uk.shape[1], cfg.d_c
+    q = w.q_c[0, 0].astype(np.float64)
+    qr = w.q_r[0, 0].astype(np.float64)
+    k = om.default_scale(d_hc, cfg.d_R) / math.log(2.0)
+    rows = np.asarray(rows, np.float64)
+    ps = cfg.page_size
+
+    def t(j):
+        return k * (rows[j, :d_hc] @ q + rows[j, d_c:] @ qr)
+
+    t0 = t(0)
+    return [t(ps + slots[0]) - t0, t(2 * ps + slots[1]) - t0]

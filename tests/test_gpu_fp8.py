@@ -21,6 +21,7 @@ import torch
 import oracle.fp8_cache as f8
 import oracle.mla_oracle as om
 import parity_log
+import spike_cases
 from mla_latent_kv_09_amd import harness, mla
 from mla_latent_kv_09_amd import workloads as wl
 
@@ -96,6 +97,28 @@ def test_fp8_decode_parity_small(case, kind, monkeypatch):
     _check(_f64(step.out), ref["out"], "out", show=kind is None, lse_err=lse_err)
     _check(_f64(step.o_latent), ref["o_latent"], "o_latent")
     assert lse_err <= 2e-2
+
+
+@pytest.mark.parametrize("kind", ["mfma32-128", "mfma32-64"])
+@pytest.mark.parametrize("slots", [(5, 9), (37, 40)])
+def test_fp8_reference_moves_keep_earlier_pages(kind, slots, monkeypatch):
+    """The FP8 decode's softmax on a score maximum that climbs twice within a split (the
+    bf16 decode's spike case, quantized): page 2's reference move must rescale page 1's
+    spike.  The gaps are checked on the dequantized rows the oracle decodes."""
+    cfg = _small("dsv3_b16_l4096", batch=1, seq_len=4 * 64 - 7, q_len=1)
+    w, _ = spike_cases.climbing_spikes_workload(cfg, slots=slots)
+    pool, deq = _quantized(w)
+    gaps = spike_cases.realized_gaps(w, deq[0], slots)
+    assert 62.0 < gaps[0] < 64.0 and 64.0 < gaps[1] < 66.0, gaps
+    monkeypatch.setenv("MLA_KV_DECODE_KERNEL", kind)
+    print(f"fp8 kernel {kind}: spikes in rows {slots} at +{gaps[0]:.2f} and +{gaps[1]:.2f}", flush=True)
+    d = harness.to_device(w, rope=False, kv=pool)
+    step = harness.make_step(w, d, 1)
+    step()
+    torch.cuda.synchronize()
+    ref = om.mla_decode(w.q_c, w.q_r, deq, w.w_uk, w.w_uv, w.cu_q, rope_base=None, causal=w.cfg.causal)
+    _check(_f64(step.o_latent), ref["o_latent"], "o_latent")
+    _check(_f64(step.out), ref["out"], "out")
 
 
 def _with_lengths(cfg, lens, q_lens):
