@@ -13,11 +13,13 @@ namespace {
 
 // Cost of one split in units of one page (streaming 72 KB and computing 128 heads over
 // it): a fixed part for the prologue (queries fetched, first page in flight) and the
-// epilogue (the split's partial written), measured at about 2.5 pages on MI355X, plus
-// one unit per page.  A split with no keys exits at once.
-constexpr double kSplitOverheadPages = 2.5;
+// epilogue (the split's partial written), fitted at about 4 pages to the decode times of
+// ragged_b64's candidate plans on MI355X, plus one unit per page.  A split with no keys
+// exits at once.
+constexpr double kSplitOverheadPages = 4.0;
 constexpr double kEmptySplitPages = 0.2;
 constexpr int kXcds = 8;
+constexpr int kEngines = 4;  // shader engines per XCD
 constexpr int kMaxSplits = 256;
 constexpr int kMaxCusPerXcd = 512;
 // Longest split (pages) for which two 64-head workgroups per (token, split) pay off: the
@@ -32,37 +34,66 @@ long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
 int pages_of(int32_t L) { return L <= 64 ? 1 : static_cast<int>(ceil_div(L, 64)); }
 
+// One workgroup of the model: the XCD deals its k-th workgroup to shader engine
+// k mod engines, to the engine's first CU to come free, never before the XCD's previous
+// workgroup started (a workgroup whose engine is full holds back the ones behind it).
+struct XcdQueue {
+  double free_at[kEngines][kMaxCusPerXcd / kEngines];  // per_engine <= 512 / 4
+  double last_start = 0.0;
+  long long k = 0;
+  void place(int engines, int per_engine, double cost) {
+    double* f = free_at[k % engines];
+    int c = 0;
+    for (int i = 1; i < per_engine; ++i)
+      if (f[i] < f[c]) c = i;
+    const double start = std::max(last_start, f[c]);
+    f[c] = start + cost;
+    last_start = start;
+    ++k;
+  }
+};
+
 // Finish time, in page units, of the decode grid with splits of `pps` pages.  The grid
-// runs in split-fastest order (workgroup L = token * S + split); the dispatcher deals
-// workgroup L to XCD L mod 8 and each XCD hands its workgroups to the first of its CUs
-// to come free, one workgroup per CU at a time (a min-heap of CU free times per XCD).
+// runs every sequence's non-empty splits first (sequence, token, split order), then the
+// empty ones; the dispatcher deals workgroup L to XCD L mod 8 (XcdQueue above).
 double makespan(const int32_t* seq_lens, const int32_t* q_lens, int batch, int pps, int cu_count) {
   int n_splits = 1;
   for (int b = 0; b < batch; ++b)
     n_splits = std::max(n_splits, static_cast<int>(ceil_div(pages_of(seq_lens[b]), pps)));
   const int per_xcd = std::max(1, cu_count / kXcds);
-  double free_at[kXcds][kMaxCusPerXcd];
-  for (int x = 0; x < kXcds; ++x)
-    for (int c = 0; c < per_xcd; ++c) free_at[x][c] = 0.0;
+  const int engines = std::min(kEngines, per_xcd);
+  const int per_engine = std::max(1, per_xcd / engines);
+  XcdQueue q[kXcds];  // 32 KB on the stack
+  for (int x = 0; x < kXcds; ++x) {
+    for (int e = 0; e < engines; ++e)
+      for (int c = 0; c < per_engine; ++c) q[x].free_at[e][c] = 0.0;
+    q[x].last_start = 0.0;
+    q[x].k = 0;
+  }
   long long wg = 0;
-  for (int b = 0; b < batch; ++b) {
-    const int p = pages_of(seq_lens[b]);
-    for (int i = 0; i < q_lens[b]; ++i) {
-      for (int y = 0; y < n_splits; ++y) {
-        const long long work = std::min<long long>(pps, p - static_cast<long long>(y) * pps);
-        const double cost = work > 0 ? kSplitOverheadPages + static_cast<double>(work)
-                                     : kEmptySplitPages;
-        double* f = free_at[wg % kXcds];
-        std::pop_heap(f, f + per_xcd, std::greater<double>());
-        f[per_xcd - 1] += cost;
-        std::push_heap(f, f + per_xcd, std::greater<double>());
-        ++wg;
+  for (int pass = 0; pass < 2; ++pass)
+    for (int b = 0; b < batch; ++b) {
+      const int p = pages_of(seq_lens[b]);
+      const long long active = ceil_div(p, pps);
+      for (int i = 0; i < q_lens[b]; ++i) {
+        if (pass == 0) {
+          for (long long y = 0; y < active; ++y) {
+            const long long work = std::min<long long>(pps, p - y * pps);
+            q[wg % kXcds].place(engines, per_engine, kSplitOverheadPages + static_cast<double>(work));
+            ++wg;
+          }
+        } else {
+          for (long long y = active; y < n_splits; ++y) {
+            q[wg % kXcds].place(engines, per_engine, kEmptySplitPages);
+            ++wg;
+          }
+        }
       }
     }
-  }
   double m = 0.0;
   for (int x = 0; x < kXcds; ++x)
-    for (int c = 0; c < per_xcd; ++c) m = std::max(m, free_at[x][c]);
+    for (int e = 0; e < engines; ++e)
+      for (int c = 0; c < per_engine; ++c) m = std::max(m, q[x].free_at[e][c]);
   return m;
 }
 

@@ -10,31 +10,46 @@ PAGE_SIZE = 64
 
 # Cost of one split in units of one page (streaming 72 KB and computing 128 heads
 # over it): a fixed part for the prologue (queries fetched, first page in flight) and
-# the epilogue (bf16 partial written, 128 KB), measured at about 2.5 pages on MI355X,
-# plus one unit per page.  A split with no keys exits at once.
-SPLIT_OVERHEAD_PAGES = 2.5
+# the epilogue (bf16 partial written, 128 KB), fitted at about 4 pages to the decode
+# times of ragged_b64's candidate plans on MI355X, plus one unit per page.  A split with
+# no keys exits at once.
+SPLIT_OVERHEAD_PAGES = 4.0
 EMPTY_SPLIT_PAGES = 0.2
 XCDS = 8
+ENGINES = 4  # shader engines per XCD
 
 
 def plan_makespan(pages, q_lens, pages_per_split: int, cu_count: int = 256) -> float:
     """Finish time, in page units, of the decode grid under the cost model above.  The
-    grid is launched in split-fastest order (workgroup L = token * S + split); the
-    dispatcher deals workgroup L to XCD L mod 8, and each XCD hands its workgroups to
-    the first of its CUs to come free, one workgroup per CU at a time."""
+    grid runs every sequence's non-empty splits first (sequence, token, split order),
+    then the empty ones; the dispatcher deals workgroup L to XCD L mod 8, and each XCD
+    deals its k-th workgroup to shader engine k mod 4, to the first of that engine's
+    CUs to come free, never before the XCD's previous workgroup started (a workgroup
+    whose engine is full holds back the ones behind it)."""
     n_splits = max(math.ceil(p / pages_per_split) for p in pages)
     per_xcd = max(1, cu_count // XCDS)
-    free = [[0.0] * per_xcd for _ in range(XCDS)]
-    wg = 0
+    engines = min(ENGINES, per_xcd)
+    per_engine = max(1, per_xcd // engines)
+    costs, empties = [], 0
     for p, n in zip(pages, q_lens):
+        active = math.ceil(p / pages_per_split)
         for _ in range(n):
-            for y in range(n_splits):
-                work = min(pages_per_split, p - y * pages_per_split)
-                cost = SPLIT_OVERHEAD_PAGES + work if work > 0 else EMPTY_SPLIT_PAGES
-                f = free[wg % XCDS]
-                heapq.heapreplace(f, f[0] + cost)
-                wg += 1
-    return max(max(f) for f in free)
+            costs += [SPLIT_OVERHEAD_PAGES + min(pages_per_split, p - y * pages_per_split)
+                      for y in range(active)]
+        empties += n * (n_splits - active)
+    costs += [EMPTY_SPLIT_PAGES] * empties
+    span = 0.0
+    for x in range(XCDS):
+        free = [[0.0] * per_engine for _ in range(engines)]
+        last_start = 0.0
+        for k, c in enumerate(costs[x::XCDS]):
+            f = free[k % engines]
+            heapq.heapify(f)
+            start = max(last_start, f[0])
+            heapq.heapreplace(f, start + c)
+            last_start = start
+        span = max([span] + [max(f) for f in free])
+    return span
 
 
 # Longest split (pages) for which two 64-head workgroups per (token, split) pay off: the

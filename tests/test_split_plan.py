@@ -109,6 +109,21 @@ def test_makespan_model_by_hand():
     assert pr.plan_makespan([4] * 9, [1] * 9, 4, cu_count=8) == pytest.approx(2 * one)
 
 
+def test_makespan_model_engine_blocking_and_empty_splits_last():
+    over = pr.SPLIT_OVERHEAD_PAGES
+    # 64 CUs: per XCD 4 shader engines of 2 CUs.  65 one-split sequences; XCD 0 gets
+    # sequences 0, 8, .., 64 and deals them to engines 0, 1, 2, 3, 0, 1, 2, 3, 0.  The
+    # two on engine 0 before the last are 20 pages long, every other one 1 page: the
+    # last waits for engine 0 (it may not pass to the idle engines), so the XCD ends at
+    # (over + 20) + (over + 1), not at over + 20.
+    pages = [20 if j in (0, 32) else 1 for j in range(65)]
+    assert pr.plan_makespan(pages, [1] * 65, 20, cu_count=64) == pytest.approx(2 * over + 21)
+    # Empty splits run after every non-empty one: one CU per XCD, sequence 0's eight
+    # 1-page splits take XCDs 0..7, sequence 1's one page XCD 0 again, and its seven
+    # empty splits (0.2 each) come last, on XCDs 1..7.
+    assert pr.plan_makespan([8, 1], [1, 1], 1, cu_count=8) == pytest.approx(2 * (over + 1))
+
+
 def test_ragged_plan_no_worse_than_any_candidate_length():
     L, q = _lens(wl.CONFIGS["ragged_b64"])
     pages = [math.ceil(x / pr.PAGE_SIZE) for x in L]
