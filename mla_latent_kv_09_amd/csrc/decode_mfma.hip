@@ -170,6 +170,28 @@ __device__ __forceinline__ void load_page(uint32_t smem_base, int stage, const c
 
 constexpr int kRing = 4;  // LDS fragments in flight per wave
 
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const __bf16 a = static_cast<__bf16>(lo), b = static_cast<__bf16>(hi);
+  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
+         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+}
+
+// Writes two output tiles of this lane's row: x = columns 16nb + 4g .. +3 and
+// y = columns 16(nb+1) + 4g .. +3 (nb even).  v_permlane16_swap trades x of lane rows 1
+// and 3 for y of rows 0 and 2, after which lane row g holds the 8 consecutive columns
+// 16nb + 16(g & 1) + 8(g >> 1) .. +7 and writes them as one 16-byte store: 64 contiguous
+// bytes per head and store instead of 32, which halves the stores and the L2 write
+// requests of the partials.
+__device__ __forceinline__ void store_pair(__bf16* o_row, int nb, const f32x4& x, const f32x4& y, int g) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  const uint32_t x0 = pack_bf16x2(x[0], x[1]), x1 = pack_bf16x2(x[2], x[3]);
+  const uint32_t y0 = pack_bf16x2(y[0], y[1]), y1 = pack_bf16x2(y[2], y[3]);
+  const auto s0 = __builtin_amdgcn_permlane16_swap(x0, y0, false, false);
+  const auto s1 = __builtin_amdgcn_permlane16_swap(x1, y1, false, false);
+  *reinterpret_cast<u32x4*>(o_row + 16 * nb + 16 * (g & 1) + 8 * (g >> 1)) =
+      u32x4{s0[0], s1[0], s0[1], s1[1]};
+}
+
 // Latent score fragment (mb, k): A operand of S^T for tokens 16mb + j, latent dims
 // 32k + 8g .. +7 (chunk 4k + g).  The token blocks alternate in the step order so that
 // consecutive MFMAs accumulate into different registers.  With key 2j the chunk sits
@@ -235,8 +257,27 @@ decode_mfma_kernel(DecodeArgs a) {
   const int head = h2 * kHeadsWG + hl;
   const int grp = wave / Sh::kWavesPerGroup;             // latent group of this wave
   const uint32_t grp_off = static_cast<uint32_t>(grp) * kDcg * 2;  // its columns in a token row
+  // Three independent loads go out before the first wait: the sequence table, the page
+  // ids of the first pages this split would read if token t were sequence t (true of a
+  // batch with one query row per sequence), and this lane's query rows.  Only one round
+  // trip then precedes the first page's copies; the guessed ids are used only once the
+  // lookup has confirmed the guess.
   SeqIndex ix;
   ix.load(a.cu_q, a.seq_lens, a.batch);
+  const int page0_guess = split * a.pages_per_split;
+  const bool can_guess = t < a.batch && a.pages_per_split > 0;
+  int pid_guess = 0;
+  if (can_guess && page0_guess + lane < a.max_pages)
+    pid_guess = a.page_table[static_cast<size_t>(t) * a.max_pages + page0_guess + lane];
+  // Q fragments: B operand of S^T = C . Q^T.  K-step k covers latent dims 32k .. 32k+31;
+  // this lane holds dims 32k + 8g .. +7 of its head.
+  bf16x8 q[kQSteps];  // latent part of the query
+  {
+    const uint16_t* qa = static_cast<const uint16_t*>(a.q_abs) +
+                         (static_cast<size_t>(t) * kHeads + head) * kDcg + g * 8;
+#pragma unroll
+    for (int k = 0; k < kQSteps; ++k) q[k] = *reinterpret_cast<const bf16x8*>(qa + 32 * k);
+  }
   const QueryWork w = query_work(ix, t, split, S, a.pages_per_split, kTok, a.max_pages, a.causal);
   const size_t row = (static_cast<size_t>(t) * kHeads + head) * S + split;
   __bf16* o_out = static_cast<__bf16*>(a.o_part) + row * kDcg;  // bf16 partials
@@ -260,23 +301,18 @@ decode_mfma_kernel(DecodeArgs a) {
     const int id = clamp_page(__builtin_amdgcn_readlane(pid_v, i & 63), a.num_pool_pages);
     return kv + static_cast<size_t>(id) * kTok * kRowBytes;
   };
-  fetch_ids(0);
+  if (can_guess && w.b == t && page0 == page0_guess)
+    pid_v = pid_guess;  // lanes past the split's pages hold ids that are never read
+  else
+    fetch_ids(0);
 
   // First page in flight before anything else.
   int j0 = w.k0;
   load_page(lds_addr(smem), 0, page_ptr(0), min(kTok, w.k1 - j0), wave, lane);
 
-  // Q fragments: B operand of S^T = C . Q^T.  K-step k covers latent dims 32k .. 32k+31;
-  // this lane holds dims 32k + 8g .. +7 of its head.  The RoPE half of the query is
-  // rotated here in fp32 and parked, as bf16, in LDS (read back twice per page; with
-  // HS = 2 the token-half-0 wave of a head block writes it for both).
-  bf16x8 q[kQSteps];  // latent part of the query
-  {
-    const uint16_t* qa = static_cast<const uint16_t*>(a.q_abs) +
-                         (static_cast<size_t>(t) * kHeads + head) * kDcg + g * 8;
-#pragma unroll
-    for (int k = 0; k < kQSteps; ++k) q[k] = *reinterpret_cast<const bf16x8*>(qa + 32 * k);
-  }
+  // The RoPE half of the query is rotated here in fp32 and parked, as bf16, in LDS (read
+  // back twice per page; with HS = 2 the token-half-0 wave of a head block writes it for
+  // both).
   if (th == 0) {
     const uint16_t* qr = static_cast<const uint16_t*>(a.q_r) +
                          (static_cast<size_t>(t) * kHeads + head) * kDr + g * 8;
@@ -477,12 +513,7 @@ decode_mfma_kernel(DecodeArgs a) {
   if constexpr (HS == 1) {
     const float inv = 1.f / l_tot;
 #pragma unroll
-    for (int nb = 0; nb < kColBlocks; ++nb) {
-      const f32x4 v = o[nb] * inv;
-      *reinterpret_cast<bf16x4*>(o_out + nb * 16 + 4 * g) =
-          bf16x4{static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]), static_cast<__bf16>(v[2]),
-                 static_cast<__bf16>(v[3])};
-    }
+    for (int nb = 0; nb < kColBlocks; nb += 2) store_pair(o_out, nb, o[nb] * inv, o[nb + 1] * inv, g);
     if (g == 0) a.lse_part[row] = (m_ref + __log2f(l_tot)) * kLn2;
   } else {
     // Merge the two token halves of each head: wave w keeps output columns
@@ -514,20 +545,18 @@ decode_mfma_kernel(DecodeArgs a) {
     const float l = l_tot * a_me + l_p * a_p;
     const float inv = 1.f / l;
     const float w_me = a_me * inv, w_p = a_p * inv;
-    auto emit = [&](int nb, const f32x4& mine, uint32_t slot) {
-      const f32x4 other = *(lds_f32x4_t*)(uintptr_t)(slot);
-      const f32x4 v = mine * w_me + other * w_p;
-      *reinterpret_cast<bf16x4*>(o_out + nb * 16 + 4 * g) =
-          bf16x4{static_cast<__bf16>(v[0]), static_cast<__bf16>(v[1]), static_cast<__bf16>(v[2]),
-                 static_cast<__bf16>(v[3])};
+    auto emit = [&](int nb, const f32x4& m0, const f32x4& m1, uint32_t slot) {
+      const f32x4 p0 = *(lds_f32x4_t*)(uintptr_t)(slot);
+      const f32x4 p1 = *(lds_f32x4_t*)(uintptr_t)(slot + 1024);
+      store_pair(o_out, nb, m0 * w_me + p0 * w_p, m1 * w_me + p1 * w_p, g);
     };
     if (th == 0) {
 #pragma unroll
-      for (int i = 0; i < kHalf; ++i) emit(i, o[i], xo_part + i * 1024);
+      for (int i = 0; i < kHalf; i += 2) emit(i, o[i], o[i + 1], xo_part + i * 1024);
       if (g == 0) a.lse_part[row] = (m + __log2f(l)) * kLn2;
     } else {
 #pragma unroll
-      for (int i = 0; i < kHalf; ++i) emit(kHalf + i, o[kHalf + i], xo_part + i * 1024);
+      for (int i = 0; i < kHalf; i += 2) emit(kHalf + i, o[kHalf + i], o[kHalf + i + 1], xo_part + i * 1024);
     }
   }
 }
