@@ -6,7 +6,8 @@
 
 A step is the whole hot path over one batch of synthetic input already resident
 in HBM: mla_absorb_q -> mla_decode_paged -> mla_combine -> mla_up_v, all on the
-current HIP stream.
+current HIP stream; the last two run as one launch (mla_combine_up_v) where its fused
+kernel covers the shape.
 
 Timing (default).  The step's inputs, outputs and workspace exist in n copies (n >= 2,
 enough that n steps read more than twice the 256 MB Infinity Cache), used in turn,
@@ -27,7 +28,7 @@ Prints one JSON line.  `value` is the algorithmic TFLOP/s of the whole step
 (attention flops of the absorbed method plus the two projections, divided by the
 step time); the line also carries latent-KV GB/s, sequences/s, the roofline
 object of the dominant kernel (the split-KV decode), the roofline fractions of the
-attention calls (decode + combine) and of the whole step against the nominal 8 TB/s
+attention calls (decode + merge) and of the whole step against the nominal 8 TB/s
 and against a measured 1 GiB device copy (`roofline_path`), and the CPU oracle
 baseline.
 """
@@ -151,39 +152,46 @@ def cpu_baseline(w, att_flops_full, min_s=10.0):
     }
 
 
-def flush_timing(args, w, torch, harness, stream, names):
+def step_calls(step):
+    """(name, DecodeStep method) of the calls one step issues: the merge and W_UV are one
+    launch (mla_combine_up_v) where the fused kernel covers the shape."""
+    calls = [("absorb_q", "absorb"), ("decode_paged", "attend")]
+    if step.fused:
+        return calls + [("combine_up_v", "merge_project")]
+    return calls + [("combine", "merge"), ("up_v", "project")]
+
+
+def flush_timing(args, w, torch, harness, stream):
     """The earlier method, kept for comparison (--flush): one input copy, a 1 GiB
     read-only flush before every step, events around each step and between the calls
     of a second pass."""
     d = harness.to_device(w)
-    step = harness.make_step(w, d, args.splits, args.pages_per_split)
+    step = harness.make_step(w, d, args.splits, args.pages_per_split, keep_latent=args.keep_latent)
     flush_buf = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+
+    calls = step_calls(step)
 
     def one_step(ev=None):
         if ev is None:
             step()
             return
         ev[0].record(stream)
-        step.absorb()
-        ev[1].record(stream)
-        step.attend()
-        ev[2].record(stream)
-        step.merge()
-        ev[3].record(stream)
-        step.project()
-        ev[4].record(stream)
+        for i, (_, attr) in enumerate(calls):
+            getattr(step, attr)()
+            ev[i + 1].record(stream)
 
     for _ in range(args.warmup):
         flush_buf.max()
         one_step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+              for _ in range(args.steps)]
     for k in range(args.steps):
         flush_buf.max()
         one_step(events[k])
     torch.cuda.synchronize()
     parts = {name: statistics.median([e[i].elapsed_time(e[i + 1]) for e in events])
-             for i, name in enumerate(names)}
+             for i, (name, _) in enumerate(calls)}
     graph = None
     if not args.no_graph:
         graph = torch.cuda.CUDAGraph()
@@ -227,13 +235,14 @@ def measure_copy_gbps(torch, stream, mib=1024, reps=5):
 
 
 def path_roofline(att, proj, kv_bytes, w_bytes, parts, step_ms, peak_tflops, copy_gbps):
-    """Roofline fractions of the attention calls (decode + combine) and of the whole step
+    """Roofline fractions of the attention calls (decode + merge) and of the whole step
     (all four calls): the binding roof's time, max(bytes / bandwidth, flops / peak), over the
     measured time, against the nominal 8 TB/s and against the measured copy rate."""
     def frac(flops, nbytes, ms, gbps):
         t_roof = max(nbytes / (gbps * 1e9), flops / (peak_tflops * 1e12))
         return t_roof / (ms * 1e-3)
-    att_ms = parts["decode_paged"] + parts["combine"]
+    # decode + merge; a fused merge launch also carries the value projection
+    att_ms = parts["decode_paged"] + parts.get("combine", parts.get("combine_up_v", 0.0))
     return {
         "hbm_copy_gbps": copy_gbps,
         "attention": {"ms": att_ms, "frac": frac(att, kv_bytes, att_ms, HBM_PEAK_GBPS),
@@ -266,6 +275,9 @@ def main():
     ap.add_argument("--kv-dtype", choices=["bf16", "fp8"], default="bf16",
                     help="latent cache format: bf16 rows (default) or FP8 E4M3 pages written by "
                          "mla_append_kv_fp8 (a separate line, never the headline)")
+    ap.add_argument("--keep-latent", action="store_true",
+                    help="have a fused merge launch also write the merged latent rows (the "
+                         "step's output is out and lse either way)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the decode path is built "
@@ -289,7 +301,6 @@ def main():
         sys.exit(2)
     att, proj, kv_bytes, w_bytes = algorithmic_work(cfg, w.seq_lens, w.q_lens, args.kv_dtype)
     stream = torch.cuda.current_stream()
-    names = ["absorb_q", "decode_paged", "combine", "up_v"]
     if mla.branch(w.q_lens.tolist(), args.threshold) == mla.BRANCH_DECOMPRESSED:
         if args.kv_dtype != "bf16" or args.flush:
             print("the decompressed branch takes the bf16 cache and the default timing", file=sys.stderr)
@@ -305,7 +316,7 @@ def main():
         # timed back to back inside HIP graphs, as a serving loop runs them.
         n_copies = max(2, min(8, math.ceil(2 * MALL_BYTES / (kv_bytes + w_bytes))))
         steps = [harness.make_step(w, device_copy(w, harness, args.kv_dtype), args.splits,
-                                   args.pages_per_split)
+                                   args.pages_per_split, keep_latent=args.keep_latent)
                  for _ in range(n_copies)]
         step = steps[0]
         S = step.num_splits
@@ -345,7 +356,7 @@ def main():
         # 5 runs of about K calls).
         reps = max(1, math.ceil(args.steps / per_graph))
         parts = {}
-        for name, attr in zip(names, ["absorb", "attend", "merge", "project"]):
+        for name, attr in step_calls(step):
             run = runner([getattr(steps[i % n_copies], attr) for i in range(per_graph)])
             parts[name] = statistics.median(timed(run, reps) / (reps * per_graph) for _ in range(5))
             del run
@@ -371,7 +382,7 @@ def main():
         timing = {"method": "rotate", "copies": n_copies, "steps_per_graph": per_graph}
         graph_used = not args.no_graph
     else:
-        ms, parts, dec, S, step, wall, graph_used = flush_timing(args, w, torch, harness, stream, names)
+        ms, parts, dec, S, step, wall, graph_used = flush_timing(args, w, torch, harness, stream)
         timing = {"method": "flush"}
         append = None
 
@@ -409,6 +420,7 @@ def main():
                    "seq_len": cfg.seq_len, "seq_len_range": cfg.seq_len_range,
                    "total_q": int(w.total_q), "num_splits": S,
                    "pages_per_split": step.pages_per_split, "timing": timing,
+                   "merge_and_up_v": "one launch" if step.fused else "two launches",
                    "hip_graph": graph_used},
         "latent_kv_gbps": kv_gbps, "latent_kv_frac_hbm_peak": kv_gbps / HBM_PEAK_GBPS,
         "tflops_frac_mfma_peak": tflops / peak_f, "seqs_per_s": seqs,

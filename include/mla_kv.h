@@ -11,6 +11,8 @@
  *   mla_combine       log-sum-exp merge of the splits -> o_latent
  *   mla_up_v          out[t,h,:] = W_UV[h] . o_latent[t,h,:]            (value up-projection)
  *
+ * (mla_combine_up_v issues the last two as one launch where its fused kernel covers
+ * the shape, with the same results),
  * plus mla_rope_table (the fp32 cos/sin table the decode call reads),
  * mla_append_kv (writes the new tokens' latent rows, with their rotated RoPE keys,
  * into the paged cache before the decode reads them), mla_decode_plan (host-only
@@ -227,6 +229,26 @@ int mla_combine(const void* o_part, const float* lse_part, void* o_latent, float
 int mla_up_v(const void* o_latent, const void* w_uv, void* out,
              int total_q, int heads, int groups, int d_hc, int d_c,
              int dtype, void* stream);
+
+/*
+ * mla_combine_up_v -- mla_combine followed by mla_up_v (same arguments, same results bit
+ * for bit), in one launch where a fused kernel covers the shape: bf16, d_hc a multiple
+ * of 64, d_c / groups = 512 with num_splits <= 16 or 256 with num_splits <= 32
+ * (mla_combine_up_v_fused tells).  The merged rows then stay on chip.
+ *
+ *   o_part, lse_part  as for mla_combine;  w_uv, out  as for mla_up_v
+ *   o_latent [T, H, d_cg] dtype: optional output of the merged rows.  Required (as the
+ *            two calls' intermediate) for a shape the fused kernel does not cover:
+ *            MLA_ERR_UNSUPPORTED if it is NULL there.
+ *   lse_out  [T, H] float32 output, or NULL
+ */
+int mla_combine_up_v(const void* o_part, const float* lse_part, const void* w_uv, void* o_latent,
+                     void* out, float* lse_out, int total_q, int heads, int groups, int d_hc,
+                     int d_c, int num_splits, int dtype, void* stream);
+
+/* 1 when mla_combine_up_v runs this shape as one fused launch, else 0 (host only, no GPU
+ * call). */
+int mla_combine_up_v_fused(int heads, int groups, int d_hc, int d_c, int num_splits, int dtype);
 
 /*
  * FP8 latent cache (P3 intro and §5: a quantized gather of the latent cache whose 16-byte

@@ -533,4 +533,34 @@ int mla_up_v(const void* o_latent, const void* w_uv, void* out, int total_q, int
                                                 d_c / groups, bf16, s));
 }
 
+int mla_combine_up_v_fused(int heads, int groups, int d_hc, int d_c, int num_splits, int dtype) {
+  if (check_dtype(dtype) != MLA_OK || check_heads(heads, groups, d_c) != MLA_OK) return 0;
+  return mla::merge_up_v_supported(d_hc, d_c / groups, num_splits, dtype == MLA_DTYPE_BF16) ? 1 : 0;
+}
+
+int mla_combine_up_v(const void* o_part, const float* lse_part, const void* w_uv, void* o_latent,
+                     void* out, float* lse_out, int total_q, int heads, int groups, int d_hc,
+                     int d_c, int num_splits, int dtype, void* stream) {
+  int st = check_dtype(dtype);
+  if (st != MLA_OK) return st;
+  if (total_q < 0 || num_splits <= 0 || d_hc <= 0) return MLA_ERR_DIM;
+  if ((st = check_heads(heads, groups, d_c)) != MLA_OK) return st;
+  if (num_splits > kMaxSplits || d_c / groups > kMaxGenericCols) return MLA_ERR_UNSUPPORTED;
+  const bool fused = mla_combine_up_v_fused(heads, groups, d_hc, d_c, num_splits, dtype) != 0;
+  if (!fused && o_latent == nullptr) return MLA_ERR_UNSUPPORTED;
+  if (total_q == 0) return MLA_OK;
+  if (!o_part || !lse_part || !w_uv || !out) return MLA_ERR_NULL;
+  if (!aligned16(o_part) || !aligned16(lse_part) || !aligned16(w_uv) || !aligned16(out) ||
+      (o_latent && !aligned16(o_latent)) || (lse_out && !aligned16(lse_out)))
+    return MLA_ERR_ALIGN;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  if (fused)
+    return launch_status(mla::launch_merge_up_v(o_part, lse_part, w_uv, o_latent, out, lse_out,
+                                                total_q, heads, d_hc, d_c / groups, num_splits, s));
+  st = mla_combine(o_part, lse_part, o_latent, lse_out, total_q, heads, groups, d_c, num_splits,
+                   dtype, stream);
+  if (st != MLA_OK) return st;
+  return mla_up_v(o_latent, w_uv, out, total_q, heads, groups, d_hc, d_c, dtype, stream);
+}
+
 }  // extern "C"

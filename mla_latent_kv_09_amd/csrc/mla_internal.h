@@ -143,4 +143,10 @@ hipError_t launch_absorb_mfma(const void* q_c, const void* w_uk, void* q_abs, in
                               int d_hc, int d_cg, hipStream_t s);
 hipError_t launch_up_v_mfma(const void* o_lat, const void* w_uv, void* out, int T, int H, int d_hc,
                             int d_cg, hipStream_t s);
+// The split merge and up_v in one launch: bf16, d_hc % 64 == 0, d_cg 512 with S <= 16 or
+// d_cg 256 with S <= 32.  o_lat and lse_out may be null.
+bool merge_up_v_supported(int d_hc, int d_cg, int S, bool bf16);
+hipError_t launch_merge_up_v(const void* o_part, const float* lse_part, const void* w_uv, void* o_lat,
+                             void* out, float* lse_out, int T, int H, int d_hc, int d_cg, int S,
+                             hipStream_t s);
 }  // namespace mla

@@ -8,7 +8,8 @@
 //
 // Both are batched GEMMs with small M (the T query rows) and read each weight
 // element exactly once, so they are bound by streaming the 2*H*d_hc*d_cg bytes of
-// weights.  Tiles use v_mfma_f32_16x16x32_bf16 (M = 16 query rows per block),
+// weights.  up_v also comes fused with the split merge that produces its input
+// (merge_up_v_kernel, mla_combine_up_v).  Tiles use v_mfma_f32_16x16x32_bf16 (M = 16 query rows per block),
 // fp32 accumulation, one rounding to bf16 on the way out.
 #include "mla_device.h"
 #include "mla_internal.h"
@@ -253,6 +254,144 @@ absorb_mfma_kernel(const uint16_t* __restrict__ q_c, const uint16_t* __restrict_
   }
 }
 
+// ---------------------------------------------------------------- split merge + up_v
+// mla_combine followed by mla_up_v in one launch, for the shapes up_v_lds_kernel takes
+// (bf16, d_hc a multiple of 64, d_cg 256 or 512) and up to 16 (d_cg 512) or 32 (d_cg
+// 256) splits.  Same grid as up_v_lds_kernel (one workgroup per head and 64 output
+// dims, the two workgroups of a head on one XCD), 16 waves.  The workgroup's
+// [64 x d_cg] slice of W_UV[h] is staged in LDS (rows padded by 16 bytes, as the
+// activation block).  Per 16-row block of query rows, wave w merges row t0 + w from the
+// split partials exactly as the combine does (lane l owns columns kE l .. +kE-1, all of
+// the row's partials requested together with its LSEs), rounds it to bf16 and puts it in
+// the LDS block; then waves 0-3 take the block's MFMAs as up_v_lds_kernel (wave w: dims
+// 16 w .. +15, one accumulator chain over the K-steps), with the W_UV operand from LDS.
+// Sixteen merging waves keep four rows in flight per SIMD, which hides the merge's
+// memory and reduction latency.  The arithmetic and its order are the combine's and
+// then up_v's, so out (and o_latent / lse_out, written by the x = 0 workgroup of each
+// head when given) are bit for bit those of the two calls; the merged rows need not go
+// through memory, and a launch boundary goes.
+constexpr int kMergeWaves = 16;
+
+template <int kSteps, int kChunk>  // d_cg / 32, largest split count
+__global__ void __launch_bounds__(kMergeWaves * 64)
+merge_up_v_kernel(const uint16_t* __restrict__ o_part, const float* __restrict__ lse_part,
+                  const uint16_t* __restrict__ w_uv, uint16_t* __restrict__ o_lat,
+                  uint16_t* __restrict__ out, float* __restrict__ lse_out, int T, int H, int d_hc,
+                  int S) {
+  constexpr int d_cg = kSteps * 32;
+  constexpr int kE = d_cg / 64;  // columns per lane in the merge
+  constexpr int kW = kE / 2;     // 32-bit words per lane and split
+  constexpr int kRowBytes = d_cg * 2 + 16;
+  constexpr int kPieces = kUpCols * d_cg / 8 / (kMergeWaves * 64);  // 16-byte W pieces per thread
+  static_assert(kChunk * kW <= 64, "at most 64 words of partials per lane");
+  static_assert(kPieces * kMergeWaves * 64 * 8 == kUpCols * d_cg, "the W slice splits evenly");
+  static_assert(kMergeWaves == 16, "one merged row per wave and 16-row block");
+  __shared__ __attribute__((aligned(16))) char wsm[kUpCols * kRowBytes];
+  __shared__ __attribute__((aligned(16))) char buf[16 * kRowBytes];
+  const HeadTile ht = head_tile(d_hc / kUpCols, H);
+  const int h = ht.head;
+  const bool writer = ht.x == 0;  // writes o_latent and lse_out for this head
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int g = lane >> 4, j = lane & 15;
+  // W_UV[h][64 x + r][:] -> wsm row r; thread piece i = row (tid + 1024 i) / (d_cg / 8).
+  bf16x8 wp[kPieces];
+  const uint16_t* wslice = w_uv + (static_cast<size_t>(h) * d_hc + ht.x * kUpCols) * d_cg;
+#pragma unroll
+  for (int i = 0; i < kPieces; ++i) {
+    const int pc = tid + kMergeWaves * 64 * i;
+    wp[i] = *reinterpret_cast<const bf16x8*>(wslice + static_cast<size_t>(pc) * 8);
+  }
+  bool staged = false;
+  for (int t0 = 0; t0 < T; t0 += 16) {
+    const int t = t0 + wave;
+    const bool valid = t < T;
+    const size_t row = static_cast<size_t>(valid ? t : 0) * H + h;
+    const float l_lane = (valid && lane < S) ? lse_part[row * S + lane] : -INFINITY;
+    uint32_t x[kChunk][kW];
+    const uint16_t* base = o_part + row * S * d_cg + kE * lane;
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u)
+      if (valid && u < S) {
+        if constexpr (kW == 4) {
+          const uint4 v = *reinterpret_cast<const uint4*>(base + static_cast<size_t>(u) * d_cg);
+          x[u][0] = v.x, x[u][1] = v.y, x[u][2] = v.z, x[u][3] = v.w;
+        } else {
+          const uint2 v = *reinterpret_cast<const uint2*>(base + static_cast<size_t>(u) * d_cg);
+          x[u][0] = v.x, x[u][1] = v.y;
+        }
+      }
+    if (!staged) {  // first block: the W slice into LDS while the partials are in flight
+#pragma unroll
+      for (int i = 0; i < kPieces; ++i) {
+        const int pc = tid + kMergeWaves * 64 * i, r = pc / (d_cg / 8), ch = pc % (d_cg / 8);
+        *reinterpret_cast<bf16x8*>(wsm + r * kRowBytes + ch * 16) = wp[i];
+      }
+      staged = true;
+    }
+    // The largest LSE of the row (lane u < S holds split u's): the same value as the
+    // combine's butterfly, taken here with lane reads.
+    float mx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u)
+      if (u < S) mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_lane), u)));
+    float acc[kE];
+#pragma unroll
+    for (int e = 0; e < kE; ++e) acc[e] = 0.f;
+    float sum = 0.f;
+#pragma unroll
+    for (int u = 0; u < kChunk; ++u) {
+      const float l = u < S ? __int_as_float(__builtin_amdgcn_readlane(__float_as_int(l_lane), u))
+                            : -INFINITY;
+      const float wt = (l == -INFINITY || mx == -INFINITY) ? 0.f : expf(l - mx);
+      sum += wt;
+      if (wt != 0.f) {
+#pragma unroll
+        for (int e = 0; e < kE; ++e) {
+          const uint32_t wd = x[u][e >> 1];
+          acc[e] += wt * __uint_as_float((e & 1) ? (wd & 0xffff0000u) : (wd << 16));
+        }
+      }
+    }
+    const float inv = mx == -INFINITY ? 0.f : 1.f / sum;
+    uint32_t y[kW];
+#pragma unroll
+    for (int w = 0; w < kW; ++w)
+      y[w] = static_cast<uint32_t>(f32_to_bf16(acc[2 * w] * inv)) |
+             (static_cast<uint32_t>(f32_to_bf16(acc[2 * w + 1] * inv)) << 16);
+    char* dst = buf + wave * kRowBytes + kE * 2 * lane;
+    uint16_t* gdst = o_lat + (static_cast<size_t>(t) * H + h) * d_cg + kE * lane;
+    if constexpr (kW == 4) {
+      *reinterpret_cast<uint4*>(dst) = uint4{y[0], y[1], y[2], y[3]};
+      if (writer && o_lat != nullptr && valid) *reinterpret_cast<uint4*>(gdst) = uint4{y[0], y[1], y[2], y[3]};
+    } else {
+      *reinterpret_cast<uint2*>(dst) = uint2{y[0], y[1]};
+      if (writer && o_lat != nullptr && valid) *reinterpret_cast<uint2*>(gdst) = uint2{y[0], y[1]};
+    }
+    if (writer && lse_out != nullptr && lane == 0 && valid)
+      lse_out[static_cast<size_t>(t) * H + h] = mx == -INFINITY ? -INFINITY : mx + logf(sum);
+    __syncthreads();
+    if (wave < 4) {
+      // A: row j of the block, columns 32 k + 8 g .. +7; B: W_UV row 16 wave + j, same columns.
+      const char* arow = buf + j * kRowBytes + 16 * g;
+      const char* brow = wsm + (16 * wave + j) * kRowBytes + 16 * g;
+      f32x4 o4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < kSteps; ++k)
+        o4 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const bf16x8*>(arow + 64 * k),
+                                                     *reinterpret_cast<const bf16x8*>(brow + 64 * k), o4,
+                                                     0, 0, 0);
+      const int d = ht.x * kUpCols + 16 * wave + j;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int tt = t0 + 4 * g + i;
+        if (tt < T) out[(static_cast<size_t>(tt) * H + h) * d_hc + d] = f32_to_bf16(o4[i]);
+      }
+    }
+    __syncthreads();  // the block buffer is rewritten by the next block's merge
+  }
+}
+
 }  // namespace
 
 bool up_v_mfma_supported(int d_hc, int d_cg, bool bf16) {
@@ -281,6 +420,33 @@ hipError_t launch_up_v_mfma(const void* o_lat, const void* w_uv, void* out, int 
     up_v_mfma_kernel<16><<<grid, 64, 0, s>>>(o, wt, dst, T, H, d_hc);
   else
     up_v_mfma_kernel<8><<<grid, 64, 0, s>>>(o, wt, dst, T, H, d_hc);
+  return hipGetLastError();
+}
+
+bool merge_up_v_supported(int d_hc, int d_cg, int S, bool bf16) {
+  return bf16 && d_hc % kUpCols == 0 && S >= 1 &&
+         ((d_cg == 512 && S <= 16) || (d_cg == 256 && S <= 32));
+}
+
+hipError_t launch_merge_up_v(const void* o_part, const float* lse_part, const void* w_uv, void* o_lat,
+                             void* out, float* lse_out, int T, int H, int d_hc, int d_cg, int S,
+                             hipStream_t s) {
+  const auto* op = static_cast<const uint16_t*>(o_part);
+  const auto* wt = static_cast<const uint16_t*>(w_uv);
+  auto* ol = static_cast<uint16_t*>(o_lat);
+  auto* dst = static_cast<uint16_t*>(out);
+  const dim3 grid((d_hc / kUpCols) * H), block(kMergeWaves * 64);
+  if (d_cg == 512) {
+    if (S <= 8)
+      merge_up_v_kernel<16, 8><<<grid, block, 0, s>>>(op, lse_part, wt, ol, dst, lse_out, T, H, d_hc, S);
+    else
+      merge_up_v_kernel<16, 16><<<grid, block, 0, s>>>(op, lse_part, wt, ol, dst, lse_out, T, H, d_hc, S);
+  } else {
+    if (S <= 16)
+      merge_up_v_kernel<8, 16><<<grid, block, 0, s>>>(op, lse_part, wt, ol, dst, lse_out, T, H, d_hc, S);
+    else
+      merge_up_v_kernel<8, 32><<<grid, block, 0, s>>>(op, lse_part, wt, ol, dst, lse_out, T, H, d_hc, S);
+  }
   return hipGetLastError();
 }
 

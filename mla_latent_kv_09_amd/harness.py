@@ -59,15 +59,18 @@ def to_device(w: Workload, device="cuda", *, rope: bool = True,
 
 
 def make_step(w: Workload, d: DeviceWorkload, num_splits: Optional[int] = None,
-              pages_per_split: int = 0, threshold: Optional[int] = None) -> mla.DecodeStep:
+              pages_per_split: int = 0, threshold: Optional[int] = None,
+              keep_latent: bool = True) -> mla.DecodeStep:
     """The step over `d`: the planner's split plan, or num_splits splits of
     pages_per_split pages each (0: each sequence cut into num_splits equal parts).  With a
-    threshold the library's dispatch picks the absorbed calls or the decompressed branch."""
+    threshold the library's dispatch picks the absorbed calls or the decompressed branch.
+    keep_latent=False lets a fused merge launch skip writing the merged rows."""
     return mla.DecodeStep(q_c=d.q_c, q_r=d.q_r, w_uk=d.w_uk, w_uv=d.w_uv, kv_cache=d.kv,
                           page_table=d.page_table, seq_lens=d.seq_lens, cu_q=d.cu_q,
                           groups=w.cfg.groups, num_splits=num_splits, rope=d.rope,
                           causal=w.cfg.causal, seq_lens_host=w.seq_lens.tolist(),
-                          pages_per_split=pages_per_split, threshold=threshold)
+                          pages_per_split=pages_per_split, threshold=threshold,
+                          keep_latent=keep_latent)
 
 
 def new_tokens_to_device(w: Workload, new: NewTokens, device="cuda"):

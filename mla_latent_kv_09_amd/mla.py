@@ -22,6 +22,7 @@ DTYPE_FP32 = 1
 PAGE_SIZE = 64
 
 EXPORTED = ("mla_absorb_q", "mla_rope_table", "mla_decode_paged", "mla_combine", "mla_up_v",
+            "mla_combine_up_v", "mla_combine_up_v_fused",
             "mla_append_kv", "mla_decode_workspace_bytes", "mla_decode_plan", "mla_attend_noalloc",
             "mla_decode_paged_fp8", "mla_append_kv_fp8", "mla_fp8_page_bytes", "mla_branch",
             "mla_prefill_paged", "mla_prefill_workspace_bytes", "mla_decompress_kv",
@@ -52,6 +53,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_decode_paged.argtypes = ([P] * 8 + [I] + [P] * 2 + [I] * 12 + [F, I, I, P])
     lib.mla_combine.argtypes = [P, P, P, P, I, I, I, I, I, I, P]
     lib.mla_up_v.argtypes = [P, P, P, I, I, I, I, I, I, P]
+    lib.mla_combine_up_v.argtypes = [P] * 6 + [I] * 7 + [P]
+    lib.mla_combine_up_v_fused.argtypes = [I] * 6
+    lib.mla_combine_up_v_fused.restype = I
     lib.mla_append_kv.argtypes = [P] * 8 + [I] * 9 + [P]
     lib.mla_decode_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.mla_decode_workspace_bytes.restype = ctypes.c_size_t
@@ -70,7 +74,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_status_string.argtypes = [I]
     lib.mla_status_string.restype = ctypes.c_char_p
     for name in ("mla_absorb_q", "mla_rope_table", "mla_decode_paged", "mla_combine", "mla_up_v",
-                 "mla_append_kv", "mla_decode_plan", "mla_attend_noalloc", "mla_decode_paged_fp8",
+                 "mla_combine_up_v", "mla_append_kv", "mla_decode_plan", "mla_attend_noalloc", "mla_decode_paged_fp8",
                  "mla_append_kv_fp8", "mla_branch", "mla_prefill_paged", "mla_decompress_kv",
                  "mla_prefill_attention"):
         getattr(lib, name).restype = I
@@ -461,6 +465,34 @@ def up_v(o_latent, w_uv, out=None, *, groups: int = 1, stream=None):
     return out
 
 
+def combine_up_v_fused(heads: int, groups: int, d_hc: int, d_c: int, num_splits: int,
+                       dtype=torch.bfloat16) -> bool:
+    """Whether mla_combine_up_v runs this shape as one launch (host only)."""
+    code = DTYPE_BF16 if dtype == torch.bfloat16 else DTYPE_FP32
+    return bool(load().mla_combine_up_v_fused(heads, groups, d_hc, d_c, num_splits, code))
+
+
+def combine_up_v(o_part, lse_part, w_uv, out=None, *, o_latent=None, lse_out=None, groups: int = 1,
+                 stream=None):
+    """combine then up_v in one call (one launch where the fused kernel covers the shape;
+    o_latent, if given, receives the merged rows and is required otherwise)."""
+    T, H, S, d_cg = o_part.shape
+    d_hc = w_uv.shape[1]
+    if w_uv.shape != (H, d_hc, d_cg) or w_uv.dtype != o_part.dtype or lse_part.dtype != torch.float32:
+        raise ValueError("w_uv must be [H, d_hc, d_c/G] with o_part's dtype; lse_part float32")
+    if out is None:
+        out = torch.empty((T, H, d_hc), dtype=o_part.dtype, device=o_part.device)
+    _expect("lse_part", lse_part, (T, H, S), torch.float32)
+    _expect("o_latent", o_latent, (T, H, d_cg), o_part.dtype)
+    _expect("out", out, (T, H, d_hc), o_part.dtype)
+    _expect("lse_out", lse_out, (T, H), torch.float32)
+    _dev(o_part, lse_part, w_uv, out, o_latent, lse_out)
+    _check("mla_combine_up_v", load().mla_combine_up_v(
+        _ptr(o_part), _ptr(lse_part), _ptr(w_uv), _ptr(o_latent), _ptr(out), _ptr(lse_out), T, H,
+        groups, d_hc, d_cg * groups, S, _dtype_code(o_part), _stream(stream)))
+    return out
+
+
 def split_plan(seq_lens_host, q_lens_host, cu_count: int = 256, groups: int = 1):
     """(num_splits, pages_per_split) for a batch, from the library's host-only planner
     ``mla_decode_plan`` (host lists or arrays of int; no GPU is touched)."""
@@ -480,10 +512,14 @@ class DecodeStep:
 
     def __init__(self, *, q_c, q_r, w_uk, w_uv, kv_cache, page_table, seq_lens, cu_q, groups=1,
                  num_splits=None, rope=None, causal=True, seq_lens_host=None, pages_per_split=0,
-                 threshold=None):
+                 threshold=None, keep_latent=True):
         self.q_c, self.q_r, self.w_uk, self.w_uv = q_c, q_r, w_uk, w_uv
         self.kv, self.page_table, self.seq_lens, self.cu_q = kv_cache, page_table, seq_lens, cu_q
         self.groups, self.rope, self.causal = groups, rope, causal
+        self.fused = False
+        # keep_latent: the merged rows (self.o_latent) are written even when the merge and
+        # W_UV run as one launch (they are the two-call path's intermediate anyway)
+        self.keep_latent = keep_latent
         T, H, d_hc = q_c.shape
         d_cg = w_uk.shape[2]
         cu = cu_q.cpu().tolist()
@@ -508,6 +544,8 @@ class DecodeStep:
             self.q_abs = torch.empty((T, H, d_cg), dtype=q_c.dtype, device=dev)
             self.o_part, self.lse_part = workspace(T, H, d_cg, num_splits, dev, q_c.dtype)
             self.o_latent = torch.empty((T, H, d_cg), dtype=q_c.dtype, device=dev)
+            # merge and W_UV in one launch where the fused kernel covers the shape
+            self.fused = combine_up_v_fused(H, groups, d_hc, d_cg * groups, num_splits, q_c.dtype)
         self.lse = torch.empty((T, H), dtype=torch.float32, device=dev)
         self.out = torch.empty((T, H, d_hc), dtype=q_c.dtype, device=dev)
         self.d_hc = d_hc
@@ -532,6 +570,13 @@ class DecodeStep:
     def project(self, stream=None):
         up_v(self.o_latent, self.w_uv, self.out, groups=self.groups, stream=stream)
 
+    def merge_project(self, stream=None):
+        """merge then project: one launch when self.fused (the merged rows stay on chip)."""
+        combine_up_v(self.o_part, self.lse_part, self.w_uv, self.out,
+                     o_latent=None if self.fused and not self.keep_latent else self.o_latent,
+                     lse_out=self.lse,
+                     groups=self.groups, stream=stream)
+
     def prefill(self, stream=None):
         prefill_paged(self.q_c, self.q_r, self.kv, self.page_table, self.seq_lens, self.cu_q,
                       self.w_uk, self.w_uv, self.workspace, self.out, self.lse,
@@ -554,6 +599,5 @@ class DecodeStep:
             return self.out
         self.absorb(stream)
         self.attend(stream)
-        self.merge(stream)
-        self.project(stream)
+        self.merge_project(stream)
         return self.out

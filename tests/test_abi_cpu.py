@@ -105,6 +105,35 @@ def test_combine_validation(lib):
     assert f(dt=3) == DTYPE
 
 
+def test_combine_up_v_fused_shapes(lib):
+    """The fused merge + W_UV launch covers bf16, d_hc % 64 == 0, d_cg 512 with S <= 16 and
+    d_cg 256 with S <= 32; everything else runs as the two calls."""
+    fz = lambda H=128, G=1, d_hc=128, d_c=512, S=8, dt=0: lib.mla_combine_up_v_fused(H, G, d_hc, d_c, S, dt)
+    assert fz() == 1 and fz(S=1) == 1 and fz(S=16) == 1
+    assert fz(S=17) == 0 and fz(S=0) == 0
+    assert fz(G=2, S=32) == 1 and fz(G=2, S=33) == 0       # d_cg 256
+    assert fz(d_hc=96) == 0 and fz(d_hc=64) == 1
+    assert fz(dt=1) == 0                                     # fp32
+    assert fz(d_c=1024) == 0 and fz(G=4) == 0                # d_cg 1024, 128
+    assert fz(H=100, G=3) == 0                               # heads not divisible by groups
+
+
+def test_combine_up_v_validation(lib):
+    f = lambda op=A, lp=A, w=A, ol=None, out=A, lo=None, T=16, H=128, G=1, d_hc=128, d_c=512, S=8, dt=0: \
+        lib.mla_combine_up_v(op, lp, w, ol, out, lo, T, H, G, d_hc, d_c, S, dt, None)
+    assert f(op=None) == NULL
+    assert f(out=None) == NULL
+    assert f(w=MIS) == ALIGN
+    assert f(lo=MIS) == ALIGN
+    assert f(ol=MIS) == ALIGN
+    assert f(S=0) == DIM and f(d_hc=0) == DIM and f(T=-1) == DIM
+    assert f(S=257) == UNSUP
+    assert f(S=17) == UNSUP            # outside the fused kernel and no o_latent to go through
+    assert f(S=17, ol=A, T=0) == OK    # ... accepted with one (nothing to do at T = 0)
+    assert f(dt=3) == DTYPE
+    assert f(T=0, op=None) == OK
+
+
 def test_rope_table_validation(lib):
     assert lib.mla_rope_table(A, A, 0, 64, 10000.0, None) == DIM
     assert lib.mla_rope_table(A, A, 10, 63, 10000.0, None) == DIM
