@@ -178,10 +178,12 @@ decompress_kernel(PrefillArgs a) {
 //           rescales what was accumulated).
 //   output  O[32 queries x 128] += P . V over 4 K-steps of 16 keys: A = P from the score
 //           registers (no LDS round trip), B = V^T through transposing reads.
-// K/V row t (256 B) holds chunk c at position c ^ g(t), g(t) = ((t >> 1) & 3) << 2 |
-// (t >> 3) & 3: a row-wise read of 32 keys and a transposing read of 8 keys x 4 chunks
-// each meet 32 distinct 16-byte slots of a 512-byte bank row.  k_R row t (128 B) holds
-// chunk c at c ^ ((t >> 2) & 7).
+// Stage swizzles (16-byte chunk c of row t at position c ^ key(t)), chosen with an LDS
+// probe's bank-conflict counters on gfx950 (SQ_LDS_BANK_CONFLICT: 0 for each of the three
+// reads below, 2-way for the layouts first used here):
+//   K row (256 B):   swz_k(t) = (t & 15) ^ ((t >> 4) & 1)   row-wise reads of 32 keys
+//   V row (256 B):   swz_v(t) = (t & 3) << 2                transposing reads, 8 keys x 4 chunks
+//   k_R row (128 B): swz_r(t) = (t >> 1) & 7                row-wise reads of 32 keys
 constexpr int kAttWaves = 4;
 constexpr int kAttThreads = kAttWaves * 64;
 constexpr int kQBlock = 32 * kAttWaves;
@@ -190,16 +192,25 @@ constexpr int kRBytes = kTok * kDr * 2;   // 8 KB
 constexpr int kAttStage = 2 * kKBytes + kRBytes;
 constexpr int kAttLds = 2 * kAttStage;
 
-__device__ __forceinline__ uint32_t swz_g(int t) {
-  return static_cast<uint32_t>((((t >> 1) & 3) << 2) | ((t >> 3) & 3));
-}
+__device__ __forceinline__ int swz_k(int t) { return (t & 15) ^ ((t >> 4) & 1); }
+__device__ __forceinline__ int swz_v(int t) { return (t & 3) << 2; }
+__device__ __forceinline__ int swz_r(int t) { return (t >> 1) & 7; }
 
 __global__ void __launch_bounds__(kAttThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 prefill_attn_kernel(PrefillArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int n_qb = (a.max_q_len + kQBlock - 1) / kQBlock;
   const int L = static_cast<int>(blockIdx.x);
-  const int qb = L % n_qb, pair = L / n_qb;
+  // The n_qb query blocks of a (sequence, head) pair take n_qb consecutive workgroups
+  // (their K/V pages meet in L2), in an order rotated by 9 per pair.  Causal blocks differ
+  // in length (block i reads 2 (i + 1) pages), and the dispatcher deals an XCD's
+  // workgroups to its shader engines in turn, holding the line at an engine with no free
+  // slot: without the rotation, engine (j / 8) mod 4 of every XCD would always receive
+  // blocks 8 ((j / 8) mod 4) .. +7 of every pair, the last engine four times the first
+  // one's work, and the chip would run at about half its workgroup slots.  With it, each
+  // (XCD, engine) slot sees every block length in turn (9 is coprime to n_qb's factors of 2).
+  const int pair = L / n_qb;
+  const int qb = (L % n_qb + 9 * pair) % n_qb;
   const int h = pair % a.heads, b = pair / a.heads;
   const int q0 = a.cu_q[b], q1 = a.cu_q[b + 1];
   const int q_len = q1 - q0;
@@ -262,19 +273,18 @@ prefill_attn_kernel(PrefillArgs a) {
     for (int r = 0; r < 4; ++r) {
       const int t0 = 16 * wave + 4 * r;
       const int tk = t0 + (lane >> 4);
-      const uint32_t off = static_cast<uint32_t>(
-          ((static_cast<size_t>(tk) * a.heads + h) * kDhc * 2) + (((lane & 15) ^ static_cast<int>(swz_g(tk))) << 4));
+      const uint32_t row = static_cast<uint32_t>((static_cast<size_t>(tk) * a.heads + h) * kDhc * 2);
       const char* kbase = ws_k + static_cast<size_t>(id) * kTok * a.heads * kDhc * 2;
       const char* vbase = ws_v + static_cast<size_t>(id) * kTok * a.heads * kDhc * 2;
-      dma16(kbase, off, st + t0 * 256);
-      dma16(vbase, off, st + kKBytes + t0 * 256);
+      dma16(kbase, row + (((lane & 15) ^ swz_k(tk)) << 4), st + t0 * 256);
+      dma16(vbase, row + (((lane & 15) ^ swz_v(tk)) << 4), st + kKBytes + t0 * 256);
     }
     const char* page = kv + static_cast<size_t>(id) * kTok * kRowBytes;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
       const int t0 = 16 * wave + 8 * r;
       const int tk = t0 + (lane >> 3);
-      dma16(page, static_cast<uint32_t>(tk * kRowBytes + kDc * 2 + (((lane & 7) ^ ((tk >> 2) & 7)) << 4)),
+      dma16(page, static_cast<uint32_t>(tk * kRowBytes + kDc * 2 + (((lane & 7) ^ swz_r(tk)) << 4)),
             st + 2 * kKBytes + t0 * 128);
     }
   };
@@ -284,8 +294,8 @@ prefill_attn_kernel(PrefillArgs a) {
   float m_ref = -INFINITY, l_run = 0.f;
   f32x16 o[4] = {};
   // Lane parts of the LDS addresses.
-  //   K read, block mb, K-step ks (0..7):  st + (32 mb + n) * 256 + (((2 ks + hh) ^ g(n)) << 4)
-  //   k_R read, step rs:                   st + 2 kKBytes + (32 mb + n) * 128 + (((2 rs + hh) ^ ((n >> 2) & 7)) << 4)
+  //   K read, block mb, K-step ks (0..7):  st + (32 mb + n) * 256 + (((2 ks + hh) ^ swz_k(n)) << 4)
+  //   k_R read, step rs:                   st + 2 kKBytes + (32 mb + n) * 128 + (((2 rs + hh) ^ swz_r(n)) << 4)
   //   V^T read (nb, mb, q, part pp): lane i = lane % 16 of group gr = lane / 16 reads key
   //     32 mb + 16 q + 8 pp + 4 (gr >> 1) + i / 4, columns 32 nb + 16 (gr & 1) + 4 (i % 4) .. +3.
   const int li = lane & 15, lg = lane >> 4;
@@ -306,7 +316,7 @@ prefill_attn_kernel(PrefillArgs a) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const int key = 32 * mb + n;
-        const bf16x8 kf = lds_read8(st + key * 256 + (((2 * ks + hh) ^ static_cast<int>(swz_g(key))) << 4));
+        const bf16x8 kf = lds_read8(st + key * 256 + (((2 * ks + hh) ^ swz_k(key)) << 4));
         s[mb] = mfma32(kf, q[ks], s[mb]);
       }
 #pragma unroll
@@ -314,7 +324,7 @@ prefill_attn_kernel(PrefillArgs a) {
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
         const int key = 32 * mb + n;
-        const bf16x8 rf = lds_read8(st + 2 * kKBytes + key * 128 + (((2 * rs + hh) ^ ((key >> 2) & 7)) << 4));
+        const bf16x8 rf = lds_read8(st + 2 * kKBytes + key * 128 + (((2 * rs + hh) ^ swz_r(key)) << 4));
         s[mb] = mfma32(rf, q[8 + rs], s[mb]);
       }
 
@@ -382,7 +392,7 @@ prefill_attn_kernel(PrefillArgs a) {
         for (int pp = 0; pp < 2; ++pp) {
           const int key = 32 * mb + 16 * qq + 8 * pp + tv;
           const int c = 4 * nb + 2 * (lg & 1) + ((li & 3) >> 1);
-          const uint32_t addr = st + kKBytes + key * 256 + ((c ^ static_cast<int>(swz_g(key))) << 4) + vpart;
+          const uint32_t addr = st + kKBytes + key * 256 + ((c ^ swz_v(key)) << 4) + vpart;
           part[pp] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(uintptr_t)addr);
         }
         const bf16x8 vf = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
