@@ -76,6 +76,7 @@ struct PrefillArgs {
   int heads, groups, d_hc, d_c, d_R, page_size;
   float scale;
   int causal;
+  int dec_pages;  // pages per decompress workgroup; set by launch_decompress
 };
 bool prefill_supported(const PrefillArgs& a);
 hipError_t launch_decompress(const PrefillArgs& a, hipStream_t s);    // K / V into the workspace

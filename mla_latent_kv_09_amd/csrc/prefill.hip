@@ -70,7 +70,7 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 
 // ------------------------------------------------------------------ 1. decompression
 //
-// Workgroup = 8 waves, one head h, a run of up to kDecPages pages of one sequence.  Wave w
+// Workgroup = 8 waves, one head h, a run of up to a.dec_pages pages of one sequence.  Wave w
 // computes columns 32 (w % 4) .. +31 of K (w < 4) or V (w >= 4) for all 64 rows of each
 // page, its 32-column slice of W_UK[h] or W_UV[h] (the B operand of all 32 K-steps) held in
 // registers for the whole run.  Pages stream through two 64 KB LDS stages (the latent part
@@ -81,7 +81,11 @@ __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const
 // page meet in L2), run (L / H) mod runs_per_seq of sequence (L / H) / runs_per_seq.
 constexpr int kDecWaves = 8;
 constexpr int kDecThreads = kDecWaves * 64;
-constexpr int kDecPages = 8;
+// Pages per workgroup: as many as keep about four workgroups per CU (8 to 64).  Each
+// workgroup first loads its head's 256 KB of W_UK and W_UV slices, so longer runs load
+// them fewer times: on prefill_b8_l4096, 8 pages per run took 1.34 ms, 16 took 1.23, 32
+// took 1.19 and 64 took 1.17 ms (interleaved A/B).
+constexpr int kDecMinPages = 8, kDecMaxPages = 64, kDecTargetGroups = 1024;
 constexpr int kDecStage = kTok * kDc * 2;  // 64 KB
 constexpr int kDecLds = 2 * kDecStage;
 
@@ -95,13 +99,13 @@ decompress_kernel(PrefillArgs a) {
   const int L = static_cast<int>(blockIdx.x);
   const int h = L % a.heads;
   const int u = L / a.heads;
-  const int runs = (a.max_pages + kDecPages - 1) / kDecPages;
+  const int runs = (a.max_pages + a.dec_pages - 1) / a.dec_pages;
   const int b = u / runs, run = u - b * runs;
   const int cap = a.max_pages * kTok;
   int len = a.seq_lens[b];
   len = len < 0 ? 0 : (len > cap ? cap : len);
   const int n_pages = (len + kTok - 1) / kTok;
-  const int p0 = run * kDecPages, p1 = min(p0 + kDecPages, n_pages);
+  const int p0 = run * a.dec_pages, p1 = min(p0 + a.dec_pages, n_pages);
   if (p0 >= p1) return;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -432,8 +436,12 @@ hipError_t launch_decompress(const PrefillArgs& a, hipStream_t s) {
   static std::atomic<uint64_t> dec_set{0};
   const hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(decompress_kernel), kDecLds, dec_set);
   if (e != hipSuccess) return e;
-  const long long runs = (a.max_pages + kDecPages - 1) / kDecPages;
-  decompress_kernel<<<dim3(static_cast<unsigned>(runs * a.batch * a.heads)), kDecThreads, kDecLds, s>>>(a);
+  PrefillArgs d = a;
+  const long long work = static_cast<long long>(a.batch) * a.max_pages * a.heads;
+  d.dec_pages = kDecMinPages;
+  while (d.dec_pages < kDecMaxPages && work / (2 * d.dec_pages) >= kDecTargetGroups) d.dec_pages *= 2;
+  const long long runs = (a.max_pages + d.dec_pages - 1) / d.dec_pages;
+  decompress_kernel<<<dim3(static_cast<unsigned>(runs * a.batch * a.heads)), kDecThreads, kDecLds, s>>>(d);
   return hipGetLastError();
 }
 
