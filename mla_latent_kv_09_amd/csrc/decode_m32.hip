@@ -40,16 +40,14 @@
 //
 // FP8 cache (F8 = true; the quantized latent gather of nxmr.cn/news/151634, intro and §5,
 // on gfx950's E4M3 format): a page holds the latent codes [64][512] (E4M3, 32 KB), k_R
-// [64][64] (bf16, 8 KB) and one float32 scale per token (256 B), 41 KB in all, so three
-// stages fit next to q_R and the copies run two pages ahead.  A latent row (512 B) holds
-// 16-byte chunk c at position c ^ 2 (t mod 16).  Scores: one 16-byte read per lane and
-// token feeds two K-steps (K-step pair j, lane half h: dims 32 j + 16 h .. +15, the query
-// registers loaded in the same order); codes are converted to bf16 exactly
-// (v_cvt_scalef32_pk_bf16_fp8 with scale 1), the latent part of each score is multiplied
-// by its token's scale, and the RoPE K-steps then accumulate on top.  Output: P^T is
-// multiplied by the token scales before the bf16 rounding, and each C^T fragment is one
-// transposing 8-bit read (ds_read_b64_tr_b8: lanes 2e, 2e + 1 of a 16-lane group supply
-// row e, 8 columns each; lane j receives column j of the 8 rows) and four conversions.
+// [64][64] (bf16, 8 KB) and one float32 scale per token (256 B), 41 KB in all.  The copies
+// land in an FP8 stage; once per page the four waves convert its codes to bf16 exactly
+// (v_cvt_scalef32_pk_bf16_fp8 with scale 1) into one stage of the bf16 form's layout and
+// move the page's k_R rows and scales beside them, so the score and output loops are the
+// bf16 form's.  The scale stays in float32: the latent part of each score is multiplied by
+// its token's scale before the RoPE K-steps accumulate on top, and P^T is multiplied by it
+// before the bf16 rounding.  LDS: the bf16 stage (72 KB), the scales, the FP8 stage (41 KB)
+// and q_R (16 KB); the copies of page i + 1 go out once page i is converted.
 #include <math.h>
 
 #include <type_traits>
@@ -86,23 +84,27 @@ constexpr int kColBlocks = kDc / 32;     // 16 output blocks of 32 columns
 constexpr float kJump = 64.f;            // reference move threshold, log2 units
 static_assert(kLdsBytes <= 160 * 1024, "stages + q_R must fit the 160 KB LDS of a gfx950 CU");
 
-// FP8 cache page (= one LDS stage): codes, then k_R, then the token scales.
+// FP8 cache page in HBM: codes, then k_R, then the token scales.
 constexpr int kC8Bytes = kTok * kDc;              // 32 KB of E4M3 codes
 constexpr int kR8Off = kC8Bytes;                  // k_R [64][64] bf16
 constexpr int kS8Off = kC8Bytes + kRBytes;        // scales [64] float32
-constexpr int kStage8Bytes = kS8Off + kTok * 4;   // 41216 B, also the page stride in HBM
-constexpr int kQrOff8 = 3 * kStage8Bytes;
-constexpr int kLds8Bytes = kQrOff8 + kHeads * kDr * 2;
+constexpr int kPage8Bytes = kS8Off + kTok * 4;    // 41216 B, the page stride in HBM
 constexpr int kCopies8 = 11;                      // global->LDS copies per wave and page
-static_assert(kLds8Bytes <= 160 * 1024, "three FP8 stages + q_R must fit the 160 KB LDS");
-static_assert(kStage8Bytes % 16 == 0, "FP8 pages are whole 16-byte units");
+// FP8 LDS: one bf16 stage (read by the loops), the page's scales, the FP8 stage the copies
+// land in (latent row t at 512 t, k_R and scales as in HBM, k_R rows swizzled as in the
+// bf16 stage), then q_R.  The 64-head form's final merge uses the first 130 KB.
+constexpr int kScaleOff8 = kStageBytes;
+constexpr int kF8Off = kScaleOff8 + kTok * 4;
+constexpr int kQrOff8 = kF8Off + kPage8Bytes;
+constexpr int kMergeBytes = 4 * 32768 + kThreads * 8;
+constexpr int kLds8Bytes = kQrOff8 + kHeads * kDr * 2 > kMergeBytes ? kQrOff8 + kHeads * kDr * 2 : kMergeBytes;
+static_assert(kLds8Bytes <= 160 * 1024, "the FP8 form's LDS must fit the 160 KB of a gfx950 CU");
+static_assert(kPage8Bytes % 16 == 0 && kF8Off % 16 == 0, "FP8 pages are whole 16-byte units");
+static_assert(kLdsBytes >= kMergeBytes, "the 64-head merge fits the bf16 form's LDS");
 
 template <bool F8>
 struct Form {
-  static constexpr int kStages = F8 ? 3 : 2;
-  static constexpr int kStage = F8 ? kStage8Bytes : kStageBytes;
-  static constexpr int kPage = F8 ? kStage8Bytes : kTok * kRowBytes;  // page stride in HBM
-  static constexpr int kRopeOff = F8 ? kR8Off : kCBytes;              // k_R block in a stage
+  static constexpr int kPage = F8 ? kPage8Bytes : kTok * kRowBytes;  // page stride in HBM
   static constexpr int kQr = F8 ? kQrOff8 : kQrOff;
   static constexpr int kLds = F8 ? kLds8Bytes : kLdsBytes;
 };
@@ -189,41 +191,83 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t v) {
     asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, 1.0" : "=v"(r) : "v"(v));
   return r;
 }
-// 8 codes (two dwords) -> one bf16x8 MFMA operand.  The pad, tied to the result, keeps
-// two wait states between the last conversion (a vector-ALU write the compiler does not
-// see as one) and the MFMA that reads the operand.
-__device__ __forceinline__ bf16x8 fp8x8_to_bf16x8(uint32_t lo, uint32_t hi) {
-  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-  u32x4 r{fp8x2_to_bf16x2<false>(lo), fp8x2_to_bf16x2<true>(lo), fp8x2_to_bf16x2<false>(hi),
-          fp8x2_to_bf16x2<true>(hi)};
-  asm("s_nop 1" : "+v"(r));
-  return __builtin_bit_cast(bf16x8, r);
-}
-// FP8 latent row swizzle: chunk c of token t at 16-byte position c ^ swz8(t).
-__device__ __forceinline__ uint32_t swz8(int t) { return static_cast<uint32_t>(2 * (t & 15)); }
-
-// FP8 form: copy `row` (0..10) of this wave's share of a page into stage `c_base`: rows
-// 0..7 are the latent rows of tokens 16w + 2 row and 16w + 2 row + 1 (512 B each, one per
-// lane half), rows 8, 9 the RoPE rows of tokens 16w + 8 (row - 8) .. +7, row 10 the scales
+// FP8 form: copy `row` (0..10) of this wave's share of a page into the FP8 stage `f8`:
+// rows 0..7 are the codes of tokens 16w + 2 row and 16w + 2 row + 1 (512 B each, one per
+// lane half), rows 8, 9 the k_R rows of tokens 16w + 8 (row - 8) .. +7, row 10 the scales
 // of tokens 16w .. 16w+15 (lanes 0..3).  Rows at or past n_valid fetch token 0.
-__device__ __forceinline__ void load_row8(uint32_t c_base, const char* page, int n_valid,
-                                          int wave, int lane, int row) {
+__device__ __forceinline__ void load_row8(uint32_t f8, const char* page, int n_valid, int wave,
+                                          int lane, int row) {
   if (row < 8) {
     const int t0 = wave * 16 + 2 * row;
     const int t = t0 + (lane >> 5);
     const int src_t = t < n_valid ? t : 0;
-    dma16(page, static_cast<uint32_t>(src_t * kDc + (((lane & 31) ^ static_cast<int>(swz8(t))) << 4)),
-          c_base + t0 * kDc);
+    dma16(page, static_cast<uint32_t>(src_t * kDc + ((lane & 31) << 4)), f8 + t0 * kDc);
   } else if (row < 10) {
     const int t0 = wave * 16 + 8 * (row - 8);
     const int t = t0 + (lane >> 3);
     const int src_t = t < n_valid ? t : 0;
     dma16(page, static_cast<uint32_t>(kR8Off + src_t * 128 + (((lane & 7) ^ ((t >> 2) & 7)) << 4)),
-          c_base + kR8Off + t0 * 128);
+          f8 + kR8Off + t0 * 128);
   } else if (lane < 4) {
     // Scales of tokens past n_valid may be anything: the softmax masks those tokens and
     // their P entries are set to 0, not multiplied by the scale.
-    dma16(page, static_cast<uint32_t>(kS8Off + wave * 64 + 16 * lane), c_base + kS8Off + wave * 64);
+    dma16(page, static_cast<uint32_t>(kS8Off + wave * 64 + 16 * lane), f8 + kS8Off + wave * 64);
+  }
+}
+
+// FP8 form: the page in the FP8 stage becomes the bf16 stage at `base`.  Wave w takes
+// tokens 16w .. 16w+15: lane l converts codes 8l .. 8l+7 of each latent row (exactly) into
+// the 16-byte chunk l of that bf16 row, stored at its swizzled position l ^ f(t); the k_R
+// rows (already in the bf16 stage's order) and the scales are moved as they are.  Both
+// the 8-byte reads and the 16-byte writes meet distinct banks.
+template <int kBatch>
+__device__ __forceinline__ void convert_page8(uint32_t base, int wave, int lane) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) u32x2 lds_u32x2_t;
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
+  const uint32_t f8 = base + kF8Off;
+  const uint32_t src = f8 + static_cast<uint32_t>(wave * 16 * kDc + 8 * lane);
+  // token 16w + r: swz_f(16w + r) = swz_f(r) | 16 (w & 1), swz_f(r) < 16
+  const uint32_t dst = base + static_cast<uint32_t>(wave * 16 * 1024) +
+                       (static_cast<uint32_t>(lane ^ (16 * (wave & 1))) << 4);
+  // The reads of kBatch code rows (with one batch, the k_R rows and the scales too), then
+  // their conversions and writes, so that the LDS latency is paid once per batch.  (The
+  // 64-head form takes two batches and moves k_R and the scales after them: it has fewer
+  // registers to spare here.)
+  const uint32_t kr_off = static_cast<uint32_t>(wave * 2048 + 16 * lane);
+  const uint32_t sc_off = static_cast<uint32_t>(wave * 64 + 16 * (lane & 3));
+#pragma unroll
+  for (int r0 = 0; r0 < 16; r0 += kBatch) {
+    const bool last = kBatch == 16;
+    u32x2 raw[kBatch];
+    u32x4 kr0, kr1, sc;
+#pragma unroll
+    for (int r = 0; r < kBatch; ++r) raw[r] = *(const lds_u32x2_t*)(uintptr_t)(src + (r0 + r) * kDc);
+    if (last) {
+      kr0 = *(const lds_u32x4_t*)(uintptr_t)(f8 + kR8Off + kr_off);
+      kr1 = *(const lds_u32x4_t*)(uintptr_t)(f8 + kR8Off + kr_off + 1024);
+      sc = *(const lds_u32x4_t*)(uintptr_t)(f8 + kS8Off + sc_off);
+    }
+#pragma unroll
+    for (int r = 0; r < kBatch; ++r) {
+      const u32x4 v{fp8x2_to_bf16x2<false>(raw[r][0]), fp8x2_to_bf16x2<true>(raw[r][0]),
+                    fp8x2_to_bf16x2<false>(raw[r][1]), fp8x2_to_bf16x2<true>(raw[r][1])};
+      *(lds_u32x4_t*)(uintptr_t)((dst + (r0 + r) * 1024) ^ (swz_f(r0 + r) << 4)) = v;
+    }
+    if (last) {
+      *(lds_u32x4_t*)(uintptr_t)(base + kCBytes + kr_off) = kr0;
+      *(lds_u32x4_t*)(uintptr_t)(base + kCBytes + kr_off + 1024) = kr1;
+      if (lane < 4) *(lds_u32x4_t*)(uintptr_t)(base + kScaleOff8 + sc_off) = sc;
+    }
+  }
+  if constexpr (kBatch < 16) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      *(lds_u32x4_t*)(uintptr_t)(base + kCBytes + kr_off + 1024 * j) =
+          *(const lds_u32x4_t*)(uintptr_t)(f8 + kR8Off + kr_off + 1024 * j);
+    if (lane < 4)
+      *(lds_u32x4_t*)(uintptr_t)(base + kScaleOff8 + sc_off) = *(const lds_u32x4_t*)(uintptr_t)(f8 + kS8Off + sc_off);
   }
 }
 
@@ -306,22 +350,16 @@ decode_m32_kernel(DecodeArgs a) {
   fetch_ids(0);
   const uint32_t smem_base = lds_addr(smem);
   int j0 = w.k0;
-  if constexpr (F8) {  // pages 0 and 1 into stages 0 and 1
+  {  // page 0 into stage 0 (FP8: into the FP8 stage)
     const char* p0 = page_ptr(0);
     const int nv = min(kTok, w.k1 - j0);
+    if constexpr (F8) {
 #pragma unroll
-    for (int r = 0; r < kCopies8; ++r) load_row8(smem_base, p0, nv, wave, lane, r);
-    if (n_split_pages > 1) {
-      const char* p1 = page_ptr(1);
-      const int nv1 = min(kTok, w.k1 - j0 - kTok);
+      for (int r = 0; r < kCopies8; ++r) load_row8(smem_base + kF8Off, p0, nv, wave, lane, r);
+    } else {
 #pragma unroll
-      for (int r = 0; r < kCopies8; ++r) load_row8(smem_base + kStage8Bytes, p1, nv1, wave, lane, r);
+      for (int r = 0; r < 18; ++r) load_row(smem_base, p0, nv, wave, lane, r);
     }
-  } else {
-    const char* p0 = page_ptr(0);
-    const int nv = min(kTok, w.k1 - j0);
-#pragma unroll
-    for (int r = 0; r < 18; ++r) load_row(smem_base, p0, nv, wave, lane, r);
   }
 
   // Query: latent part in registers (B operand of the scores: head n, dims 16 ks + 8 h ..),
@@ -330,12 +368,8 @@ decode_m32_kernel(DecodeArgs a) {
   {
     const uint16_t* qa = static_cast<const uint16_t*>(a.q_abs) +
                          (static_cast<size_t>(t) * kHeads + head) * kDc + 8 * h;
-    // FP8: K-step 2j + s takes dims 32 j + 16 h + 8 s .. +7 (one 16-byte LDS read of the
-    // codes then feeds K-steps 2j and 2j + 1); bf16: K-step k takes dims 16 k + 8 h .. +7.
 #pragma unroll
-    for (int k = 0; k < kQSteps; ++k)
-      q[k] = *reinterpret_cast<const bf16x8*>(
-          F8 ? qa + 32 * (k >> 1) + 8 * h + 8 * (k & 1) : qa + 16 * k);
+    for (int k = 0; k < kQSteps; ++k) q[k] = *reinterpret_cast<const bf16x8*>(qa + 16 * k);  // dims 16 k + 8 h ..
   }
   if (th == 0) {
     const uint16_t* qr = static_cast<const uint16_t*>(a.q_r) +
@@ -388,18 +422,6 @@ decode_m32_kernel(DecodeArgs a) {
   const uint32_t key_l = static_cast<uint32_t>((2 * (lg & 1) + ((li & 3) >> 1)) ^ (((li >> 2) << 2) | (lg >> 1)));
   const uint32_t o_lane = static_cast<uint32_t>(tok_l * 1024 + 8 * (li & 1)) | (key_l << 4);
 
-  // FP8 lane parts: score read of K-step pair j, block mb:
-  //   st + 16384 mb + n * 512 + 16 h + ((32 j) ^ (32 (n mod 16)));
-  // transposing output read of (nb, mb, q): lane jj = lane % 16 of group g = lane / 16 supplies
-  //   row e = jj / 2 (token T = 32 mb + 16 q + tl, tl = 8 (e / 4) + 4 (g / 2) + e % 4), bytes
-  //   8 (jj % 2) .. +7 of chunk 2 nb + g % 2:
-  //   st + (32 mb + 16 q) * 512 + tl * 512 + 16 (g % 2) + 8 (jj % 2) + ((32 nb) ^ (32 tl)).
-  const uint32_t s8_lane = static_cast<uint32_t>(n * 512 + 16 * h);
-  const uint32_t s8_x = static_cast<uint32_t>(32 * (n & 15));
-  const int tl8 = 8 * ((li >> 1) >> 2) + 4 * (lg >> 1) + ((li >> 1) & 3);
-  const uint32_t o8_lane = static_cast<uint32_t>(tl8 * 512 + 16 * (lg & 1) + 8 * (li & 1));
-  const uint32_t o8_x = static_cast<uint32_t>(32 * tl8);
-
   // Latent-row copies, 128-head form: wave w copies tokens 16 w + r, whose chunk c sits at
   // c ^ swz_f(16 w + r) = c ^ swz_f(r) ^ 16 (w & 1); the lane part of the source offset.
   const uint32_t cp_lane = static_cast<uint32_t>(lane ^ (16 * (wave & 1))) << 4;
@@ -407,20 +429,15 @@ decode_m32_kernel(DecodeArgs a) {
   int stage = 0;
   for (; j0 < w.k1; j0 += kTok) {
     const int n_valid = min(kTok, w.k1 - j0);
-    if constexpr (F8) {
-      // This wave's copies of this page have landed once at most the next page's are
-      // still in flight (vector-memory operations complete in issue order).
-      if (j0 + kTok < w.k1)
-        __builtin_amdgcn_s_waitcnt(0x0f70 | kCopies8);  // vmcnt(11)
-      else
-        __builtin_amdgcn_s_waitcnt(0x0f70);             // vmcnt(0)
-    } else {
-      __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's page copies have landed
-    }
+    __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's page copies have landed
     __syncthreads();  // ... and every wave's; the stage of the previous page is free again
-    // The page whose copies this iteration issues: the next one (bf16, two stages) or the
-    // one after (FP8, three stages).
-    const int j_next = j0 + (F8 ? 2 : 1) * kTok;
+    if constexpr (F8) {
+      convert_page8<HS == 1 ? 16 : 8>(smem_base, wave, lane);
+      __syncthreads();  // the bf16 stage is complete and the FP8 stage free for the next page
+    }
+    // The page whose copies this iteration issues: the next one, into the other stage
+    // (FP8: into the FP8 stage).
+    const int j_next = j0 + kTok;
     const bool has_next = j_next < w.k1;
     const char* next_page = kv;
     const int next_valid = min(kTok, w.k1 - j_next);
@@ -429,93 +446,54 @@ decode_m32_kernel(DecodeArgs a) {
       if ((i_next & 63) == 0) fetch_ids(i_next >> 6);
       next_page = page_ptr(i_next);
     }
-    const int next_stage = F8 ? (stage == 0 ? 2 : stage - 1) : (stage ^ 1);
-    const uint32_t next_base = smem_base + next_stage * Fm::kStage;
-    const uint32_t st_base = smem_base + stage * Fm::kStage;
+    const uint32_t next_base = F8 ? smem_base + kF8Off : smem_base + (stage ^ 1) * kStageBytes;
+    const uint32_t st_base = smem_base + stage * kStageBytes;
     const uint32_t sb = opaque(st_base + s_lane);
-
-    // ---- scores.  HS = 1: the latent steps, then the RoPE steps, the two 32-token blocks
-    // alternating.  HS = 2: this wave's one 32-token block, RoPE steps first, two chains
-    // over alternate K-steps (summed below).
-    f32x16 s[2];
-    if constexpr (F8) {
-      // Latent K-step pairs first.  HS = 1: per pair, one read for each 32-token block and
-      // four MFMAs, the two blocks' chains alternating.  HS = 2: this wave's block, the two
-      // chains taking the pair's first and second K-step (summed below).
-      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-      typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
-      constexpr int kPairs = kDc / 32;
-      constexpr int kMBs = HS == 1 ? 2 : 1;
-      const uint32_t sb8 = opaque(st_base + s8_lane);
-      auto rd = [&](int j, int mb) {
-        return *(const lds_u32x4_t*)(uintptr_t)(sb8 + 16384 * (HS == 1 ? mb : th) +
-                                                 ((32u * static_cast<uint32_t>(j)) ^ s8_x));
+    // FP8: the latent part of each score times its token's scale (s[mb] holds block mb of
+    // HS = 1, this wave's block of HS = 2 in s[0]), once the latent chains have ended; the
+    // pad gives the wait states between these vector-ALU writes and the MFMAs that then read
+    // them as srcC.
+    auto scale_latent = [&](f32x16 (&acc)[2]) {
+      auto scale_read = [&](int mb, int g) {
+        return *(const lds_f32x4_t*)(uintptr_t)(
+            smem_base + kScaleOff8 + 4 * (32 * (HS == 1 ? mb : th) + 8 * g + 4 * h));
       };
-      u32x4 raw[3][kMBs];
+      if constexpr (HS == 1) {
+        f32x4 sc[2][4];  // read before the pad, so that their latency hides under it
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int mb = 0; mb < kMBs; ++mb) raw[j][mb] = rd(j, mb);
+          for (int g = 0; g < 4; ++g) sc[mb][g] = scale_read(mb, g);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_results_ready(acc[0], acc[1]);
 #pragma unroll
-      for (int j = 0; j < kPairs; ++j) {
-        u32x4 cur[kMBs];
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int mb = 0; mb < kMBs; ++mb) cur[mb] = raw[j % 3][mb];
-        if (j + 2 < kPairs) {
+          for (int g = 0; g < 4; ++g)
 #pragma unroll
-          for (int mb = 0; mb < kMBs; ++mb) raw[(j + 2) % 3][mb] = rd(j + 2, mb);
-        }
-#pragma unroll
-        for (int sub = 0; sub < 2; ++sub) {
-#pragma unroll
-          for (int mb = 0; mb < kMBs; ++mb) {
-            const bf16x8 af = fp8x8_to_bf16x8(cur[mb][2 * sub], cur[mb][2 * sub + 1]);
-            f32x16& acc = s[HS == 1 ? mb : sub];
-            if (j == 0 && (HS == 1 ? sub == 0 : true))
-              mfma32_first(acc, af, q[2 * j + sub]);
-            else
-              mfma32_acc(acc, af, q[2 * j + sub]);
-          }
-        }
-        if (j < kCopies8 && has_next)
-          load_row8(next_base, next_page, next_valid, wave, static_cast<int>(opaque(lane)), j);
-      }
-      // Latent part times the token's scale, then the RoPE K-steps on top.
-      mfma_results_ready(s[0], s[1]);
-      if constexpr (HS == 2) s[0] += s[1];
-#pragma unroll
-      for (int mb = 0; mb < kMBs; ++mb)
+            for (int i = 0; i < 4; ++i) acc[mb][4 * g + i] *= sc[mb][g][i];
+      } else {  // (the 64-head form has no registers to hold them across the pad)
+        mfma_results_ready(acc[0], acc[1]);
+        acc[0] += acc[1];
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const f32x4 sc = *(const lds_f32x4_t*)(uintptr_t)(
-              st_base + kS8Off + 4 * (32 * (HS == 1 ? mb : th) + 8 * g + 4 * h));
+          const f32x4 sc = scale_read(0, g);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) s[mb][4 * g + i] *= sc[i];
-        }
-      // wait states between these vector-ALU writes and the MFMAs that read them as srcC
-      asm volatile("s_nop 7" : "+v"(s[0]), "+v"(s[1]));
-      const uint32_t rb = opaque(st_base + kR8Off + n * 128);
-      const uint32_t qb = smem_base + kQrOff8 + hl * 128;
-      const int swr = (n >> 2) & 7, swq = (hl >> 2) & 7;
-#pragma unroll
-      for (int rs = 0; rs < kRSteps; ++rs) {
-        const int c = 2 * rs + h;
-        const bf16x8 qrf = lds_read8(qb + ((c ^ swq) << 4));
-        if constexpr (HS == 1) {
-#pragma unroll
-          for (int mb = 0; mb < 2; ++mb)
-            mfma32_acc(s[mb], lds_read8(rb + ((c ^ swr) << 4) + 4096 * mb), qrf);
-        } else {
-          const bf16x8 cf = lds_read8(rb + ((c ^ swr) << 4) + 4096 * th);
-          if (rs == 1)
-            mfma32_first(s[1], cf, qrf);
-          else
-            mfma32_acc(s[rs & 1], cf, qrf);
+          for (int i = 0; i < 4; ++i) acc[0][4 * g + i] *= sc[i];
         }
       }
-    } else {
+      asm volatile("s_nop 7" : "+v"(acc[0]), "+v"(acc[1]));
+      __builtin_amdgcn_sched_barrier(0);
+    };
+
+    // ---- scores.  HS = 1: the latent steps, then the RoPE steps, the two 32-token blocks
+    // alternating.  HS = 2: this wave's one 32-token block, two chains over alternate
+    // K-steps (summed below); bf16: RoPE steps first, FP8: after the latent steps.
+    f32x16 s[2];
+    {
       const uint32_t rb = opaque(st_base + kCBytes + n * 128);
-      const uint32_t qb = smem_base + kQrOff + hl * 128;
+      // (FP8: through an empty asm, so that the q_R addresses are not kept across the loop)
+      const uint32_t qb = F8 ? opaque(smem_base + Fm::kQr + hl * 128) : smem_base + Fm::kQr + hl * 128;
       const int swr = (n >> 2) & 7, swq = (hl >> 2) & 7;
       auto qr_frag = [&](int rs) { return lds_read8(qb + (((2 * rs + h) ^ swq) << 4)); };
       auto rope_frag = [&](int rs, int mb) { return lds_read8(rb + (((2 * rs + h) ^ swr) << 4) + 4096 * mb); };
@@ -525,26 +503,43 @@ decode_m32_kernel(DecodeArgs a) {
       constexpr int kRing = 4;
       bf16x8 ring[kRing];
       if constexpr (HS == 2) {
-        // RoPE steps first, then the 32 latent steps of this wave's block through a ring of
-        // reads, the two chains over alternate K-steps; the copies go with the odd steps.
+        // The 32 latent steps of this wave's block through a ring of reads, the two chains
+        // over alternate K-steps, the copies on the odd steps; the RoPE steps first (bf16) or
+        // after the scale (FP8).
+        auto rope_steps = [&]() {
 #pragma unroll
-        for (int rs = 0; rs < kRSteps; ++rs) {
-          const bf16x8 qrf = qr_frag(rs);
-          const bf16x8 cf = rope_frag(rs, th);
-          if (rs < 2)
-            mfma32_first(s[rs & 1], cf, qrf);
-          else
-            mfma32_acc(s[rs & 1], cf, qrf);
-        }
+          for (int rs = 0; rs < kRSteps; ++rs) {
+            const bf16x8 qrf = qr_frag(rs);
+            const bf16x8 cf = rope_frag(rs, th);
+            if (F8 ? rs == 1 : rs < 2)
+              mfma32_first(s[rs & 1], cf, qrf);
+            else
+              mfma32_acc(s[rs & 1], cf, qrf);
+          }
+        };
+        if constexpr (!F8) rope_steps();
 #pragma unroll
         for (int st = 0; st < kRing; ++st) ring[st] = lat_frag(st, th);
 #pragma unroll
         for (int st = 0; st < kQSteps; ++st) {
           const bf16x8 cf = ring[st % kRing];
           if (st + kRing < kQSteps) ring[st % kRing] = lat_frag(st + kRing, th);
-          mfma32_acc(s[st & 1], cf, q[st]);
-          if ((st & 1) == 1 && has_next)  // latent rows 0..15 over the 32 steps
-            load_row(next_base, next_page, next_valid, wave, static_cast<int>(opaque(lane)), st >> 1);
+          if (F8 && st < 2)
+            mfma32_first(s[st & 1], cf, q[st]);
+          else
+            mfma32_acc(s[st & 1], cf, q[st]);
+          if ((st & 1) == 1 && has_next) {
+            if constexpr (F8) {  // the 11 copies of the next FP8 page
+              if ((st >> 1) < kCopies8)
+                load_row8(next_base, next_page, next_valid, wave, static_cast<int>(opaque(lane)), st >> 1);
+            } else {  // latent rows 0..15 over the 32 steps
+              load_row(next_base, next_page, next_valid, wave, static_cast<int>(opaque(lane)), st >> 1);
+            }
+          }
+        }
+        if constexpr (F8) {
+          scale_latent(s);
+          rope_steps();
         }
       } else {
         // The 64 latent (ks, mb) steps, then the 8 RoPE (rs, mb) steps, all through one
@@ -562,26 +557,48 @@ decode_m32_kernel(DecodeArgs a) {
             if (rn >= 0 && (rn & 1) == 0) qr_ring[(rn >> 1) % 3] = qr_frag(rn >> 1);
           }
         };
-        // Copies of the next page's rows into the other stage: copy k (latent rows k < 16,
-        // RoPE rows k = 16, 17) is prepared at step 4k and issued at step 4k + 2, so each
-        // gap between two MFMAs takes only a few of its instructions.  The last page copies
-        // itself into the unused stage instead, so the copies need no branch.
+        // Copies of the next page's rows: copy k is prepared at step 4k and issued at step
+        // 4k + 2, so each gap between two MFMAs takes only a few of its instructions.  bf16:
+        // latent rows k < 16, RoPE rows k = 16, 17, into the other stage.  FP8: code rows
+        // k < 8, k_R rows k = 8, 9, the scales k = 10, into the FP8 stage.  The last page
+        // copies itself instead (into the unused stage, or the FP8 stage it has converted),
+        // so the copies need no branch.
+        constexpr int kCopies = F8 ? kCopies8 : 18;
         const char* cp_page = has_next ? next_page : cur_page;
         const int cp_valid = has_next ? next_valid : kTok;
         const int cp_lim = cp_valid - 16 * wave;  // latent row r of this wave is a key iff r < cp_lim
         const uint32_t cp_m0 = next_base + 16384u * static_cast<uint32_t>(wave);
         uint32_t cp_voff = 0, cp_lds = 0;
         auto cp_prepare = [&](int k) {
-          if (k < 16) {  // token 16 w + k; rows past the keys fetch token 0
+          if constexpr (F8) {
+            // lane through an empty asm, so that no lane constant is kept across the loop
+            const int ln = static_cast<int>(opaque(lane));
+            if (k < 8) {  // codes of tokens 16 w + 2 k and + 1, one per lane half
+              const int t0 = 16 * wave + 2 * k;
+              const int tt = t0 + (ln >> 5);
+              const int src_t = tt < cp_valid ? tt : 0;
+              cp_voff = static_cast<uint32_t>(src_t * kDc + ((ln & 31) << 4));
+              cp_lds = next_base + static_cast<uint32_t>(t0 * kDc);
+            } else if (k < 10) {  // k_R rows of tokens t0 .. t0 + 7
+              const int t0 = wave * 16 + 8 * (k - 8);
+              const int tt = t0 + (ln >> 3);
+              const int src_t = tt < cp_valid ? tt : 0;
+              cp_voff = static_cast<uint32_t>(kR8Off + src_t * 128 + (((ln & 7) ^ ((tt >> 2) & 7)) << 4));
+              cp_lds = next_base + static_cast<uint32_t>(kR8Off + t0 * 128);
+            } else {  // the scales of tokens 16 w .. +15 (lanes 0..3)
+              cp_voff = static_cast<uint32_t>(kS8Off + wave * 64 + 16 * ln);
+              cp_lds = next_base + static_cast<uint32_t>(kS8Off + wave * 64);
+            }
+          } else if (k < 16) {  // token 16 w + k; rows past the keys fetch token 0
             const int roff = k < cp_lim ? (16 * wave + k) * kRowBytes : 0;
             cp_voff = (cp_lane ^ (swz_f(k) << 4)) + static_cast<uint32_t>(roff);
             cp_lds = cp_m0 + 1024u * static_cast<uint32_t>(k);
           } else {  // RoPE rows of tokens t0 .. t0 + 7
             const int t0 = wave * 16 + 8 * (k - 16);
-            const int t = t0 + (static_cast<int>(opaque(lane)) >> 3);
-            const int src_t = t < cp_valid ? t : 0;
+            const int tt = t0 + (static_cast<int>(opaque(lane)) >> 3);
+            const int src_t = tt < cp_valid ? tt : 0;
             cp_voff = static_cast<uint32_t>(src_t * kRowBytes + kDc * 2 +
-                                            (((lane & 7) ^ ((t >> 2) & 7)) << 4));
+                                            (((lane & 7) ^ ((tt >> 2) & 7)) << 4));
             cp_lds = next_base + kCBytes + static_cast<uint32_t>(t0 * 128);
           }
         };
@@ -589,8 +606,15 @@ decode_m32_kernel(DecodeArgs a) {
         // MFMA of step st, the copy's part.  (Left to itself the scheduler may move each read
         // next to its MFMA, which then waits for it.)
         auto copy_part = [&](int st) {
-          if ((st & 3) == 0) cp_prepare(st >> 2);
-          if ((st & 3) == 2) dma16(cp_page, cp_voff, cp_lds);
+          const int k = st >> 2;
+          if ((st & 3) == 0 && k < kCopies) cp_prepare(k);
+          if ((st & 3) == 2 && k < kCopies) {
+            if (F8 && k == 10) {
+              if (lane < 4) dma16(cp_page, cp_voff, cp_lds);
+            } else {
+              dma16(cp_page, cp_voff, cp_lds);
+            }
+          }
           __builtin_amdgcn_sched_barrier(0);
         };
 #pragma unroll
@@ -605,6 +629,7 @@ decode_m32_kernel(DecodeArgs a) {
             mfma32_acc(s[st & 1], cf, q[st >> 1]);
           copy_part(st);
         }
+        if constexpr (F8) scale_latent(s);
 #pragma unroll
         for (int st = kLat; st < kSteps; ++st) {
           const bf16x8 cf = ring[st % kRing];
@@ -662,13 +687,15 @@ decode_m32_kernel(DecodeArgs a) {
     l_run += psum;
     if constexpr (F8) {
       // P^T times each token's scale (the latent rows are code * scale); tokens past the
-      // page's keys get 0 whatever their scale slot holds.
+      // page's keys get 0 whatever their scale slot holds.  The scales are read again
+      // (an empty asm on the address), not kept in registers from the score phase.
+      const uint32_t scb = opaque(smem_base + kScaleOff8);
 #pragma unroll
       for (int mb = 0; mb < kBlocks; ++mb)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int tok = 32 * (HS == 1 ? mb : th) + 8 * g + 4 * h;
-          const f32x4 sc = *(const lds_f32x4_t*)(uintptr_t)(st_base + kS8Off + 4 * tok);
+          const f32x4 sc = *(const lds_f32x4_t*)(uintptr_t)(scb + 4 * tok);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             s[mb][4 * g + i] = tok + i < n_valid ? s[mb][4 * g + i] * sc[i] : 0.f;
@@ -687,31 +714,7 @@ decode_m32_kernel(DecodeArgs a) {
 
     // ---- O^T[cols 32 nb .. +31] += C^T . P^T, (kq, nb) steps through a ring
     const uint32_t ob = opaque(st_base + o_lane);
-    if constexpr (F8) {
-      typedef int i32x2 __attribute__((ext_vector_type(2)));
-      typedef __attribute__((address_space(3))) i32x2 lds_i32x2_t;
-      constexpr int kSteps = kKQ * kColBlocks;
-      constexpr int kRing = 4;
-      const uint32_t ob8 = opaque(st_base + o8_lane);
-      auto frag = [&](int st) {
-        const int kq = st / kColBlocks, nb = st % kColBlocks;
-        const int mb = HS == 1 ? kq >> 1 : th, qq = HS == 1 ? (kq & 1) : kq;
-        const uint32_t addr = ob8 + static_cast<uint32_t>((32 * mb + 16 * qq) * 512) +
-                              ((32u * static_cast<uint32_t>(nb)) ^ o8_x);
-        return __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2_t*)(uintptr_t)addr);
-      };
-      i32x2 ring[kRing];
-#pragma unroll
-      for (int st = 0; st < kRing; ++st) ring[st] = frag(st);
-#pragma unroll
-      for (int st = 0; st < kSteps; ++st) {
-        const i32x2 raw8 = ring[st % kRing];
-        if (st + kRing < kSteps) ring[st % kRing] = frag(st + kRing);
-        const bf16x8 cf = fp8x8_to_bf16x8(static_cast<uint32_t>(raw8[0]), static_cast<uint32_t>(raw8[1]));
-        const int kq = st / kColBlocks, nb = st % kColBlocks;
-        o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cf, pb[kq], o[nb], 0, 0, 0);
-      }
-    } else {
+    {
       constexpr int kSteps = kKQ * kColBlocks;
       constexpr int kRing = 4;
       auto frag = [&](int st) {
@@ -734,7 +737,7 @@ decode_m32_kernel(DecodeArgs a) {
         if (st + kRing < kSteps) ring[st % kRing] = frag(st + kRing);
         const int kq = st / kColBlocks, nb = st % kColBlocks;
         o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cf, pb[kq], o[nb], 0, 0, 0);
-        if constexpr (HS == 2) {  // the RoPE rows of the next page
+        if constexpr (HS == 2 && !F8) {  // the RoPE rows of the next page
           if ((st == 8 || st == 24) && has_next)
             load_row(next_base, next_page, next_valid, wave, static_cast<int>(opaque(lane)),
                      st == 8 ? 16 : 17);
@@ -745,12 +748,12 @@ decode_m32_kernel(DecodeArgs a) {
     // allocator otherwise moves some of them to VGPRs and spills).
 #pragma unroll
     for (int nb = 0; nb < kColBlocks; ++nb) asm volatile("" : "+a"(o[nb]));
-    stage = F8 ? (stage == 2 ? 0 : stage + 1) : (stage ^ 1);
+    if constexpr (!F8) stage ^= 1;
     if (has_next) cur_page = next_page;
   }
-  // The 128-head bf16 form copies on every page, the last one included: its copies must land
+  // The 128-head form copies on every page, the last one included: its copies must land
   // before the workgroup's LDS is released.
-  if constexpr (HS == 1 && !F8) __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
+  if constexpr (HS == 1) __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
 
   // ---- finalize: normalise and write this split's partial output (bf16) and LSE
   const float l_tot = halves_sum(l_run);
