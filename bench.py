@@ -55,14 +55,18 @@ FP32_PEAK_TFLOPS = 157.3
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode.json")
 CSRC = os.path.join(ROOT, "mla_latent_kv_09_amd", "csrc")
 KERNEL_SRC = {"decode_mfma_kernel": "decode_mfma.hip", "decode_m32_kernel": "decode_m32.hip",
-              "decode_m32_kernel_fp8": "decode_m32.hip", "decode_generic_kernel": "kernels_generic.hip"}
+              "decode_m32_kernel_fp8": "decode_m32.hip", "decode_m32_kernel_mxfp4": "decode_m32.hip",
+              "decode_generic_kernel": "kernels_generic.hip"}
 
 
 def cache_row_bytes(cfg, kv_dtype="bf16"):
     """Bytes one token occupies in the latent cache: d_c + d_R elements of the storage
-    type, or for the FP8 cache d_c E4M3 codes, d_R bf16 and one float32 scale."""
+    type; for the FP8 cache d_c E4M3 codes, d_R bf16 and one float32 scale; for the MXFP4
+    cache d_c / 2 bytes of codes, d_R bf16 and d_c / 32 scale bytes."""
     if kv_dtype == "fp8":
         return cfg.d_c + 2 * cfg.d_R + 4
+    if kv_dtype == "mxfp4":
+        return cfg.d_c // 2 + 2 * cfg.d_R + cfg.d_c // 32
     return (cfg.d_c + cfg.d_R) * (2 if cfg.dtype == "bf16" else 4)
 
 
@@ -272,9 +276,10 @@ def main():
                     help="query rows at which the library's dispatch takes the decompressed "
                          "branch (batches whose largest q_len reaches it, e.g. --config "
                          "prefill_b8_l4096)")
-    ap.add_argument("--kv-dtype", choices=["bf16", "fp8"], default="bf16",
-                    help="latent cache format: bf16 rows (default) or FP8 E4M3 pages written by "
-                         "mla_append_kv_fp8 (a separate line, never the headline)")
+    ap.add_argument("--kv-dtype", choices=["bf16", "fp8", "mxfp4"], default="bf16",
+                    help="latent cache format: bf16 rows (default), FP8 E4M3 pages written by "
+                         "mla_append_kv_fp8 or MXFP4 pages written by mla_append_kv_mxfp4 (a "
+                         "separate line, never the headline)")
     ap.add_argument("--keep-latent", action="store_true",
                     help="have a fused merge launch also write the merged latent rows (the "
                          "step's output is out and lse either way)")
@@ -296,8 +301,8 @@ def main():
 
     cfg = wl.CONFIGS[args.config]
     w = wl.make_workload(cfg)
-    if args.kv_dtype == "fp8" and args.flush:
-        print("--kv-dtype fp8 takes the default (rotated copies) timing", file=sys.stderr)
+    if args.kv_dtype != "bf16" and args.flush:
+        print("a quantized cache takes the default (rotated copies) timing", file=sys.stderr)
         sys.exit(2)
     att, proj, kv_bytes, w_bytes = algorithmic_work(cfg, w.seq_lens, w.q_lens, args.kv_dtype)
     stream = torch.cuda.current_stream()
@@ -414,7 +419,7 @@ def main():
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": cfg.dtype, "data": "synthetic",
-        "config": {"workload": cfg.name, "kv_cache": "fp8_e4m3" if args.kv_dtype == "fp8" else cfg.dtype,
+        "config": {"workload": cfg.name, "kv_cache": {"fp8": "fp8_e4m3", "mxfp4": "mxfp4"}.get(args.kv_dtype, cfg.dtype),
                    "batch": cfg.batch, "heads": cfg.heads, "d_hc": cfg.d_hc,
                    "d_c": cfg.d_c, "d_R": cfg.d_R, "groups": cfg.groups, "page_size": cfg.page_size,
                    "seq_len": cfg.seq_len, "seq_len_range": cfg.seq_len_range,
@@ -441,12 +446,12 @@ def measure_append(args, w, torch, harness, mla, wl, steps, runner, timed, reps,
     (2) a prefill-shaped bulk append that writes every slot of the first sequences (at
     most 65536 rows; q_len = seq_len, so each sequence's rows 0 .. L-1), rotated over the
     copies like the step, whose bytes (each row read once and written once in the cache's
-    format) give the kernel's HBM roofline.  With --kv-dtype fp8 the call is
-    mla_append_kv_fp8, which also quantizes the latent."""
+    format) give the kernel's HBM roofline.  With --kv-dtype fp8 / mxfp4 the call is
+    mla_append_kv_fp8 / mla_append_kv_mxfp4, which also quantizes the latent."""
     cfg = w.cfg
     elem = 2 if cfg.dtype == "bf16" else 4
     kv_dtype = args.kv_dtype
-    append = mla.append_kv_fp8 if kv_dtype == "fp8" else mla.append_kv
+    append = {"fp8": mla.append_kv_fp8, "mxfp4": mla.append_kv_mxfp4}.get(kv_dtype, mla.append_kv)
     n = len(steps)
     new = wl.make_new_tokens(w)
     tensors = [harness.new_tokens_to_device(w, new, st.kv.device) for st in steps]
@@ -576,11 +581,12 @@ def prefill_bench(args, w, torch, harness, mla, stream):
 
 
 def device_copy(w, harness, kv_dtype):
-    """One device copy of the workload; with kv_dtype fp8 its cache replaced by FP8 pages
-    that the library's FP8 append writes from the bf16 rows (the bf16 pool is freed)."""
+    """One device copy of the workload; with kv_dtype fp8 / mxfp4 its cache replaced by
+    pages of that format that the library's append writes from the bf16 rows (the bf16
+    pool is freed)."""
     d = harness.to_device(w)
-    if kv_dtype == "fp8":
-        d.kv = harness.fp8_pool_by_append(w, d)
+    if kv_dtype in ("fp8", "mxfp4"):
+        d.kv = harness.quant_pool_by_append(w, d, kv_dtype)
     return d
 
 
@@ -592,8 +598,8 @@ def decode_kernel_name(cfg, total_q, num_splits, kv_dtype="bf16", cu_count=256):
     mfma_shape = (cfg.dtype == "bf16" and cfg.heads == 128 and cfg.groups in (1, 2)
                   and cfg.d_c == 512 and cfg.d_R == 64 and cfg.page_size == 64)
     choice = os.environ.get("MLA_KV_DECODE_KERNEL", "")
-    if kv_dtype == "fp8":  # one kernel form over FP8 pages
-        return "decode_m32_kernel_fp8"
+    if kv_dtype in ("fp8", "mxfp4"):  # one kernel form over quantized pages
+        return "decode_m32_kernel_" + kv_dtype
     if choice == "generic" or not mfma_shape:
         return "decode_generic_kernel"
     if cfg.groups != 1 or choice in ("mfma128", "mfma64"):

@@ -16,7 +16,8 @@
  * plus mla_rope_table (the fp32 cos/sin table the decode call reads),
  * mla_append_kv (writes the new tokens' latent rows, with their rotated RoPE keys,
  * into the paged cache before the decode reads them), mla_decode_plan (host-only
- * split plan) and mla_status_string.
+ * split plan) and mla_status_string.  Further down: the quantized caches (FP8 and MXFP4
+ * pages, with their own append and decode calls) and the decompressed branch.
  *
  * Sources, cited by page address and section:
  *   P3 = www.nxmr.cn/news/151634  (MLA operators: absorption, paged latent cache)
@@ -296,6 +297,54 @@ int mla_decode_paged_fp8(const void* q_abs, const void* q_r, const void* kv_cach
                          int heads, int groups, int d_hc, int d_c, int d_R, int page_size,
                          int num_splits, int pages_per_split, float softmax_scale, int causal,
                          void* stream);
+
+/*
+ * MXFP4 latent cache (P3 intro and §5: the page's quantized gather is of 4-bit values, two
+ * per byte, loaded 16 bytes at a time; it names NVIDIA's NVFP4 and gives no layout).  The
+ * format here is the library's reading on gfx950's native 4-bit format, OCP MXFP4:
+ * elements E2M1 (1 sign bit, 2 exponent bits with bias 1, 1 mantissa bit: magnitudes 0,
+ * 0.5, 1, 1.5, 2, 3, 4, 6; no infinity or NaN), one E8M0 scale byte s (2^(s - 127)) per
+ * 32 consecutive latent elements of a token:
+ *   one page = { codes [64][d_c / 2] uint8 (byte j of a row: element 2j in the low nibble,
+ *   2j + 1 in the high nibble) | k_R [64][d_R] bf16 | scales [64][d_c / 32] uint8 },
+ *   mla_mxfp4_page_bytes(d_c, d_R) = 64 * (d_c / 2 + 2 d_R + d_c / 32) bytes (25600 for
+ *   512 / 64), 0 when d_c is not a multiple of 32.  Element value = E2M1(code) * 2^(s - 127);
+ *   k_R stays bf16 as in the FP8 cache.
+ */
+size_t mla_mxfp4_page_bytes(int d_c, int d_R);
+
+/*
+ * mla_append_kv_mxfp4 -- mla_append_kv into an MXFP4 cache.  Each 32-element block of the
+ * new token's latent row x gets the shared exponent e = floor(log2 amax) - 2 (amax = the
+ * block's max |x_i|; 2 is the exponent of E2M1's largest value), clamped to [-126, 127]
+ * (-126 for an all-zero block), stored as the byte e + 127 (so 1 .. 254: the decode builds
+ * the scale as a normal float32); code_i = the E2M1 value nearest to x_i * 2^-e (an exact
+ * product), ties to the even code, magnitudes past 6 saturating to 6, with x_i's sign.
+ * k_R is rotated and rounded as mla_append_kv does.  c_kv_new [T, d_c] and k_r_new
+ * [T, d_R] are bf16.  d_c must be a multiple of 32 and d_R of 8, both at most 512
+ * (MLA_ERR_UNSUPPORTED otherwise); other arguments and errors as mla_append_kv.
+ */
+int mla_append_kv_mxfp4(const void* c_kv_new, const void* k_r_new, void* kv_cache,
+                        const int32_t* page_table, const int32_t* seq_lens, const int32_t* cu_q,
+                        const float* rope_cos, const float* rope_sin, int rope_max_pos,
+                        int batch, int total_q, int max_pages_per_seq, int num_pool_pages,
+                        int d_c, int d_R, int page_size, void* stream);
+
+/*
+ * mla_decode_paged_mxfp4 -- mla_decode_paged over an MXFP4 cache: same arguments, results,
+ * split plan and shapes as mla_decode_paged_fp8, with kv_cache the MXFP4 pages above: the
+ * result of mla_decode_paged on the dequantized rows.  The codes times their block's scale
+ * are converted to bf16 exactly for the MFMAs (a scale byte of 0 or 255, which the append
+ * never writes, is outside the format: its block reads as zero or not a number).
+ */
+int mla_decode_paged_mxfp4(const void* q_abs, const void* q_r, const void* kv_cache,
+                           const int32_t* page_table, const int32_t* seq_lens, const int32_t* cu_q,
+                           const float* rope_cos, const float* rope_sin, int rope_max_pos,
+                           void* o_part, float* lse_part,
+                           int batch, int total_q, int max_pages_per_seq, int num_pool_pages,
+                           int heads, int groups, int d_hc, int d_c, int d_R, int page_size,
+                           int num_splits, int pages_per_split, float softmax_scale, int causal,
+                           void* stream);
 
 /*
  * Prefill/decode dispatch (P3 §3: kPrefillThresh = 256, the "absorption / decompression

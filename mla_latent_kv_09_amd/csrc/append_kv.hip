@@ -223,12 +223,125 @@ __global__ void __launch_bounds__(kBlock) append_kv_fp8_kernel(
     *reinterpret_cast<float*>(pg + static_cast<size_t>(page_size) * (d_c + 2 * d_R) + 4 * slot) = scale;
 }
 
+// Nearest E2M1 code to the magnitude m (ties to the even code, past 6 saturating to 6):
+// the magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4, 6 (codes 0 .. 7) and the midpoints between
+// neighbours 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5; a midpoint goes to the even code, so
+// the comparison is inclusive below an even code and strict below an odd one.
+__device__ __forceinline__ uint32_t e2m1_magnitude_code(float m) {
+  return static_cast<uint32_t>(m > 0.25f) + static_cast<uint32_t>(m >= 0.75f) +
+         static_cast<uint32_t>(m > 1.25f) + static_cast<uint32_t>(m >= 1.75f) +
+         static_cast<uint32_t>(m > 2.5f) + static_cast<uint32_t>(m >= 3.5f) +
+         static_cast<uint32_t>(m > 5.0f);
+}
+
+// MXFP4 cache append (the OCP microscaling 4-bit format): one wave per new token row.
+// The page holds the packed codes [64][d_c / 2] (byte j: element 2j in the low nibble,
+// 2j + 1 in the high one), then k_R [64][d_R] (bf16), then the scale bytes [64][d_c / 32]
+// (E8M0, one per 32 latent elements).  Lane l takes latent elements 8l .. 8l+7, so lanes
+// 4k .. 4k+3 hold block k.  Its shared exponent is e = floor(log2 amax) - 2 (2: the
+// exponent of E2M1's largest value, 6 = 1.5 * 2^2), at least -126, and its scale byte
+// e + 127 = max(E - 2, 1) with E the float32 exponent field of amax (0 for a zero or
+// subnormal amax).  Each code is the E2M1 value nearest to x * 2^-e, an exact product,
+// with x's sign.  k_R is rotated at the token's position as in the bf16 append.  The
+// launcher requires d_c a multiple of 32 and d_R of 8, both at most 512.
+__global__ void __launch_bounds__(kBlock) append_kv_mxfp4_kernel(
+    const uint16_t* __restrict__ c_new, const uint16_t* __restrict__ k_new, uint8_t* __restrict__ kv,
+    const int32_t* __restrict__ page_table, const int32_t* __restrict__ seq_lens,
+    const int32_t* __restrict__ cu_q, const float* __restrict__ rope_cos,
+    const float* __restrict__ rope_sin, int rope_max_pos, int batch, int total_q, int max_pages,
+    int num_pool_pages, int d_c, int d_R, int page_size) {
+  const int lane = threadIdx.x & 63;
+  const int t = __builtin_amdgcn_readfirstlane(static_cast<int>(blockIdx.x) * (kBlock / 64) +
+                                               static_cast<int>(threadIdx.x >> 6));
+  if (t >= total_q) return;
+  const bool has_c = lane < d_c / 8, has_k = lane < d_R / 8;
+  uint4 cv{}, kvv{};
+  if (has_c) cv = *reinterpret_cast<const uint4*>(c_new + static_cast<size_t>(t) * d_c + 8 * lane);
+  if (has_k) kvv = *reinterpret_cast<const uint4*>(k_new + static_cast<size_t>(t) * d_R + 8 * lane);
+
+  const int b = find_seq(cu_q, batch, t);
+  const int q0 = cu_q[b];
+  const int q_len = cu_q[b + 1] - q0;
+  const int cap = max_pages * page_size;
+  int L = seq_lens[b];
+  L = L < 0 ? 0 : (L > cap ? cap : L);
+  const int pos = L - q_len + (t - q0);
+  if (pos < 0 || pos >= cap) return;
+  const int page = clamp_page(page_table[static_cast<size_t>(b) * max_pages + pos / page_size],
+                              num_pool_pages);
+  const int slot = pos % page_size;
+  const size_t row_codes = static_cast<size_t>(d_c) / 2, row_scales = static_cast<size_t>(d_c) / 32;
+  uint8_t* pg = kv + static_cast<size_t>(page) * page_size * (row_codes + 2 * d_R + row_scales);
+
+  // Latent: the block maximum over lanes 4k .. 4k+3, then the codes.
+  float x[8];
+  const uint16_t* xs = reinterpret_cast<const uint16_t*>(&cv);
+  float amax = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    x[e] = bf16_to_f32(xs[e]);
+    amax = fmaxf(amax, fabsf(x[e]));
+  }
+  amax = fmaxf(amax, __shfl_xor(amax, 1));
+  amax = fmaxf(amax, __shfl_xor(amax, 2));
+  const int E = static_cast<int>(__float_as_uint(amax) >> 23);  // amax >= 0: no sign bit
+  const int sbyte = E - 2 > 1 ? E - 2 : 1;                        // e + 127, e >= -126
+  const float inv = __uint_as_float(static_cast<uint32_t>(254 - sbyte) << 23);  // 2^-e
+  if (has_c) {
+    uint32_t w = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float y = x[e] * inv;  // exact: a power of two, |y| < 8
+      const uint32_t code = e2m1_magnitude_code(fabsf(y)) | ((__float_as_uint(y) >> 28) & 8u);
+      w |= code << (4 * e);
+    }
+    *reinterpret_cast<uint32_t*>(pg + static_cast<size_t>(slot) * row_codes + 4 * lane) = w;
+    if ((lane & 3) == 0)
+      pg[static_cast<size_t>(page_size) * (row_codes + 2 * d_R) + slot * row_scales + (lane >> 2)] =
+          static_cast<uint8_t>(sbyte);
+  }
+  if (has_k) {
+    float k[8];
+    const uint16_t* ks = reinterpret_cast<const uint16_t*>(&kvv);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) k[e] = bf16_to_f32(ks[e]);
+    if (rope_cos != nullptr) {
+      const int p = min(pos, rope_max_pos - 1);
+      const size_t off = static_cast<size_t>(p) * (d_R / 2) + 4 * lane;
+      float cs[4], sn[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        cs[i] = rope_cos[off + i];
+        sn[i] = rope_sin[off + i];
+      }
+      rotate_pairs(k, 8, cs, sn);
+    }
+    uint4 o;
+    uint16_t* os = reinterpret_cast<uint16_t*>(&o);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) os[e] = f32_to_bf16(k[e]);
+    *reinterpret_cast<uint4*>(pg + static_cast<size_t>(page_size) * row_codes +
+                              (static_cast<size_t>(slot) * d_R + 8 * lane) * 2) = o;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_append_kv_fp8(const AppendArgs& a, hipStream_t s) {
   const long long rows_per_block = kBlock / 64;
   const dim3 grid(static_cast<unsigned>((a.total_q + rows_per_block - 1) / rows_per_block));
   append_kv_fp8_kernel<<<grid, kBlock, 0, s>>>(
+      static_cast<const uint16_t*>(a.c_new), static_cast<const uint16_t*>(a.k_new),
+      static_cast<uint8_t*>(a.kv), a.page_table, a.seq_lens, a.cu_q, a.rope_cos, a.rope_sin,
+      a.rope_max_pos, a.batch, a.total_q, a.max_pages, a.num_pool_pages, a.d_c, a.d_R,
+      a.page_size);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_kv_mxfp4(const AppendArgs& a, hipStream_t s) {
+  const long long rows_per_block = kBlock / 64;
+  const dim3 grid(static_cast<unsigned>((a.total_q + rows_per_block - 1) / rows_per_block));
+  append_kv_mxfp4_kernel<<<grid, kBlock, 0, s>>>(
       static_cast<const uint16_t*>(a.c_new), static_cast<const uint16_t*>(a.k_new),
       static_cast<uint8_t*>(a.kv), a.page_table, a.seq_lens, a.cu_q, a.rope_cos, a.rope_sin,
       a.rope_max_pos, a.batch, a.total_q, a.max_pages, a.num_pool_pages, a.d_c, a.d_R,

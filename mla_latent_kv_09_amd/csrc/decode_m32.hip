@@ -94,19 +94,36 @@ constexpr int kCopies8 = 11;                      // global->LDS copies per wave
 // land in (latent row t at 512 t, k_R and scales as in HBM, k_R rows swizzled as in the
 // bf16 stage), then q_R.  The 64-head form's final merge uses the first 130 KB.
 constexpr int kScaleOff8 = kStageBytes;
-constexpr int kF8Off = kScaleOff8 + kTok * 4;
-constexpr int kQrOff8 = kF8Off + kPage8Bytes;
+constexpr int kQOff = kScaleOff8 + kTok * 4;
+constexpr int kQrOff8 = kQOff + kPage8Bytes;
 constexpr int kMergeBytes = 4 * 32768 + kThreads * 8;
 constexpr int kLds8Bytes = kQrOff8 + kHeads * kDr * 2 > kMergeBytes ? kQrOff8 + kHeads * kDr * 2 : kMergeBytes;
 static_assert(kLds8Bytes <= 160 * 1024, "the FP8 form's LDS must fit the 160 KB of a gfx950 CU");
-static_assert(kPage8Bytes % 16 == 0 && kF8Off % 16 == 0, "FP8 pages are whole 16-byte units");
+static_assert(kPage8Bytes % 16 == 0 && kQOff % 16 == 0, "FP8 pages are whole 16-byte units");
 static_assert(kLdsBytes >= kMergeBytes, "the 64-head merge fits the bf16 form's LDS");
 
-template <bool F8>
+// MXFP4 cache page in HBM: packed E2M1 codes (byte j of a row: elements 2j, 2j + 1 in its
+// low and high nibble), then k_R, then one E8M0 scale byte per 32 latent elements.
+constexpr int kC4Bytes = kTok * kDc / 2;               // 16 KB of codes
+constexpr int kR4Off = kC4Bytes;                       // k_R [64][64] bf16
+constexpr int kS4Off = kC4Bytes + kRBytes;             // scale bytes [64][16]
+constexpr int kPage4Bytes = kS4Off + kTok * kDc / 32;  // 25600 B, the page stride in HBM
+constexpr int kCopies4 = 7;                            // global->LDS copies per wave and page
+// MXFP4 LDS: the FP8 form's layout with the MXFP4 page in the quantized stage (the scale
+// slots beside the bf16 stage unused: the scales are applied in the conversion).
+constexpr int kQrOff4 = kQOff + kPage4Bytes;
+constexpr int kLds4Bytes = kQrOff4 + kHeads * kDr * 2 > kMergeBytes ? kQrOff4 + kHeads * kDr * 2 : kMergeBytes;
+static_assert(kLds4Bytes <= 160 * 1024 && kPage4Bytes % 16 == 0, "MXFP4 stage layout");
+
+// Cache formats of the kernel template.
+enum : int { kFmtBf16 = 0, kFmtFp8 = 1, kFmtFp4 = 2 };
+
+template <int KF>
 struct Form {
-  static constexpr int kPage = F8 ? kPage8Bytes : kTok * kRowBytes;  // page stride in HBM
-  static constexpr int kQr = F8 ? kQrOff8 : kQrOff;
-  static constexpr int kLds = F8 ? kLds8Bytes : kLdsBytes;
+  static constexpr int kPage = KF == kFmtFp8 ? kPage8Bytes : KF == kFmtFp4 ? kPage4Bytes : kTok * kRowBytes;
+  static constexpr int kQr = KF == kFmtFp8 ? kQrOff8 : KF == kFmtFp4 ? kQrOff4 : kQrOff;
+  static constexpr int kLds = KF == kFmtFp8 ? kLds8Bytes : KF == kFmtFp4 ? kLds4Bytes : kLdsBytes;
+  static constexpr int kCopies = KF == kFmtFp8 ? kCopies8 : KF == kFmtFp4 ? kCopies4 : 18;
 };
 
 __device__ __forceinline__ uint32_t swz_f(int t) {
@@ -226,7 +243,7 @@ __device__ __forceinline__ void convert_page8(uint32_t base, int wave, int lane)
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) u32x2 lds_u32x2_t;
   typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
-  const uint32_t f8 = base + kF8Off;
+  const uint32_t f8 = base + kQOff;
   const uint32_t src = f8 + static_cast<uint32_t>(wave * 16 * kDc + 8 * lane);
   // token 16w + r: swz_f(16w + r) = swz_f(r) | 16 (w & 1), swz_f(r) < 16
   const uint32_t dst = base + static_cast<uint32_t>(wave * 16 * 1024) +
@@ -271,6 +288,88 @@ __device__ __forceinline__ void convert_page8(uint32_t base, int wave, int lane)
   }
 }
 
+// MXFP4 form: copy `row` (0..6) of this wave's share of a page into the quantized stage
+// `f4` (the page's own layout): rows 0..3 are the codes of tokens 16w + 4 row .. +3 (256 B
+// each, one per 16-lane group), rows 4, 5 the k_R rows of tokens 16w + 8 (row - 4) .. +7
+// (swizzled as in the bf16 stage), row 6 the scale bytes of tokens 16w .. 16w+15 (lanes
+// 0..15).  Rows at or past n_valid fetch token 0.
+__device__ __forceinline__ void load_row4(uint32_t f4, const char* page, int n_valid, int wave,
+                                          int lane, int row) {
+  if (row < 4) {
+    const int t0 = wave * 16 + 4 * row;
+    const int t = t0 + (lane >> 4);
+    const int src_t = t < n_valid ? t : 0;
+    dma16(page, static_cast<uint32_t>(src_t * (kDc / 2) + ((lane & 15) << 4)), f4 + t0 * (kDc / 2));
+  } else if (row < 6) {
+    const int t0 = wave * 16 + 8 * (row - 4);
+    const int t = t0 + (lane >> 3);
+    const int src_t = t < n_valid ? t : 0;
+    dma16(page, static_cast<uint32_t>(kR4Off + src_t * 128 + (((lane & 7) ^ ((t >> 2) & 7)) << 4)),
+          f4 + kR4Off + t0 * 128);
+  } else if (lane < 16) {
+    const int t = wave * 16 + lane;
+    const int src_t = t < n_valid ? t : 0;
+    dma16(page, static_cast<uint32_t>(kS4Off + src_t * 16), f4 + kS4Off + wave * 256);
+  }
+}
+
+// Exact E2M1 -> bf16 of the two codes in byte kByte of v, times the power of two `scale`
+// (v_cvt_scalef32_pk_bf16_fp4: the low nibble to the low half).  Inline asm, as for the
+// FP8 conversion.
+template <int kByte>
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t v, float scale) {
+  uint32_t r;
+  if constexpr (kByte == 0)
+    asm("v_cvt_scalef32_pk_bf16_fp4 %0, %1, %2" : "=v"(r) : "v"(v), "v"(scale));
+  else if constexpr (kByte == 1)
+    asm("v_cvt_scalef32_pk_bf16_fp4 %0, %1, %2 op_sel:[1,0,0]" : "=v"(r) : "v"(v), "v"(scale));
+  else if constexpr (kByte == 2)
+    asm("v_cvt_scalef32_pk_bf16_fp4 %0, %1, %2 op_sel:[0,1,0]" : "=v"(r) : "v"(v), "v"(scale));
+  else
+    asm("v_cvt_scalef32_pk_bf16_fp4 %0, %1, %2 op_sel:[1,1,0]" : "=v"(r) : "v"(v), "v"(scale));
+  return r;
+}
+
+// MXFP4 form: the page in the quantized stage becomes the bf16 stage at `base`.  Wave w
+// takes tokens 16w .. 16w+15: lane l converts the 8 codes of dword l of a row (elements
+// 8l .. 8l+7, one block, so one scale: byte l / 4 of the row's scales) into the 16-byte
+// chunk l of that bf16 row at its swizzled position l ^ f(t); the value is code * 2^(s-127)
+// exactly (the scale bytes are 1 .. 254, normal float32 powers of two).  The k_R rows are
+// moved as they are.
+template <int kBatch>
+__device__ __forceinline__ void convert_page4(uint32_t base, int wave, int lane) {
+  typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) uint32_t lds_u32_t;
+  typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
+  const uint32_t f4 = base + kQOff;
+  const uint32_t src = f4 + static_cast<uint32_t>(wave * 16 * (kDc / 2) + 4 * lane);
+  const uint32_t ssrc = f4 + static_cast<uint32_t>(kS4Off + wave * 256 + (lane >> 2));
+  const uint32_t dst = base + static_cast<uint32_t>(wave * 16 * 1024) +
+                       (static_cast<uint32_t>(lane ^ (16 * (wave & 1))) << 4);
+  const uint32_t kr_off = static_cast<uint32_t>(wave * 2048 + 16 * lane);
+#pragma unroll
+  for (int r0 = 0; r0 < 16; r0 += kBatch) {
+    uint32_t raw[kBatch], sb[kBatch];
+#pragma unroll
+    for (int r = 0; r < kBatch; ++r) {
+      raw[r] = *(const lds_u32_t*)(uintptr_t)(src + (r0 + r) * (kDc / 2));
+      sb[r] = *(const lds_u8_t*)(uintptr_t)(ssrc + (r0 + r) * 16);
+    }
+#pragma unroll
+    for (int r = 0; r < kBatch; ++r) {
+      const float sc = __uint_as_float(sb[r] << 23);
+      const u32x4 v{fp4x2_to_bf16x2<0>(raw[r], sc), fp4x2_to_bf16x2<1>(raw[r], sc),
+                    fp4x2_to_bf16x2<2>(raw[r], sc), fp4x2_to_bf16x2<3>(raw[r], sc)};
+      *(lds_u32x4_t*)(uintptr_t)((dst + (r0 + r) * 1024) ^ (swz_f(r0 + r) << 4)) = v;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+    *(lds_u32x4_t*)(uintptr_t)(base + kCBytes + kr_off + 1024 * j) =
+        *(const lds_u32x4_t*)(uintptr_t)(f4 + kR4Off + kr_off + 1024 * j);
+}
+
 // Copy `row` (0..17) of this wave's share of a page into stage `c_base`: rows 0..15 are
 // the latent rows of tokens 16w + row (1 KB each), rows 16, 17 the RoPE rows of tokens
 // 16w + 8 (row - 16) .. +7.  Rows at or past n_valid fetch token 0 (always valid).
@@ -295,10 +394,12 @@ __device__ __forceinline__ void load_row(uint32_t c_base, const char* page, int 
 // HS = 2: two workgroups of 64 heads per (token, split).  Wave w owns heads
 // 32 (w % 2) .. +31 of its half over tokens 32 (w / 2) .. +31 of each page; waves w and
 // w ^ 2 (same heads, other token half) merge their outputs through LDS at the end.
-template <int HS, bool F8>
+template <int HS, int KF>
 __global__ void __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 decode_m32_kernel(DecodeArgs a) {
-  using Fm = Form<F8>;
+  using Fm = Form<KF>;
+  constexpr bool F8 = KF == kFmtFp8, F4 = KF == kFmtFp4;
+  constexpr bool Q = F8 || F4;  // a quantized cache: copies land in the quantized stage
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int S = a.num_splits;
   // Launch order (HS = 1): every sequence's non-empty (token, split) units first, then
@@ -355,7 +456,10 @@ decode_m32_kernel(DecodeArgs a) {
     const int nv = min(kTok, w.k1 - j0);
     if constexpr (F8) {
 #pragma unroll
-      for (int r = 0; r < kCopies8; ++r) load_row8(smem_base + kF8Off, p0, nv, wave, lane, r);
+      for (int r = 0; r < kCopies8; ++r) load_row8(smem_base + kQOff, p0, nv, wave, lane, r);
+    } else if constexpr (F4) {
+#pragma unroll
+      for (int r = 0; r < kCopies4; ++r) load_row4(smem_base + kQOff, p0, nv, wave, lane, r);
     } else {
 #pragma unroll
       for (int r = 0; r < 18; ++r) load_row(smem_base, p0, nv, wave, lane, r);
@@ -431,12 +535,15 @@ decode_m32_kernel(DecodeArgs a) {
     const int n_valid = min(kTok, w.k1 - j0);
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's page copies have landed
     __syncthreads();  // ... and every wave's; the stage of the previous page is free again
-    if constexpr (F8) {
-      convert_page8<HS == 1 ? 16 : 8>(smem_base, wave, lane);
-      __syncthreads();  // the bf16 stage is complete and the FP8 stage free for the next page
+    if constexpr (Q) {
+      if constexpr (F8)
+        convert_page8<HS == 1 ? 16 : 8>(smem_base, wave, lane);
+      else
+        convert_page4<HS == 1 ? 16 : 8>(smem_base, wave, lane);
+      __syncthreads();  // the bf16 stage is complete and the quantized stage free again
     }
     // The page whose copies this iteration issues: the next one, into the other stage
-    // (FP8: into the FP8 stage).
+    // (a quantized cache: into the quantized stage).
     const int j_next = j0 + kTok;
     const bool has_next = j_next < w.k1;
     const char* next_page = kv;
@@ -446,7 +553,7 @@ decode_m32_kernel(DecodeArgs a) {
       if ((i_next & 63) == 0) fetch_ids(i_next >> 6);
       next_page = page_ptr(i_next);
     }
-    const uint32_t next_base = F8 ? smem_base + kF8Off : smem_base + (stage ^ 1) * kStageBytes;
+    const uint32_t next_base = Q ? smem_base + kQOff : smem_base + (stage ^ 1) * kStageBytes;
     const uint32_t st_base = smem_base + stage * kStageBytes;
     const uint32_t sb = opaque(st_base + s_lane);
     // FP8: the latent part of each score times its token's scale (s[mb] holds block mb of
@@ -492,8 +599,9 @@ decode_m32_kernel(DecodeArgs a) {
     f32x16 s[2];
     {
       const uint32_t rb = opaque(st_base + kCBytes + n * 128);
-      // (FP8: through an empty asm, so that the q_R addresses are not kept across the loop)
-      const uint32_t qb = F8 ? opaque(smem_base + Fm::kQr + hl * 128) : smem_base + Fm::kQr + hl * 128;
+      // (quantized caches: through an empty asm, so that the q_R addresses are not kept
+      // across the loop)
+      const uint32_t qb = Q ? opaque(smem_base + Fm::kQr + hl * 128) : smem_base + Fm::kQr + hl * 128;
       const int swr = (n >> 2) & 7, swq = (hl >> 2) & 7;
       auto qr_frag = [&](int rs) { return lds_read8(qb + (((2 * rs + h) ^ swq) << 4)); };
       auto rope_frag = [&](int rs, int mb) { return lds_read8(rb + (((2 * rs + h) ^ swr) << 4) + 4096 * mb); };
@@ -532,6 +640,9 @@ decode_m32_kernel(DecodeArgs a) {
             if constexpr (F8) {  // the 11 copies of the next FP8 page
               if ((st >> 1) < kCopies8)
                 load_row8(next_base, next_page, next_valid, wave, static_cast<int>(opaque(lane)), st >> 1);
+            } else if constexpr (F4) {  // the 7 copies of the next MXFP4 page
+              if ((st >> 1) < kCopies4)
+                load_row4(next_base, next_page, next_valid, wave, static_cast<int>(opaque(lane)), st >> 1);
             } else {  // latent rows 0..15 over the 32 steps
               load_row(next_base, next_page, next_valid, wave, static_cast<int>(opaque(lane)), st >> 1);
             }
@@ -563,7 +674,7 @@ decode_m32_kernel(DecodeArgs a) {
         // k < 8, k_R rows k = 8, 9, the scales k = 10, into the FP8 stage.  The last page
         // copies itself instead (into the unused stage, or the FP8 stage it has converted),
         // so the copies need no branch.
-        constexpr int kCopies = F8 ? kCopies8 : 18;
+        constexpr int kCopies = Fm::kCopies;
         const char* cp_page = has_next ? next_page : cur_page;
         const int cp_valid = has_next ? next_valid : kTok;
         const int cp_lim = cp_valid - 16 * wave;  // latent row r of this wave is a key iff r < cp_lim
@@ -589,6 +700,26 @@ decode_m32_kernel(DecodeArgs a) {
               cp_voff = static_cast<uint32_t>(kS8Off + wave * 64 + 16 * ln);
               cp_lds = next_base + static_cast<uint32_t>(kS8Off + wave * 64);
             }
+          } else if constexpr (F4) {
+            const int ln = static_cast<int>(opaque(lane));
+            if (k < 4) {  // codes of tokens 16 w + 4 k .. +3, one per 16-lane group
+              const int t0 = 16 * wave + 4 * k;
+              const int tt = t0 + (ln >> 4);
+              const int src_t = tt < cp_valid ? tt : 0;
+              cp_voff = static_cast<uint32_t>(src_t * (kDc / 2) + ((ln & 15) << 4));
+              cp_lds = next_base + static_cast<uint32_t>(t0 * (kDc / 2));
+            } else if (k < 6) {  // k_R rows of tokens t0 .. t0 + 7
+              const int t0 = wave * 16 + 8 * (k - 4);
+              const int tt = t0 + (ln >> 3);
+              const int src_t = tt < cp_valid ? tt : 0;
+              cp_voff = static_cast<uint32_t>(kR4Off + src_t * 128 + (((ln & 7) ^ ((tt >> 2) & 7)) << 4));
+              cp_lds = next_base + static_cast<uint32_t>(kR4Off + t0 * 128);
+            } else {  // the scale bytes of tokens 16 w .. +15 (lanes 0..15)
+              const int tt = 16 * wave + ln;
+              const int src_t = tt < cp_valid ? tt : 0;
+              cp_voff = static_cast<uint32_t>(kS4Off + src_t * 16);
+              cp_lds = next_base + static_cast<uint32_t>(kS4Off + wave * 256);
+            }
           } else if (k < 16) {  // token 16 w + k; rows past the keys fetch token 0
             const int roff = k < cp_lim ? (16 * wave + k) * kRowBytes : 0;
             cp_voff = (cp_lane ^ (swz_f(k) << 4)) + static_cast<uint32_t>(roff);
@@ -611,6 +742,8 @@ decode_m32_kernel(DecodeArgs a) {
           if ((st & 3) == 2 && k < kCopies) {
             if (F8 && k == 10) {
               if (lane < 4) dma16(cp_page, cp_voff, cp_lds);
+            } else if (F4 && k == 6) {
+              if (lane < 16) dma16(cp_page, cp_voff, cp_lds);
             } else {
               dma16(cp_page, cp_voff, cp_lds);
             }
@@ -737,7 +870,7 @@ decode_m32_kernel(DecodeArgs a) {
         if (st + kRing < kSteps) ring[st % kRing] = frag(st + kRing);
         const int kq = st / kColBlocks, nb = st % kColBlocks;
         o[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cf, pb[kq], o[nb], 0, 0, 0);
-        if constexpr (HS == 2 && !F8) {  // the RoPE rows of the next page
+        if constexpr (HS == 2 && !Q) {  // the RoPE rows of the next page
           if ((st == 8 || st == 24) && has_next)
             load_row(next_base, next_page, next_valid, wave, static_cast<int>(opaque(lane)),
                      st == 8 ? 16 : 17);
@@ -748,7 +881,7 @@ decode_m32_kernel(DecodeArgs a) {
     // allocator otherwise moves some of them to VGPRs and spills).
 #pragma unroll
     for (int nb = 0; nb < kColBlocks; ++nb) asm volatile("" : "+a"(o[nb]));
-    if constexpr (!F8) stage ^= 1;
+    if constexpr (!Q) stage ^= 1;
     if (has_next) cur_page = next_page;
   }
   // The 128-head form copies on every page, the last one included: its copies must land
@@ -834,19 +967,19 @@ bool decode_m32_supported(const DecodeArgs& a, bool bf16) {
          a.page_size == kTok;
 }
 
-template <int HS, bool F8>
+template <int HS, int KF>
 hipError_t launch_decode_m32_k(const DecodeArgs& a, hipStream_t s) {
   static std::atomic<uint64_t> lds_limit_set{0};
-  const hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(decode_m32_kernel<HS, F8>),
-                                        Form<F8>::kLds, lds_limit_set);
+  const hipError_t e = ensure_lds_limit(reinterpret_cast<const void*>(decode_m32_kernel<HS, KF>),
+                                        Form<KF>::kLds, lds_limit_set);
   if (e != hipSuccess) return e;
   const dim3 grid(a.total_q * a.num_splits * HS);
-  decode_m32_kernel<HS, F8><<<grid, kThreads, Form<F8>::kLds, s>>>(a);
+  decode_m32_kernel<HS, KF><<<grid, kThreads, Form<KF>::kLds, s>>>(a);
   return hipGetLastError();
 }
 
 hipError_t launch_decode_m32(const DecodeArgs& a, int head_split, hipStream_t s) {
-  return head_split == 2 ? launch_decode_m32_k<2, false>(a, s) : launch_decode_m32_k<1, false>(a, s);
+  return head_split == 2 ? launch_decode_m32_k<2, kFmtBf16>(a, s) : launch_decode_m32_k<1, kFmtBf16>(a, s);
 }
 
 bool decode_fp8_supported(const DecodeArgs& a) {
@@ -854,7 +987,11 @@ bool decode_fp8_supported(const DecodeArgs& a) {
 }
 
 hipError_t launch_decode_fp8(const DecodeArgs& a, int head_split, hipStream_t s) {
-  return head_split == 2 ? launch_decode_m32_k<2, true>(a, s) : launch_decode_m32_k<1, true>(a, s);
+  return head_split == 2 ? launch_decode_m32_k<2, kFmtFp8>(a, s) : launch_decode_m32_k<1, kFmtFp8>(a, s);
+}
+
+hipError_t launch_decode_mxfp4(const DecodeArgs& a, int head_split, hipStream_t s) {
+  return head_split == 2 ? launch_decode_m32_k<2, kFmtFp4>(a, s) : launch_decode_m32_k<1, kFmtFp4>(a, s);
 }
 
 }  // namespace mla

@@ -495,6 +495,80 @@ int mla_decode_paged_fp8(const void* q_abs, const void* q_r, const void* kv_cach
   return launch_status(mla::launch_decode_fp8(a, hs, static_cast<hipStream_t>(stream)));
 }
 
+size_t mla_mxfp4_page_bytes(int d_c, int d_R) {
+  if (d_c <= 0 || d_R <= 0 || (d_R & 1) || d_c % 32 != 0) return 0;
+  return static_cast<size_t>(MLA_PAGE_SIZE) * (static_cast<size_t>(d_c) / 2 + 2 * d_R + d_c / 32);
+}
+
+int mla_append_kv_mxfp4(const void* c_kv_new, const void* k_r_new, void* kv_cache,
+                        const int32_t* page_table, const int32_t* seq_lens, const int32_t* cu_q,
+                        const float* rope_cos, const float* rope_sin, int rope_max_pos, int batch,
+                        int total_q, int max_pages_per_seq, int num_pool_pages, int d_c, int d_R,
+                        int page_size, void* stream) {
+  if (total_q < 0 || batch <= 0 || d_c <= 0 || d_R <= 0 || (d_R & 1) || max_pages_per_seq <= 0 ||
+      num_pool_pages <= 0 || page_size <= 0)
+    return MLA_ERR_DIM;
+  if (page_size != MLA_PAGE_SIZE) return MLA_ERR_UNSUPPORTED;
+  if (d_c % 32 != 0 || d_R % 8 != 0 || d_c > 512 || d_R > 512) return MLA_ERR_UNSUPPORTED;
+  if (static_cast<long long>(max_pages_per_seq) * page_size > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+  if ((rope_cos == nullptr) != (rope_sin == nullptr)) return MLA_ERR_NULL;
+  if (rope_cos != nullptr && rope_max_pos <= 0) return MLA_ERR_DIM;
+  if (total_q == 0) return MLA_OK;
+  if (!c_kv_new || !k_r_new || !kv_cache || !page_table || !seq_lens || !cu_q) return MLA_ERR_NULL;
+  const void* ptrs[] = {c_kv_new, k_r_new, kv_cache, page_table, seq_lens, cu_q};
+  for (const void* p : ptrs)
+    if (!aligned16(p)) return MLA_ERR_ALIGN;
+  if (rope_cos && (!aligned16(rope_cos) || !aligned16(rope_sin))) return MLA_ERR_ALIGN;
+  mla::AppendArgs a{};
+  a.c_new = c_kv_new;
+  a.k_new = k_r_new;
+  a.kv = kv_cache;
+  a.page_table = page_table;
+  a.seq_lens = seq_lens;
+  a.cu_q = cu_q;
+  a.rope_cos = rope_cos;
+  a.rope_sin = rope_sin;
+  a.rope_max_pos = rope_max_pos;
+  a.batch = batch;
+  a.total_q = total_q;
+  a.max_pages = max_pages_per_seq;
+  a.num_pool_pages = num_pool_pages;
+  a.d_c = d_c;
+  a.d_R = d_R;
+  a.page_size = page_size;
+  return launch_status(mla::launch_append_kv_mxfp4(a, static_cast<hipStream_t>(stream)));
+}
+
+int mla_decode_paged_mxfp4(const void* q_abs, const void* q_r, const void* kv_cache,
+                           const int32_t* page_table, const int32_t* seq_lens, const int32_t* cu_q,
+                           const float* rope_cos, const float* rope_sin, int rope_max_pos,
+                           void* o_part, float* lse_part, int batch, int total_q,
+                           int max_pages_per_seq, int num_pool_pages, int heads, int groups,
+                           int d_hc, int d_c, int d_R, int page_size, int num_splits,
+                           int pages_per_split, float softmax_scale, int causal, void* stream) {
+  mla::DecodeArgs a{};
+  bool bf16 = false;
+  int st = mla::decode_validate(q_abs, q_r, kv_cache, page_table, seq_lens, cu_q, rope_cos,
+                                rope_sin, rope_max_pos, o_part, lse_part, batch, total_q,
+                                max_pages_per_seq, num_pool_pages, heads, groups, d_hc, d_c, d_R,
+                                page_size, num_splits, pages_per_split, softmax_scale, causal,
+                                MLA_DTYPE_BF16, true, &a, &bf16);
+  if (st != MLA_OK) return st;
+  mla::DecodeArgs shape{};
+  shape.heads = heads;
+  shape.groups = groups;
+  shape.d_c = d_c;
+  shape.d_R = d_R;
+  shape.page_size = page_size;
+  if (!mla::decode_fp8_supported(shape)) return MLA_ERR_UNSUPPORTED;  // the same shapes
+  if (total_q == 0) return MLA_OK;
+  const DecodeKernel choice = decode_kernel_choice();
+  a.head_split = choice == DecodeKernel::kMfma32x128 ? 1 : choice == DecodeKernel::kMfma32x64 ? 2 : 0;
+  const int hs = mla::decode_mfma_head_split(a, cu_count_of_current_device());
+  if (static_cast<long long>(total_q) * num_splits * hs > INT32_MAX) return MLA_ERR_UNSUPPORTED;
+  return launch_status(mla::launch_decode_mxfp4(a, hs, static_cast<hipStream_t>(stream)));
+}
+
 int mla_combine(const void* o_part, const float* lse_part, void* o_latent, float* lse_out,
                 int total_q, int heads, int groups, int d_c, int num_splits, int dtype,
                 void* stream) {

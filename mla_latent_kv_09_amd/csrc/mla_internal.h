@@ -99,6 +99,9 @@ struct AppendArgs {
 hipError_t launch_append_kv(const AppendArgs& a, bool bf16, hipStream_t s);
 // FP8 cache: bf16 inputs, pages of [64][d_c] E4M3 codes, [64][d_R] bf16 k_R, [64] f32 scales.
 hipError_t launch_append_kv_fp8(const AppendArgs& a, hipStream_t s);
+// MXFP4 cache: bf16 inputs, pages of [64][d_c / 2] packed E2M1 codes, [64][d_R] bf16 k_R,
+// [64][d_c / 32] E8M0 scale bytes.
+hipError_t launch_append_kv_mxfp4(const AppendArgs& a, hipStream_t s);
 
 // Generic kernels: any (d_cg <= 1024, d_R <= 256), bf16 or fp32 storage.
 hipError_t launch_absorb_generic(const void* q_c, const void* w_uk, void* q_abs, int T, int H,
@@ -131,6 +134,9 @@ hipError_t launch_decode_m32(const DecodeArgs& a, int head_split, hipStream_t s)
 // [64] float32 scales): 128 heads, one latent group, d_c 512, d_R 64.
 bool decode_fp8_supported(const DecodeArgs& a);
 hipError_t launch_decode_fp8(const DecodeArgs& a, int head_split, hipStream_t s);
+// The same kernel over an MXFP4 cache (pages of [64][256] packed E2M1 codes, [64][64] bf16
+// k_R and [64][16] E8M0 scale bytes): the shapes decode_fp8_supported accepts.
+hipError_t launch_decode_mxfp4(const DecodeArgs& a, int head_split, hipStream_t s);
 int decode_mfma_head_split(const DecodeArgs& a, int cu_count);
 hipError_t launch_decode_mfma(const DecodeArgs& a, int head_split, hipStream_t s);
 }  // namespace mla

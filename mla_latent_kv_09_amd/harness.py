@@ -39,7 +39,7 @@ def _storage_tensor(w: Workload, x: np.ndarray, device) -> torch.Tensor:
 def to_device(w: Workload, device="cuda", *, rope: bool = True,
               kv: Optional[np.ndarray] = None) -> DeviceWorkload:
     """Copy ``w`` to ``device``; with ``rope`` the fp32 table is built there by the library.
-    ``kv`` replaces the workload's bf16 pool (an FP8 pool: uint8 [P, page bytes])."""
+    ``kv`` replaces the workload's bf16 pool (an FP8 or MXFP4 pool: uint8 [P, page bytes])."""
     dev = torch.device(device)
     table = None
     if rope and w.cfg.rope_base is not None:
@@ -79,11 +79,12 @@ def new_tokens_to_device(w: Workload, new: NewTokens, device="cuda"):
     return _storage_tensor(w, new.c_kv, dev), _storage_tensor(w, new.k_r, dev)
 
 
-def fp8_pool_by_append(w: Workload, d: DeviceWorkload) -> torch.Tensor:
-    """An FP8 cache holding ``w``'s sequences, written by the library's FP8 append
-    (mla_append_kv_fp8) from the bf16 rows already on the device: every sequence appended
-    whole from position 0, k_R copied unrotated (it is stored rotated already).  Unused
-    slots hold 0xFF bytes (NaN codes, NaN k_R, NaN scales)."""
+def quant_pool_by_append(w: Workload, d: DeviceWorkload, fmt: str = "fp8") -> torch.Tensor:
+    """A quantized cache ("fp8" or "mxfp4") holding ``w``'s sequences, written by the
+    library's append for that format from the bf16 rows already on the device: every
+    sequence appended whole from position 0, k_R copied unrotated (it is stored rotated
+    already).  Unused slots hold 0xFF bytes (FP8: NaN codes, NaN k_R, NaN scales; MXFP4:
+    codes -6, NaN k_R, the out-of-format scale byte 255)."""
     cfg = w.cfg
     ps = cfg.page_size
     lens = [int(L) for L in w.seq_lens]
@@ -94,8 +95,14 @@ def fp8_pool_by_append(w: Workload, d: DeviceWorkload) -> torch.Tensor:
     c = rows[:, :cfg.d_c].contiguous()
     k = rows[:, cfg.d_c:].contiguous()
     P = w.num_pool_pages
-    kv8 = torch.full((P, mla.fp8_page_bytes(cfg.d_c, cfg.d_R)), 0xFF, dtype=torch.uint8,
-                     device=d.kv.device)
+    page_bytes = mla.fp8_page_bytes if fmt == "fp8" else mla.mxfp4_page_bytes
+    kvq = torch.full((P, page_bytes(cfg.d_c, cfg.d_R)), 0xFF, dtype=torch.uint8, device=d.kv.device)
     cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)).to(d.kv.device)
-    mla.append_kv_fp8(c, k, kv8, d.page_table, d.seq_lens, cu)
-    return kv8
+    append = mla.append_kv_fp8 if fmt == "fp8" else mla.append_kv_mxfp4
+    append(c, k, kvq, d.page_table, d.seq_lens, cu)
+    return kvq
+
+
+def fp8_pool_by_append(w: Workload, d: DeviceWorkload) -> torch.Tensor:
+    """quant_pool_by_append for the FP8 cache."""
+    return quant_pool_by_append(w, d, "fp8")

@@ -24,7 +24,8 @@ PAGE_SIZE = 64
 EXPORTED = ("mla_absorb_q", "mla_rope_table", "mla_decode_paged", "mla_combine", "mla_up_v",
             "mla_combine_up_v", "mla_combine_up_v_fused",
             "mla_append_kv", "mla_decode_workspace_bytes", "mla_decode_plan", "mla_attend_noalloc",
-            "mla_decode_paged_fp8", "mla_append_kv_fp8", "mla_fp8_page_bytes", "mla_branch",
+            "mla_decode_paged_fp8", "mla_append_kv_fp8", "mla_fp8_page_bytes",
+            "mla_decode_paged_mxfp4", "mla_append_kv_mxfp4", "mla_mxfp4_page_bytes", "mla_branch",
             "mla_prefill_paged", "mla_prefill_workspace_bytes", "mla_decompress_kv",
             "mla_prefill_attention", "mla_status_string")
 
@@ -63,6 +64,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_attend_noalloc.argtypes = ([P] * 8 + [I] + [P] * 2 + [I] * 12 + [F, I, I, P])
     lib.mla_decode_paged_fp8.argtypes = ([P] * 8 + [I] + [P] * 2 + [I] * 12 + [F, I, P])
     lib.mla_append_kv_fp8.argtypes = [P] * 8 + [I] * 8 + [P]
+    lib.mla_decode_paged_mxfp4.argtypes = ([P] * 8 + [I] + [P] * 2 + [I] * 12 + [F, I, P])
+    lib.mla_append_kv_mxfp4.argtypes = [P] * 8 + [I] * 8 + [P]
     lib.mla_branch.argtypes = [P, I, I]
     lib.mla_prefill_paged.argtypes = [P] * 8 + [I] + [P] * 5 + [I] * 11 + [F, I, I, P]
     lib.mla_decompress_kv.argtypes = [P] * 6 + [I] * 10 + [P]
@@ -71,11 +74,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.mla_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.mla_fp8_page_bytes.argtypes = [I, I]
     lib.mla_fp8_page_bytes.restype = ctypes.c_size_t
+    lib.mla_mxfp4_page_bytes.argtypes = [I, I]
+    lib.mla_mxfp4_page_bytes.restype = ctypes.c_size_t
     lib.mla_status_string.argtypes = [I]
     lib.mla_status_string.restype = ctypes.c_char_p
     for name in ("mla_absorb_q", "mla_rope_table", "mla_decode_paged", "mla_combine", "mla_up_v",
                  "mla_combine_up_v", "mla_append_kv", "mla_decode_plan", "mla_attend_noalloc", "mla_decode_paged_fp8",
-                 "mla_append_kv_fp8", "mla_branch", "mla_prefill_paged", "mla_decompress_kv",
+                 "mla_append_kv_fp8", "mla_decode_paged_mxfp4", "mla_append_kv_mxfp4",
+                 "mla_branch", "mla_prefill_paged", "mla_decompress_kv",
                  "mla_prefill_attention"):
         getattr(lib, name).restype = I
     _lib = lib
@@ -315,21 +321,41 @@ def fp8_page_bytes(d_c: int, d_R: int) -> int:
     return int(load().mla_fp8_page_bytes(int(d_c), int(d_R)))
 
 
-def decode_paged_fp8(q_abs, q_r, kv_fp8, page_table, seq_lens, cu_q, o_part, lse_part, *,
-                     d_hc: int, d_R: int, groups: int = 1, rope: Optional[tuple] = None,
-                     softmax_scale: float = 0.0, causal: bool = True, pages_per_split: int = 0,
-                     stream=None) -> None:
-    """mla_decode_paged over an FP8 cache kv_fp8 (uint8 [P, fp8_page_bytes(d_c, d_R)]):
-    bf16 queries and partials, as mla_decode_paged."""
+def mxfp4_page_bytes(d_c: int, d_R: int) -> int:
+    """Bytes of one MXFP4 cache page: 64 x (d_c / 2 bytes of packed E2M1 codes + d_R bf16 +
+    d_c / 32 E8M0 scale bytes); 0 when d_c is not a multiple of 32."""
+    return int(load().mla_mxfp4_page_bytes(int(d_c), int(d_R)))
+
+
+# The quantized cache formats: page bytes and the library's append and decode calls.
+_QUANT = {"fp8": (fp8_page_bytes, "mla_append_kv_fp8", "mla_decode_paged_fp8"),
+          "mxfp4": (mxfp4_page_bytes, "mla_append_kv_mxfp4", "mla_decode_paged_mxfp4")}
+
+
+def cache_format(kv, d_c: int, d_R: int) -> str:
+    """"bf16" / "fp32" for row caches, "fp8" or "mxfp4" for uint8 pages (told apart by their
+    size: the two page sizes never coincide)."""
+    if kv.dtype != torch.uint8:
+        return "bf16" if kv.dtype == torch.bfloat16 else "fp32"
+    for fmt, (page_bytes, _, _) in _QUANT.items():
+        if kv.shape[1] == page_bytes(d_c, d_R):
+            return fmt
+    raise ValueError(f"uint8 pages of {kv.shape[1]} bytes are neither FP8 nor MXFP4 pages "
+                     f"for d_c {d_c}, d_R {d_R}")
+
+
+def _decode_paged_quant(fmt, q_abs, q_r, kv, page_table, seq_lens, cu_q, o_part, lse_part, *,
+                        d_hc, d_R, groups, rope, softmax_scale, causal, pages_per_split, stream):
+    page_bytes_fn, _, call = _QUANT[fmt]
     T, H, d_cg = q_abs.shape
-    P, page_bytes = kv_fp8.shape
+    P, page_bytes = kv.shape
     B, max_pages = page_table.shape
     S = o_part.shape[2]
     d_c = d_cg * groups
-    if kv_fp8.dtype != torch.uint8 or page_bytes != fp8_page_bytes(d_c, d_R):
-        raise ValueError("kv_fp8 must be uint8 [P, fp8_page_bytes(d_c, d_R)]")
+    if kv.dtype != torch.uint8 or page_bytes != page_bytes_fn(d_c, d_R):
+        raise ValueError(f"the {fmt} cache must be uint8 [P, {fmt}_page_bytes(d_c, d_R)]")
     if q_abs.dtype != torch.bfloat16 or q_r.dtype != torch.bfloat16:
-        raise TypeError("the FP8 cache decode takes bf16 queries")
+        raise TypeError(f"the {fmt} cache decode takes bf16 queries")
     if q_r.shape != (T, H, d_R):
         raise ValueError("q_r must be [T, H, d_R]")
     _expect("o_part", o_part, (T, H, S, d_cg), torch.bfloat16)
@@ -340,36 +366,73 @@ def decode_paged_fp8(q_abs, q_r, kv_fp8, page_table, seq_lens, cu_q, o_part, lse
     if seq_lens.shape != (B,) or cu_q.shape != (B + 1,):
         raise ValueError("seq_lens must be [B] and cu_q [B+1]")
     cos, sin, rope_max_pos = _rope_pair(rope, d_R, q_abs.device)
-    _dev(q_abs, q_r, kv_fp8, page_table, seq_lens, cu_q, o_part, lse_part, cos, sin)
-    _check("mla_decode_paged_fp8", load().mla_decode_paged_fp8(
-        _ptr(q_abs), _ptr(q_r), _ptr(kv_fp8), _ptr(page_table), _ptr(seq_lens), _ptr(cu_q),
+    _dev(q_abs, q_r, kv, page_table, seq_lens, cu_q, o_part, lse_part, cos, sin)
+    _check(call, getattr(load(), call)(
+        _ptr(q_abs), _ptr(q_r), _ptr(kv), _ptr(page_table), _ptr(seq_lens), _ptr(cu_q),
         _ptr(cos), _ptr(sin), rope_max_pos, _ptr(o_part), _ptr(lse_part),
         B, T, max_pages, P, H, groups, d_hc, d_c, d_R, 64, S, int(pages_per_split),
         float(softmax_scale), int(bool(causal)), _stream(stream)))
+
+
+def _append_kv_quant(fmt, c_kv_new, k_r_new, kv, page_table, seq_lens, cu_q, *, rope, stream):
+    page_bytes_fn, call, _ = _QUANT[fmt]
+    T, d_c = c_kv_new.shape
+    d_R = k_r_new.shape[1]
+    P, page_bytes = kv.shape
+    B, max_pages = page_table.shape
+    if k_r_new.shape[0] != T or c_kv_new.dtype != torch.bfloat16 or k_r_new.dtype != torch.bfloat16:
+        raise ValueError("c_kv_new [T, d_c] and k_r_new [T, d_R] must be bf16")
+    if kv.dtype != torch.uint8 or page_bytes != page_bytes_fn(d_c, d_R):
+        raise ValueError(f"the {fmt} cache must be uint8 [P, {fmt}_page_bytes(d_c, d_R)]")
+    for t in (page_table, seq_lens, cu_q):
+        if t.dtype != torch.int32:
+            raise TypeError(f"expected int32, got {t.dtype}")
+    if seq_lens.shape != (B,) or cu_q.shape != (B + 1,):
+        raise ValueError("seq_lens must be [B] and cu_q [B+1]")
+    cos, sin, rope_max_pos = _rope_pair(rope, d_R, kv.device)
+    _dev(c_kv_new, k_r_new, kv, page_table, seq_lens, cu_q, cos, sin)
+    _check(call, getattr(load(), call)(
+        _ptr(c_kv_new), _ptr(k_r_new), _ptr(kv), _ptr(page_table), _ptr(seq_lens), _ptr(cu_q),
+        _ptr(cos), _ptr(sin), rope_max_pos, B, T, max_pages, P, d_c, d_R, 64, _stream(stream)))
+
+
+def decode_paged_fp8(q_abs, q_r, kv_fp8, page_table, seq_lens, cu_q, o_part, lse_part, *,
+                     d_hc: int, d_R: int, groups: int = 1, rope: Optional[tuple] = None,
+                     softmax_scale: float = 0.0, causal: bool = True, pages_per_split: int = 0,
+                     stream=None) -> None:
+    """mla_decode_paged over an FP8 cache kv_fp8 (uint8 [P, fp8_page_bytes(d_c, d_R)]):
+    bf16 queries and partials, as mla_decode_paged."""
+    _decode_paged_quant("fp8", q_abs, q_r, kv_fp8, page_table, seq_lens, cu_q, o_part, lse_part,
+                        d_hc=d_hc, d_R=d_R, groups=groups, rope=rope, softmax_scale=softmax_scale,
+                        causal=causal, pages_per_split=pages_per_split, stream=stream)
+
+
+def decode_paged_mxfp4(q_abs, q_r, kv_fp4, page_table, seq_lens, cu_q, o_part, lse_part, *,
+                       d_hc: int, d_R: int, groups: int = 1, rope: Optional[tuple] = None,
+                       softmax_scale: float = 0.0, causal: bool = True, pages_per_split: int = 0,
+                       stream=None) -> None:
+    """mla_decode_paged over an MXFP4 cache kv_fp4 (uint8 [P, mxfp4_page_bytes(d_c, d_R)]):
+    bf16 queries and partials, as mla_decode_paged."""
+    _decode_paged_quant("mxfp4", q_abs, q_r, kv_fp4, page_table, seq_lens, cu_q, o_part, lse_part,
+                        d_hc=d_hc, d_R=d_R, groups=groups, rope=rope, softmax_scale=softmax_scale,
+                        causal=causal, pages_per_split=pages_per_split, stream=stream)
 
 
 def append_kv_fp8(c_kv_new, k_r_new, kv_fp8, page_table, seq_lens, cu_q, *,
                   rope: Optional[tuple] = None, stream=None) -> None:
     """Quantize the new tokens' latents into the FP8 cache kv_fp8 (uint8 [P, page bytes]):
     codes and scale per token, k_R rotated at its position and kept bf16."""
-    T, d_c = c_kv_new.shape
-    d_R = k_r_new.shape[1]
-    P, page_bytes = kv_fp8.shape
-    B, max_pages = page_table.shape
-    if k_r_new.shape[0] != T or c_kv_new.dtype != torch.bfloat16 or k_r_new.dtype != torch.bfloat16:
-        raise ValueError("c_kv_new [T, d_c] and k_r_new [T, d_R] must be bf16")
-    if kv_fp8.dtype != torch.uint8 or page_bytes != fp8_page_bytes(d_c, d_R):
-        raise ValueError("kv_fp8 must be uint8 [P, fp8_page_bytes(d_c, d_R)]")
-    for t in (page_table, seq_lens, cu_q):
-        if t.dtype != torch.int32:
-            raise TypeError(f"expected int32, got {t.dtype}")
-    if seq_lens.shape != (B,) or cu_q.shape != (B + 1,):
-        raise ValueError("seq_lens must be [B] and cu_q [B+1]")
-    cos, sin, rope_max_pos = _rope_pair(rope, d_R, kv_fp8.device)
-    _dev(c_kv_new, k_r_new, kv_fp8, page_table, seq_lens, cu_q, cos, sin)
-    _check("mla_append_kv_fp8", load().mla_append_kv_fp8(
-        _ptr(c_kv_new), _ptr(k_r_new), _ptr(kv_fp8), _ptr(page_table), _ptr(seq_lens), _ptr(cu_q),
-        _ptr(cos), _ptr(sin), rope_max_pos, B, T, max_pages, P, d_c, d_R, 64, _stream(stream)))
+    _append_kv_quant("fp8", c_kv_new, k_r_new, kv_fp8, page_table, seq_lens, cu_q, rope=rope,
+                     stream=stream)
+
+
+def append_kv_mxfp4(c_kv_new, k_r_new, kv_fp4, page_table, seq_lens, cu_q, *,
+                    rope: Optional[tuple] = None, stream=None) -> None:
+    """Quantize the new tokens' latents into the MXFP4 cache kv_fp4 (uint8 [P, page bytes]):
+    packed E2M1 codes and one E8M0 scale byte per 32 elements, k_R rotated at its position
+    and kept bf16."""
+    _append_kv_quant("mxfp4", c_kv_new, k_r_new, kv_fp4, page_table, seq_lens, cu_q, rope=rope,
+                     stream=stream)
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20
@@ -554,11 +617,14 @@ class DecodeStep:
         absorb_q(self.q_c, self.w_uk, self.q_abs, groups=self.groups, stream=stream)
 
     def attend(self, stream=None):
-        if self.kv.dtype == torch.uint8:  # FP8 cache pages
-            decode_paged_fp8(self.q_abs, self.q_r, self.kv, self.page_table, self.seq_lens, self.cu_q,
-                             self.o_part, self.lse_part, d_hc=self.d_hc, d_R=self.q_r.shape[2],
-                             groups=self.groups, rope=self.rope, causal=self.causal,
-                             pages_per_split=self.pages_per_split, stream=stream)
+        if self.kv.dtype == torch.uint8:  # FP8 or MXFP4 cache pages
+            d_R = self.q_r.shape[2]
+            fmt = cache_format(self.kv, self.q_abs.shape[2] * self.groups, d_R)
+            _decode_paged_quant(fmt, self.q_abs, self.q_r, self.kv, self.page_table, self.seq_lens,
+                                self.cu_q, self.o_part, self.lse_part, d_hc=self.d_hc, d_R=d_R,
+                                groups=self.groups, rope=self.rope, softmax_scale=0.0,
+                                causal=self.causal, pages_per_split=self.pages_per_split,
+                                stream=stream)
             return
         decode_paged(self.q_abs, self.q_r, self.kv, self.page_table, self.seq_lens, self.cu_q,
                      self.o_part, self.lse_part, d_hc=self.d_hc, groups=self.groups, rope=self.rope,

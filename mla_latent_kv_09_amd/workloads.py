@@ -294,6 +294,38 @@ def gather_sequence(w: Workload, b: int) -> np.ndarray:
     return bf16_bits_to_f32(pages) if w.cfg.dtype == "bf16" else pages.astype(np.float32)
 
 
+def mxfp4_pool(w: Workload, packed: Sequence, scales: Sequence, *, nan_fill: bool = True) -> np.ndarray:
+    """Place per-sequence MXFP4 latent codes (uint8 [L_b, d_c / 2], two per byte) and scale
+    bytes (uint8 [L_b, d_c / 32]) into MXFP4 cache pages laid out as {codes [64][d_c / 2] |
+    k_R [64][d_R] bf16 | scales [64][d_c / 32]}, the k_R rows taken from ``w``'s bf16
+    pool.  Pure data placement: the codes and scales are given.  Slots past a sequence's
+    end hold 0xFF codes (-6), NaN k_R and the out-of-format scale byte 255 when
+    ``nan_fill``.  Returns uint8 [P, 64 (d_c / 2 + 2 d_R + d_c / 32)]."""
+    cfg = w.cfg
+    if cfg.dtype != "bf16":
+        raise ValueError("MXFP4 pages take a bf16 workload's k_R rows")
+    ps, d_c, d_R = cfg.page_size, cfg.d_c, cfg.d_R
+    cb, sb = d_c // 2, d_c // 32
+    P = w.num_pool_pages
+    pool = np.zeros((P, ps * (cb + 2 * d_R + sb)), np.uint8)
+    code_part = pool[:, : ps * cb].reshape(P, ps, cb)
+    rope_part = pool[:, ps * cb: ps * (cb + 2 * d_R)].view(np.uint16).reshape(P, ps, d_R)
+    scale_part = pool[:, ps * (cb + 2 * d_R):].reshape(P, ps, sb)
+    if nan_fill:
+        code_part[...] = 0xFF
+        rope_part[...] = BF16_NAN_BITS
+        scale_part[...] = 0xFF
+    for b in range(len(w.seq_lens)):
+        L = int(w.seq_lens[b])
+        for k in range((L + ps - 1) // ps):
+            pg = int(w.page_table[b, k])
+            n = min(ps, L - k * ps)
+            code_part[pg, :n] = packed[b][k * ps: k * ps + n]
+            scale_part[pg, :n] = scales[b][k * ps: k * ps + n]
+            rope_part[pg, :n] = w.pool[pg, :n, d_c:]
+    return pool
+
+
 def fp8_pool(w: Workload, codes: Sequence, scales: Sequence, *, nan_fill: bool = True) -> np.ndarray:
     """Place per-sequence FP8 latent codes (uint8 [L_b, d_c]) and token scales (float32
     [L_b]) into FP8 cache pages laid out as {codes [64][d_c] | k_R [64][d_R] bf16 |
