@@ -11,18 +11,22 @@ base and element offsets that are whole 16-byte units.  The page gives no format
 that, so the format here is this library's reading, on the 8-bit float format gfx950
 converts natively:
 
-* Each token's 512-d latent c_KV is stored as 8-bit E4M3 codes with one float32 scale
-  per token: value = decode(code) * scale.  The 64-d RoPE key k_R stays bf16: it carries
-  position, and P3 §4 warns that reduced precision in the RoPE part is what breaks the
-  absorbed scores.
+* Each token's 512-d latent c_KV is stored as 8-bit E4M3 codes with one power-of-two
+  scale per token, kept in a float32 slot: value = decode(code) * scale.  The 64-d RoPE key
+  k_R stays bf16: it carries position, and P3 §4 warns that reduced precision in the RoPE
+  part is what breaks the absorbed scores.
 * E4M3 ("fn" variant, as in the OCP 8-bit float specification): 1 sign bit, 4 exponent
   bits with bias 7, 3 mantissa bits; exponent field 0 encodes subnormals m/8 * 2^-6;
   no infinities; 0x7F and 0xFF are NaN; the largest finite value is 448.
-* Quantization of a row x (its values exact in bf16): amax = max |x_i|;
-  scale = amax / 448 rounded once to float32 (1 when amax is 0); q_i = x_i / scale
-  rounded once to float32; code_i = the E4M3 value nearest to q_i, ties to the even
-  code, magnitudes past 448 saturating to 448.  The two divisions are taken in float32
-  because that is the precision the quantizing kernel decides the codes in.
+* Quantization of a row x (its values exact in bf16): amax = max |x_i|; scale = 2^e with
+  e the smallest integer such that amax <= 448 * 2^e, clamped to [-124, 117] (e = 0 for
+  an all-zero row); code_i = the E4M3 value nearest to x_i / scale (an exact quotient),
+  ties to the even code, magnitudes past 448 saturating to 448.  The scale is a power of
+  two so that every decode(code) * scale is exact in bf16: the decoding kernel converts
+  code and scale in one exact step.  E4M3's relative precision is the same in every
+  binade, so a power-of-two scale costs at most one binade at the low end of the range;
+  the row maximum lands in (224, 448].  The clamps keep 448 * scale below bf16's largest
+  value and every subnormal E4M3 value times the scale on bf16's subnormal grid.
 
 The decode over an FP8 cache is then the plain non-absorbed decode
 (``mla_oracle.mla_decode``) over the dequantized rows [decode(code) * scale | k_R].
@@ -68,16 +72,35 @@ def e4m3_round(x) -> np.ndarray:
     return np.where(np.isnan(x), np.uint8(E4M3_NAN), code).astype(np.uint8)
 
 
+SCALE_EXP_MIN, SCALE_EXP_MAX = -124, 117
+
+
+def scale_exponent(amax) -> np.ndarray:
+    """The smallest integer e with amax <= 448 * 2^e, clamped to [-124, 117]; 0 where amax
+    is 0.  amax is float64 here, so the comparisons are exact."""
+    amax = np.asarray(amax, dtype=np.float64)
+    pos = amax > 0
+    with np.errstate(divide="ignore"):
+        e = np.ceil(np.log2(np.where(pos, amax, E4M3_MAX) / E4M3_MAX))
+    # settle the rounding of log2 with exact comparisons against 448 * 2^e
+    e = np.where(E4M3_MAX * np.power(2.0, e) < amax, e + 1, e)
+    e = np.where(E4M3_MAX * np.power(2.0, e - 1) >= amax, e - 1, e)
+    e = np.clip(e, SCALE_EXP_MIN, SCALE_EXP_MAX)
+    return np.where(pos, e, 0).astype(np.int64)
+
+
 def quantize_rows(latent) -> tuple[np.ndarray, np.ndarray]:
     """Per-token E4M3 quantization of latent rows [n, d_c] (values exact in bf16):
-    (codes uint8 [n, d_c], scales float32 [n]) as defined in the module docstring."""
+    (codes uint8 [n, d_c], scales float32 [n], each a power of two) as defined in the
+    module docstring."""
     x = np.asarray(latent, dtype=np.float32)
-    amax = np.max(np.abs(x), axis=-1)
-    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    amax = np.max(np.abs(x), axis=-1).astype(np.float64)
+    e = scale_exponent(amax)
+    scale = np.power(2.0, e).astype(np.float32)
     codes = np.empty(x.shape, np.uint8)
     step = 4096  # rows at a time (the same arithmetic, in cache-sized pieces)
     for r in range(0, x.shape[0], step):
-        q = (x[r:r + step] / scale[r:r + step, None]).astype(np.float32)
+        q = x[r:r + step].astype(np.float64) / np.power(2.0, e[r:r + step])[:, None]
         codes[r:r + step] = e4m3_round(q)
     return codes, scale
 

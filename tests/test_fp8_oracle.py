@@ -68,30 +68,51 @@ def test_saturation_nan_and_signed_zero():
     assert list(f8.e4m3_round([-0.0, 0.0, -1e-30])) == [0x80, 0x00, 0x80]
 
 
-def test_quantized_row_maximum_lands_on_448_and_error_is_one_rounding():
+def test_scale_exponent_by_hand():
+    # smallest e with amax <= 448 * 2^e: 448 -> 0, 448.0001 -> 1, 224 -> -1, 224.5 -> 0,
+    # 1 -> -8 (448 / 256 = 1.75 >= 1), 1.75 -> -8, 1.76 -> -7; clamps at -124 and 117
+    amax = [448.0, 448.0001, 224.0, 224.5, 1.0, 1.75, 1.76, 2.0 ** -130, 2.0 ** 127, 0.0]
+    assert list(f8.scale_exponent(amax)) == [0, 1, -1, 0, -8, -8, -7, -124, 117, 0]
+
+
+def test_quantized_row_maximum_lands_in_224_448_and_error_is_one_rounding():
     rng = np.random.default_rng(1)
     x = rng.standard_normal((300, 512)).astype(np.float32)
     x[7] *= 1e-3
     x[8] *= 300.0
     codes, scale = f8.quantize_rows(x)
     assert codes.dtype == np.uint8 and scale.dtype == np.float32
+    m, e = np.frexp(scale.astype(np.float64))
+    assert np.all(m == 0.5)                                   # every scale a power of two
+    top = np.max(np.abs(x.astype(np.float64)), axis=1) / scale
+    assert np.all((top > 224) & (top <= 448))
     deq = f8.dequantize_rows(codes, scale)
-    assert np.array_equal(np.max(np.abs(f8.e4m3_value(codes)), axis=1), np.full(300, 448.0))
     # one rounding to 3 mantissa bits: at most half a unit in the last place, i.e.
     # 2^-4 of the value in the normal range, 2^-10 * scale below it (the subnormal step)
     err = np.abs(deq - x.astype(np.float64))
-    bound = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * scale[:, None].astype(np.float64)) * (1 + 1e-6)
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * scale[:, None].astype(np.float64))
     assert np.all(err <= bound)
     assert np.all(np.sign(deq) * np.sign(x) >= 0)
+    # planted mistake: the old amax / 448 scale is not a power of two, and a scale one
+    # binade too small saturates the row maximum
+    assert not np.all(np.frexp(np.max(np.abs(x), axis=1) / 448.0)[0] == 0.5)
+    assert np.any(top * 2 > 448)
 
 
-def test_zero_row_and_tiny_rows():
+def test_zero_row_tiny_and_huge_rows():
     codes, scale = f8.quantize_rows(np.zeros((2, 16), np.float32))
     assert np.all(codes == 0) and np.all(scale == 1.0)
     row = np.zeros((1, 16), np.float32)
-    row[0, 3] = -2.0 ** -100                   # single nonzero element: it becomes -448 * scale
+    row[0, 3] = -2.0 ** -100                   # one nonzero element: -256 * 2^-108
     codes, scale = f8.quantize_rows(row)
-    assert codes[0, 3] == 0xFE and f8.dequantize_rows(codes, scale)[0, 3] == pytest.approx(-2.0 ** -100)
+    assert scale[0] == 2.0 ** -108 and codes[0, 3] == 0xF8
+    assert f8.dequantize_rows(codes, scale)[0, 3] == -2.0 ** -100
+    row[0, 3] = 2.0 ** -133                    # below the clamp: scale 2^-124, the smallest
+    codes, scale = f8.quantize_rows(row)       # subnormal code 2^-9 (and bf16's smallest)
+    assert scale[0] == 2.0 ** -124 and codes[0, 3] == 0x01 and codes[0, 2] == 0
+    row[0, 3] = 3.0e38                         # past the upper clamp: saturates to 448
+    codes, scale = f8.quantize_rows(row)
+    assert scale[0] == 2.0 ** 117 and codes[0, 3] == 0x7E
 
 
 def test_dequantized_cache_rows_keep_the_rope_part():
