@@ -259,17 +259,18 @@ int mla_combine_up_v_fused(int heads, int groups, int d_hc, int d_c, int num_spl
  * no infinities):
  *   one page = { codes [64][d_c] uint8 E4M3 | k_R [64][d_R] bf16 | scale [64] float32 },
  *   mla_fp8_page_bytes(d_c, d_R) = 64 * (d_c + 2 d_R + 4) bytes (41216 for 512 / 64), pages
- *   back to back, a multiple of 16 bytes each.  Token j's latent is code_i * scale_j; its
- *   k_R stays bf16 (P3 §4: reduced RoPE precision is what breaks the absorbed scores).
+ *   back to back, a multiple of 16 bytes each.  Token j's latent is code_i * scale_j, the
+ *   scale a power of two kept in a float32 slot; its k_R stays bf16 (P3 §4: reduced RoPE
+ *   precision is what breaks the absorbed scores).
  */
 size_t mla_fp8_page_bytes(int d_c, int d_R);
 
 /*
  * mla_append_kv_fp8 -- mla_append_kv into an FP8 cache: the new token's latent row x gets
- * scale = amax / 448 (amax = max |x_i|; 1 for an all-zero row) and code_i = the E4M3 value
- * nearest to x_i / scale (ties to the even code, saturating at 448), both divisions
- * correctly rounded float32; k_R is rotated at the token's position and rounded to bf16
- * exactly as mla_append_kv does.  c_kv_new [T, d_c] and k_r_new [T, d_R] are bf16.
+ * scale = 2^e, e the smallest integer with amax <= 448 * 2^e (amax = max |x_i|), clamped
+ * to [-124, 117] (e = 0 for an all-zero row), and code_i = the E4M3 value nearest to
+ * x_i / scale (an exact quotient; ties to the even code, saturating at 448); k_R is rotated
+ * at the token's position and rounded to bf16 exactly as mla_append_kv does.  c_kv_new [T, d_c] and k_r_new [T, d_R] are bf16.
  * d_c and d_R must be multiples of 8 and at most 512 (MLA_ERR_UNSUPPORTED otherwise);
  * other arguments and errors as mla_append_kv.
  */
@@ -282,10 +283,10 @@ int mla_append_kv_fp8(const void* c_kv_new, const void* k_r_new, void* kv_cache,
 /*
  * mla_decode_paged_fp8 -- mla_decode_paged over an FP8 cache: same arguments, results
  * and split plan, with kv_cache the FP8 pages above, q_abs, q_r and o_part bf16 (the
- * storage type is bf16; there is no dtype argument).  The scores are
- * scale_j (q_abs . code_j) + RoPE(q_R) . k_R_j times softmax_scale, the output weights
- * are p_j scale_j: the result of mla_decode_paged on the dequantized rows.  The codes are
- * converted to bf16 exactly for the MFMAs.  Implemented for 128 heads, one latent group,
+ * storage type is bf16; there is no dtype argument): the result of mla_decode_paged on the
+ * dequantized rows [code * scale | k_R].  Each code times its token's scale is converted to
+ * bf16 exactly for the MFMAs; the scales must be powers of two, as the append writes them
+ * (other scales are outside the format and their results unspecified).  Implemented for 128 heads, one latent group,
  * d_c 512 and d_R 64 (MLA_ERR_UNSUPPORTED otherwise); MLA_KV_DECODE_KERNEL "mfma32-128" /
  * "mfma32-64" force one or two workgroups per (token, split).
  */

@@ -142,9 +142,11 @@ __device__ __forceinline__ uint32_t e4m3_from_f32(float x) {
 
 // FP8 cache append: one wave per new token row.  The page holds the latent codes
 // [64][d_c] (E4M3), then k_R [64][d_R] (bf16), then one float32 scale per token; the
-// row's latent gets scale = amax / 448 (1 for an all-zero row) and code_i =
-// e4m3(x_i / scale), both divisions correctly rounded fp32; k_R is rotated at the
-// token's position as in the bf16 append.  Lane l takes latent elements 8l .. 8l+7 and
+// row's latent gets scale = 2^e, e the smallest integer with amax <= 448 * 2^e clamped to
+// [-124, 117] (e = 0 for an all-zero row), and code_i = e4m3(x_i * 2^-e), an exact
+// product; k_R is rotated at the token's position as in the bf16 append.  With amax in
+// [2^k, 2^(k+1)) (k from its exponent field) e is k - 8 when amax <= 1.75 * 2^k = 448 * 2^(k-8)
+// and k - 7 otherwise; a subnormal amax takes the lower clamp.  Lane l takes latent elements 8l .. 8l+7 and
 // k_R elements 8l .. 8l+7 (the launcher requires d_c <= 512, d_R <= 512, both multiples
 // of 8).
 __global__ void __launch_bounds__(kBlock) append_kv_fp8_kernel(
@@ -186,13 +188,25 @@ __global__ void __launch_bounds__(kBlock) append_kv_fp8_kernel(
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-  const float scale = amax > 0.f ? __fdiv_rn(amax, 448.f) : 1.f;
+  int sexp = 0;  // e of scale = 2^e
+  if (amax > 0.f) {
+    const int E = static_cast<int>(__float_as_uint(amax) >> 23);  // amax >= 0: no sign bit
+    if (E == 0) {
+      sexp = -124;
+    } else {
+      const float lim = __uint_as_float(static_cast<uint32_t>(E) << 23) * 1.75f;  // 1.75 * 2^k, exact
+      sexp = amax <= lim ? E - 127 - 8 : E - 127 - 7;
+      sexp = sexp < -124 ? -124 : (sexp > 117 ? 117 : sexp);
+    }
+  }
+  const float scale = __uint_as_float(static_cast<uint32_t>(127 + sexp) << 23);
+  const float inv = __uint_as_float(static_cast<uint32_t>(127 - sexp) << 23);
   if (has_c) {
     uint32_t w0 = 0, w1 = 0;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      w0 |= e4m3_from_f32(__fdiv_rn(x[e], scale)) << (8 * e);
-      w1 |= e4m3_from_f32(__fdiv_rn(x[4 + e], scale)) << (8 * e);
+      w0 |= e4m3_from_f32(x[e] * inv) << (8 * e);
+      w1 |= e4m3_from_f32(x[4 + e] * inv) << (8 * e);
     }
     *reinterpret_cast<uint2*>(pg + static_cast<size_t>(slot) * d_c + 8 * lane) = uint2{w0, w1};
   }

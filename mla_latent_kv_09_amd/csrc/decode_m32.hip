@@ -38,16 +38,16 @@
 // a 512-byte bank row, and so does a transposing read (4 tokens x 4 chunks x 2 halves).
 // RoPE row t (128 B) holds chunk c at c ^ ((t >> 2) & 7); q_R of head n the same with n.
 //
-// FP8 cache (F8 = true; the quantized latent gather of nxmr.cn/news/151634, intro and §5,
+// FP8 cache (kFmtFp8; the quantized latent gather of nxmr.cn/news/151634, intro and §5,
 // on gfx950's E4M3 format): a page holds the latent codes [64][512] (E4M3, 32 KB), k_R
 // [64][64] (bf16, 8 KB) and one float32 scale per token (256 B), 41 KB in all.  The copies
-// land in an FP8 stage; once per page the four waves convert its codes to bf16 exactly
-// (v_cvt_scalef32_pk_bf16_fp8 with scale 1) into one stage of the bf16 form's layout and
-// move the page's k_R rows and scales beside them, so the score and output loops are the
-// bf16 form's.  The scale stays in float32: the latent part of each score is multiplied by
-// its token's scale before the RoPE K-steps accumulate on top, and P^T is multiplied by it
-// before the bf16 rounding.  LDS: the bf16 stage (72 KB), the scales, the FP8 stage (41 KB)
-// and q_R (16 KB); the copies of page i + 1 go out once page i is converted.
+// land in an FP8 stage; once per page the four waves convert each code times its token's
+// scale, a power of two, to bf16 exactly (v_cvt_scalef32_pk_bf16_fp8) into one stage of the
+// bf16 form's layout and move the page's k_R rows beside them, so the score and output
+// loops are the bf16 form's, with no scale work.  LDS: the bf16 stage (72 KB), the FP8 stage
+// (41 KB) and q_R (16 KB); the copies of page i + 1 go out once page i is converted.  The
+// MXFP4 cache (kFmtFp4: packed E2M1 codes, one power-of-two scale byte per 32 elements,
+// 25 KB pages) takes the same path with its own copies and conversion.
 #include <math.h>
 
 #include <type_traits>
@@ -90,11 +90,10 @@ constexpr int kR8Off = kC8Bytes;                  // k_R [64][64] bf16
 constexpr int kS8Off = kC8Bytes + kRBytes;        // scales [64] float32
 constexpr int kPage8Bytes = kS8Off + kTok * 4;    // 41216 B, the page stride in HBM
 constexpr int kCopies8 = 11;                      // global->LDS copies per wave and page
-// FP8 LDS: one bf16 stage (read by the loops), the page's scales, the FP8 stage the copies
-// land in (latent row t at 512 t, k_R and scales as in HBM, k_R rows swizzled as in the
-// bf16 stage), then q_R.  The 64-head form's final merge uses the first 130 KB.
-constexpr int kScaleOff8 = kStageBytes;
-constexpr int kQOff = kScaleOff8 + kTok * 4;
+// FP8 LDS: one bf16 stage (read by the loops), the FP8 stage the copies land in (latent row
+// t at 512 t, k_R and scales as in HBM, k_R rows swizzled as in the bf16 stage), then q_R.
+// The 64-head form's final merge uses the first 130 KB.
+constexpr int kQOff = kStageBytes;
 constexpr int kQrOff8 = kQOff + kPage8Bytes;
 constexpr int kMergeBytes = 4 * 32768 + kThreads * 8;
 constexpr int kLds8Bytes = kQrOff8 + kHeads * kDr * 2 > kMergeBytes ? kQrOff8 + kHeads * kDr * 2 : kMergeBytes;
@@ -109,8 +108,7 @@ constexpr int kR4Off = kC4Bytes;                       // k_R [64][64] bf16
 constexpr int kS4Off = kC4Bytes + kRBytes;             // scale bytes [64][16]
 constexpr int kPage4Bytes = kS4Off + kTok * kDc / 32;  // 25600 B, the page stride in HBM
 constexpr int kCopies4 = 7;                            // global->LDS copies per wave and page
-// MXFP4 LDS: the FP8 form's layout with the MXFP4 page in the quantized stage (the scale
-// slots beside the bf16 stage unused: the scales are applied in the conversion).
+// MXFP4 LDS: the FP8 form's layout with the MXFP4 page in the quantized stage.
 constexpr int kQrOff4 = kQOff + kPage4Bytes;
 constexpr int kLds4Bytes = kQrOff4 + kHeads * kDr * 2 > kMergeBytes ? kQrOff4 + kHeads * kDr * 2 : kMergeBytes;
 static_assert(kLds4Bytes <= 160 * 1024 && kPage4Bytes % 16 == 0, "MXFP4 stage layout");
@@ -197,15 +195,17 @@ __device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t
                : "memory", "m0");
 }
 
-// Exact E4M3 -> bf16 of the two codes in the low (kHi = false) or high 16 bits of v.
-// Inline asm: the builtin's bf16x2 result is split wrongly by the compiler.
+// E4M3 -> bf16 of the two codes in the low (kHi = false) or high 16 bits of v, times the
+// power of two `scale`: exact (code * 2^e has at most 4 significant bits and stays in bf16's
+// range for the scales the append writes).  Inline asm: the builtin's bf16x2 result is
+// split wrongly by the compiler.
 template <bool kHi>
-__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t v) {
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t v, float scale) {
   uint32_t r;
   if constexpr (kHi)
-    asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, 1.0 op_sel:[1,0,0]" : "=v"(r) : "v"(v));
+    asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, %2 op_sel:[1,0,0]" : "=v"(r) : "v"(v), "v"(scale));
   else
-    asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, 1.0" : "=v"(r) : "v"(v));
+    asm("v_cvt_scalef32_pk_bf16_fp8 %0, %1, %2" : "=v"(r) : "v"(v), "v"(scale));
   return r;
 }
 // FP8 form: copy `row` (0..10) of this wave's share of a page into the FP8 stage `f8`:
@@ -226,56 +226,62 @@ __device__ __forceinline__ void load_row8(uint32_t f8, const char* page, int n_v
     dma16(page, static_cast<uint32_t>(kR8Off + src_t * 128 + (((lane & 7) ^ ((t >> 2) & 7)) << 4)),
           f8 + kR8Off + t0 * 128);
   } else if (lane < 4) {
-    // Scales of tokens past n_valid may be anything: the softmax masks those tokens and
-    // their P entries are set to 0, not multiplied by the scale.
+    // Scales of tokens past n_valid may be anything: the conversion takes 1 for those rows.
     dma16(page, static_cast<uint32_t>(kS8Off + wave * 64 + 16 * lane), f8 + kS8Off + wave * 64);
   }
 }
 
 // FP8 form: the page in the FP8 stage becomes the bf16 stage at `base`.  Wave w takes
-// tokens 16w .. 16w+15: lane l converts codes 8l .. 8l+7 of each latent row (exactly) into
-// the 16-byte chunk l of that bf16 row, stored at its swizzled position l ^ f(t); the k_R
-// rows (already in the bf16 stage's order) and the scales are moved as they are.  Both
-// the 8-byte reads and the 16-byte writes meet distinct banks.
+// tokens 16w .. 16w+15: lane l converts codes 8l .. 8l+7 of each latent row times the
+// token's scale (exactly) into the 16-byte chunk l of that bf16 row, stored at its
+// swizzled position l ^ f(t); rows at or past n_valid (copies of token 0) take scale 1,
+// whatever their scale slot holds, so every row of the stage is finite.  The k_R rows
+// (already in the bf16 stage's order) are moved as they are.  Both the 8-byte reads and
+// the 16-byte writes meet distinct banks.
 template <int kBatch>
-__device__ __forceinline__ void convert_page8(uint32_t base, int wave, int lane) {
+__device__ __forceinline__ void convert_page8(uint32_t base, int wave, int lane, int n_valid) {
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
   typedef __attribute__((address_space(3))) u32x2 lds_u32x2_t;
   typedef __attribute__((address_space(3))) u32x4 lds_u32x4_t;
+  typedef __attribute__((address_space(3))) float lds_f32_t;
   const uint32_t f8 = base + kQOff;
   const uint32_t src = f8 + static_cast<uint32_t>(wave * 16 * kDc + 8 * lane);
+  const uint32_t ssrc = f8 + static_cast<uint32_t>(kS8Off + wave * 64);
   // token 16w + r: swz_f(16w + r) = swz_f(r) | 16 (w & 1), swz_f(r) < 16
   const uint32_t dst = base + static_cast<uint32_t>(wave * 16 * 1024) +
                        (static_cast<uint32_t>(lane ^ (16 * (wave & 1))) << 4);
-  // The reads of kBatch code rows (with one batch, the k_R rows and the scales too), then
-  // their conversions and writes, so that the LDS latency is paid once per batch.  (The
-  // 64-head form takes two batches and moves k_R and the scales after them: it has fewer
-  // registers to spare here.)
+  // The reads of kBatch code rows and their scales (with one batch, the k_R rows too), then
+  // the conversions and writes, so that the LDS latency is paid once per batch.  (The
+  // 64-head form takes two batches and moves k_R after them: it has fewer registers to
+  // spare here.)
   const uint32_t kr_off = static_cast<uint32_t>(wave * 2048 + 16 * lane);
-  const uint32_t sc_off = static_cast<uint32_t>(wave * 64 + 16 * (lane & 3));
+  const int lim = n_valid - 16 * wave;  // row r of this wave is a key iff r < lim
 #pragma unroll
   for (int r0 = 0; r0 < 16; r0 += kBatch) {
     const bool last = kBatch == 16;
     u32x2 raw[kBatch];
-    u32x4 kr0, kr1, sc;
+    float sc[kBatch];
+    u32x4 kr0, kr1;
 #pragma unroll
-    for (int r = 0; r < kBatch; ++r) raw[r] = *(const lds_u32x2_t*)(uintptr_t)(src + (r0 + r) * kDc);
+    for (int r = 0; r < kBatch; ++r) {
+      raw[r] = *(const lds_u32x2_t*)(uintptr_t)(src + (r0 + r) * kDc);
+      sc[r] = *(const lds_f32_t*)(uintptr_t)(ssrc + 4 * (r0 + r));
+    }
     if (last) {
       kr0 = *(const lds_u32x4_t*)(uintptr_t)(f8 + kR8Off + kr_off);
       kr1 = *(const lds_u32x4_t*)(uintptr_t)(f8 + kR8Off + kr_off + 1024);
-      sc = *(const lds_u32x4_t*)(uintptr_t)(f8 + kS8Off + sc_off);
     }
 #pragma unroll
     for (int r = 0; r < kBatch; ++r) {
-      const u32x4 v{fp8x2_to_bf16x2<false>(raw[r][0]), fp8x2_to_bf16x2<true>(raw[r][0]),
-                    fp8x2_to_bf16x2<false>(raw[r][1]), fp8x2_to_bf16x2<true>(raw[r][1])};
+      const float s = r0 + r < lim ? sc[r] : 1.f;
+      const u32x4 v{fp8x2_to_bf16x2<false>(raw[r][0], s), fp8x2_to_bf16x2<true>(raw[r][0], s),
+                    fp8x2_to_bf16x2<false>(raw[r][1], s), fp8x2_to_bf16x2<true>(raw[r][1], s)};
       *(lds_u32x4_t*)(uintptr_t)((dst + (r0 + r) * 1024) ^ (swz_f(r0 + r) << 4)) = v;
     }
     if (last) {
       *(lds_u32x4_t*)(uintptr_t)(base + kCBytes + kr_off) = kr0;
       *(lds_u32x4_t*)(uintptr_t)(base + kCBytes + kr_off + 1024) = kr1;
-      if (lane < 4) *(lds_u32x4_t*)(uintptr_t)(base + kScaleOff8 + sc_off) = sc;
     }
   }
   if constexpr (kBatch < 16) {
@@ -283,8 +289,6 @@ __device__ __forceinline__ void convert_page8(uint32_t base, int wave, int lane)
     for (int j = 0; j < 2; ++j)
       *(lds_u32x4_t*)(uintptr_t)(base + kCBytes + kr_off + 1024 * j) =
           *(const lds_u32x4_t*)(uintptr_t)(f8 + kR8Off + kr_off + 1024 * j);
-    if (lane < 4)
-      *(lds_u32x4_t*)(uintptr_t)(base + kScaleOff8 + sc_off) = *(const lds_u32x4_t*)(uintptr_t)(f8 + kS8Off + sc_off);
   }
 }
 
@@ -537,7 +541,7 @@ decode_m32_kernel(DecodeArgs a) {
     __syncthreads();  // ... and every wave's; the stage of the previous page is free again
     if constexpr (Q) {
       if constexpr (F8)
-        convert_page8<HS == 1 ? 16 : 8>(smem_base, wave, lane);
+        convert_page8<HS == 1 ? 16 : 8>(smem_base, wave, lane, n_valid);
       else
         convert_page4<HS == 1 ? 16 : 8>(smem_base, wave, lane);
       __syncthreads();  // the bf16 stage is complete and the quantized stage free again
@@ -556,43 +560,6 @@ decode_m32_kernel(DecodeArgs a) {
     const uint32_t next_base = Q ? smem_base + kQOff : smem_base + (stage ^ 1) * kStageBytes;
     const uint32_t st_base = smem_base + stage * kStageBytes;
     const uint32_t sb = opaque(st_base + s_lane);
-    // FP8: the latent part of each score times its token's scale (s[mb] holds block mb of
-    // HS = 1, this wave's block of HS = 2 in s[0]), once the latent chains have ended; the
-    // pad gives the wait states between these vector-ALU writes and the MFMAs that then read
-    // them as srcC.
-    auto scale_latent = [&](f32x16 (&acc)[2]) {
-      auto scale_read = [&](int mb, int g) {
-        return *(const lds_f32x4_t*)(uintptr_t)(
-            smem_base + kScaleOff8 + 4 * (32 * (HS == 1 ? mb : th) + 8 * g + 4 * h));
-      };
-      if constexpr (HS == 1) {
-        f32x4 sc[2][4];  // read before the pad, so that their latency hides under it
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) sc[mb][g] = scale_read(mb, g);
-        __builtin_amdgcn_sched_barrier(0);
-        mfma_results_ready(acc[0], acc[1]);
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-          for (int g = 0; g < 4; ++g)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[mb][4 * g + i] *= sc[mb][g][i];
-      } else {  // (the 64-head form has no registers to hold them across the pad)
-        mfma_results_ready(acc[0], acc[1]);
-        acc[0] += acc[1];
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x4 sc = scale_read(0, g);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[0][4 * g + i] *= sc[i];
-        }
-      }
-      asm volatile("s_nop 7" : "+v"(acc[0]), "+v"(acc[1]));
-      __builtin_amdgcn_sched_barrier(0);
-    };
-
     // ---- scores.  HS = 1: the latent steps, then the RoPE steps, the two 32-token blocks
     // alternating.  HS = 2: this wave's one 32-token block, two chains over alternate
     // K-steps (summed below); bf16: RoPE steps first, FP8: after the latent steps.
@@ -611,31 +578,24 @@ decode_m32_kernel(DecodeArgs a) {
       constexpr int kRing = 4;
       bf16x8 ring[kRing];
       if constexpr (HS == 2) {
-        // The 32 latent steps of this wave's block through a ring of reads, the two chains
-        // over alternate K-steps, the copies on the odd steps; the RoPE steps first (bf16) or
-        // after the scale (FP8).
-        auto rope_steps = [&]() {
+        // RoPE steps first, then the 32 latent steps of this wave's block through a ring of
+        // reads, the two chains over alternate K-steps; the copies go with the odd steps.
 #pragma unroll
-          for (int rs = 0; rs < kRSteps; ++rs) {
-            const bf16x8 qrf = qr_frag(rs);
-            const bf16x8 cf = rope_frag(rs, th);
-            if (F8 ? rs == 1 : rs < 2)
-              mfma32_first(s[rs & 1], cf, qrf);
-            else
-              mfma32_acc(s[rs & 1], cf, qrf);
-          }
-        };
-        if constexpr (!F8) rope_steps();
+        for (int rs = 0; rs < kRSteps; ++rs) {
+          const bf16x8 qrf = qr_frag(rs);
+          const bf16x8 cf = rope_frag(rs, th);
+          if (rs < 2)
+            mfma32_first(s[rs & 1], cf, qrf);
+          else
+            mfma32_acc(s[rs & 1], cf, qrf);
+        }
 #pragma unroll
         for (int st = 0; st < kRing; ++st) ring[st] = lat_frag(st, th);
 #pragma unroll
         for (int st = 0; st < kQSteps; ++st) {
           const bf16x8 cf = ring[st % kRing];
           if (st + kRing < kQSteps) ring[st % kRing] = lat_frag(st + kRing, th);
-          if (F8 && st < 2)
-            mfma32_first(s[st & 1], cf, q[st]);
-          else
-            mfma32_acc(s[st & 1], cf, q[st]);
+          mfma32_acc(s[st & 1], cf, q[st]);
           if ((st & 1) == 1 && has_next) {
             if constexpr (F8) {  // the 11 copies of the next FP8 page
               if ((st >> 1) < kCopies8)
@@ -647,10 +607,6 @@ decode_m32_kernel(DecodeArgs a) {
               load_row(next_base, next_page, next_valid, wave, static_cast<int>(opaque(lane)), st >> 1);
             }
           }
-        }
-        if constexpr (F8) {
-          scale_latent(s);
-          rope_steps();
         }
       } else {
         // The 64 latent (ks, mb) steps, then the 8 RoPE (rs, mb) steps, all through one
@@ -762,7 +718,6 @@ decode_m32_kernel(DecodeArgs a) {
             mfma32_acc(s[st & 1], cf, q[st >> 1]);
           copy_part(st);
         }
-        if constexpr (F8) scale_latent(s);
 #pragma unroll
         for (int st = kLat; st < kSteps; ++st) {
           const bf16x8 cf = ring[st % kRing];
@@ -818,22 +773,6 @@ decode_m32_kernel(DecodeArgs a) {
         psum += p;
       }
     l_run += psum;
-    if constexpr (F8) {
-      // P^T times each token's scale (the latent rows are code * scale); tokens past the
-      // page's keys get 0 whatever their scale slot holds.  The scales are read again
-      // (an empty asm on the address), not kept in registers from the score phase.
-      const uint32_t scb = opaque(smem_base + kScaleOff8);
-#pragma unroll
-      for (int mb = 0; mb < kBlocks; ++mb)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int tok = 32 * (HS == 1 ? mb : th) + 8 * g + 4 * h;
-          const f32x4 sc = *(const lds_f32x4_t*)(uintptr_t)(scb + 4 * tok);
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-            s[mb][4 * g + i] = tok + i < n_valid ? s[mb][4 * g + i] * sc[i] : 0.f;
-        }
-    }
 
     // ---- P^T operands: K-step kq = 2 mb + q holds elements 8q .. 8q+7 of block mb
     constexpr int kKQ = 4 / HS;  // 16-token K-steps of the output
