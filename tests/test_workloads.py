@@ -73,3 +73,41 @@ def test_config_table_shapes():
     assert [c[k].row for k in wl.CONFIG_ORDER] == [80, 576, 576, 576, 576]
     assert c["gla2_b32_l16384"].d_cg == 256 and c["gla2_b32_l16384"].heads // 2 == 64
     assert c["long_b16_l65536"].batch * c["long_b16_l65536"].seq_len * 576 * 2 == 1_207_959_552
+
+
+def test_quantized_pool_placement():
+    """fp8_pool and mxfp4_pool place given per-sequence codes and scales (here arbitrary
+    bytes) into their page layouts: every key slot holds its token's codes, scale and the
+    bf16 pool's k_R row; slots past a sequence's end hold the fill."""
+    cfg = wl.CONFIGS["dsv3_b16_l4096"].replace(batch=3, seq_len=None, seq_len_range=(1, 200))
+    w = wl.make_workload(cfg)
+    rng = np.random.default_rng(7)
+    d_c, d_R, ps = cfg.d_c, cfg.d_R, cfg.page_size
+    lens = [int(L) for L in w.seq_lens]
+    for fmt in ("fp8", "mxfp4"):
+        if fmt == "fp8":
+            cb, sb = d_c, 4
+            codes = [rng.integers(0, 0x7F, (L, cb), dtype=np.uint8) for L in lens]
+            scales = [rng.standard_normal(L).astype(np.float32) for L in lens]
+            pool = wl.fp8_pool(w, codes, scales)
+        else:
+            cb, sb = d_c // 2, d_c // 32
+            codes = [rng.integers(0, 256, (L, cb), dtype=np.uint8) for L in lens]
+            scales = [rng.integers(1, 255, (L, sb), dtype=np.uint8) for L in lens]
+            pool = wl.mxfp4_pool(w, codes, scales)
+        P = w.num_pool_pages
+        assert pool.shape == (P, ps * (cb + 2 * d_R + sb))
+        code_part = pool[:, : ps * cb].reshape(P, ps, cb)
+        rope_part = pool[:, ps * cb: ps * (cb + 2 * d_R)].view(np.uint16).reshape(P, ps, d_R)
+        scale_part = pool[:, ps * (cb + 2 * d_R):].reshape(P, ps, sb)
+        for b, L in enumerate(lens):
+            for t in range(L):
+                pg, slot = int(w.page_table[b, t // ps]), t % ps
+                assert np.array_equal(code_part[pg, slot], codes[b][t])
+                assert np.array_equal(scale_part[pg, slot].view(np.uint8),
+                                      np.atleast_1d(scales[b][t]).view(np.uint8))
+                assert np.array_equal(rope_part[pg, slot], w.pool[pg, slot, d_c:])
+            if L % ps:
+                pg = int(w.page_table[b, (L - 1) // ps])
+                assert np.all(code_part[pg, L % ps:] == (0x7F if fmt == "fp8" else 0xFF))
+                assert np.all(rope_part[pg, L % ps:] == wl.BF16_NAN_BITS)
