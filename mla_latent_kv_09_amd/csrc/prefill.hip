@@ -155,14 +155,20 @@ decompress_kernel(PrefillArgs a) {
       }
     }
     // Row 32 mb + 8 (r / 4) + 4 hh + r % 4, column 32 cb + n: 32 lanes write 64 contiguous bytes.
+    // The page's base (uniform) and the row offsets (compile-time multiples of the uniform
+    // row stride) are scalar; each lane adds one fixed 32-bit offset.
     const int phys = clamp_page(ptab[p], a.num_pool_pages);
+    const size_t row_elems = static_cast<size_t>(a.heads) * kDhc;
+    __bf16* page_out = reinterpret_cast<__bf16*>(ws) + static_cast<size_t>(phys) * kTok * row_elems +
+                       static_cast<size_t>(h) * kDhc + 32 * cb;
+    const uint32_t lane_off = static_cast<uint32_t>(4 * hh) * static_cast<uint32_t>(row_elems) +
+                              static_cast<uint32_t>(n);
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = 32 * mb + 8 * (r >> 2) + 4 * hh + (r & 3);
-        const size_t idx = ((static_cast<size_t>(phys) * kTok + row) * a.heads + h) * kDhc + 32 * cb + n;
-        reinterpret_cast<__bf16*>(ws)[idx] = static_cast<__bf16>(acc[mb][r]);
+        const int c = 32 * mb + 8 * (r >> 2) + (r & 3);  // the row less 4 hh
+        page_out[static_cast<size_t>(c) * row_elems + lane_off] = static_cast<__bf16>(acc[mb][r]);
       }
     stage ^= 1;
   }
@@ -305,6 +311,21 @@ prefill_attn_kernel(PrefillArgs a) {
   const int li = lane & 15, lg = lane >> 4;
   const int tv = 4 * (lg >> 1) + (li >> 2);            // key within an 8-key group
   const uint32_t vpart = static_cast<uint32_t>(8 * (li & 1));
+  // The swizzle of key 32 mb + n is that of key n, and the V^T swizzle depends only on tv,
+  // so mb, qq and pp shift an address by a constant (the LDS offset field): one lane part
+  // per K-step of K (8), of k_R (4) and per column block of V (4).
+  uint32_t k_off[8], r_off[4], v_off[4];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks)
+    k_off[ks] = static_cast<uint32_t>(n * 256 + (((2 * ks + hh) ^ swz_k(n)) << 4));
+#pragma unroll
+  for (int rs = 0; rs < 4; ++rs)
+    r_off[rs] = static_cast<uint32_t>(2 * kKBytes + n * 128 + (((2 * rs + hh) ^ swz_r(n)) << 4));
+#pragma unroll
+  for (int nb = 0; nb < 4; ++nb) {
+    const int c = 4 * nb + 2 * (lg & 1) + ((li & 3) >> 1);
+    v_off[nb] = static_cast<uint32_t>(kKBytes + tv * 256 + ((c ^ swz_v(tv)) << 4)) + vpart;
+  }
   int stage = 0;
   for (int p = 0; p < n_pages; ++p) {
     __builtin_amdgcn_s_waitcnt(0x0f70);
@@ -319,16 +340,14 @@ prefill_attn_kernel(PrefillArgs a) {
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        const int key = 32 * mb + n;
-        const bf16x8 kf = lds_read8(st + key * 256 + (((2 * ks + hh) ^ swz_k(key)) << 4));
+        const bf16x8 kf = lds_read8(st + k_off[ks] + 32 * 256 * mb);
         s[mb] = mfma32(kf, q[ks], s[mb]);
       }
 #pragma unroll
     for (int rs = 0; rs < 4; ++rs)
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb) {
-        const int key = 32 * mb + n;
-        const bf16x8 rf = lds_read8(st + 2 * kKBytes + key * 128 + (((2 * rs + hh) ^ swz_r(key)) << 4));
+        const bf16x8 rf = lds_read8(st + r_off[rs] + 32 * 128 * mb);
         s[mb] = mfma32(rf, q[8 + rs], s[mb]);
       }
 
@@ -386,6 +405,9 @@ prefill_attn_kernel(PrefillArgs a) {
     }
 
     // ---- O[32 queries x 128] += P . V
+    uint32_t vb[4];  // opaque, so the row constants below stay in the offset field
+#pragma unroll
+    for (int nb = 0; nb < 4; ++nb) vb[nb] = opaque(st + v_off[nb]);
 #pragma unroll
     for (int kq = 0; kq < 4; ++kq) {
       const int mb = kq >> 1, qq = kq & 1;
@@ -394,9 +416,7 @@ prefill_attn_kernel(PrefillArgs a) {
         bf16x4 part[2];
 #pragma unroll
         for (int pp = 0; pp < 2; ++pp) {
-          const int key = 32 * mb + 16 * qq + 8 * pp + tv;
-          const int c = 4 * nb + 2 * (lg & 1) + ((li & 3) >> 1);
-          const uint32_t addr = st + kKBytes + key * 256 + ((c ^ swz_v(key)) << 4) + vpart;
+          const uint32_t addr = vb[nb] + (32 * mb + 16 * qq + 8 * pp) * 256;
           part[pp] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)(uintptr_t)addr);
         }
         const bf16x8 vf = __builtin_shufflevector(part[0], part[1], 0, 1, 2, 3, 4, 5, 6, 7);
