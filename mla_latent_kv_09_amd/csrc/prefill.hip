@@ -64,6 +64,12 @@ __device__ __forceinline__ void dma16(const char* sbase, uint32_t voff, uint32_t
                : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(voff), "s"(sbase)
                : "memory", "m0");
 }
+// A page-table entry read through the constant address space.  The table is not written
+// while these kernels run, and there a uniform index gives a scalar load, whose wait does
+// not also wait for the copies in flight (vector loads and copies share one counter).
+__device__ __forceinline__ int32_t table_entry(const int32_t* t, int i) {
+  return ((const __attribute__((address_space(4))) int32_t*)t)[i];
+}
 __device__ __forceinline__ f32x16 mfma32(const bf16x8& a, const bf16x8& b, const f32x16& c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -97,10 +103,12 @@ __global__ void __launch_bounds__(kDecThreads) __attribute__((amdgpu_waves_per_e
 decompress_kernel(PrefillArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int L = static_cast<int>(blockIdx.x);
-  const int h = L % a.heads;
-  const int u = L / a.heads;
+  // Uniform values computed by VALU divisions, moved to scalar registers so that the page
+  // table is read with scalar loads (a vector load's wait would also wait for the copies).
+  const int h = __builtin_amdgcn_readfirstlane(L % a.heads);
+  const int u = __builtin_amdgcn_readfirstlane(L / a.heads);
   const int runs = (a.max_pages + a.dec_pages - 1) / a.dec_pages;
-  const int b = u / runs, run = u - b * runs;
+  const int b = __builtin_amdgcn_readfirstlane(u / runs), run = u - b * runs;
   const int cap = a.max_pages * kTok;
   int len = a.seq_lens[b];
   len = len < 0 ? 0 : (len > cap ? cap : len);
@@ -122,8 +130,8 @@ decompress_kernel(PrefillArgs a) {
   const int32_t* ptab = a.page_table + static_cast<size_t>(b) * a.max_pages;
   const uint32_t smem_base = lds_addr(smem);
   // Rows 8 w .. 8 w + 7 of a page are this wave's copies (one 1 KB latent row each).
-  auto copy_page = [&](int p, uint32_t stage) {
-    const int id = clamp_page(ptab[p], a.num_pool_pages);
+  auto page_id = [&](int p) { return clamp_page(table_entry(ptab, p), a.num_pool_pages); };
+  auto copy_page = [&](int p, int id, uint32_t stage) {
     const char* page = kv + static_cast<size_t>(id) * kTok * kRowBytes;
     const int nv = min(kTok, len - p * kTok);
 #pragma unroll
@@ -134,7 +142,10 @@ decompress_kernel(PrefillArgs a) {
             stage + t * 1024);
     }
   };
-  copy_page(p0, smem_base);
+  // Page ids are read one page ahead of their copies; the stores of page p reuse its id.
+  int id_cur = page_id(p0);
+  copy_page(p0, id_cur, smem_base);
+  int id_next = p0 + 1 < p1 ? page_id(p0 + 1) : 0;
   const uint32_t s_lane = static_cast<uint32_t>(n * 1024) | ((swz_f(n) ^ static_cast<uint32_t>(hh)) << 4);
   char* ws = static_cast<char*>(a.workspace) +
              (part ? static_cast<size_t>(a.num_pool_pages) * kTok * a.heads * kDhc * 2 : 0);
@@ -143,7 +154,8 @@ decompress_kernel(PrefillArgs a) {
     __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): this wave's copies of page p landed
     __syncthreads();                     // ... and every wave's; the other stage is free
     const uint32_t st = smem_base + stage * kDecStage;
-    if (p + 1 < p1) copy_page(p + 1, smem_base + (stage ^ 1) * kDecStage);
+    if (p + 1 < p1) copy_page(p + 1, id_next, smem_base + (stage ^ 1) * kDecStage);
+    const int id_after = p + 2 < p1 ? page_id(p + 2) : 0;
     f32x16 acc[2] = {};
     const uint32_t sb = opaque(st + s_lane);
 #pragma unroll
@@ -154,10 +166,18 @@ decompress_kernel(PrefillArgs a) {
         acc[mb] = mfma32(lds_read8(addr), wreg[ks], acc[mb]);
       }
     }
+    // Keep eight reads in flight ahead of the products.
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 2 * kDc / 16 - 8; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
     // Row 32 mb + 8 (r / 4) + 4 hh + r % 4, column 32 cb + n: 32 lanes write 64 contiguous bytes.
     // The page's base (uniform) and the row offsets (compile-time multiples of the uniform
     // row stride) are scalar; each lane adds one fixed 32-bit offset.
-    const int phys = clamp_page(ptab[p], a.num_pool_pages);
+    const int phys = id_cur;
     const size_t row_elems = static_cast<size_t>(a.heads) * kDhc;
     __bf16* page_out = reinterpret_cast<__bf16*>(ws) + static_cast<size_t>(phys) * kTok * row_elems +
                        static_cast<size_t>(h) * kDhc + 32 * cb;
@@ -170,6 +190,8 @@ decompress_kernel(PrefillArgs a) {
         const int c = 32 * mb + 8 * (r >> 2) + (r & 3);  // the row less 4 hh
         page_out[static_cast<size_t>(c) * row_elems + lane_off] = static_cast<__bf16>(acc[mb][r]);
       }
+    id_cur = id_next;
+    id_next = id_after;
     stage ^= 1;
   }
 }
@@ -221,7 +243,9 @@ prefill_attn_kernel(PrefillArgs a) {
   // (XCD, engine) slot sees every block length in turn (9 is coprime to n_qb's factors of 2).
   const int pair = L / n_qb;
   const int qb = (L % n_qb + 9 * pair) % n_qb;
-  const int h = pair % a.heads, b = pair / a.heads;
+  // Scalar registers for these uniform values (see the decompression kernel).
+  const int h = __builtin_amdgcn_readfirstlane(pair % a.heads);
+  const int b = __builtin_amdgcn_readfirstlane(pair / a.heads);
   const int q0 = a.cu_q[b], q1 = a.cu_q[b + 1];
   const int q_len = q1 - q0;
   if (qb * kQBlock >= q_len) return;
@@ -277,8 +301,8 @@ prefill_attn_kernel(PrefillArgs a) {
   const uint32_t smem_base = lds_addr(smem);
   // Copies of page p: K and V rows 16 w .. 16 w + 15 (4 rows of 256 B per instruction),
   // k_R rows 16 w .. +15 (8 rows of 128 B per instruction): 10 per wave.
-  auto copy_page = [&](int p, uint32_t st) {
-    const int id = clamp_page(ptab[p], a.num_pool_pages);
+  auto page_id = [&](int p) { return clamp_page(table_entry(ptab, p), a.num_pool_pages); };
+  auto copy_page = [&](int id, uint32_t st) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t0 = 16 * wave + 4 * r;
@@ -298,7 +322,8 @@ prefill_attn_kernel(PrefillArgs a) {
             st + 2 * kKBytes + t0 * 128);
     }
   };
-  if (n_pages > 0) copy_page(0, smem_base);
+  if (n_pages > 0) copy_page(page_id(0), smem_base);
+  int id_next = n_pages > 1 ? page_id(1) : 0;  // ids are read one page ahead of their copies
 
   const float scale_log2 = a.scale * kLog2e;
   float m_ref = -INFINITY, l_run = 0.f;
@@ -331,7 +356,8 @@ prefill_attn_kernel(PrefillArgs a) {
     __builtin_amdgcn_s_waitcnt(0x0f70);
     __syncthreads();
     const uint32_t st = smem_base + stage * kAttStage;
-    if (p + 1 < n_pages) copy_page(p + 1, smem_base + (stage ^ 1) * kAttStage);
+    if (p + 1 < n_pages) copy_page(id_next, smem_base + (stage ^ 1) * kAttStage);
+    id_next = p + 2 < n_pages ? page_id(p + 2) : 0;
     const int j0 = p * kTok;
 
     // ---- scores
@@ -350,6 +376,14 @@ prefill_attn_kernel(PrefillArgs a) {
         const bf16x8 rf = lds_read8(st + r_off[rs] + 32 * 128 * mb);
         s[mb] = mfma32(rf, q[8 + rs], s[mb]);
       }
+    // Keep six reads in flight ahead of the products.
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);
+#pragma unroll
+    for (int i = 0; i < 18; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, 6, 0);
 
     // ---- softmax.  s[mb][r] is key j0 + 32 mb + 8 (r / 4) + 4 hh + r % 4 of query n.
     const bool partial = j0 + kTok > vis;
