@@ -56,7 +56,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_decode.json")
 CSRC = os.path.join(ROOT, "mla_latent_kv_09_amd", "csrc")
 KERNEL_SRC = {"decode_mfma_kernel": "decode_mfma.hip", "decode_m32_kernel": "decode_m32.hip",
               "decode_m32_kernel_fp8": "decode_m32.hip", "decode_m32_kernel_mxfp4": "decode_m32.hip",
-              "decode_generic_kernel": "kernels_generic.hip"}
+              "decode_generic_kernel": "kernels_generic.hip",
+              "prefill_attn_kernel": "prefill.hip", "decompress_kernel": "prefill.hip"}
 
 
 def cache_row_bytes(cfg, kv_dtype="bf16"):
@@ -100,9 +101,9 @@ def source_hash(path):
 
 
 def measured_traffic(kernel, workload, splits):
-    """HBM bytes per decode launch from committed rocprofv3 counters (one record per
-    kernel and workload), if they were taken on this kernel, its current source, this
-    workload and this split count."""
+    """HBM bytes per launch from committed rocprofv3 counters (one record per kernel and
+    workload), if they were taken on this kernel, its current source, this workload and
+    this split count (1 for the prefill kernels, which do not split)."""
     try:
         with open(TRAFFIC_FILE) as f:
             recs = json.load(f).get("records", [])
@@ -570,10 +571,12 @@ def prefill_bench(args, w, torch, harness, mla, stream):
         "kernel_ms": parts, "wall_s_timed_region": wall,
         "seqs_per_s": cfg.batch / (ms * 1e-3),
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,
+                     "traffic": measured_traffic("prefill_attn_kernel", cfg.name, 1),
                      "kernel": "prefill_attn_kernel", "kernel_ms": t_att, "algorithmic_flops": att},
         "decompress": {"ms": parts["decompress_kv"], "algorithmic_flops": dec,
                        "tflops": dec / (parts["decompress_kv"] * 1e-3) / 1e12,
+                       "traffic": measured_traffic("decompress_kernel", cfg.name, 1),
                        "workspace_bytes": ws_bytes, "latent_kv_bytes": kv_bytes},
         "absorbed_branch": {"ms_per_step": abs_ms, "algorithmic_flops": abs_att + abs_proj,
                             "speedup_of_dispatch": abs_ms / ms},
