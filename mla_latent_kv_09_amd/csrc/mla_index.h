@@ -200,4 +200,14 @@ __host__ __device__ inline Unit unit_m32(int L, int S, int q0, int nq, int T) {
   return u;
 }
 
+// Logical index of workgroup j in a grid of G that numbers each XCD's workgroups
+// consecutively.  The dispatcher deals workgroup j to XCD j mod 8, so XCD x receives
+// G / 8 workgroups, plus one if x < G mod 8.  It takes logical indices base_x, base_x + 1,
+// ... in its dispatch order, with base_x = x (G / 8) + min(x, G mod 8).  A bijection of
+// [0, G).
+__host__ __device__ inline int xcd_grouped(int j, int G) {
+  const int x = j & 7, per = G >> 3, extra = G & 7;
+  return x * per + (x < extra ? x : extra) + (j >> 3);
+}
+
 }  // namespace mla

@@ -236,9 +236,7 @@ prefill_attn_kernel(PrefillArgs a) {
   // each XCD's workgroups consecutively (XCD x takes L = base_x .. base_x + count_x - 1),
   // so the query blocks of a (sequence, head) pair, which read the same K/V pages, share
   // one L2 instead of fetching every page once per XCD.
-  const int G = static_cast<int>(gridDim.x), j = static_cast<int>(blockIdx.x);
-  const int xcd = j & 7, per_xcd = G >> 3, extra = G & 7;
-  const int L = xcd * per_xcd + min(xcd, extra) + (j >> 3);
+  const int L = xcd_grouped(static_cast<int>(blockIdx.x), static_cast<int>(gridDim.x));
   // The n_qb query blocks of a pair take n_qb consecutive logical indices, in an order
   // rotated by 9 per pair.  Causal blocks differ in length (block i reads 2 (i + 1) pages),
   // and the dispatcher deals an XCD's workgroups to its shader engines in turn, holding

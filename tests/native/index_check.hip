@@ -205,6 +205,28 @@ static void check_splits(std::mt19937& g) {
   printf("split_work: %lld key ranges ok\n", n);
 }
 
+// The XCD-grouped logical order: a bijection of [0, G), and each XCD's logical indices
+// form one consecutive range taken in that XCD's dispatch order.
+static void check_xcd(std::mt19937& g) {
+  long long n = 0;
+  for (int k = 0; k < 400; ++k) {
+    const int G = k < 200 ? 1 + k : 1 + static_cast<int>(g() % 100000);
+    std::vector<int> seen(G, -1);
+    std::vector<int> last(8, -1);
+    for (int j = 0; j < G; ++j, ++n) {
+      const int L = mla::xcd_grouped(j, G);
+      CHECK(L >= 0 && L < G, "xcd_grouped range G=%d j=%d -> %d", G, j, L);
+      if (L < 0 || L >= G) continue;
+      CHECK(seen[L] < 0, "xcd_grouped G=%d: logical %d hit twice", G, L);
+      seen[L] = j;
+      const int x = j & 7;
+      CHECK(last[x] < 0 || L == last[x] + 1, "xcd_grouped G=%d: XCD %d not consecutive", G, x);
+      last[x] = L;
+    }
+  }
+  printf("xcd_grouped: %lld indices ok\n", n);
+}
+
 int main() {
   std::mt19937 g(20261203);
   check_lookup(g);
@@ -213,6 +235,7 @@ int main() {
   check_halves(g, false);
   check_halves(g, true);
   check_splits(g);
+  check_xcd(g);
   if (failures) {
     printf("%d failures\n", failures);
     return 1;
